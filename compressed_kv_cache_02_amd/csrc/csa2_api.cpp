@@ -1,0 +1,182 @@
+// C ABI of libcsa2: argument validation, workspace sizing and dispatch to the
+// kernels. Every check happens before anything is enqueued; no exception leaves
+// this file. See include/csa2.h for the contract of each call.
+#include "csa2.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "launchers.hpp"
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+inline size_t round_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+inline bool aligned16(const void* p) { return p && (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+inline bool opt_aligned16(const void* p) { return !p || (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+inline bool sizes_ok(int B, int T, int64_t n_cap) {
+  if (B < 1 || T < 1 || n_cap < 1 || n_cap >= (int64_t(1) << 31)) return false;
+  if ((int64_t)B * T > 65535) return false;   // one grid row per query
+  return true;
+}
+
+inline int status_of(hipError_t e) { return e == hipSuccess ? CSA2_OK : CSA2_EHIP; }
+
+inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+size_t pool_bmax_bytes(int Q, int64_t n_cap) {
+  return round_up((size_t)Q * (size_t)((n_cap + CSA2_BLOCK - 1) / CSA2_BLOCK) * sizeof(float));
+}
+
+}  // namespace
+
+extern "C" {
+
+int csa2_abi_version(void) { return CSA2_ABI_VERSION; }
+
+const char* csa2_status_string(int status) {
+  switch (status) {
+    case CSA2_OK: return "ok";
+    case CSA2_EINVAL: return "invalid argument";
+    case CSA2_EUNSUPPORTED: return "unsupported request";
+    case CSA2_EWORKSPACE: return "workspace too small";
+    case CSA2_EHIP: return "HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+size_t csa2_workspace_bytes(int op, int mode, int B, int T, int64_t n_cap) {
+  if (!sizes_ok(B, T, n_cap)) return 0;
+  const int Q = B * T;
+  switch (op) {
+    case CSA2_OP_INDEX_SCORE: return 0;
+    case CSA2_OP_BUILD_POOL:
+      return pool_bmax_bytes(Q, n_cap) + round_up(csa2::select_workspace_bytes(Q, CSA2_POOL_BLOCKS));
+    case CSA2_OP_TOPK:
+      if (mode == CSA2_REUSE) return 0;
+      if (mode != CSA2_FULL && mode != CSA2_REINDEX) return 0;
+      return round_up(csa2::select_workspace_bytes(Q, CSA2_TOPK));
+    case CSA2_OP_SPARSE_ATTN: return round_up(csa2::attn_workspace_bytes(Q));
+    default: return 0;
+  }
+}
+
+int csa2_rope_table(const int64_t* pos, int64_t n, float* cos_sin) {
+  if (n < 0 || (n > 0 && (!pos || !cos_sin))) return CSA2_EINVAL;
+  double theta[CSA2_ROPE_PAIRS];
+  for (int i = 0; i < CSA2_ROPE_PAIRS; ++i) theta[i] = std::pow(10000.0, -(double)i / 32.0);
+  for (int64_t r = 0; r < n; ++r)
+    if (pos[r] < 0) return CSA2_EINVAL;
+  for (int64_t r = 0; r < n; ++r) {
+    const double p = (double)pos[r];
+    for (int i = 0; i < CSA2_ROPE_PAIRS; ++i) {
+      const double ang = p * theta[i];
+      cos_sin[(r * CSA2_ROPE_PAIRS + i) * 2 + 0] = (float)std::cos(ang);
+      cos_sin[(r * CSA2_ROPE_PAIRS + i) * 2 + 1] = (float)std::sin(ang);
+    }
+  }
+  return CSA2_OK;
+}
+
+int csa2_quantize_kv(const void* kv_bf16, const float* cos_sin, const int64_t* dst_slot, int64_t n,
+                     uint8_t* cache, int64_t cache_rows, void* stream) {
+  if (n < 0 || cache_rows < 1) return CSA2_EINVAL;
+  if (n == 0) return CSA2_OK;
+  if (!aligned16(kv_bf16) || !aligned16(cos_sin) || !aligned16(cache) || !opt_aligned16(dst_slot))
+    return CSA2_EINVAL;
+  if (!dst_slot && n > cache_rows) return CSA2_EINVAL;
+  return status_of(csa2::launch_quantize_kv(static_cast<const uint16_t*>(kv_bf16), cos_sin,
+                                            dst_slot, n, cache, cache_rows, as_stream(stream)));
+}
+
+int csa2_index_score(int mode, const uint8_t* q_idx, const float* w, const uint8_t* k_idx,
+                     const int32_t* n_vis, const int32_t* pool, int B, int T, int64_t n_cap,
+                     float* scores, float* bmax, void* stream) {
+  if (mode != CSA2_FULL && mode != CSA2_REINDEX) return CSA2_EINVAL;
+  if (!sizes_ok(B, T, n_cap)) return CSA2_EINVAL;
+  if (!aligned16(q_idx) || !aligned16(w) || !aligned16(k_idx) || !aligned16(n_vis) ||
+      !aligned16(scores) || !opt_aligned16(bmax))
+    return CSA2_EINVAL;
+  if (mode == CSA2_REINDEX && (!aligned16(pool) || bmax)) return CSA2_EINVAL;
+  hipError_t e;
+  if (mode == CSA2_FULL && T >= 64)
+    e = csa2::launch_index_score_prefill(q_idx, w, k_idx, n_vis, B, T, n_cap, scores, bmax,
+                                         as_stream(stream));
+  else
+    e = csa2::launch_index_score_decode(mode, q_idx, w, k_idx, n_vis, pool, B, T, n_cap, scores,
+                                        bmax, as_stream(stream));
+  return status_of(e);
+}
+
+int csa2_build_pool(const float* src, int is_bmax, const int32_t* n_vis, int B, int T,
+                    int64_t n_cap, int32_t* pool, void* ws, size_t ws_bytes, void* stream) {
+  if (!sizes_ok(B, T, n_cap)) return CSA2_EINVAL;
+  if (!aligned16(src) || !aligned16(n_vis) || !aligned16(pool)) return CSA2_EINVAL;
+  const size_t need = csa2_workspace_bytes(CSA2_OP_BUILD_POOL, 0, B, T, n_cap);
+  if (!aligned16(ws)) return ws ? CSA2_EINVAL : CSA2_EWORKSPACE;
+  if (ws_bytes < need) return CSA2_EWORKSPACE;
+  const int Q = B * T;
+  const int64_t n_blk = (n_cap + CSA2_BLOCK - 1) / CSA2_BLOCK;
+  hipStream_t st = as_stream(stream);
+  const float* bm = src;
+  if (!is_bmax) {
+    float* tmp = static_cast<float*>(ws);
+    hipError_t e = csa2::launch_block_max(src, n_vis, Q, n_cap, tmp, st);
+    if (e != hipSuccess) return CSA2_EHIP;
+    bm = tmp;
+  }
+  void* sel_ws = static_cast<uint8_t*>(ws) + pool_bmax_bytes(Q, n_cap);
+  return status_of(csa2::launch_select(csa2::kSelPool, bm, n_vis, nullptr, Q, n_blk, n_cap,
+                                       CSA2_POOL_BLOCKS, pool, sel_ws, st));
+}
+
+int csa2_topk(int mode, const float* scores, const int32_t* n_vis, const int32_t* pool,
+              const int32_t* src_idx, int B, int T, int64_t n_cap, int32_t* idx, void* ws,
+              size_t ws_bytes, void* stream) {
+  if (!sizes_ok(B, T, n_cap)) return CSA2_EINVAL;
+  if (!aligned16(idx)) return CSA2_EINVAL;
+  const int Q = B * T;
+  hipStream_t st = as_stream(stream);
+  if (mode == CSA2_REUSE) {
+    if (!aligned16(src_idx)) return CSA2_EINVAL;
+    if (src_idx == idx) return CSA2_OK;
+    return status_of(csa2::launch_copy_i32(src_idx, idx, (int64_t)Q * CSA2_TOPK, st));
+  }
+  if (mode != CSA2_FULL && mode != CSA2_REINDEX) return CSA2_EINVAL;
+  if (!aligned16(scores) || !aligned16(n_vis)) return CSA2_EINVAL;
+  if (mode == CSA2_REINDEX && !aligned16(pool)) return CSA2_EINVAL;
+  const size_t need = csa2_workspace_bytes(CSA2_OP_TOPK, mode, B, T, n_cap);
+  if (!aligned16(ws)) return ws ? CSA2_EINVAL : CSA2_EWORKSPACE;
+  if (ws_bytes < need) return CSA2_EWORKSPACE;
+  const int kind = mode == CSA2_FULL ? csa2::kSelFull : csa2::kSelReindex;
+  const int64_t n_items = mode == CSA2_FULL ? n_cap : (int64_t)CSA2_POOL_CAND;
+  return status_of(
+      csa2::launch_select(kind, scores, n_vis, pool, Q, n_items, n_cap, CSA2_TOPK, idx, ws, st));
+}
+
+int csa2_sparse_attn(const void* q_bf16, const uint8_t* cache, const int32_t* idx,
+                     const uint8_t* swa, const int64_t* q_pos, const int64_t* swa_pos0, int B,
+                     int T, int64_t n_cap, int S, float softmax_scale, float* out, void* ws,
+                     size_t ws_bytes, void* stream) {
+  if (!sizes_ok(B, T, n_cap) || S < 1) return CSA2_EINVAL;
+  if (!std::isfinite(softmax_scale)) return CSA2_EINVAL;
+  if (!aligned16(q_bf16) || !aligned16(cache) || !aligned16(idx) || !aligned16(swa) ||
+      !aligned16(q_pos) || !aligned16(swa_pos0) || !aligned16(out))
+    return CSA2_EINVAL;
+  const size_t need = csa2_workspace_bytes(CSA2_OP_SPARSE_ATTN, 0, B, T, n_cap);
+  if (need > 0) {
+    if (!aligned16(ws)) return ws ? CSA2_EINVAL : CSA2_EWORKSPACE;
+    if (ws_bytes < need) return CSA2_EWORKSPACE;
+  }
+  return status_of(csa2::launch_sparse_attn(static_cast<const uint16_t*>(q_bf16), cache, idx, swa,
+                                            q_pos, swa_pos0, B, T, n_cap, S, softmax_scale, out,
+                                            ws, as_stream(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,42 @@
+// Host-side launchers of the CSA2 kernels; called by the C-ABI layer after it
+// has validated every argument. Each returns the hipError_t of its launches.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace csa2 {
+
+hipError_t launch_quantize_kv(const uint16_t* kv, const float* cos_sin, const int64_t* slot,
+                              int64_t n, uint8_t* cache, int64_t cache_rows, hipStream_t st);
+
+// Decode-shaped scan: one query per grid row, positions split over work-groups.
+hipError_t launch_index_score_decode(int mode, const uint8_t* q_idx, const float* w,
+                                     const uint8_t* k_idx, const int32_t* n_vis,
+                                     const int32_t* pool, int B, int T, int64_t n_cap,
+                                     float* scores, float* bmax, hipStream_t st);
+
+// Prefill-shaped scan: a dense FP8 contraction over (queries x 32 heads) x positions.
+hipError_t launch_index_score_prefill(const uint8_t* q_idx, const float* w, const uint8_t* k_idx,
+                                      const int32_t* n_vis, int B, int T, int64_t n_cap,
+                                      float* scores, float* bmax, hipStream_t st);
+
+// Exact Top-K selection.
+enum SelectKind { kSelFull = 0, kSelReindex = 1, kSelPool = 2 };
+size_t select_workspace_bytes(int Q, int K);
+hipError_t launch_select(int kind, const float* values, const int32_t* n_vis, const int32_t* pool,
+                         int Q, int64_t n_items, int64_t n_cap, int K, int32_t* out, void* ws,
+                         hipStream_t st);
+hipError_t launch_block_max(const float* scores, const int32_t* n_vis, int Q, int64_t n_cap,
+                            float* bmax, hipStream_t st);
+hipError_t launch_copy_i32(const int32_t* src, int32_t* dst, int64_t n, hipStream_t st);
+
+// Sparse attention.
+size_t attn_workspace_bytes(int Q);
+hipError_t launch_sparse_attn(const uint16_t* q, const uint8_t* cache, const int32_t* idx,
+                              const uint8_t* swa, const int64_t* q_pos, const int64_t* swa_pos0,
+                              int B, int T, int64_t n_cap, int S, float scale, float* out,
+                              void* ws, hipStream_t st);
+
+}  // namespace csa2

@@ -1,0 +1,119 @@
+"""Layer-group step: the sequence of libcsa2 calls for one decode (or prefill)
+step through a group of CSA2 layers.
+
+Pages: each layer is statically Full, Reindex or Reuse ("DeepSeek V4.1-Flash
+为什么这么强？CED 与 CSA2 架构全拆解", §二 mode table); encoder groups are
+[Full + 5 Reuse] at m = 2 and decoder groups [Full or Reindex + 3 Reuse] at
+m = 1 (same §二, layer layout); the first Full layer builds the candidate pool
+that later Reindex layers score inside (same §二, hierarchical sparse indexer);
+every layer keeps its own main query and window KV ("DeepSeek V4.1 Flash vs V4
+Pro", 黑科技之二).
+
+This module only sequences calls and owns the intermediate device buffers; all
+arithmetic runs in the library's kernels.
+"""
+
+import torch
+
+from . import (CSA2_FULL, CSA2_REINDEX, CSA2_REUSE, CSA2_OP_BUILD_POOL, CSA2_OP_SPARSE_ATTN,
+               CSA2_OP_TOPK, POOL_BLOCKS, POOL_CAND, TOPK, HEADS, DIM, BLOCK,
+               csa2_build_pool, csa2_index_score, csa2_quantize_kv, csa2_sparse_attn,
+               csa2_topk, csa2_workspace_bytes)
+
+FULL, REINDEX, REUSE = "F", "X", "U"
+
+
+def schedule(kind):
+    """(mode, source layer) per layer: 'full' = [F]; 'encoder' = [F, U x5];
+    'decoder' = [F, X, U, X, U, X, U] where each U reuses the X just before it
+    and every X reads the Full layer's keys, main KV and pool."""
+    if kind == "full":
+        return [(FULL, None)]
+    if kind == "encoder":
+        return [(FULL, None)] + [(REUSE, 0)] * 5
+    if kind == "decoder":
+        s = [(FULL, None)]
+        for _ in range(3):
+            s.append((REINDEX, 0))
+            s.append((REUSE, len(s) - 1))
+        return s
+    raise ValueError(kind)
+
+
+def visible_entries(t, m):
+    """Complete compressed entries visible at token t: floor((t + 1) / m)."""
+    return (t + 1) // m
+
+
+class LayerGroup:
+    """Intermediate buffers for one group step of B sequences x T queries."""
+
+    def __init__(self, kind, B, T, n_cap, device="cuda", keep_scores=False):
+        self.sched = schedule(kind)
+        self.B, self.T, self.n_cap = B, T, n_cap
+        dev = torch.device(device)
+        L = len(self.sched)
+        n_blk = (n_cap + BLOCK - 1) // BLOCK
+        need_pool = any(m == REINDEX for m, _ in self.sched)
+        self.scores = torch.empty((B, T, n_cap), dtype=torch.float32, device=dev)
+        self.bmax = torch.empty((B, T, n_blk), dtype=torch.float32, device=dev) if need_pool else None
+        self.pool = torch.empty((B, T, POOL_BLOCKS), dtype=torch.int32, device=dev) if need_pool else None
+        self.scores_pool = (torch.empty((B, T, POOL_CAND), dtype=torch.float32, device=dev)
+                            if need_pool else None)
+        self.idx = [None] * L
+        for li, (m, src) in enumerate(self.sched):
+            # a Reuse layer aliases its source's index buffer (no copy)
+            self.idx[li] = self.idx[src] if m == REUSE else torch.empty(
+                (B, T, TOPK), dtype=torch.int32, device=dev)
+        self.out = [torch.empty((B, T, HEADS, DIM), dtype=torch.float32, device=dev)
+                    for _ in range(L)]
+        ws = max(csa2_workspace_bytes(CSA2_OP_TOPK, CSA2_FULL, B, T, n_cap),
+                 csa2_workspace_bytes(CSA2_OP_TOPK, CSA2_REINDEX, B, T, n_cap),
+                 csa2_workspace_bytes(CSA2_OP_SPARSE_ATTN, 0, B, T, n_cap),
+                 csa2_workspace_bytes(CSA2_OP_BUILD_POOL, 0, B, T, n_cap) if need_pool else 0)
+        self.ws = torch.empty((max(ws, 256),), dtype=torch.uint8, device=dev)
+        self.keep_scores = keep_scores
+        self.saved_scores = {}
+
+    def step(self, k_idx, cache, n_vis, q_pos, swa_pos0, q_idx, w, q, swa, scale=1.0,
+             write=None, stream=None, hooks=None):
+        """One pass of the whole group.
+
+        k_idx [B,n_cap,128], cache [B,n_cap,288]: the group's shared keys and
+        packed main KV; n_vis [B,T] int32; q_pos [B,T] int64; swa_pos0 [B] int64;
+        q_idx / w: per index-producing layer (dict or list indexed by layer);
+        q / swa: per layer. write = (kv_bf16 [n,512], cos_sin [n,32,2],
+        dst_slot [n]) runs the write path first. hooks: optional dict of
+        callables ('scan_begin', 'scan_end') run around the Full-layer scan."""
+        hooks = hooks or {}
+        if write is not None:
+            kv, cs, slot = write
+            csa2_quantize_kv(kv, cs, slot, cache, stream=stream)
+        for li, (mode, src) in enumerate(self.sched):
+            if mode == FULL:
+                if "scan_begin" in hooks:
+                    hooks["scan_begin"]()
+                csa2_index_score(CSA2_FULL, q_idx[li], w[li], k_idx, n_vis, None, self.scores,
+                                 self.bmax, stream=stream)
+                if "scan_end" in hooks:
+                    hooks["scan_end"]()
+                if self.pool is not None:
+                    csa2_build_pool(self.bmax, True, n_vis, self.n_cap, self.pool, self.ws,
+                                    stream=stream)
+                csa2_topk(CSA2_FULL, self.scores, n_vis, None, None, self.n_cap, self.idx[li],
+                          self.ws, stream=stream)
+                if self.keep_scores:
+                    self.saved_scores[li] = self.scores.clone()
+            elif mode == REINDEX:
+                csa2_index_score(CSA2_REINDEX, q_idx[li], w[li], k_idx, n_vis, self.pool,
+                                 self.scores_pool, None, stream=stream)
+                csa2_topk(CSA2_REINDEX, self.scores_pool, n_vis, self.pool, None, self.n_cap,
+                          self.idx[li], self.ws, stream=stream)
+                if self.keep_scores:
+                    self.saved_scores[li] = self.scores_pool.clone()
+            else:
+                csa2_topk(CSA2_REUSE, None, None, None, self.idx[src], self.n_cap, self.idx[li],
+                          None, stream=stream)
+            csa2_sparse_attn(q[li], cache, self.idx[li], swa[li], q_pos, swa_pos0, scale,
+                             self.out[li], self.ws, stream=stream)
+        return self.out

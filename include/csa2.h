@@ -1,0 +1,187 @@
+/*
+ * csa2.h -- C ABI of libcsa2, the per-layer hot path of CSA2 (Compressed Sparse
+ * Attention 2) on AMD Instinct MI355X (gfx950).
+ *
+ * Pages the operations come from (cited below by tag):
+ *   [P1] "DeepSeek V4.1-Flash 为什么这么强？CED 与 CSA2 架构全拆解" (deepseek.csdn.net)
+ *   [P2] "DeepSeek V4.1 Flash vs V4 Pro" (my-blog-5oz.pages.dev)
+ *   [P3] "DeepSeek-V4.1-Flash：全局 KV 仅 890 B/token，百万上下文怎么做成的？"
+ *        (landx.limxdynamics.com)
+ *   [P4] "DeepSeek-V4.1-Flash KV cache compression architecture analysis" (www.ic.work)
+ *
+ * Conventions shared by every call:
+ *   - "device" pointers are HIP device (or managed) memory; "host" pointers are
+ *     ordinary host memory. Every device pointer must be 16-byte aligned.
+ *     Tensors are contiguous and row-major in the order written.
+ *   - The caller owns every buffer, the workspace and the stream. The library
+ *     never allocates or frees memory, never synchronises, never copies between
+ *     host and device, and keeps no state between calls; every device call only
+ *     enqueues kernels on `stream` (a hipStream_t passed as void*; NULL = the
+ *     default stream), so it can be captured into a HIP graph.
+ *   - Arguments are validated on the host before anything is enqueued; a bad
+ *     argument returns CSA2_EINVAL (or CSA2_EUNSUPPORTED / CSA2_EWORKSPACE) and
+ *     launches nothing. CSA2_EHIP reports a launch failure. Device-side faults
+ *     surface at the caller's next synchronisation. No C++ exception crosses
+ *     this boundary.
+ *   - Values inside device buffers cannot be checked on the host. Where a
+ *     device value is out of range (an index, a slot, a position) the kernels
+ *     skip it rather than touch memory outside the buffer, as stated per call.
+ *
+ * Fixed shapes (from [P1] §二 layer layout and hierarchical indexer):
+ *   indexer: 32 query heads x 128 (E4M3), one 128-wide key per position;
+ *   main attention: 64 heads x 512 over one shared 512-wide latent per position;
+ *   Top-512 per query; pool = 2,048 blocks x 8 positions = 16,384 candidates;
+ *   sliding window of 128 tokens ([P1] §一, [P2] 黑科技之一).
+ */
+#ifndef CSA2_H
+#define CSA2_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define CSA2_ABI_VERSION 1
+
+#define CSA2_IDX_HEADS 32
+#define CSA2_IDX_DIM 128
+#define CSA2_HEADS 64
+#define CSA2_DIM 512
+#define CSA2_ROW_BYTES 288      /* 256 bytes of E2M1 codes + 32 E4M3 scales */
+#define CSA2_TOPK 512
+#define CSA2_POOL_BLOCKS 2048
+#define CSA2_BLOCK 8
+#define CSA2_POOL_CAND 16384
+#define CSA2_WINDOW 128
+#define CSA2_ROPE_PAIRS 32      /* RoPE on channels 448..511, adjacent pairs */
+
+/* Layer mode ([P1] §二 mode table; [P2] 黑科技之二; [P3] 第二刀, Fig. 4):
+ *   FULL    -- own indexer keys, own scores over every visible position, own Top-K;
+ *   REINDEX -- an earlier layer's keys, own indexer query, scores only inside the
+ *              candidate pool, own Top-K;
+ *   REUSE   -- an earlier layer's Top-K indices, unchanged. */
+typedef enum { CSA2_FULL = 0, CSA2_REINDEX = 1, CSA2_REUSE = 2 } csa2_mode;
+
+enum {
+  CSA2_OK = 0,
+  CSA2_EINVAL = -1,        /* null/misaligned pointer, bad size, bad mode combination */
+  CSA2_EUNSUPPORTED = -2,  /* valid request this build does not implement */
+  CSA2_EWORKSPACE = -3,    /* workspace smaller than csa2_workspace_bytes() */
+  CSA2_EHIP = -4           /* a HIP launch failed */
+};
+
+/* Operation ids for csa2_workspace_bytes(). */
+enum { CSA2_OP_INDEX_SCORE = 0, CSA2_OP_BUILD_POOL = 1, CSA2_OP_TOPK = 2, CSA2_OP_SPARSE_ATTN = 3 };
+
+/* Version of this ABI (CSA2_ABI_VERSION). */
+int csa2_abi_version(void);
+
+/* Static, human-readable text for a status code. Never NULL. */
+const char* csa2_status_string(int status);
+
+/* Workspace (device bytes) an operation needs for the given sizes; 0 if none.
+ * `mode` matters for CSA2_OP_TOPK only. Returns 0 for invalid sizes. */
+size_t csa2_workspace_bytes(int op, int mode, int B, int T, int64_t n_cap);
+
+/* HOST. RoPE table for the main-KV write path (the main KV is quantised after
+ * RoPE: [P1] §三, [P3] 第三刀). For each of `n` positions pos[r] (host) and pair
+ * i = 0..31 writes cos_sin[r][i][0] = (float)cos(pos[r] * theta_i) and
+ * cos_sin[r][i][1] = (float)sin(pos[r] * theta_i), theta_i = 10000^(-i/32),
+ * evaluated in double and rounded once (host buffer of n*64 floats).
+ * Errors: CSA2_EINVAL if a pointer is NULL, n < 0 or a position is negative. */
+int csa2_rope_table(const int64_t* pos, int64_t n, float* cos_sin);
+
+/* DEVICE. Write path: RoPE, then FP4 packing, then the store ([P1] §三; [P2]
+ * 黑科技之三; [P3] 第三刀).
+ *   kv_bf16   [n][512] bf16 latent rows (device);
+ *   cos_sin   [n][32][2] float table for each row's position (device; see
+ *             csa2_rope_table);
+ *   dst_slot  [n] int64 destination row in `cache` (device), or NULL to store
+ *             row r at row r; slots outside [0, cache_rows) are skipped;
+ *   cache     [cache_rows][288] packed rows (device, written).
+ * Per row: channels 448 + 2i and 449 + 2i are rotated in float32 with each
+ * product and sum rounded separately; then per 16-channel group g the scale is
+ * the E4M3 value nearest amax/6 (ties to even, saturating at 448) stored at byte
+ * 256 + g, and each element is the E2M1 code nearest |y|/scale (ties to even,
+ * saturating at 6; sign bit = sign of y; a zero scale gives magnitude 0), two
+ * codes per byte with the even channel in the low nibble. Inputs must be finite.
+ * Errors: CSA2_EINVAL for NULL/misaligned pointers, n < 0, cache_rows < 1. */
+int csa2_quantize_kv(const void* kv_bf16, const float* cos_sin, const int64_t* dst_slot,
+                     int64_t n, uint8_t* cache, int64_t cache_rows, void* stream);
+
+/* DEVICE. Sparse-indexer scores ([P1] §二 layer layout and hierarchical sparse
+ * indexer; [P3] 第二刀, Fig. 5). For query (b,t) and position n:
+ *   score = sum_{h<32} w[b][t][h] * max(0, sum_{c<128} q_idx[b][t][h][c] * k_idx[b][n][c]).
+ *   mode FULL:    scores[b][t][n] for every n < n_cap; n >= n_vis[b][t] gets -inf.
+ *                 If `bmax` is not NULL, bmax[b][t][j] = max of scores over
+ *                 positions 8j..8j+7 (visible ones; -inf if none), j < ceil(n_cap/8).
+ *   mode REINDEX: scores[b][t][i] for i < 16384 at position 8*pool[b][t][i/8] + i%8;
+ *                 -inf where the pool entry is -1 or the position is >= n_vis.
+ *                 `bmax` must be NULL.
+ *   q_idx [B][T][32][128] E4M3, w [B][T][32] float, k_idx [B][n_cap][128] E4M3,
+ *   n_vis [B][T] int32 (device; values are clamped to [0, n_cap]),
+ *   pool  [B][T][2048] int32 (device, REINDEX only; entries >= ceil(n_cap/8) are
+ *         treated as -1).
+ * Products are exact; sums are float32 (MFMA accumulation order).
+ * Errors: CSA2_EINVAL for REUSE, NULL/misaligned pointers, REINDEX without a
+ * pool, B < 1, T < 1, n_cap < 1 or n_cap >= 2^31. */
+int csa2_index_score(int mode, const uint8_t* q_idx, const float* w, const uint8_t* k_idx,
+                     const int32_t* n_vis, const int32_t* pool, int B, int T, int64_t n_cap,
+                     float* scores, float* bmax, void* stream);
+
+/* DEVICE. Hierarchical candidate pool ([P1] §二 hierarchical sparse indexer;
+ * [P3] 第二刀, Fig. 5): per query, among blocks j < ceil(n_vis/8), the 2,048
+ * with the largest block max (ties to the lower block id), written as block ids
+ * in ascending order and padded with -1.
+ *   src    [B][T][ceil(n_cap/8)] block maxima when is_bmax != 0 (as written by
+ *          csa2_index_score), else [B][T][n_cap] FULL scores (device);
+ *   pool   [B][T][2048] int32 (device, written);
+ *   ws     device workspace of at least csa2_workspace_bytes(CSA2_OP_BUILD_POOL, ...).
+ * Errors: CSA2_EINVAL (pointers, sizes), CSA2_EWORKSPACE. */
+int csa2_build_pool(const float* src, int is_bmax, const int32_t* n_vis, int B, int T,
+                    int64_t n_cap, int32_t* pool, void* ws, size_t ws_bytes, void* stream);
+
+/* DEVICE. Top-512 per query ([P1] §二 mode table and layer layout; [P2] 黑科技之二).
+ *   FULL:    the 512 highest of scores[b][t][0 .. n_vis) ([B][T][n_cap]);
+ *   REINDEX: the 512 highest of the pool candidates scores[b][t][i], i < 16384
+ *            ([B][T][16384], from csa2_index_score REINDEX with the same pool);
+ *   REUSE:   idx = src_idx byte for byte (a device copy; nothing when idx == src_idx).
+ * Ranking is by (score descending, position ascending); the selected positions
+ * are written to idx [B][T][512] int32 in ascending order, padded with -1 when
+ * fewer than 512 candidates exist. Scores must not be NaN. FULL/REINDEX need a
+ * workspace of csa2_workspace_bytes(CSA2_OP_TOPK, mode, ...) bytes.
+ * Errors: CSA2_EINVAL (pointers, sizes, REINDEX without pool, REUSE without
+ * src_idx), CSA2_EWORKSPACE. */
+int csa2_topk(int mode, const float* scores, const int32_t* n_vis, const int32_t* pool,
+              const int32_t* src_idx, int B, int T, int64_t n_cap, int32_t* idx, void* ws,
+              size_t ws_bytes, void* stream);
+
+/* DEVICE. Sparse MQA attention over the selected FP4 main-KV rows plus the
+ * 128-token FP8 window ([P1] §二 layer layout, §三; [P3] 第三刀: dequantise
+ * before attention, window KV stays FP8; [P2] 黑科技之二: every layer has its
+ * own query and window KV).
+ *   q        [B][T][64][512] bf16 (device);
+ *   cache    [B][n_cap][288] packed rows (device); key = value = the dequantised row;
+ *   idx      [B][T][512] int32 selected positions (device); -1 and values outside
+ *            [0, n_cap) are skipped;
+ *   swa      [B][S][512] E4M3 window rows (device), row s of sequence b holds
+ *            token swa_pos0[b] + s;
+ *   q_pos    [B][T] int64 token position t of each query (device);
+ *   swa_pos0 [B] int64 (device).
+ * Keys = the selected rows and the window tokens max(0, t-127) .. t (tokens
+ * outside [swa_pos0, swa_pos0 + S) are skipped); one softmax over all of them of
+ * scale * q_h . key; out[b][t][h] = sum_j p_hj key_j, float32 [B][T][64][512].
+ * Needs csa2_workspace_bytes(CSA2_OP_SPARSE_ATTN, 0, B, T, n_cap) bytes of workspace.
+ * Errors: CSA2_EINVAL (pointers, sizes, S < 1), CSA2_EWORKSPACE. */
+int csa2_sparse_attn(const void* q_bf16, const uint8_t* cache, const int32_t* idx,
+                     const uint8_t* swa, const int64_t* q_pos, const int64_t* swa_pos0, int B,
+                     int T, int64_t n_cap, int S, float softmax_scale, float* out, void* ws,
+                     size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CSA2_H */

@@ -48,7 +48,7 @@ def gather_keys(cache_rows, idx, swa_codes, t, swa_pos0):
     order, then the window rows in token order."""
     idx = np.asarray(idx, dtype=np.int64)
     sel = idx[idx >= 0]
-    main = dequantize_rows(np.asarray(cache_rows)[sel])
+    main = dequantize_rows(np.asarray(cache_rows[sel]))
     toks = swa_tokens(t)
     swa = e4m3_decode(np.asarray(swa_codes)[toks - int(swa_pos0)])
     return np.concatenate([main, swa], axis=0)

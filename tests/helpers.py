@@ -1,0 +1,109 @@
+"""Shared test helpers: acceptance rules and host copies of device inputs.
+
+The acceptance rules follow the tolerances stated for this path:
+  * FP4 packing, the pool and Top-K on identical float32 scores: bit-exact;
+  * scores: |gpu - oracle| <= 160 * 2^-24 * sum_h w_h sum_c |q_hc k_c|
+    (Higham's gamma_n for the 128 + 32 float32 additions);
+  * Top-K end to end: the sets agree except for positions whose oracle score is
+    within 1e-5 (relative) of the oracle's K-th score;
+  * attention: max-abs <= 2e-3 and relative L2 <= 1e-3 against float64.
+"""
+
+import numpy as np
+import torch
+
+from oracle import formats as OF
+from oracle import rope as OR
+
+SCORE_GAMMA = 160.0 * 2.0 ** -24
+ATTN_MAX_ABS = 2e-3
+ATTN_REL_L2 = 1e-3
+NEAR_TIE = 1e-5
+
+
+def has_gpu():
+    return torch.cuda.is_available()
+
+
+def to_np(t):
+    return t.detach().cpu().numpy()
+
+
+def bf16_to_np_f32(t):
+    return t.detach().cpu().float().numpy()
+
+
+def score_bound(q_codes, w, k_codes):
+    """Per-position absolute error bound of a float32 evaluation of the score."""
+    q = np.abs(OF.e4m3_decode(q_codes.reshape(32, 128)))
+    k = np.abs(OF.e4m3_decode(k_codes))
+    return SCORE_GAMMA * (k @ q.T) @ np.abs(np.asarray(w, dtype=np.float64).reshape(32))
+
+
+def assert_scores_close(gpu, ref, bound, what=""):
+    gpu = np.asarray(gpu, dtype=np.float32)
+    ref = np.asarray(ref, dtype=np.float32)
+    ninf_g, ninf_r = np.isneginf(gpu), np.isneginf(ref)
+    assert np.array_equal(ninf_g, ninf_r), "%s: -inf pattern differs" % what
+    fin = ~ninf_r
+    err = np.abs(gpu[fin].astype(np.float64) - ref[fin].astype(np.float64))
+    assert np.all(err <= bound[fin] + 1e-30), "%s: max err %g > bound" % (what, float((err - bound[fin]).max()))
+
+
+def kth_value(scores, k):
+    """The k-th largest value (1-based) of a float32 array."""
+    s = np.sort(np.asarray(scores, dtype=np.float32))[::-1]
+    return float(s[min(k, s.shape[0]) - 1])
+
+
+def assert_topk_near(gpu_idx, ref_idx, score_of_pos, k=512, extra_allowed=None, what=""):
+    """Sets equal except near-ties of the K-th oracle score.
+
+    score_of_pos: dict/callable position -> oracle float32 score."""
+    g = set(int(x) for x in gpu_idx if x >= 0)
+    o = set(int(x) for x in ref_idx if x >= 0)
+    assert len(g) == len(o), "%s: %d vs %d selected" % (what, len(g), len(o))
+    assert list(gpu_idx) == sorted(gpu_idx[gpu_idx >= 0].tolist()) + [-1] * int((gpu_idx < 0).sum())
+    diff = g ^ o
+    if not diff:
+        return 0
+    kth = min(float(score_of_pos(p)) for p in o)
+    for p in diff:
+        if extra_allowed is not None and extra_allowed(p):
+            continue
+        s = float(score_of_pos(p))
+        assert abs(s - kth) <= NEAR_TIE * abs(kth), "%s: position %d score %r vs K-th %r" % (what, p, s, kth)
+    return len(diff)
+
+
+def assert_attn_close(gpu, ref, what=""):
+    gpu = np.asarray(gpu, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    err = np.abs(gpu - ref)
+    rel = np.linalg.norm(gpu - ref) / max(np.linalg.norm(ref), 1e-30)
+    assert np.all(np.isfinite(gpu)), what + ": non-finite output"
+    assert err.max() <= ATTN_MAX_ABS, "%s: max-abs %g" % (what, err.max())
+    assert rel <= ATTN_REL_L2, "%s: rel-L2 %g" % (what, rel)
+    return float(err.max()), float(rel)
+
+
+class OracleCache:
+    """Oracle-side packed main-KV rows of one sequence, quantised lazily by the
+    oracle from the bf16 source rows (RoPE at position j * m, then FP4)."""
+
+    def __init__(self, main_bf16_rows, m):
+        self.src = main_bf16_rows          # torch bf16 [n_cap, 512] (device or host)
+        self.m = m
+        self.cache = {}
+
+    def __getitem__(self, sel):
+        sel = np.asarray(sel, dtype=np.int64).reshape(-1)
+        need = [int(j) for j in sel if int(j) not in self.cache]
+        if need:
+            need = sorted(set(need))
+            x = self.src[torch.tensor(need, device=self.src.device)].float().cpu().numpy()
+            y = OR.apply_rope(x, [j * self.m for j in need])
+            rows = OF.quantize_rows(y)
+            for j, r in zip(need, rows):
+                self.cache[j] = r
+        return np.stack([self.cache[int(j)] for j in sel]) if sel.size else np.zeros((0, 288), np.uint8)

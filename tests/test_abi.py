@@ -1,0 +1,125 @@
+"""The C ABI without a GPU: the library loads, exports every function
+include/csa2.h declares, the host RoPE table matches the oracle bit for bit, and
+every argument error is rejected before anything is launched.
+
+Calls here that pass placeholder pointers are all ones the library must reject
+during host-side validation; none of them can reach a kernel launch."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import compressed_kv_cache_02_amd as C
+from oracle import rope as OR
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "csa2.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(C.lib_path()),
+                                reason="libcsa2.so not built")
+
+FAKE = 0x10000          # aligned placeholder, only used where validation must fail
+FAKE_MIS = 0x10004      # misaligned placeholder
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(csa2_[a-z_]+)\s*\(", text)))
+
+
+def test_header_functions_are_exported():
+    names = declared_functions()
+    assert len(names) == 9, names
+    L = C.lib()
+    for n in names:
+        assert hasattr(L, n), n
+    assert C.csa2_abi_version() == 1
+
+
+def test_status_strings():
+    for s in (0, -1, -2, -3, -4, 7):
+        assert isinstance(C.csa2_status_string(s), str)
+
+
+def test_rope_table_matches_oracle_bit_for_bit():
+    pos = np.array([0, 1, 2, 3, 1000, 131070, 524287 * 2, 1048575], dtype=np.int64)
+    t = C.csa2_rope_table(pos)
+    c, s = OR.rope_cos_sin(pos)
+    assert np.array_equal(t[:, :, 0], c) and np.array_equal(t[:, :, 1], s)
+    with pytest.raises(C.Csa2Error):
+        C.csa2_rope_table(np.array([-1], dtype=np.int64))
+
+
+def test_workspace_sizes():
+    ws = C.csa2_workspace_bytes
+    assert ws(C.CSA2_OP_INDEX_SCORE, 0, 8, 1, 1 << 20) == 0
+    assert ws(C.CSA2_OP_TOPK, C.CSA2_REUSE, 8, 1, 1 << 20) == 0
+    assert ws(C.CSA2_OP_TOPK, C.CSA2_FULL, 8, 1, 1 << 20) > 0
+    assert ws(C.CSA2_OP_BUILD_POOL, 0, 8, 1, 1 << 20) > 0
+    assert ws(C.CSA2_OP_TOPK, C.CSA2_FULL, 0, 1, 100) == 0         # invalid sizes
+    assert ws(C.CSA2_OP_TOPK, C.CSA2_FULL, 1, 1, 1 << 31) == 0
+    for op in range(4):
+        assert ws(op, 0, 3, 5, 1000) % 256 == 0
+
+
+def _p(x):
+    return ctypes.c_void_p(x) if x else None
+
+
+def test_index_score_rejects_bad_arguments():
+    f = C.lib().csa2_index_score
+    ok = dict(q=FAKE, w=FAKE, k=FAKE, nv=FAKE, pool=FAKE, s=FAKE, bm=None)
+
+    def call(mode=0, B=1, T=1, n_cap=100, **kw):
+        a = dict(ok)
+        a.update(kw)
+        return f(mode, _p(a["q"]), _p(a["w"]), _p(a["k"]), _p(a["nv"]), _p(a["pool"]), B, T,
+                 n_cap, _p(a["s"]), _p(a["bm"]), None)
+
+    assert call(mode=2) == C.CSA2_EINVAL                       # REUSE is not a scoring mode
+    assert call(mode=7) == C.CSA2_EINVAL
+    assert call(q=0) == C.CSA2_EINVAL
+    assert call(k=FAKE_MIS) == C.CSA2_EINVAL
+    assert call(mode=1, pool=0) == C.CSA2_EINVAL                # REINDEX needs a pool
+    assert call(mode=1, bm=FAKE) == C.CSA2_EINVAL               # no block max in REINDEX
+    assert call(B=0) == C.CSA2_EINVAL
+    assert call(T=0) == C.CSA2_EINVAL
+    assert call(n_cap=0) == C.CSA2_EINVAL
+    assert call(n_cap=1 << 31) == C.CSA2_EINVAL
+    assert call(B=300, T=300) == C.CSA2_EINVAL                  # too many queries
+
+
+def test_topk_and_pool_reject_bad_arguments():
+    f = C.lib().csa2_topk
+    assert f(0, _p(FAKE), _p(FAKE), None, None, 1, 1, 100, _p(FAKE), None, 0, None) == C.CSA2_EWORKSPACE
+    assert f(0, _p(FAKE), _p(FAKE), None, None, 1, 1, 100, _p(FAKE), _p(FAKE), 16, None) == C.CSA2_EWORKSPACE
+    assert f(1, _p(FAKE), _p(FAKE), None, None, 1, 1, 100, _p(FAKE), _p(FAKE), 1 << 30, None) == C.CSA2_EINVAL
+    assert f(2, None, None, None, None, 1, 1, 100, _p(FAKE), None, 0, None) == C.CSA2_EINVAL
+    assert f(5, _p(FAKE), _p(FAKE), None, None, 1, 1, 100, _p(FAKE), _p(FAKE), 1 << 30, None) == C.CSA2_EINVAL
+    assert f(0, _p(FAKE), _p(FAKE), None, None, 1, 1, 100, _p(FAKE_MIS), _p(FAKE), 1 << 30, None) == C.CSA2_EINVAL
+    g = C.lib().csa2_build_pool
+    assert g(_p(FAKE), 1, _p(FAKE), 1, 1, 100, _p(FAKE), None, 0, None) == C.CSA2_EWORKSPACE
+    assert g(_p(FAKE), 1, _p(FAKE), 1, 1, 100, _p(FAKE), _p(FAKE), 8, None) == C.CSA2_EWORKSPACE
+    assert g(None, 1, _p(FAKE), 1, 1, 100, _p(FAKE), _p(FAKE), 1 << 30, None) == C.CSA2_EINVAL
+    assert g(_p(FAKE), 1, _p(FAKE), 1, 0, 100, _p(FAKE), _p(FAKE), 1 << 30, None) == C.CSA2_EINVAL
+
+
+def test_attn_and_quantize_reject_bad_arguments():
+    f = C.lib().csa2_sparse_attn
+    args = [_p(FAKE)] * 6
+    assert f(*args, 1, 1, 100, 0, ctypes.c_float(1.0), _p(FAKE), _p(FAKE), 1 << 30, None) == C.CSA2_EINVAL
+    assert f(*args, 1, 1, 100, 128, ctypes.c_float(float("nan")), _p(FAKE), _p(FAKE), 1 << 30, None) == C.CSA2_EINVAL
+    bad = list(args)
+    bad[2] = None
+    assert f(*bad, 1, 1, 100, 128, ctypes.c_float(1.0), _p(FAKE), _p(FAKE), 1 << 30, None) == C.CSA2_EINVAL
+    assert f(*args, 100, 1, 100, 128, ctypes.c_float(1.0), _p(FAKE), None, 0, None) == C.CSA2_EWORKSPACE
+    q = C.lib().csa2_quantize_kv
+    assert q(_p(FAKE), _p(FAKE), None, -1, _p(FAKE), 10, None) == C.CSA2_EINVAL
+    assert q(_p(FAKE), _p(FAKE), None, 11, _p(FAKE), 10, None) == C.CSA2_EINVAL   # rows beyond the cache
+    assert q(None, _p(FAKE), None, 4, _p(FAKE), 10, None) == C.CSA2_EINVAL
+    assert q(_p(FAKE), _p(FAKE), _p(FAKE_MIS), 4, _p(FAKE), 10, None) == C.CSA2_EINVAL
+    assert q(_p(FAKE), _p(FAKE), None, 0, _p(FAKE), 10, None) == C.CSA2_OK           # nothing to do

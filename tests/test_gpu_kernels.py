@@ -1,0 +1,315 @@
+"""GPU parity of each libcsa2 kernel against the oracle, through the C ABI.
+
+Sizes span several tiles and work-groups with ragged tails; inputs are seeded.
+Every oracle input comes from the seeded generators (or the oracle itself),
+never from the HIP path."""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import compressed_kv_cache_02_amd as C
+from oracle import formats as OF
+from oracle import indexer as OI
+from oracle import rope as OR
+from oracle import select as OS
+from oracle import attention as OA
+import synth
+from tests.helpers import (OracleCache, assert_attn_close, assert_scores_close, score_bound,
+                           to_np)
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _stage(*names):
+    print("[gpu-test]", *names, flush=True)
+
+
+def _cs(positions):
+    return torch.from_numpy(C.csa2_rope_table(np.asarray(positions, dtype=np.int64))).to(DEV)
+
+
+# ------------------------------------------------------------ write path -----
+
+def _special_rows():
+    rows = np.zeros((12, 512), dtype=np.float32)
+    rows[1, :] = -0.0
+    rows[2, :16] = 6 * 2.0 ** -10            # scale tie -> zero scale
+    rows[3, :] = 1e4                          # saturating scale
+    rows[3, ::3] = -3e4
+    rows[4, :] = np.tile(np.array([6, -3, .5, 1.5, 0, -0., 2, 4, 1, -6, 3, .25, .75, 5, -5, 1.25], np.float32), 32)
+    rng = np.random.default_rng(7)
+    for r in range(5, 12):                    # grid values x random E4M3 scales: exact ties
+        for g in range(32):
+            s = OF.e4m3_value_of_code(int(rng.integers(1, 127)))
+            v = rng.choice([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 6.0, 0.5, 3.0], 16) * rng.choice([-1, 1], 16)
+            v[0] = 6.0
+            rows[r, g * 16:(g + 1) * 16] = v * s
+    # bf16-representable inputs only (the write path reads bf16)
+    return torch.from_numpy(rows).to(torch.bfloat16)
+
+
+@pytest.mark.parametrize("n,outliers", [(4099, False), (2048, True)])
+def test_quantize_kv_bitexact(n, outliers):
+    _stage("quantize_kv", n, outliers)
+    x = synth.token_rows_bf16(n, DEV, 0, "t_quant", n, outliers=outliers)
+    x[:12] = _special_rows().to(DEV)
+    rng = np.random.default_rng(n)
+    pos = rng.integers(0, 1 << 21, n).astype(np.int64)
+    pos[:12] = 0
+    pos[12] = 1048574
+    slots = torch.from_numpy(rng.permutation(n + 5)[:n].astype(np.int64)).to(DEV)
+    cache = torch.full((n + 5, 288), 0xAB, dtype=torch.uint8, device=DEV)
+    C.csa2_quantize_kv(x, _cs(pos), slots, cache)
+    torch.cuda.synchronize()
+    got = to_np(cache)[to_np(slots)]
+    want = OF.quantize_rows(OR.apply_rope(x.float().cpu().numpy(), pos))
+    bad = np.nonzero(np.any(got != want, axis=1))[0]
+    assert bad.size == 0, "rows differ: %s" % bad[:10]
+    untouched = np.setdiff1d(np.arange(n + 5), to_np(slots))
+    assert np.all(to_np(cache)[untouched] == 0xAB)
+
+
+def test_quantize_kv_contiguous_and_skipped_slots():
+    _stage("quantize_kv slots")
+    n = 300
+    x = synth.token_rows_bf16(n, DEV, 1, "t_quant2")
+    pos = np.arange(n, dtype=np.int64) * 2
+    cache = torch.zeros((n, 288), dtype=torch.uint8, device=DEV)
+    C.csa2_quantize_kv(x, _cs(pos), None, cache)
+    want = OF.quantize_rows(OR.apply_rope(x.float().cpu().numpy(), pos))
+    assert np.array_equal(to_np(cache), want)
+    slots = torch.tensor([-1, n, 5] + [10 ** 9] * (n - 3), dtype=torch.int64, device=DEV)
+    cache2 = cache.clone()
+    C.csa2_quantize_kv(x.flip(0).contiguous(), _cs(pos[::-1].copy()), slots, cache2)
+    torch.cuda.synchronize()
+    ref = to_np(cache).copy()
+    ref[5] = want[n - 1 - 2]
+    assert np.array_equal(to_np(cache2), ref)
+
+
+# --------------------------------------------------------------- scoring -----
+
+def _idx_inputs(B, T, n_cap, seed, outliers=False):
+    q = synth.e4m3_rows(B * T * 32, 128, DEV, seed, "q", outliers=outliers).view(B, T, 32, 128)
+    w = synth.head_weights(B * T, DEV, seed, "w").view(B, T, 32)
+    k = synth.e4m3_rows(B * n_cap, 128, DEV, seed, "k", outliers=outliers).view(B, n_cap, 128)
+    return q, w, k
+
+
+@pytest.mark.parametrize("B,T,n_cap", [(2, 3, 5003), (1, 1, 31), (3, 2, 40000)])
+def test_index_score_full(B, T, n_cap):
+    _stage("index_score full", B, T, n_cap)
+    q, w, k = _idx_inputs(B, T, n_cap, n_cap, outliers=(n_cap == 40000))
+    rng = np.random.default_rng(n_cap)
+    nv = rng.integers(0, n_cap + 1, (B, T)).astype(np.int32)
+    nv.flat[0] = n_cap
+    if nv.size > 2:
+        nv.flat[1] = 0
+        nv.flat[2] = min(n_cap, 33)
+    n_vis = torch.from_numpy(nv).to(DEV)
+    scores = torch.empty((B, T, n_cap), dtype=torch.float32, device=DEV)
+    nb = (n_cap + 7) // 8
+    bmax = torch.empty((B, T, nb), dtype=torch.float32, device=DEV)
+    C.csa2_index_score(C.CSA2_FULL, q, w, k, n_vis, None, scores, bmax)
+    torch.cuda.synchronize()
+    qn, wn, kn, sn, bn = to_np(q), to_np(w), to_np(k), to_np(scores), to_np(bmax)
+    for b in range(B):
+        for t in range(T):
+            ref = OI.index_scores(qn[b, t], wn[b, t], kn[b], nv[b, t])
+            assert_scores_close(sn[b, t], ref, score_bound(qn[b, t], wn[b, t], kn[b]),
+                                "b%d t%d" % (b, t))
+            assert np.array_equal(bn[b, t], OI.block_max(sn[b, t], nv[b, t]))
+
+
+def test_index_score_reindex():
+    _stage("index_score reindex")
+    B, T, n_cap = 2, 2, 30000
+    q, w, k = _idx_inputs(B, T, n_cap, 11)
+    rng = np.random.default_rng(11)
+    nb = (n_cap + 7) // 8
+    pool = np.full((B, T, 2048), -1, dtype=np.int32)
+    nv = np.array([[n_cap, 20001], [17, 29999]], dtype=np.int32)
+    for b in range(B):
+        for t in range(T):
+            cnt = 2048 if (b, t) != (1, 0) else 3
+            pool[b, t, :cnt] = np.sort(rng.choice(nb, cnt, replace=False))
+    scores = torch.empty((B, T, 16384), dtype=torch.float32, device=DEV)
+    C.csa2_index_score(C.CSA2_REINDEX, q, w, k, torch.from_numpy(nv).to(DEV),
+                       torch.from_numpy(pool).to(DEV), scores, None)
+    torch.cuda.synchronize()
+    qn, wn, kn, sn = to_np(q), to_np(w), to_np(k), to_np(scores)
+    for b in range(B):
+        for t in range(T):
+            p = pool[b, t]
+            pos = (np.maximum(p, 0)[:, None] * 8 + np.arange(8)[None, :]).reshape(-1)
+            ref = OI.index_scores(qn[b, t], wn[b, t], kn[b], nv[b, t], positions=pos)
+            ref[np.repeat(p < 0, 8)] = -np.inf
+            bound = score_bound(qn[b, t], wn[b, t], kn[b][np.minimum(pos, n_cap - 1)])
+            assert_scores_close(sn[b, t], ref, bound, "reindex b%d t%d" % (b, t))
+
+
+# -------------------------------------------------------------- selection -----
+
+def _score_sets(n, seed):
+    rng = np.random.default_rng(seed)
+    yield "ties", rng.integers(0, 6, n).astype(np.float32)
+    yield "normal", np.abs(rng.standard_normal(n)).astype(np.float32)
+    yield "all-equal", np.ones(n, dtype=np.float32)
+    x = rng.standard_normal(n).astype(np.float32)     # signed, with zeros of both signs
+    x[::7] = 0.0
+    x[3::7] = -0.0
+    yield "signed", x
+
+
+@pytest.mark.parametrize("n_cap", [100, 512, 513, 5000, 70001])
+def test_topk_full_bitexact(n_cap):
+    for name, vals in _score_sets(2 * n_cap, n_cap):
+        _stage("topk full", n_cap, name)
+        B, T = 2, 1
+        s = vals.reshape(B, T, n_cap)
+        nv = np.array([[n_cap], [max(0, n_cap - 37)]], dtype=np.int32)
+        if n_cap == 5000:
+            nv[1, 0] = 0
+        scores = torch.from_numpy(s).to(DEV)
+        idx = torch.empty((B, T, 512), dtype=torch.int32, device=DEV)
+        ws = torch.empty(C.csa2_workspace_bytes(C.CSA2_OP_TOPK, C.CSA2_FULL, B, T, n_cap),
+                         dtype=torch.uint8, device=DEV)
+        C.csa2_topk(C.CSA2_FULL, scores, torch.from_numpy(nv).to(DEV), None, None, n_cap, idx, ws)
+        torch.cuda.synchronize()
+        got = to_np(idx)
+        for b in range(B):
+            v = int(nv[b, 0])
+            want = OS.topk_positions(s[b, 0, :v], np.arange(v))
+            assert np.array_equal(got[b, 0], want), (name, b)
+
+
+def test_topk_reindex_and_reuse():
+    _stage("topk reindex")
+    B, T, n_cap = 3, 1, 100000
+    nb = (n_cap + 7) // 8
+    rng = np.random.default_rng(5)
+    pool = np.full((B, T, 2048), -1, dtype=np.int32)
+    pool[0, 0] = np.sort(rng.choice(nb, 2048, replace=False))
+    pool[1, 0, :40] = np.sort(rng.choice(nb, 40, replace=False))   # fewer than 512 candidates
+    pool[2, 0] = np.sort(rng.choice(nb, 2048, replace=False))
+    nv = np.array([[n_cap], [n_cap], [50000]], dtype=np.int32)
+    s = rng.integers(0, 4, (B, T, 16384)).astype(np.float32)
+    ws = torch.empty(C.csa2_workspace_bytes(C.CSA2_OP_TOPK, C.CSA2_REINDEX, B, T, n_cap),
+                     dtype=torch.uint8, device=DEV)
+    idx = torch.empty((B, T, 512), dtype=torch.int32, device=DEV)
+    C.csa2_topk(C.CSA2_REINDEX, torch.from_numpy(s).to(DEV), torch.from_numpy(nv).to(DEV),
+                torch.from_numpy(pool).to(DEV), None, n_cap, idx, ws)
+    torch.cuda.synchronize()
+    got = to_np(idx)
+    for b in range(B):
+        cand = OS.reindex_candidates(pool[b, 0], nv[b, 0])
+        p = pool[b, 0]
+        pos_all = (np.maximum(p, 0)[:, None] * 8 + np.arange(8)[None, :]).reshape(-1)
+        valid = np.repeat(p >= 0, 8) & (pos_all < nv[b, 0])
+        assert np.array_equal(pos_all[valid], cand)
+        want = OS.topk_positions(s[b, 0][valid], cand)
+        assert np.array_equal(got[b, 0], want), b
+    # REUSE: a byte copy, and nothing at all when aliased
+    dst = torch.full_like(idx, 7)
+    C.csa2_topk(C.CSA2_REUSE, None, None, None, idx, n_cap, dst, None)
+    C.csa2_topk(C.CSA2_REUSE, None, None, None, idx, n_cap, idx, None)
+    torch.cuda.synchronize()
+    assert to_np(dst).tobytes() == got.tobytes() and to_np(idx).tobytes() == got.tobytes()
+
+
+@pytest.mark.parametrize("n_cap", [9000, 100001])
+def test_build_pool_bitexact(n_cap):
+    B, T = 2, 2
+    nv = np.array([[n_cap, n_cap - 3], [1, 16385]], dtype=np.int32)
+    for name, vals in _score_sets(B * T * n_cap, n_cap + 1):
+        _stage("build_pool", n_cap, name)
+        s = np.abs(vals).reshape(B, T, n_cap)
+        ws = torch.empty(C.csa2_workspace_bytes(C.CSA2_OP_BUILD_POOL, 0, B, T, n_cap),
+                         dtype=torch.uint8, device=DEV)
+        pool = torch.empty((B, T, 2048), dtype=torch.int32, device=DEV)
+        pool2 = torch.empty_like(pool)
+        masked = s.copy()
+        for b in range(B):
+            for t in range(T):
+                masked[b, t, nv[b, t]:] = -np.inf
+        bm = np.stack([np.stack([OI.block_max(masked[b, t], nv[b, t]) for t in range(T)]) for b in range(B)])
+        n_vis = torch.from_numpy(nv).to(DEV)
+        C.csa2_build_pool(torch.from_numpy(bm).to(DEV), True, n_vis, n_cap, pool, ws)
+        C.csa2_build_pool(torch.from_numpy(s).to(DEV), False, n_vis, n_cap, pool2, ws)
+        torch.cuda.synchronize()
+        for b in range(B):
+            for t in range(T):
+                want = OS.build_pool(bm[b, t], nv[b, t])
+                assert np.array_equal(to_np(pool)[b, t], want), (name, b, t)
+                assert np.array_equal(to_np(pool2)[b, t], want), (name, b, t)
+
+
+# -------------------------------------------------------------- attention -----
+
+def _attn_case(B, T, n_cap, S, t0, n_sel, seed, outliers=False):
+    main = synth.token_rows_bf16(B * n_cap, DEV, seed, "attn_main", outliers=outliers).view(B, n_cap, 512)
+    cache = torch.empty((B, n_cap, 288), dtype=torch.uint8, device=DEV)
+    pos = np.arange(n_cap, dtype=np.int64)
+    cs = _cs(pos)
+    for b in range(B):
+        C.csa2_quantize_kv(main[b].contiguous(), cs, None, cache[b])
+    q = synth.main_queries(B * T, DEV, seed, "attn_q", outliers=outliers).view(B, T, 64, 512)
+    swa = synth.e4m3_rows(B * S, 512, DEV, seed, "attn_swa").view(B, S, 512)
+    rng = np.random.default_rng(seed)
+    idx = np.full((B, T, 512), -1, dtype=np.int32)
+    for b in range(B):
+        for t in range(T):
+            k = n_sel[(b * T + t) % len(n_sel)]
+            idx[b, t, :k] = np.sort(rng.choice(n_cap, k, replace=False))
+    q_pos = np.array([[t0 + t for t in range(T)]] * B, dtype=np.int64)
+    pos0 = np.array([max(0, t0 - 127)] * B, dtype=np.int64)
+    return main, cache, q, swa, idx, q_pos, pos0
+
+
+@pytest.mark.parametrize("B,T,n_cap,t0,n_sel", [
+    (2, 2, 3000, 5000, [512, 300]),     # full window, short selections
+    (1, 3, 700, 40, [0, 512, 17]),      # window clipped at token 0, empty selection
+    (8, 1, 20000, 20000, [512]),        # decode shape (many key splits)
+    (70, 1, 5000, 9000, [512]),         # more queries (fewer splits)
+])
+def test_sparse_attn_vs_oracle(B, T, n_cap, t0, n_sel):
+    _stage("sparse_attn", B, T, n_cap, t0)
+    S = min(t0, 127) + T
+    main, cache, q, swa, idx, q_pos, pos0 = _attn_case(B, T, n_cap, S, t0, n_sel, B * 7 + T)
+    out = torch.empty((B, T, 64, 512), dtype=torch.float32, device=DEV)
+    ws = torch.empty(max(256, C.csa2_workspace_bytes(C.CSA2_OP_SPARSE_ATTN, 0, B, T, n_cap)),
+                     dtype=torch.uint8, device=DEV)
+    C.csa2_sparse_attn(q, cache, torch.from_numpy(idx).to(DEV), swa, torch.from_numpy(q_pos).to(DEV),
+                       torch.from_numpy(pos0).to(DEV), 1.0, out, ws)
+    torch.cuda.synchronize()
+    o = to_np(out)
+    qn = q.float().cpu().numpy()
+    swn = to_np(swa)
+    for b in range(B):
+        oc = OracleCache(main[b], 1)
+        for t in range(T):
+            ref = OA.sparse_attention(qn[b, t], oc, idx[b, t], swn[b], q_pos[b, t], pos0[b])
+            assert_attn_close(o[b, t], ref, "b%d t%d" % (b, t))
+
+
+def test_sparse_attn_scale_and_outliers():
+    _stage("sparse_attn scale/outliers")
+    B, T, n_cap, t0 = 3, 1, 4000, 4000
+    S = 128
+    main, cache, q, swa, idx, q_pos, pos0 = _attn_case(B, T, n_cap, S, t0, [512], 99, outliers=True)
+    out = torch.empty((B, T, 64, 512), dtype=torch.float32, device=DEV)
+    ws = torch.empty(max(256, C.csa2_workspace_bytes(C.CSA2_OP_SPARSE_ATTN, 0, B, T, n_cap)),
+                     dtype=torch.uint8, device=DEV)
+    C.csa2_sparse_attn(q, cache, torch.from_numpy(idx).to(DEV), swa, torch.from_numpy(q_pos).to(DEV),
+                       torch.from_numpy(pos0).to(DEV), 0.5, out, ws)
+    torch.cuda.synchronize()
+    o = to_np(out)
+    qn = q.float().cpu().numpy()
+    for b in range(B):
+        ref = OA.sparse_attention(qn[b, 0], OracleCache(main[b], 1), idx[b, 0], to_np(swa)[b],
+                                  q_pos[b, 0], pos0[b], scale=0.5)
+        assert_attn_close(o[b, 0], ref, "outliers b%d" % b)
