@@ -1,0 +1,255 @@
+"""Benchmark of the CSA2 per-layer hot path on one MI355X.
+
+A step is one pass of the whole path over one batch of decode queries: the
+write path (one new main-KV row per sequence, RoPE + FP4, into the newest
+slot), then the layer group -- for the 1M-context decoder group
+[Full, Reindex, Reuse, Reindex, Reuse, Reindex, Reuse]: the Full-mode scan of
+all 1,048,576 positions with block maxima, the 2,048-block pool, Top-512,
+Reindex scans inside the pool, Reuse, and sparse attention in every layer.
+Inputs are seeded synthetic tensors already resident in HBM.
+
+Prints ONE JSON line (rank 0) with the queries/s, the roofline of the dominant
+kernel (the Full-mode scan; its duration is measured with HIP events around
+its launches inside the timed region, on the stream it is launched on), and
+the oracle's throughput on the host cores for a bounded sample.
+
+Usage: python bench.py [--steps K] [--warmup W] [--gpus 1] [--workload c2|c4|c1]
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, HERE)
+
+HBM_PEAK_GBS = 8000.0
+SCAN_KERNEL = "k_index_score_decode"
+TRAFFIC_FILE = os.path.join(HERE, "profiles", "traffic_index_score_full_c2.json")
+SCAN_SOURCE = os.path.join(HERE, "compressed_kv_cache_02_amd", "csrc", "index_score.hip")
+
+
+def log(msg):
+    print("[bench] " + msg, file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--workload", default="c2", choices=["c1", "c2", "c4"])
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="also run a plain 1 GiB device copy (for counter calibration)")
+    return p.parse_args()
+
+
+def scan_algorithmic_bytes(B, T, n_vis_total):
+    """Bytes the Full-mode scan must move per launch: 128 B of indexer key per
+    visible position plus each query's 32x128 E4M3 query and 32 float weights."""
+    return 128 * n_vis_total + (32 * 128 + 32 * 4) * B * T
+
+
+def step_algorithmic_bytes(w, n_vis_total):
+    """Whole-step bytes per the path's definition: scans, attention, write path."""
+    q = w.B * w.T
+    full = 128 * n_vis_total + (4096 + 128 + 2048) * q
+    reindex = (2097152 + 4224 + 8192 + 2048) * q
+    attn = 411648 * q
+    n_x = {"decoder": 3}.get(w.kind, 0)
+    return full + n_x * reindex + w.n_layers * attn + 1568 * w.B
+
+
+def source_sha(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def read_traffic(n_launch_bytes):
+    """HBM traffic per scan launch from the committed rocprofv3 counter summary,
+    or None if missing or taken on another version of the kernel."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_sha") != source_sha(SCAN_SOURCE):
+        return None
+    return t.get("traffic_bytes_per_launch")
+
+
+def cpu_baseline(w, inp, seed, new_rows):
+    """The oracle, single-threaded, on one query (sequence 0) through the whole
+    group: about 10-30 s of CPU work."""
+    import numpy as np
+    try:
+        from threadpoolctl import threadpool_limits
+    except ImportError:           # pragma: no cover
+        threadpool_limits = None
+    import torch
+    from oracle import group as OG
+    from oracle import rope as OR, formats as OF
+    from oracle.compress import n_visible
+    import synth
+
+    b, t = 0, 0
+    n_cap, m = w.n_cap, w.m
+    main0 = synth.pooled_main_rows(n_cap, m, "cuda", seed, w.name, "main", b, outliers=w.outliers)
+    main0[n_cap - 1] = new_rows[b]
+
+    class Cache:
+        def __getitem__(self, sel):
+            sel = np.asarray(sel, dtype=np.int64)
+            x = main0[torch.from_numpy(sel).to(main0.device)].float().cpu().numpy()
+            return OF.quantize_rows(OR.apply_rope(x, sel * m))
+
+    kn = inp["k_idx"][b].cpu().numpy()
+    sched = OG.layer_schedule(w.kind)
+    qi = {li: inp["q_idx"][li][b, t].cpu().numpy() for li in inp["q_idx"]}
+    wi = {li: inp["w"][li][b, t].cpu().numpy() for li in inp["w"]}
+    q = {li: inp["q"][li][b, t].float().cpu().numpy() for li in range(len(sched))}
+    swa = {li: inp["swa"][li][b].cpu().numpy() for li in range(len(sched))}
+    tq = w.q_positions[t]
+    nv = int(n_visible(tq, m))
+
+    def run():
+        return OG.run_group(sched, qi, wi, q, swa, kn, Cache(), nv, tq, w.swa_pos0)
+
+    if threadpool_limits is not None:
+        with threadpool_limits(limits=1):
+            t0 = time.perf_counter()
+            run()
+            el = time.perf_counter() - t0
+    else:
+        t0 = time.perf_counter()
+        run()
+        el = time.perf_counter() - t0
+    return {"value": 1.0 / el, "unit": "queries/s", "cores": 1, "kind": "oracle",
+            "sample": "1 of %d queries (sequence 0) through all %d layers, incl. the write-path row; "
+                      "%.1f s single-threaded" % (w.B * w.T, len(sched), el)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+    import compressed_kv_cache_02_amd as C
+    from compressed_kv_cache_02_amd.group import LayerGroup, visible_entries
+    from synth.configs import WORKLOADS, make_inputs
+
+    w = WORKLOADS[args.workload]
+    dev = "cuda"
+    torch.cuda.set_device(0)
+    seed = 0
+    log("generating inputs for %s" % w.name)
+    inp = make_inputs(w, dev, seed=seed)
+    B, T, n_cap, m = w.B, w.T, w.n_cap, w.m
+    # cache build: every sequence's rows through the write-path kernel
+    cache = torch.empty((B, n_cap, 288), dtype=torch.uint8, device=dev)
+    cs_all = torch.from_numpy(C.csa2_rope_table(np.arange(n_cap, dtype=np.int64) * m)).to(dev)
+    for b in range(B):
+        C.csa2_quantize_kv(inp["main_rows_per_seq"][b], cs_all, None, cache[b])
+    del cs_all
+    inp["main_rows_per_seq"] = None
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    # per-step write path: one new row per sequence into the newest slot
+    if "write_bf16" in inp:
+        new_rows = inp["write_bf16"]
+    else:
+        import synth
+        new_rows = synth.token_rows_bf16(B, dev, seed, w.name, "write")
+    slot = torch.arange(B, dtype=torch.int64, device=dev) * n_cap + (n_cap - 1)
+    cs_new = torch.from_numpy(C.csa2_rope_table(np.full(B, (n_cap - 1) * m, dtype=np.int64))).to(dev)
+    write = (new_rows, cs_new, slot)
+
+    n_vis = visible_entries(inp["q_pos"], m).to(torch.int32)
+    n_vis_total = int(n_vis.sum().item())
+    g = LayerGroup(w.kind, B, T, n_cap, device=dev)
+    stream = torch.cuda.current_stream()
+
+    ev = []
+
+    def begin():
+        e = torch.cuda.Event(enable_timing=True)
+        e.record(stream)
+        ev.append([e, None])
+
+    def end():
+        e = torch.cuda.Event(enable_timing=True)
+        e.record(stream)
+        ev[-1][1] = e
+
+    def step(timed):
+        hooks = {"scan_begin": begin, "scan_end": end} if timed else None
+        g.step(inp["k_idx"], cache, n_vis, inp["q_pos"], inp["swa_pos0"], inp["q_idx"], inp["w"],
+               inp["q"], inp["swa"], write=write, hooks=hooks)
+
+    log("cache built; warmup %d steps" % args.warmup)
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(True)
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    if args.copy_calibration:
+        a = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+        b2 = torch.empty_like(a)
+        b2.copy_(a)
+        torch.cuda.synchronize()
+        del a, b2
+
+    ms = el * 1e3 / args.steps
+    qps = B * T * args.steps / el
+    scan_ms = float(np.mean([s.elapsed_time(e) for s, e in ev]))
+    scan_bytes = scan_algorithmic_bytes(B, T, n_vis_total)
+    achieved = scan_bytes / (scan_ms * 1e-3) / 1e9
+    traffic = read_traffic(scan_bytes)
+    step_bytes = step_algorithmic_bytes(w, n_vis_total)
+    res = {
+        "metric": "CSA2 decode queries/s at 1M ctx (Top-512 + SWA-128); % HBM/MFMA roofline",
+        "value": round(qps, 2),
+        "unit": "queries/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8-e4m3/fp4-e2m1 storage; fp32 scores; bf16/fp16 MFMA attention",
+        "data": "synthetic (seeded N(0,1) per the workload recipe)",
+        "config": {"workload": "%s: %s" % (w.name, {
+            "c2": "decoder layer group [F,X,U,X,U,X,U] at 1,048,576 positions (m=1), batch 8 decode, + write path",
+            "c4": "encoder group [F,U x5] at 1,048,576 tokens (m=2, 524,288 entries), batch 64 decode, write path, outliers",
+            "c1": "Full-mode decode, batch 32, 131,072 tokens (m=2, 65,536 entries)"}[w.name]),
+            "batch": B, "queries_per_seq": T, "n_cap": n_cap, "layers": len(g.sched),
+            "topk": 512, "window": 128},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic, "kernel": SCAN_KERNEL,
+                     "kernel_ms": round(scan_ms, 4), "algorithmic_bytes_per_launch": scan_bytes},
+        "step_roofline": {"algorithmic_bytes": step_bytes,
+                          "achieved_GBps": round(step_bytes / (ms * 1e-3) / 1e9, 1),
+                          "frac": round(step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
+    }
+    log("timed %d steps: %.3f ms/step; running the oracle sample" % (args.steps, ms))
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(w, inp, seed, new_rows)
+    else:
+        res["cpu_baseline"] = None
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()
