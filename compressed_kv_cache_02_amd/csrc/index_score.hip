@@ -87,34 +87,39 @@ __global__ __launch_bounds__(256) void k_index_score_decode(
 
   const int64_t wave_base = (int64_t)blockIdx.x * kItemsPerWG + (int64_t)wave * kTilePos * kTilesPerWave;
 
-  auto position_of = [&](int64_t item, bool& ok) -> int64_t {
+  // Reindex: the pool entries of all of this wave's tiles are fetched first, so
+  // a tile's key loads never wait on a pool lookup.
+  int32_t blk[kTilesPerWave];
+#pragma unroll
+  for (int it = 0; it < kTilesPerWave; ++it) {
+    const int64_t item = wave_base + (int64_t)it * kTilePos + col;
+    blk[it] = (MODE == 1 && item < n_items) ? pl[item >> 3] : -1;
+  }
+  auto position_of = [&](int it, bool& ok) __attribute__((always_inline)) -> int64_t {
+    const int64_t item = wave_base + (int64_t)it * kTilePos + col;
     if (MODE == 0) {
       ok = item < nv;
-      return item;
-    } else {
-      int64_t blk = item < n_items ? (int64_t)pl[item >> 3] : -1;
-      if (blk < 0 || blk >= n_blk) { ok = false; return 0; }
-      const int64_t pos = blk * kBlock + (item & 7);
-      ok = pos < nv;
-      return pos;
+      return ok ? item : 0;
     }
+    const int64_t b8 = blk[it];
+    const int64_t pos = b8 * kBlock + (item & 7);
+    ok = b8 >= 0 && b8 < n_blk && pos < nv;
+    return ok ? pos : 0;
   };
 
   KTile cur, nxt;
   bool cur_ok;
   {
-    const int64_t item = wave_base + col;
-    const int64_t pos = position_of(item, cur_ok);
+    const int64_t pos = position_of(0, cur_ok);
     load_tile(cur, kbase + pos * kIdxDim, cur_ok);
   }
-#pragma unroll 1
+#pragma unroll
   for (int it = 0; it < kTilesPerWave; ++it) {
     const int64_t tile0 = wave_base + (int64_t)it * kTilePos;
     if (tile0 >= n_items) break;
     bool nxt_ok = false;
     if (it + 1 < kTilesPerWave) {
-      const int64_t item = tile0 + kTilePos + col;
-      const int64_t pos = position_of(item, nxt_ok);
+      const int64_t pos = position_of(it + 1, nxt_ok);
       load_tile(nxt, kbase + pos * kIdxDim, nxt_ok);
     }
     float s = -INFINITY;

@@ -8,25 +8,39 @@
 // every layer has its own query and window ("DeepSeek V4.1 Flash vs V4 Pro",
 // 黑科技之二). Key = value = the dequantised 512-wide row (reading in csa2.h).
 //
-// Work split: one work-group per (query, slice of the 640 key slots); 4 waves,
-// wave w owns heads 16w..16w+15 and all 512 output channels. Keys are
-// processed 32 at a time:
-//   gather  -- the work-group loads the 32 rows (FP4 codes + E4M3 scales, or
-//              E4M3 window rows), dequantises them (exact in bf16 and fp16) and
-//              writes them to LDS twice: row-major bf16 for Q.K and transposed
-//              fp16 for P.V;
-//   Q.K     -- v_mfma_f32_16x16x32_bf16 with the keys as A (rows) and the
-//              wave's 16 query heads as B (kept in registers);
-//   softmax -- online (running max and sum per head, which is one lane column
-//              of the 16x16 result);
-//   P.V     -- v_mfma_f32_16x16x32_f16 with the transposed keys as A and the
-//              probabilities (fp16, converted in registers from the Q.K result
-//              layout) as B; 32 accumulator tiles hold 512 channels x 16 heads.
-// With more than one slice per query the partial (max, sum, unnormalised
-// output) go to the workspace and a merge kernel combines them by
-// log-sum-exp; with one slice the kernel writes the output directly.
+// Keys are processed 32 at a time. Gather: thread t of the 256 owns channels
+// 8p..8p+7 with p = 16*(t/64) + (t%16) -- so wave w owns channels
+// 128w..128w+127 -- and keys 8g..8g+7 of the chunk with g = (t%64)/16. It loads
+// the FP4 codes (4 bytes) and E4M3 scale of each of its keys, or 8 E4M3 bytes of
+// a window row, dequantises them to fp16 (exact) with the gfx950 FP4/FP8
+// converts and stores them in LDS twice:
+//   krow -- row-major fp16 [key][channel], the A operand of Q.K;
+//   vt   -- transposed fp16 [channel][key], the A operand of P.V. Its rows are
+//           80 bytes (5 slots of 16 bytes for 4 chunks of 8 keys) and chunk c of
+//           row d sits in slot (c + d/8) % 5, which spreads the 16-byte stores
+//           of a wave over the LDS banks.
+// Q.K: v_mfma_f32_16x16x32_f16 with keys as A and 16 query heads as B (kept in
+// registers, each head scaled by a power of two into fp16 range; the logits are
+// scaled back). Online softmax per head (one lane column of the 16x16 result).
+// P.V: v_mfma_f32_16x16x32_f16 with the transposed keys as A and P as B. P is
+// split as P = hi + lo with both parts in fp16 (two MFMAs per tile), which keeps
+// the product accurate to about 2^-22 of P even when rows carry large outlier
+// channels.
+//
+// Two work shapes:
+//   wide   (>= 512 queries): one work-group per query, wave w owns heads
+//          16w..16w+15 and all 512 output channels, every gathered row serves all
+//          64 heads;
+//   decode (fewer queries): one work-group per (query, 16-head group, slice of
+//          the 640 key slots); wave w forms the partial Q.K over its own 128
+//          gathered channels, the four partials are summed through LDS in a
+//          fixed order, and wave w accumulates P.V for its 128 output channels.
+//          A slice's rows are requested before its first chunk is computed.
+//          Slices are merged by log-sum-exp in a second kernel.
 #include "device_common.hpp"
 #include "launchers.hpp"
+
+#include <utility>
 
 namespace csa2 {
 namespace {
@@ -35,16 +49,27 @@ constexpr int kThreads = 256;
 constexpr int kChunkKeys = 32;
 constexpr int kSlots = kTopK + kWindow;           // 640 key slots per query
 constexpr int kChunks = kSlots / kChunkKeys;      // 20
-constexpr int kKrowStride = kDim + 8;             // bf16 elements per LDS key row
-constexpr int kVtStride = kChunkKeys + 8;         // fp16 elements per LDS channel row
+constexpr int kKrowStride = kDim + 8;             // fp16 elements per LDS key row
+constexpr int kVtRowHalves = 40;                  // fp16 elements per LDS channel row (80 B)
+constexpr int kHG = 16;                           // heads per decode work-group
+constexpr int kHeadGroups = kHeads / kHG;
+constexpr int kWideMinQueries = 512;
 
-__device__ __forceinline__ uint16_t f32_to_bf16_exact(float v) {
-  return (uint16_t)(__float_as_uint(v) >> 16);   // exact for dequantised values
+typedef _Float16 v2h __attribute__((ext_vector_type(2)));
+
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+// Calls f(integral_constant<int, i>) for i = 0..N-1, fully unrolled.
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
-__device__ __forceinline__ uint16_t f32_to_f16_bits(float v) {
-  const _Float16 h = (_Float16)v;
-  return *reinterpret_cast<const uint16_t*>(&h);
+// fp16 element offset of (channel row d, 16-byte key chunk c) in vt.
+__device__ __forceinline__ int vt_off(int d, int c) {
+  return d * kVtRowHalves + ((c + (d >> 3)) % 5) * 8;
 }
 
 struct AttnArgs {
@@ -64,106 +89,278 @@ struct AttnArgs {
   int splits;
 };
 
-__global__ __launch_bounds__(kThreads) void k_sparse_attn(AttnArgs a) {
+struct Gather {
+  const uint8_t* cache_b;
+  const uint8_t* swa_b;
+  const int32_t* idx_q;
+  int64_t n_cap, tq, pos0;
+  int S, piece, kgrp;
+
+  __device__ void init(const AttnArgs& a, int qi) {
+    const int b = qi / a.T;
+    cache_b = a.cache + (size_t)b * (size_t)a.n_cap * kRowBytes;
+    swa_b = a.swa + (size_t)b * (size_t)a.S * kDim;
+    idx_q = a.idx + (size_t)qi * kTopK;
+    n_cap = a.n_cap;
+    tq = a.q_pos[qi];
+    pos0 = a.swa_pos0[b];
+    S = a.S;
+    const int t = threadIdx.x;
+    piece = 16 * (t >> 6) + (t & 15);
+    kgrp = (t & 63) >> 4;
+  }
+
+  // Raw bytes of this thread's 8 keys (8 channels each) of chunk `chunk`; bit j
+  // of the result marks key j present. The selected positions come from `sidx`
+  // (this work-group's slice of the index list, staged in LDS by stage_idx), so
+  // no global load waits on another; every row load is issued unconditionally
+  // (an absent key reads row 0, which exists, and is masked afterwards).
+  __device__ __forceinline__ uint32_t load(int chunk, int chunk0, const int32_t* sidx,
+                                           uint2 (&r)[8]) const {
+    const int slot0 = chunk * kChunkKeys + kgrp * 8;
+    uint32_t ok = 0;
+    if (slot0 < kTopK) {
+      const int4 i0 = *reinterpret_cast<const int4*>(sidx + (slot0 - chunk0 * kChunkKeys));
+      const int4 i1 = *reinterpret_cast<const int4*>(sidx + (slot0 - chunk0 * kChunkKeys) + 4);
+      const int32_t pj[8] = {i0.x, i0.y, i0.z, i0.w, i1.x, i1.y, i1.z, i1.w};
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const bool v = pj[j] >= 0 && (int64_t)pj[j] < n_cap;
+        ok |= (v ? 1u : 0u) << j;
+        const uint8_t* row = cache_b + (size_t)(v ? pj[j] : 0) * kRowBytes;
+        r[j].x = *reinterpret_cast<const uint32_t*>(row + piece * 4);
+        r[j].y = row[kCodeBytes + (piece >> 1)];
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int64_t tok = tq - (kWindow - 1) + (slot0 + j - kTopK);
+        const int64_t rr = tok - pos0;
+        const bool v = tok >= 0 && rr >= 0 && rr < S;
+        ok |= (v ? 1u : 0u) << j;
+        r[j] = *reinterpret_cast<const uint2*>(swa_b + (size_t)(v ? rr : 0) * kDim + piece * 8);
+      }
+    }
+    return ok;
+  }
+
+  // Copies the selected positions of chunks [chunk0, chunk0 + n) into LDS.
+  __device__ __forceinline__ void stage_idx(int chunk0, int n, int32_t* sidx) const {
+    const int s0 = chunk0 * kChunkKeys;
+    const int cnt = min(n * kChunkKeys, kTopK - s0);
+    for (int i = threadIdx.x; i < cnt; i += kThreads) sidx[i] = idx_q[s0 + i];
+  }
+
+  // Dequantise and store into krow / vt; flags the keys' presence in kvalid.
+  // FP4: v_cvt_scalef32_pk_f16_fp4 applies the power-of-two part of the E4M3
+  // scale (2^(E-7), or 2^-9 for a subnormal scale), then one v_pk_mul_f16
+  // multiplies by its mantissa part (1 + M/8, or M): every step is exact
+  // because the products have at most 6 significant bits and lie in
+  // [2^-10, 2688]. FP8 window rows: v_cvt_scalef32_pk_f16_fp8 with scale 1.
+  __device__ __forceinline__ void store(bool is_main, const uint2 (&r)[8], uint32_t ok,
+                                        uint16_t* krow, uint16_t* vt, int* kvalid) const {
+    uint32_t pr[8][4];   // [key][channel pair]: fp16 pairs of channels 8p+2b, 8p+2b+1
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if (is_main) {
+        const uint32_t c = r[j].y;
+        const uint32_t E = (c >> 3) & 15u, M = c & 7u;
+        const float hw = __uint_as_float(E ? (E + 120u) << 23 : 118u << 23);
+        const _Float16 mf = E ? __builtin_bit_cast(_Float16, (uint16_t)(0x3C00u | (M << 7)))
+                              : (_Float16)(float)M;
+        const v2h m2 = {mf, mf};
+        v2h h0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(r[j].x, hw, 0) * m2;
+        v2h h1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(r[j].x, hw, 1) * m2;
+        v2h h2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(r[j].x, hw, 2) * m2;
+        v2h h3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(r[j].x, hw, 3) * m2;
+        pr[j][0] = __builtin_bit_cast(uint32_t, h0);
+        pr[j][1] = __builtin_bit_cast(uint32_t, h1);
+        pr[j][2] = __builtin_bit_cast(uint32_t, h2);
+        pr[j][3] = __builtin_bit_cast(uint32_t, h3);
+      } else {
+        pr[j][0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(r[j].x, 1.0f, false));
+        pr[j][1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(r[j].x, 1.0f, true));
+        pr[j][2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(r[j].y, 1.0f, false));
+        pr[j][3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(r[j].y, 1.0f, true));
+      }
+      if (!((ok >> j) & 1u)) pr[j][0] = pr[j][1] = pr[j][2] = pr[j][3] = 0u;
+      const int key = kgrp * 8 + j;
+      if ((threadIdx.x & 15) == 0 && (threadIdx.x >> 6) == 0) kvalid[key] = (ok >> j) & 1u;
+      *reinterpret_cast<uint4*>(&krow[key * kKrowStride + piece * 8]) =
+          make_uint4(pr[j][0], pr[j][1], pr[j][2], pr[j][3]);
+    }
+    // transpose 8 keys x 8 channels: row 8p + 2b takes the low halves of the
+    // pairs, row 8p + 2b + 1 the high halves
+    const int slot = ((kgrp + piece) % 5) * 8;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const uint4 lo = make_uint4(__builtin_amdgcn_perm(pr[1][b], pr[0][b], 0x05040100u),
+                                  __builtin_amdgcn_perm(pr[3][b], pr[2][b], 0x05040100u),
+                                  __builtin_amdgcn_perm(pr[5][b], pr[4][b], 0x05040100u),
+                                  __builtin_amdgcn_perm(pr[7][b], pr[6][b], 0x05040100u));
+      const uint4 hi = make_uint4(__builtin_amdgcn_perm(pr[1][b], pr[0][b], 0x07060302u),
+                                  __builtin_amdgcn_perm(pr[3][b], pr[2][b], 0x07060302u),
+                                  __builtin_amdgcn_perm(pr[5][b], pr[4][b], 0x07060302u),
+                                  __builtin_amdgcn_perm(pr[7][b], pr[6][b], 0x07060302u));
+      *reinterpret_cast<uint4*>(&vt[(piece * 8 + 2 * b) * kVtRowHalves + slot]) = lo;
+      *reinterpret_cast<uint4*>(&vt[(piece * 8 + 2 * b + 1) * kVtRowHalves + slot]) = hi;
+    }
+  }
+};
+
+// Exponent shift that brings a per-head maximum |q| into [2^14, 2^15): q * 2^s
+// then fits fp16 without overflow, and every element within 2^28 of the maximum
+// keeps its full bf16 precision (smaller ones contribute below 2^-28 of it).
+__device__ __forceinline__ int q_shift(float amax) {
+  if (!(amax > 0.0f)) return 0;
+  const int e = (int)((__float_as_uint(amax) >> 23) & 0xFF) - 127;
+  return 14 - e;
+}
+
+__device__ __forceinline__ v8h q_to_f16(const uint4& raw, int shift) {
+  const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+  v8h o;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    o[2 * i] = (_Float16)ldexpf(bf16_bits_to_f32(w[i] & 0xFFFFu), shift);
+    o[2 * i + 1] = (_Float16)ldexpf(bf16_bits_to_f32(w[i] >> 16), shift);
+  }
+  return o;
+}
+
+__device__ __forceinline__ float bf16x8_absmax(const uint4& raw) {
+  const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+  float m = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    m = fmaxf(m, fabsf(bf16_bits_to_f32(w[i] & 0xFFFFu)));
+    m = fmaxf(m, fabsf(bf16_bits_to_f32(w[i] >> 16)));
+  }
+  return m;
+}
+
+// P.V operand for one 16-channel tile: channel row `row`, keys
+// {4*grp..+3, 16+4*grp..+3}, matching the Q.K result layout of P.
+__device__ __forceinline__ v8h vt_operand(const uint16_t* vt, int row, int grp) {
+  const uint2 lo = *reinterpret_cast<const uint2*>(&vt[vt_off(row, grp >> 1) + (grp & 1) * 4]);
+  const uint2 hi = *reinterpret_cast<const uint2*>(&vt[vt_off(row, 2 + (grp >> 1)) + (grp & 1) * 4]);
+  const uint4 v = make_uint4(lo.x, lo.y, hi.x, hi.y);
+  return *reinterpret_cast<const v8h*>(&v);
+}
+
+// Online softmax step for one chunk. z: this lane's 8 logits (head = column,
+// -inf for absent keys). Returns alpha and writes P as hi/lo fp16 operands.
+__device__ __forceinline__ float softmax_step(const float (&z)[8], float& m_run, float& l_run,
+                                              v8h& p_hi, v8h& p_lo) {
+  float mx = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) mx = fmaxf(mx, z[i]);
+  mx = fmaxf(mx, wave_shfl_xor(mx, 16));
+  mx = fmaxf(mx, wave_shfl_xor(mx, 32));
+  const float m_new = fmaxf(m_run, mx);
+  float alpha = 1.0f, psum = 0.0f;
+  float p[8];
+  if (m_new == -INFINITY) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) p[i] = 0.0f;
+  } else {
+    alpha = __expf(m_run - m_new);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      p[i] = __expf(z[i] - m_new);
+      psum += p[i];
+    }
+  }
+  psum += wave_shfl_xor(psum, 16);
+  psum += wave_shfl_xor(psum, 32);
+  l_run = l_run * alpha + psum;
+  m_run = m_new;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const _Float16 h = (_Float16)p[i];
+    p_hi[i] = h;
+    p_lo[i] = (_Float16)(p[i] - (float)h);
+  }
+  return alpha;
+}
+
+// Runs chunk(c, raw, ok) for c = 0..CPS-1 of the slice with row loads issued PF
+// chunks ahead (register slots are indexed statically).
+template <int CPS, int PF, typename Load, typename Chunk>
+__device__ __forceinline__ void pipeline(Load&& load, Chunk&& chunk) {
+  uint2 raw[PF][8];
+  uint32_t ok[PF];
+  static_for<PF>([&](auto ii) __attribute__((always_inline)) {
+    constexpr int i = decltype(ii)::value;
+    if (i < CPS) ok[i] = load(i, raw[i]);
+  });
+  for (int c0 = 0; c0 < CPS; c0 += PF) {
+    static_for<PF>([&](auto ii) __attribute__((always_inline)) {
+      constexpr int i = decltype(ii)::value;
+      const int c = c0 + i;
+      if (c < CPS) {
+        uint2 cur[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) cur[j] = raw[i][j];
+        const uint32_t cok = ok[i];
+        if (c + PF < CPS) ok[i] = load(c + PF, raw[i]);
+        chunk(c, cur, cok);
+      }
+    });
+  }
+}
+
+// ------------------------------------------------------------ wide kernel --
+
+// One work-group per (query, slice of CPS chunks); wave w owns heads
+// 16w..16w+15 and all 512 output channels, so every gathered row serves the 64
+// heads. With one slice per query the output is written directly, otherwise
+// the partial state goes to the workspace for the merge kernel.
+template <int CPS>
+__global__ __launch_bounds__(kThreads) void k_sparse_attn_wide(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t krow[kChunkKeys * kKrowStride];
-  __shared__ __attribute__((aligned(16))) uint16_t vt[kDim * kVtStride];
+  __shared__ __attribute__((aligned(16))) uint16_t vt[kDim * kVtRowHalves];
   __shared__ int kvalid[kChunkKeys];
+  __shared__ __attribute__((aligned(16))) int32_t sidx[CPS * kChunkKeys];
 
   const int qi = blockIdx.y;
   const int split = blockIdx.x;
-  const int b = qi / a.T;
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int col = lane & 15, grp = lane >> 4;
-  const int64_t tq = a.q_pos[qi];
-  const int64_t pos0 = a.swa_pos0[b];
+  Gather g;
+  g.init(a, qi);
+  const int chunk0 = split * CPS;
 
-  // This wave's 16 heads as the B operand of Q.K: head 16*wave + col,
-  // channels kb*32 + grp*8 .. +7 for kb = 0..15.
-  v8bf qreg[16];
-  {
-    const uint16_t* qp = a.q + ((size_t)qi * kHeads + wave * 16 + col) * kDim + grp * 8;
-#pragma unroll
-    for (int kb = 0; kb < 16; ++kb) {
-      const uint4 v = *reinterpret_cast<const uint4*>(qp + kb * 32);
-      qreg[kb] = *reinterpret_cast<const v8bf*>(&v);
-    }
-  }
   v4f acc[32];
 #pragma unroll
   for (int i = 0; i < 32; ++i) acc[i] = v4f{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.0f;
+  v8h qreg[16];
+  float zscale;
 
-  const int chunks_per_split = kChunks / a.splits;
-  const int piece = tid & 63;          // channels 8*piece .. +7 in the gather
-  const int kgrp = tid >> 6;           // keys 8*kgrp .. +7 of the chunk in the gather
-  const uint8_t* cache_b = a.cache + (size_t)b * (size_t)a.n_cap * kRowBytes;
-  const uint8_t* swa_b = a.swa + (size_t)b * (size_t)a.S * kDim;
-  const int32_t* idx_q = a.idx + (size_t)qi * kTopK;
+  // This wave's 16 heads as the B operand of Q.K: head 16*wave + col,
+  // channels kb*32 + grp*8 .. +7 for kb = 0..15, in fp16 after the head's shift.
+  auto load_q = [&]() __attribute__((always_inline)) {
+    const uint16_t* qp = a.q + ((size_t)qi * kHeads + wave * 16 + col) * kDim + grp * 8;
+    uint4 raw[16];
+    float amax = 0.0f;
+#pragma unroll
+    for (int kb = 0; kb < 16; ++kb) {
+      raw[kb] = *reinterpret_cast<const uint4*>(qp + kb * 32);
+      amax = fmaxf(amax, bf16x8_absmax(raw[kb]));
+    }
+    amax = fmaxf(amax, wave_shfl_xor(amax, 16));
+    amax = fmaxf(amax, wave_shfl_xor(amax, 32));
+    const int sh = q_shift(amax);
+#pragma unroll
+    for (int kb = 0; kb < 16; ++kb) qreg[kb] = q_to_f16(raw[kb], sh);
+    zscale = ldexpf(a.scale, -sh);
+  };
 
-  for (int c = 0; c < chunks_per_split; ++c) {
-    const int slot0 = (split * chunks_per_split + c) * kChunkKeys;
-    // ---------------------------------------------------------------- gather
-    float vals[8][8];   // [key][channel]
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int key = kgrp * 8 + j;
-      const int slot = slot0 + key;
-      bool ok;
-      if (slot < kTopK) {
-        const int64_t p = idx_q[slot];
-        ok = p >= 0 && p < a.n_cap;
-        if (ok) {
-          const uint8_t* row = cache_b + (size_t)p * kRowBytes;
-          const uint32_t codes = *reinterpret_cast<const uint32_t*>(row + piece * 4);
-          const float s = e4m3_to_f32(row[kCodeBytes + (piece >> 1)]);
-#pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            const uint32_t cd = (codes >> (4 * i)) & 0xFu;
-            const float m = e2m1_mag(cd & 7u) * s;
-            vals[j][i] = (cd & 8u) ? -m : m;
-          }
-        }
-      } else {
-        const int64_t tok = tq - (kWindow - 1) + (slot - kTopK);
-        const int64_t r = tok - pos0;
-        ok = tok >= 0 && r >= 0 && r < a.S;
-        if (ok) {
-          const uint2 raw = *reinterpret_cast<const uint2*>(swa_b + (size_t)r * kDim + piece * 8);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            vals[j][i] = e4m3_to_f32((raw.x >> (8 * i)) & 0xFFu);
-            vals[j][4 + i] = e4m3_to_f32((raw.y >> (8 * i)) & 0xFFu);
-          }
-        }
-      }
-      if (!ok) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) vals[j][i] = 0.0f;
-      }
-      if (piece == 0) kvalid[key] = ok ? 1 : 0;
-      // row-major bf16 copy: key row, channels 8*piece .. +7
-      uint4 w;
-      w.x = f32_to_bf16_exact(vals[j][0]) | ((uint32_t)f32_to_bf16_exact(vals[j][1]) << 16);
-      w.y = f32_to_bf16_exact(vals[j][2]) | ((uint32_t)f32_to_bf16_exact(vals[j][3]) << 16);
-      w.z = f32_to_bf16_exact(vals[j][4]) | ((uint32_t)f32_to_bf16_exact(vals[j][5]) << 16);
-      w.w = f32_to_bf16_exact(vals[j][6]) | ((uint32_t)f32_to_bf16_exact(vals[j][7]) << 16);
-      *reinterpret_cast<uint4*>(&krow[key * kKrowStride + piece * 8]) = w;
-    }
-    // transposed fp16 copy: channel row, keys 8*kgrp .. +7
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      uint4 w;
-      w.x = f32_to_f16_bits(vals[0][i]) | ((uint32_t)f32_to_f16_bits(vals[1][i]) << 16);
-      w.y = f32_to_f16_bits(vals[2][i]) | ((uint32_t)f32_to_f16_bits(vals[3][i]) << 16);
-      w.z = f32_to_f16_bits(vals[4][i]) | ((uint32_t)f32_to_f16_bits(vals[5][i]) << 16);
-      w.w = f32_to_f16_bits(vals[6][i]) | ((uint32_t)f32_to_f16_bits(vals[7][i]) << 16);
-      *reinterpret_cast<uint4*>(&vt[(piece * 8 + i) * kVtStride + kgrp * 8]) = w;
-    }
+  auto chunk = [&](int c, const uint2 (&r)[8], uint32_t ok) __attribute__((always_inline)) {
+    g.store((chunk0 + c) * kChunkKeys < kTopK, r, ok, krow, vt, kvalid);
     __syncthreads();
-
-    // ------------------------------------------------------------------- Q.K
-    v4f sc[2];
+    float z[8];
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
       v4f s = {0.f, 0.f, 0.f, 0.f};
@@ -171,63 +368,39 @@ __global__ __launch_bounds__(kThreads) void k_sparse_attn(AttnArgs a) {
 #pragma unroll
       for (int kb = 0; kb < 16; ++kb) {
         const uint4 v = *reinterpret_cast<const uint4*>(kr + kb * 32);
-        s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*reinterpret_cast<const v8bf*>(&v), qreg[kb], s,
-                                                    0, 0, 0);
+        s = __builtin_amdgcn_mfma_f32_16x16x32_f16(*reinterpret_cast<const v8h*>(&v), qreg[kb], s,
+                                                   0, 0, 0);
       }
-      sc[mt] = s;
-    }
-    // --------------------------------------------------------------- softmax
-    // lane holds head `col`, keys mt*16 + 4*grp + i
-    float z[8];
-    float mx = -INFINITY;
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int key = mt * 16 + 4 * grp + i;
-        const float v = kvalid[key] ? sc[mt][i] * a.scale : -INFINITY;
-        z[mt * 4 + i] = v;
-        mx = fmaxf(mx, v);
-      }
-    mx = fmaxf(mx, wave_shfl_xor(mx, 16));
-    mx = fmaxf(mx, wave_shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx);
-    float alpha = 1.0f;
-    float psum = 0.0f;
-    float p[8];
-    if (m_new == -INFINITY) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) p[i] = 0.0f;
-    } else {
-      alpha = __expf(m_run - m_new);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        p[i] = __expf(z[i] - m_new);
-        psum += p[i];
+        z[mt * 4 + i] = kvalid[key] ? s[i] * zscale : -INFINITY;
       }
     }
-    psum += wave_shfl_xor(psum, 16);
-    psum += wave_shfl_xor(psum, 32);
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
+    v8h p_hi, p_lo;
+    const float alpha = softmax_step(z, m_run, l_run, p_hi, p_lo);
+    if (__any(alpha != 1.0f)) {
 #pragma unroll
-    for (int i = 0; i < 32; ++i) acc[i] *= alpha;
-    v8h pb;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) pb[i] = (_Float16)p[i];
-    // ------------------------------------------------------------------- P.V
-    // A operand: channel row 16*dt + col, keys {4*grp .. +3} and {16 + 4*grp .. +3}
+      for (int dt = 0; dt < 32; ++dt) acc[dt] *= alpha;
+    }
 #pragma unroll
     for (int dt = 0; dt < 32; ++dt) {
-      const uint16_t* vr = &vt[(dt * 16 + col) * kVtStride + 4 * grp];
-      const uint2 lo = *reinterpret_cast<const uint2*>(vr);
-      const uint2 hi = *reinterpret_cast<const uint2*>(vr + 16);
-      const uint4 v = make_uint4(lo.x, lo.y, hi.x, hi.y);
-      acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(*reinterpret_cast<const v8h*>(&v), pb,
-                                                       acc[dt], 0, 0, 0);
+      const v8h v = vt_operand(vt, dt * 16 + col, grp);
+      acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(v, p_hi, acc[dt], 0, 0, 0);
+      acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(v, p_lo, acc[dt], 0, 0, 0);
     }
     __syncthreads();
-  }
+  };
+
+  g.stage_idx(chunk0, CPS, sidx);
+  load_q();
+  __syncthreads();
+  constexpr int PF = CPS < 2 ? CPS : 2;
+  pipeline<CPS, PF>(
+      [&](int c, uint2 (&r)[8]) __attribute__((always_inline)) {
+        return g.load(chunk0 + c, chunk0, sidx, r);
+      },
+      chunk);
 
   // lane holds head 16*wave + col, channels 16*dt + 4*grp .. +3
   const int head = wave * 16 + col;
@@ -235,11 +408,9 @@ __global__ __launch_bounds__(kThreads) void k_sparse_attn(AttnArgs a) {
     const float inv = l_run > 0.0f ? 1.0f / l_run : 0.0f;
     float* o = a.out + ((size_t)qi * kHeads + head) * kDim + 4 * grp;
 #pragma unroll
-    for (int dt = 0; dt < 32; ++dt) {
-      const float4 v = make_float4(acc[dt][0] * inv, acc[dt][1] * inv, acc[dt][2] * inv,
-                                   acc[dt][3] * inv);
-      *reinterpret_cast<float4*>(o + dt * 16) = v;
-    }
+    for (int dt = 0; dt < 32; ++dt)
+      *reinterpret_cast<float4*>(o + dt * 16) =
+          make_float4(acc[dt][0] * inv, acc[dt][1] * inv, acc[dt][2] * inv, acc[dt][3] * inv);
   } else {
     const size_t ps = (size_t)qi * a.splits + split;
     float* o = a.part + (ps * kHeads + head) * kDim + 4 * grp;
@@ -247,6 +418,132 @@ __global__ __launch_bounds__(kThreads) void k_sparse_attn(AttnArgs a) {
     for (int dt = 0; dt < 32; ++dt)
       *reinterpret_cast<float4*>(o + dt * 16) = make_float4(acc[dt][0], acc[dt][1], acc[dt][2], acc[dt][3]);
     if (grp == 0) {
+      a.part_ml[(ps * kHeads + head) * 2 + 0] = m_run;
+      a.part_ml[(ps * kHeads + head) * 2 + 1] = l_run;
+    }
+  }
+}
+
+// ---------------------------------------------------------- decode kernel --
+
+template <int CPS>
+__global__ __launch_bounds__(kThreads) void k_sparse_attn_decode(AttnArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t krow[kChunkKeys * kKrowStride];
+  __shared__ __attribute__((aligned(16))) uint16_t vt[kDim * kVtRowHalves];
+  __shared__ float spart[2][4][kChunkKeys][kHG + 1];
+  __shared__ int kvalid[2][kChunkKeys];
+  __shared__ float qmax[4][kHG];
+  __shared__ __attribute__((aligned(16))) int32_t sidx[CPS * kChunkKeys];
+
+  const int qi = blockIdx.y;
+  const int hg = blockIdx.x % kHeadGroups;
+  const int split = blockIdx.x / kHeadGroups;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int col = lane & 15, grp = lane >> 4;
+  Gather g;
+  g.init(a, qi);
+  const int chunk0 = split * CPS;
+
+  v4f acc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc[i] = v4f{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.0f;
+  v8h qreg[4];
+  float zscale = 1.0f;
+
+  // One chunk: gather this wave's channel quarter, partial Q.K, exchange the
+  // partials, softmax, P.V on this wave's 128 output channels. The krow / vt
+  // regions a wave writes are the ones it reads, so only the partials need a
+  // work-group barrier (double-buffered, one barrier per chunk).
+  auto chunk = [&](int c, const uint2 (&r)[8], uint32_t ok) __attribute__((always_inline)) {
+    const int buf = c & 1;
+    g.store((chunk0 + c) * kChunkKeys < kTopK, r, ok, krow, vt, kvalid[buf]);
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+      v4f s = {0.f, 0.f, 0.f, 0.f};
+      const uint16_t* kr = &krow[(mt * 16 + col) * kKrowStride + wave * 128 + grp * 8];
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        const uint4 v = *reinterpret_cast<const uint4*>(kr + kb * 32);
+        s = __builtin_amdgcn_mfma_f32_16x16x32_f16(*reinterpret_cast<const v8h*>(&v), qreg[kb], s,
+                                                   0, 0, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) spart[buf][wave][mt * 16 + 4 * grp + i][col] = s[i];
+    }
+    __syncthreads();
+    float z[8];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int key = mt * 16 + 4 * grp + i;
+        const float sv = ((spart[buf][0][key][col] + spart[buf][1][key][col]) +
+                          spart[buf][2][key][col]) + spart[buf][3][key][col];
+        z[mt * 4 + i] = kvalid[buf][key] ? sv * zscale : -INFINITY;
+      }
+    v8h p_hi, p_lo;
+    const float alpha = softmax_step(z, m_run, l_run, p_hi, p_lo);
+    if (__any(alpha != 1.0f)) {
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) acc[dt] *= alpha;
+    }
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+      const v8h v = vt_operand(vt, wave * 128 + dt * 16 + col, grp);
+      acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(v, p_hi, acc[dt], 0, 0, 0);
+      acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(v, p_lo, acc[dt], 0, 0, 0);
+    }
+  };
+  // The wave's quarter of its 16 heads' query (channels 128*wave + kb*32 +
+  // grp*8 .. +7) in fp16 after the head's shift; the four waves agree on the
+  // per-head maximum through LDS.
+  auto load_q = [&]() __attribute__((always_inline)) {
+    const uint16_t* qp = a.q + ((size_t)qi * kHeads + hg * kHG + col) * kDim + wave * 128 + grp * 8;
+    uint4 raw[4];
+    float amax = 0.0f;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      raw[kb] = *reinterpret_cast<const uint4*>(qp + kb * 32);
+      amax = fmaxf(amax, bf16x8_absmax(raw[kb]));
+    }
+    amax = fmaxf(amax, wave_shfl_xor(amax, 16));
+    amax = fmaxf(amax, wave_shfl_xor(amax, 32));
+    if (grp == 0) qmax[wave][col] = amax;
+    __syncthreads();
+    amax = fmaxf(fmaxf(qmax[0][col], qmax[1][col]), fmaxf(qmax[2][col], qmax[3][col]));
+    const int sh = q_shift(amax);
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) qreg[kb] = q_to_f16(raw[kb], sh);
+    zscale = ldexpf(a.scale, -sh);
+  };
+
+  g.stage_idx(chunk0, CPS, sidx);
+  load_q();   // ends with a barrier, which also publishes sidx
+  constexpr int PF = CPS < 4 ? CPS : 4;
+  pipeline<CPS, PF>(
+      [&](int c, uint2 (&r)[8]) __attribute__((always_inline)) {
+        return g.load(chunk0 + c, chunk0, sidx, r);
+      },
+      chunk);
+
+  // lane holds head 16*hg + col, channels 128*wave + 16*dt + 4*grp .. +3
+  const int head = hg * kHG + col;
+  const int splits = gridDim.x / kHeadGroups;
+  if (splits == 1) {
+    const float inv = l_run > 0.0f ? 1.0f / l_run : 0.0f;
+    float* o = a.out + ((size_t)qi * kHeads + head) * kDim + wave * 128 + 4 * grp;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt)
+      *reinterpret_cast<float4*>(o + dt * 16) =
+          make_float4(acc[dt][0] * inv, acc[dt][1] * inv, acc[dt][2] * inv, acc[dt][3] * inv);
+  } else {
+    const size_t ps = (size_t)qi * splits + split;
+    float* o = a.part + (ps * kHeads + head) * kDim + wave * 128 + 4 * grp;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt)
+      *reinterpret_cast<float4*>(o + dt * 16) = make_float4(acc[dt][0], acc[dt][1], acc[dt][2], acc[dt][3]);
+    if (grp == 0 && wave == 0) {
       a.part_ml[(ps * kHeads + head) * 2 + 0] = m_run;
       a.part_ml[(ps * kHeads + head) * 2 + 1] = l_run;
     }
@@ -282,21 +579,37 @@ __global__ __launch_bounds__(128) void k_attn_merge(const float* __restrict__ pa
       make_float4(o.x * inv, o.y * inv, o.z * inv, o.w * inv);
 }
 
-int choose_splits(int Q) {
-  // enough work-groups to cover the chip; splits divide the 20 chunks
-  static const int opts[] = {1, 2, 4, 5, 10, 20};
-  int best = 1;
-  for (int s : opts)
-    if ((int64_t)Q * best < 512) best = s;
-  return best;
+// Work shape per query count: (kernel, slices). Slices divide the 20 chunks.
+struct Shape {
+  bool wide;
+  int splits;
+};
+
+Shape attn_shape(int Q) {
+  // Measured on MI355X (graph-replayed, 1M-entry caches): up to 16 queries the
+  // 16-head work-groups over 5 slices are fastest (8 queries: 22 us vs 25 us
+  // for the best 64-head shape); up to 512 queries the 64-head work-groups over
+  // 4 slices (64 queries: 49 us vs 67 us); beyond that one slice per query.
+  Shape sh;
+  if (Q <= 16) {
+    sh.wide = false;
+    sh.splits = 5;
+  } else if (Q < kWideMinQueries) {
+    sh.wide = true;
+    sh.splits = 4;
+  } else {
+    sh.wide = true;
+    sh.splits = 1;
+  }
+  return sh;
 }
 
 }  // namespace
 
 size_t attn_workspace_bytes(int Q) {
-  const int s = choose_splits(Q);
-  if (s == 1) return 0;
-  return (size_t)Q * s * kHeads * (kDim + 2) * sizeof(float);
+  const Shape sh = attn_shape(Q);
+  if (sh.splits == 1) return 0;
+  return (size_t)Q * sh.splits * kHeads * (kDim + 2) * sizeof(float);
 }
 
 hipError_t launch_sparse_attn(const uint16_t* q, const uint8_t* cache, const int32_t* idx,
@@ -316,10 +629,35 @@ hipError_t launch_sparse_attn(const uint16_t* q, const uint8_t* cache, const int
   a.S = S;
   a.scale = scale;
   a.out = out;
-  a.splits = choose_splits(Q);
-  a.part = reinterpret_cast<float*>(ws);
-  a.part_ml = a.part + (size_t)Q * a.splits * kHeads * kDim;
-  hipLaunchKernelGGL(k_sparse_attn, dim3(a.splits, Q), dim3(kThreads), 0, st, a);
+  a.part = nullptr;
+  a.part_ml = nullptr;
+  const Shape sh = attn_shape(Q);
+  a.splits = sh.splits;
+  if (a.splits > 1) {
+    a.part = reinterpret_cast<float*>(ws);
+    a.part_ml = a.part + (size_t)Q * a.splits * kHeads * kDim;
+  }
+  if (sh.wide) {
+    const dim3 grid(a.splits, Q);
+    switch (kChunks / a.splits) {
+      case 1: hipLaunchKernelGGL(k_sparse_attn_wide<1>, grid, dim3(kThreads), 0, st, a); break;
+      case 2: hipLaunchKernelGGL(k_sparse_attn_wide<2>, grid, dim3(kThreads), 0, st, a); break;
+      case 4: hipLaunchKernelGGL(k_sparse_attn_wide<4>, grid, dim3(kThreads), 0, st, a); break;
+      case 5: hipLaunchKernelGGL(k_sparse_attn_wide<5>, grid, dim3(kThreads), 0, st, a); break;
+      case 10: hipLaunchKernelGGL(k_sparse_attn_wide<10>, grid, dim3(kThreads), 0, st, a); break;
+      default: hipLaunchKernelGGL(k_sparse_attn_wide<20>, grid, dim3(kThreads), 0, st, a); break;
+    }
+  } else {
+    const dim3 grid(a.splits * kHeadGroups, Q);
+    switch (kChunks / a.splits) {
+      case 1: hipLaunchKernelGGL(k_sparse_attn_decode<1>, grid, dim3(kThreads), 0, st, a); break;
+      case 2: hipLaunchKernelGGL(k_sparse_attn_decode<2>, grid, dim3(kThreads), 0, st, a); break;
+      case 4: hipLaunchKernelGGL(k_sparse_attn_decode<4>, grid, dim3(kThreads), 0, st, a); break;
+      case 5: hipLaunchKernelGGL(k_sparse_attn_decode<5>, grid, dim3(kThreads), 0, st, a); break;
+      case 10: hipLaunchKernelGGL(k_sparse_attn_decode<10>, grid, dim3(kThreads), 0, st, a); break;
+      default: hipLaunchKernelGGL(k_sparse_attn_decode<20>, grid, dim3(kThreads), 0, st, a); break;
+    }
+  }
   if (a.splits > 1)
     hipLaunchKernelGGL(k_attn_merge, dim3(kHeads, Q), dim3(128), 0, st, a.part, a.part_ml,
                        a.splits, out);

@@ -116,7 +116,11 @@ def test_attn_and_quantize_reject_bad_arguments():
     bad = list(args)
     bad[2] = None
     assert f(*bad, 1, 1, 100, 128, ctypes.c_float(1.0), _p(FAKE), _p(FAKE), 1 << 30, None) == C.CSA2_EINVAL
-    assert f(*args, 100, 1, 100, 128, ctypes.c_float(1.0), _p(FAKE), None, 0, None) == C.CSA2_EWORKSPACE
+    # a single decode query is split over key slices, so it needs a workspace;
+    # without one the call must be rejected before any launch
+    assert C.csa2_workspace_bytes(C.CSA2_OP_SPARSE_ATTN, 0, 1, 1, 100) > 0
+    assert f(*args, 1, 1, 100, 128, ctypes.c_float(1.0), _p(FAKE), None, 0, None) == C.CSA2_EWORKSPACE
+    assert f(*args, 1, 1, 100, 128, ctypes.c_float(1.0), _p(FAKE), _p(FAKE), 64, None) == C.CSA2_EWORKSPACE
     q = C.lib().csa2_quantize_kv
     assert q(_p(FAKE), _p(FAKE), None, -1, _p(FAKE), 10, None) == C.CSA2_EINVAL
     assert q(_p(FAKE), _p(FAKE), None, 11, _p(FAKE), 10, None) == C.CSA2_EINVAL   # rows beyond the cache

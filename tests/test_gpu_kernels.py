@@ -221,7 +221,7 @@ def test_topk_reindex_and_reuse():
     assert to_np(dst).tobytes() == got.tobytes() and to_np(idx).tobytes() == got.tobytes()
 
 
-@pytest.mark.parametrize("n_cap", [9000, 100001])
+@pytest.mark.parametrize("n_cap", [9000, 100001, 200003])
 def test_build_pool_bitexact(n_cap):
     B, T = 2, 2
     nv = np.array([[n_cap, n_cap - 3], [1, 16385]], dtype=np.int32)
