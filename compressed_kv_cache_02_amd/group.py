@@ -86,17 +86,33 @@ class LayerGroup:
         dst_slot [n]) runs the write path first. hooks: optional dict of
         callables ('scan_begin', 'scan_end') run around the Full-layer scan."""
         hooks = hooks or {}
+        self.write(cache, write, stream=stream)
+        if "scan_begin" in hooks:
+            hooks["scan_begin"]()
+        self.scan(k_idx, n_vis, q_idx, w, stream=stream)
+        if "scan_end" in hooks:
+            hooks["scan_end"]()
+        self.rest(k_idx, cache, n_vis, q_pos, swa_pos0, q_idx, w, q, swa, scale, stream=stream)
+        return self.out
+
+    def write(self, cache, write, stream=None):
+        """The write path: new rows RoPE'd, packed to FP4 and stored."""
         if write is not None:
             kv, cs, slot = write
             csa2_quantize_kv(kv, cs, slot, cache, stream=stream)
+
+    def scan(self, k_idx, n_vis, q_idx, w, stream=None):
+        """The Full layer's scan of every visible position (with block maxima
+        when the group has Reindex layers)."""
+        li = [i for i, (m, _) in enumerate(self.sched) if m == FULL][0]
+        csa2_index_score(CSA2_FULL, q_idx[li], w[li], k_idx, n_vis, None, self.scores, self.bmax,
+                         stream=stream)
+
+    def rest(self, k_idx, cache, n_vis, q_pos, swa_pos0, q_idx, w, q, swa, scale=1.0,
+             stream=None):
+        """Everything after the Full scan: pool, Top-K per mode, attention per layer."""
         for li, (mode, src) in enumerate(self.sched):
             if mode == FULL:
-                if "scan_begin" in hooks:
-                    hooks["scan_begin"]()
-                csa2_index_score(CSA2_FULL, q_idx[li], w[li], k_idx, n_vis, None, self.scores,
-                                 self.bmax, stream=stream)
-                if "scan_end" in hooks:
-                    hooks["scan_end"]()
                 if self.pool is not None:
                     csa2_build_pool(self.bmax, True, n_vis, self.n_cap, self.pool, self.ws,
                                     stream=stream)
@@ -116,4 +132,3 @@ class LayerGroup:
                           None, stream=stream)
             csa2_sparse_attn(q[li], cache, self.idx[li], swa[li], q_pos, swa_pos0, scale,
                              self.out[li], self.ws, stream=stream)
-        return self.out
