@@ -1,10 +1,7 @@
 """End-to-end GPU parity of layer-group steps (the whole hot path) against the
 oracle: Full / Reindex / Reuse layers, the pool, the write path, attention.
 
-Top-K sets are compared under the near-tie rule on the oracle's scores;
-attention outputs are compared for every query whose index set equals the
-oracle's (a near-tie swap changes which row is attended, so such a query is
-counted and only its indices are checked)."""
+The comparison rules are those of tests/group_check.py."""
 
 import numpy as np
 import pytest
@@ -12,12 +9,9 @@ import torch
 
 import compressed_kv_cache_02_amd as C
 from compressed_kv_cache_02_amd.group import LayerGroup, visible_entries
-from oracle import group as OG
-from oracle import indexer as OI
-from oracle.compress import n_visible
-import synth
 from synth.configs import WORKLOADS, make_inputs, scaled
-from tests.helpers import (NEAR_TIE, OracleCache, assert_attn_close, assert_topk_near, to_np)
+from tests.group_check import check_queries
+from tests.helpers import OracleCache, to_np
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -47,53 +41,11 @@ def run_gpu(w, inp, B, write=None):
     return g, cache
 
 
-def check_group(w, inp, g, B, main_rows_np_override=None):
-    """Compare every layer of every query with the oracle."""
-    sched = OG.layer_schedule(w.kind)
-    n_attn_checked = n_swaps = 0
-    kn = to_np(inp["k_idx"])
-    for b in range(B):
-        oc = OracleCache(inp["main"][b], w.m)
-        if main_rows_np_override is not None:
-            oc.cache.update(main_rows_np_override(b))
-        for t in range(w.T):
-            tq = w.q_positions[t]
-            nv = int(n_visible(tq, w.m))
-            qi = {li: to_np(inp["q_idx"][li])[b, t] for li in inp["q_idx"]}
-            wi = {li: to_np(inp["w"][li])[b, t] for li in inp["w"]}
-            q = {li: inp["q"][li][b, t].float().cpu().numpy() for li in range(len(sched))}
-            swa = {li: to_np(inp["swa"][li])[b] for li in range(len(sched))}
-            o_idx, o_out, o_pool, o_scores = OG.run_group(sched, qi, wi, q, swa, kn[b], oc, nv, tq,
-                                                          w.swa_pos0)
-            pool_g = to_np(g.pool)[b, t] if g.pool is not None else None
-            pool_diff = set()
-            if pool_g is not None:
-                bm = OI.block_max(o_scores[0], nv)
-                a, o = set(pool_g[pool_g >= 0].tolist()), set(o_pool[o_pool >= 0].tolist())
-                pool_diff = a ^ o
-                if pool_diff:
-                    kth = min(float(bm[x]) for x in o)
-                    for x in pool_diff:
-                        assert abs(float(bm[x]) - kth) <= NEAR_TIE * abs(kth), ("pool", b, t, x)
-            for li, (mode, src) in enumerate(sched):
-                gi = to_np(g.idx[li])[b, t]
-                if mode == OG.FULL:
-                    s = o_scores[li]
-                    n_swaps += assert_topk_near(gi, o_idx[li], lambda p: s[p],
-                                                what="F b%d t%d" % (b, t))
-                elif mode == OG.REINDEX:
-                    cand, s = o_scores[li]
-                    full = OI.index_scores(qi[li], wi[li], kn[b], nv)   # all positions
-                    n_swaps += assert_topk_near(
-                        gi, o_idx[li], lambda p: full[p],
-                        extra_allowed=lambda p: (p // 8) in pool_diff,
-                        what="X%d b%d t%d" % (li, b, t))
-                else:
-                    assert gi.tobytes() == to_np(g.idx[src])[b, t].tobytes()
-                if np.array_equal(gi, o_idx[li]):
-                    assert_attn_close(to_np(g.out[li])[b, t], o_out[li], "L%d b%d t%d" % (li, b, t))
-                    n_attn_checked += 1
-    return n_attn_checked, n_swaps
+def check_group(w, inp, g, B):
+    """Compare every query of every sequence with the oracle."""
+    samples = [(b, t) for b in range(B) for t in range(w.T)]
+    return check_queries(w, inp, g, samples, lambda b: OracleCache(inp["main"][b], w.m),
+                         log=lambda *a: None)
 
 
 def _inputs(w, B, seed=0):
