@@ -56,6 +56,30 @@ __device__ __forceinline__ v8i as_v8i(const uint4& a, const uint4& b) {
   return r;
 }
 
+// max(x, 0) as one integer max on the bit pattern: every negative float
+// (including -0) is a negative int32 and maps to +0; non-negative floats keep
+// their bits. (fmaxf costs an extra canonicalising instruction per value.)
+__device__ __forceinline__ float relu_bits(float x) {
+  return __int_as_float(max(__float_as_int(x), 0));
+}
+
+// Maximum over each aligned group of 8 lanes (a pool block of 8 positions),
+// with DPP lane moves: swap neighbours, swap pairs, then mirror within 8 lanes.
+__device__ __forceinline__ float max_over_8_lanes(float m) {
+  m = fmaxf(m, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(m), 0xB1, 0xF, 0xF, false)));
+  m = fmaxf(m, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(m), 0x4E, 0xF, 0xF, false)));
+  m = fmaxf(m, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(m), 0x141, 0xF, 0xF, false)));
+  return m;
+}
+
+// sum over the lane's 16 accumulator rows of w_r * relu(acc_r), in row order
+__device__ __forceinline__ float weighted_relu_sum(const v16f& acc, const float* wr) {
+  float part = 0.0f;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) part = fmaf(wr[r], relu_bits(acc[r]), part);
+  return part;
+}
+
 template <int MODE>
 __global__ __launch_bounds__(256) void k_index_score_decode(
     const uint8_t* __restrict__ q_idx, const float* __restrict__ w,
@@ -130,23 +154,240 @@ __global__ __launch_bounds__(256) void k_index_score_decode(
                                                             0, 0, 0, 0, 0, 0);
       acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a1, as_v8i(cur.v[2], cur.v[3]), acc,
                                                             0, 0, 0, 0, 0, 0);
-      float part = 0.0f;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) part = fmaf(wr[r], fmaxf(acc[r], 0.0f), part);
+      float part = weighted_relu_sum(acc, wr);
       part += wave_shfl_xor(part, 32);
       if (cur_ok) s = part;
     }
     const int64_t item = tile0 + col;
     if (half == 0 && item < n_items) srow[item] = s;
     if (brow) {
-      float m = s;
-      m = fmaxf(m, wave_shfl_xor(m, 1));
-      m = fmaxf(m, wave_shfl_xor(m, 2));
-      m = fmaxf(m, wave_shfl_xor(m, 4));
+      const float m = max_over_8_lanes(s);
       if (half == 0 && (col & 7) == 0 && item < n_items) brow[item >> 3] = m;
     }
     cur = nxt;
     cur_ok = nxt_ok;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Prefill shape: many queries share each sequence's keys, so the scan is a
+// dense FP8 contraction of (queries x 32 heads) x 128 against positions x 128,
+// followed by the ReLU-weighted head sum. A work-group of 8 waves takes 32
+// consecutive queries of one sequence (4 per wave, their A operands and head
+// weights held in registers) and 4,096 positions, streamed through LDS in
+// double-buffered chunks of 256 keys (32 KiB each) so every key byte read from
+// L2 feeds 32 queries. The 16-byte pieces of a key row are stored at piece
+// index (p ^ (row & 7)), which makes the B-operand reads (8 consecutive rows
+// per lane group) and the chunk writes conflict-free. Per 32-position tile and
+// query: two MFMAs, then 16 max + 16 fma per lane; the two half-sums of a
+// query pair are combined with one v_permlane32_swap (lanes 0..31 end up with
+// the first query's 32 scores, lanes 32..63 with the second's), so each store
+// writes 2 x 128 contiguous bytes. The arithmetic per score is the same
+// sequence as in the decode kernel, so both produce identical bits.
+constexpr int kPfQPerWave = 4;
+constexpr int kPfWaves = 8;
+constexpr int kPfThreads = kPfWaves * 64;
+constexpr int kPfQueries = kPfQPerWave * kPfWaves;   // 32
+constexpr int kPfChunk = 256;                        // keys per LDS chunk
+constexpr int kPfChunksPerWG = 16;
+constexpr int kPfKeysPerWG = kPfChunk * kPfChunksPerWG;   // 4096
+constexpr int kPfPieces = kPfChunk * (kIdxDim / 16);      // 2048 16-byte pieces
+constexpr int kPfLoads = (kPfPieces + kPfThreads - 1) / kPfThreads;
+
+template <bool BMAX>
+__global__ __launch_bounds__(kPfThreads) void k_index_score_prefill(
+    const uint8_t* __restrict__ q_idx, const float* __restrict__ w,
+    const uint8_t* __restrict__ k_idx, const int32_t* __restrict__ n_vis, int T, int64_t n_cap,
+    int n_kb, int n_qb, float* __restrict__ scores, float* __restrict__ bmax) {
+  __shared__ uint4 lds[2][kPfPieces];
+  const int kb = blockIdx.x % n_kb;
+  const int rest = blockIdx.x / n_kb;
+  const int qb = rest % n_qb;
+  const int b = rest / n_qb;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
+  const int half = lane >> 5;
+  const int col = lane & 31;
+  const int64_t n_blk = (n_cap + kBlock - 1) / kBlock;
+
+  // this wave's queries (clamped for loads; stores check t < T)
+  int tq[kPfQPerWave];
+  int64_t nv[kPfQPerWave];
+  v8i a0[kPfQPerWave], a1[kPfQPerWave];
+  float wr[kPfQPerWave][16];
+  int64_t nv_max = 0;
+#pragma unroll
+  for (int q = 0; q < kPfQPerWave; ++q) {
+    tq[q] = qb * kPfQueries + wave * kPfQPerWave + q;
+    const int tc = tq[q] < T ? tq[q] : T - 1;
+    const size_t qi = (size_t)b * T + tc;
+    int64_t v = n_vis[qi];
+    v = v < 0 ? 0 : (v > n_cap ? n_cap : v);
+    nv[q] = tq[q] < T ? v : 0;
+    nv_max = nv[q] > nv_max ? nv[q] : nv_max;
+    const uint4* q4 = reinterpret_cast<const uint4*>(q_idx + qi * (kIdxHeads * kIdxDim) +
+                                                     col * kIdxDim + half * 64);
+    a0[q] = as_v8i(q4[0], q4[1]);
+    a1[q] = as_v8i(q4[2], q4[3]);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) wr[q][r] = w[qi * kIdxHeads + acc32_row(lane, r)];
+  }
+
+  const int64_t key0 = (int64_t)kb * kPfKeysPerWG;
+  int64_t span = n_cap - key0;
+  span = span < kPfKeysPerWG ? span : kPfKeysPerWG;
+  const int n_chunks = (int)((span + kPfChunk - 1) / kPfChunk);
+  const uint8_t* kseq = k_idx + (size_t)b * (size_t)n_cap * kIdxDim;
+
+  uint4 pre[kPfLoads];
+  auto load_chunk = [&](int c) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < kPfLoads; ++i) {
+      const int p = tid + i * kPfThreads;
+      const int64_t row = key0 + (int64_t)c * kPfChunk + (p >> 3);
+      pre[i] = (p < kPfPieces && row < n_cap)
+                   ? *reinterpret_cast<const uint4*>(kseq + row * kIdxDim + (p & 7) * 16)
+                   : make_uint4(0, 0, 0, 0);
+    }
+  };
+  auto store_chunk = [&](int buf) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < kPfLoads; ++i) {
+      const int p = tid + i * kPfThreads;
+      const int row = p >> 3;
+      if (p < kPfPieces) lds[buf][row * 8 + ((p & 7) ^ (row & 7))] = pre[i];
+    }
+  };
+
+  // B operand of tile tt of an LDS chunk (32 keys; this lane's 64 bytes)
+  auto load_b = [&](const uint4* L, int tt, v8i& b0, v8i& b1) __attribute__((always_inline)) {
+    const int row = tt * kTilePos + col;
+    const int sw = row & 7;
+    b0 = as_v8i(L[row * 8 + ((half * 4 + 0) ^ sw)], L[row * 8 + ((half * 4 + 1) ^ sw)]);
+    b1 = as_v8i(L[row * 8 + ((half * 4 + 2) ^ sw)], L[row * 8 + ((half * 4 + 3) ^ sw)]);
+  };
+  auto mfma2 = [&](int q, const v8i& b0, const v8i& b1) __attribute__((always_inline)) -> v16f {
+    v16f acc = {};
+    acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a0[q], b0, acc, 0, 0, 0, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a1[q], b1, acc, 0, 0, 0, 0, 0, 0);
+    return acc;
+  };
+  // Combine the four queries' half sums of one tile and store them (with the
+  // block maxima when requested). Lanes 0..31 take query 2qp, 32..63 query
+  // 2qp+1 after the swap.
+  auto emit = [&](int64_t tile0, const float* p) __attribute__((always_inline)) {
+    const int64_t key = tile0 + col;
+#pragma unroll
+    for (int qp = 0; qp < kPfQPerWave / 2; ++qp) {
+      const auto sw2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(p[2 * qp]),
+                                                        __float_as_uint(p[2 * qp + 1]), false, false);
+      float s = __uint_as_float(sw2[0]) + __uint_as_float(sw2[1]);
+      const int64_t nvq = half ? nv[2 * qp + 1] : nv[2 * qp];
+      const int tqq = half ? tq[2 * qp + 1] : tq[2 * qp];
+      if (key >= nvq) s = -INFINITY;
+      const bool store = tqq < T && key < n_cap;
+      const size_t qi = (size_t)b * T + (size_t)tqq;
+      if (store) scores[qi * (size_t)n_cap + key] = s;
+      if (BMAX) {
+        const float m = max_over_8_lanes(s);
+        if (store && (col & 7) == 0) bmax[qi * (size_t)n_blk + (key >> 3)] = m;
+      }
+    }
+  };
+
+  // Stores of a fast-path tile: every query of the wave is real and every key
+  // below n_cap, so the chunk's code is one basic block (no exec branches).
+  // Per chunk each lane keeps one score pointer and one visibility limit per
+  // query pair; tile t then stores at a constant offset.
+  constexpr int kPairs = kPfQPerWave / 2;
+  float* sp[kPairs];
+  float* bp[kPairs];
+  int lim[kPairs];
+  auto chunk_setup = [&](int64_t chunk0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int qp = 0; qp < kPairs; ++qp) {
+      const int64_t nvq = half ? nv[2 * qp + 1] : nv[2 * qp];
+      const int tqq = half ? tq[2 * qp + 1] : tq[2 * qp];
+      const size_t qi = (size_t)b * T + (size_t)tqq;
+      sp[qp] = scores + qi * (size_t)n_cap + chunk0 + col;
+      if (BMAX) bp[qp] = bmax + qi * (size_t)n_blk + ((chunk0 + col) >> 3);
+      int64_t l = nvq - chunk0 - col;
+      lim[qp] = (int)(l < -1 ? -1 : (l > kPfChunk ? kPfChunk : l));
+    }
+  };
+  auto emit_fast = [&](int t, const float* p) __attribute__((always_inline)) {
+#pragma unroll
+    for (int qp = 0; qp < kPairs; ++qp) {
+      const auto sw2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(p[2 * qp]),
+                                                        __float_as_uint(p[2 * qp + 1]), false, false);
+      float s = __uint_as_float(sw2[0]) + __uint_as_float(sw2[1]);
+      s = t * kTilePos < lim[qp] ? s : -INFINITY;
+      sp[qp][t * kTilePos] = s;
+      if (BMAX) {
+        const float m = max_over_8_lanes(s);
+        if ((col & 7) == 0) bp[qp][t * (kTilePos / kBlock)] = m;
+      }
+    }
+  };
+  const bool wave_full = tq[kPfQPerWave - 1] < T;
+
+  constexpr int kTiles = kPfChunk / kTilePos;     // 8
+  load_chunk(0);
+  store_chunk(0);
+  __syncthreads();
+  for (int c = 0; c < n_chunks; ++c) {
+    if (c + 1 < n_chunks) load_chunk(c + 1);
+    const uint4* L = lds[c & 1];
+    const int64_t chunk0 = key0 + (int64_t)c * kPfChunk;
+    if (wave_full && chunk0 + kPfChunk <= n_cap && chunk0 < nv_max) {
+      // Whole chunk in range: a flat software pipeline over the 32 (tile,
+      // query) steps; step j+1's MFMAs are issued before step j's epilogue, and
+      // the next tile's B operand is read from LDS as soon as the last MFMA on
+      // the current one has been issued.
+      v8i bb0, bb1;
+      v16f acc[2];
+      float p[kPfQPerWave];
+      chunk_setup(chunk0);
+      load_b(L, 0, bb0, bb1);
+      acc[0] = mfma2(0, bb0, bb1);
+#pragma unroll
+      for (int j = 0; j < kTiles * kPfQPerWave; ++j) {
+        const int t = j / kPfQPerWave, q = j % kPfQPerWave;
+        if (j + 1 < kTiles * kPfQPerWave) {
+          const int t1 = (j + 1) / kPfQPerWave, q1 = (j + 1) % kPfQPerWave;
+          acc[(j + 1) & 1] = mfma2(q1, bb0, bb1);
+          // the last MFMA on tile t1 is issued: fetch the next tile's operand
+          if (q1 == kPfQPerWave - 1 && t1 + 1 < kTiles) load_b(L, t1 + 1, bb0, bb1);
+        }
+        // Keep this order: the epilogue below reads results issued one step
+        // earlier, so it runs on the vector ALU while the matrix core works
+        // on the MFMAs just issued.
+        __builtin_amdgcn_sched_barrier(0);
+        p[q] = weighted_relu_sum(acc[j & 1], wr[q]);
+        if (q == kPfQPerWave - 1) emit_fast(t, p);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    } else {
+      // Ragged last chunk, or nothing visible to this wave's queries.
+      for (int tt = 0; tt < kTiles; ++tt) {
+        const int64_t tile0 = chunk0 + tt * kTilePos;
+        if (tile0 >= n_cap) break;
+        float p[kPfQPerWave];
+        if (tile0 < nv_max) {
+          v8i b0, b1;
+          load_b(L, tt, b0, b1);
+#pragma unroll
+          for (int q = 0; q < kPfQPerWave; ++q) p[q] = weighted_relu_sum(mfma2(q, b0, b1), wr[q]);
+        } else {
+#pragma unroll
+          for (int q = 0; q < kPfQPerWave; ++q) p[q] = 0.0f;
+        }
+        emit(tile0, p);
+      }
+    }
+    if (c + 1 < n_chunks) store_chunk((c + 1) & 1);
+    __syncthreads();
   }
 }
 
@@ -173,8 +414,17 @@ hipError_t launch_index_score_decode(int mode, const uint8_t* q_idx, const float
 hipError_t launch_index_score_prefill(const uint8_t* q_idx, const float* w, const uint8_t* k_idx,
                                       const int32_t* n_vis, int B, int T, int64_t n_cap,
                                       float* scores, float* bmax, hipStream_t st) {
-  return launch_index_score_decode(0, q_idx, w, k_idx, n_vis, nullptr, B, T, n_cap, scores, bmax,
-                                   st);
+  const int n_kb = (int)((n_cap + kPfKeysPerWG - 1) / kPfKeysPerWG);
+  const int n_qb = (T + kPfQueries - 1) / kPfQueries;
+  const int64_t grid = (int64_t)n_kb * n_qb * B;
+  if (bmax) {
+    hipLaunchKernelGGL(k_index_score_prefill<true>, dim3((unsigned)grid), dim3(kPfThreads), 0, st,
+                       q_idx, w, k_idx, n_vis, T, n_cap, n_kb, n_qb, scores, bmax);
+  } else {
+    hipLaunchKernelGGL(k_index_score_prefill<false>, dim3((unsigned)grid), dim3(kPfThreads), 0, st,
+                       q_idx, w, k_idx, n_vis, T, n_cap, n_kb, n_qb, scores, bmax);
+  }
+  return hipGetLastError();
 }
 
 }  // namespace csa2

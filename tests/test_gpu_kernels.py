@@ -125,6 +125,44 @@ def test_index_score_full(B, T, n_cap):
             assert np.array_equal(bn[b, t], OI.block_max(sn[b, t], nv[b, t]))
 
 
+@pytest.mark.parametrize("B,T,n_cap", [(2, 77, 10003), (1, 64, 4096), (1, 130, 300)])
+def test_index_score_prefill_shape(B, T, n_cap):
+    """Many queries per sequence take the prefill kernel (a shared FP8
+    contraction); its scores and block maxima must equal, bit for bit, those of
+    the per-query decode kernel, and lie within the float32 bound of the oracle.
+    T and n_cap are ragged (not multiples of the 32-query / 4,096-key tiles)."""
+    _stage("index_score prefill", B, T, n_cap)
+    q, w, k = _idx_inputs(B, T, n_cap, 7 + n_cap)
+    rng = np.random.default_rng(T)
+    # causal-like visibility plus the extremes
+    nv = np.minimum(n_cap, (np.arange(T) + n_cap - T + 1)[None, :].repeat(B, 0)).astype(np.int32)
+    nv[0, 0] = 0
+    nv[0, 1] = 1
+    nv[-1, 2] = 33
+    nv[-1, -1] = n_cap
+    nv[0, 3:8] = rng.integers(0, n_cap + 1, 5)
+    n_vis = torch.from_numpy(nv).to(DEV)
+    nb = (n_cap + 7) // 8
+    scores = torch.empty((B, T, n_cap), dtype=torch.float32, device=DEV)
+    bmax = torch.empty((B, T, nb), dtype=torch.float32, device=DEV)
+    C.csa2_index_score(C.CSA2_FULL, q, w, k, n_vis, None, scores, bmax)
+    one_s = torch.empty((1, 1, n_cap), dtype=torch.float32, device=DEV)
+    one_b = torch.empty((1, 1, nb), dtype=torch.float32, device=DEV)
+    sn, bn = to_np(scores), to_np(bmax)
+    qn, wn, kn = to_np(q), to_np(w), to_np(k)
+    for b in range(B):
+        for t in range(T):
+            C.csa2_index_score(C.CSA2_FULL, q[b:b + 1, t:t + 1], w[b:b + 1, t:t + 1], k[b:b + 1],
+                               n_vis[b:b + 1, t:t + 1].clone(), None, one_s, one_b)
+            assert np.array_equal(to_np(one_s)[0, 0].view(np.uint32), sn[b, t].view(np.uint32)), (b, t)
+            assert np.array_equal(to_np(one_b)[0, 0].view(np.uint32), bn[b, t].view(np.uint32)), (b, t)
+    for b in range(B):
+        for t in sorted({0, 1, 2, T // 2, T - 1}):
+            ref = OI.index_scores(qn[b, t], wn[b, t], kn[b], nv[b, t])
+            assert_scores_close(sn[b, t], ref, score_bound(qn[b, t], wn[b, t], kn[b]),
+                                "b%d t%d" % (b, t))
+
+
 def test_index_score_reindex():
     _stage("index_score reindex")
     B, T, n_cap = 2, 2, 30000
