@@ -44,7 +44,7 @@ _SIGS = {
     "csa2_quantize_kv": (_i32, [_vp, _vp, _vp, _i64, _vp, _i64, _vp]),
     "csa2_index_score": (_i32, [_i32, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i64, _vp, _vp, _vp]),
     "csa2_build_pool": (_i32, [_vp, _i32, _vp, _i32, _i32, _i64, _vp, _vp, _sz, _vp]),
-    "csa2_topk": (_i32, [_i32, _vp, _vp, _vp, _vp, _i32, _i32, _i64, _vp, _vp, _sz, _vp]),
+    "csa2_topk": (_i32, [_i32, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i64, _vp, _vp, _sz, _vp]),
     "csa2_sparse_attn": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i64, _i32, _f32,
                                 _vp, _vp, _sz, _vp]),
 }
@@ -182,9 +182,11 @@ def csa2_build_pool(src, is_bmax, n_vis, n_cap, pool, ws, stream=None):
                                                     _stream(stream)))
 
 
-def csa2_topk(mode, scores, n_vis, pool, src_idx, n_cap, idx, ws, stream=None):
-    """idx [B,T,512] int32 written; FULL scores [B,T,n_cap], REINDEX scores
-    [B,T,16384] with pool [B,T,2048]; REUSE copies src_idx [B,T,512]."""
+def csa2_topk(mode, scores, n_vis, pool, src_idx, n_cap, idx, ws, stream=None, bmax=None):
+    """idx [B,T,512] int32 written; FULL scores [B,T,n_cap] (optional helpers:
+    bmax [B,T,ceil(n_cap/8)] and the pool [B,T,2048] built from the same
+    scores), REINDEX scores [B,T,16384] with pool [B,T,2048]; REUSE copies
+    src_idx [B,T,512]."""
     import torch
     B, T = idx.shape[0], idx.shape[1]
     _expect(idx, "idx", torch.int32, (B, T, TOPK))
@@ -194,9 +196,13 @@ def csa2_topk(mode, scores, n_vis, pool, src_idx, n_cap, idx, ws, stream=None):
         _expect(scores, "scores", torch.float32,
                 (B, T, n_cap if mode == CSA2_FULL else POOL_CAND))
         _expect(n_vis, "n_vis", torch.int32, (B, T))
-    _check("csa2_topk", lib().csa2_topk(mode, _p(scores), _p(n_vis), _p(pool), _p(src_idx), B, T,
-                                        n_cap, _p(idx), _p(ws), 0 if ws is None else ws.numel(),
-                                        _stream(stream)))
+        if pool is not None:
+            _expect(pool, "pool", torch.int32, (B, T, POOL_BLOCKS))
+        if bmax is not None:
+            _expect(bmax, "bmax", torch.float32, (B, T, (n_cap + BLOCK - 1) // BLOCK))
+    _check("csa2_topk", lib().csa2_topk(mode, _p(scores), _p(bmax), _p(n_vis), _p(pool),
+                                        _p(src_idx), B, T, n_cap, _p(idx), _p(ws),
+                                        0 if ws is None else ws.numel(), _stream(stream)))
 
 
 def csa2_sparse_attn(q, cache, idx, swa, q_pos, swa_pos0, scale, out, ws, stream=None):

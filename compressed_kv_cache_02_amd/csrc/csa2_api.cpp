@@ -30,10 +30,6 @@ inline int status_of(hipError_t e) { return e == hipSuccess ? CSA2_OK : CSA2_EHI
 
 inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 
-size_t pool_bmax_bytes(int Q, int64_t n_cap) {
-  return round_up((size_t)Q * (size_t)((n_cap + CSA2_BLOCK - 1) / CSA2_BLOCK) * sizeof(float));
-}
-
 }  // namespace
 
 extern "C" {
@@ -56,12 +52,10 @@ size_t csa2_workspace_bytes(int op, int mode, int B, int T, int64_t n_cap) {
   const int Q = B * T;
   switch (op) {
     case CSA2_OP_INDEX_SCORE: return 0;
-    case CSA2_OP_BUILD_POOL:
-      return pool_bmax_bytes(Q, n_cap) + round_up(csa2::select_workspace_bytes(Q, CSA2_POOL_BLOCKS));
+    case CSA2_OP_BUILD_POOL: return round_up(csa2::pool_workspace_bytes(Q, n_cap));
     case CSA2_OP_TOPK:
-      if (mode == CSA2_REUSE) return 0;
-      if (mode != CSA2_FULL && mode != CSA2_REINDEX) return 0;
-      return round_up(csa2::select_workspace_bytes(Q, CSA2_TOPK));
+      if (mode == CSA2_FULL) return round_up(csa2::topk_workspace_bytes(Q, n_cap));
+      return 0;
     case CSA2_OP_SPARSE_ATTN: return round_up(csa2::attn_workspace_bytes(Q));
     default: return 0;
   }
@@ -119,26 +113,17 @@ int csa2_build_pool(const float* src, int is_bmax, const int32_t* n_vis, int B, 
   if (!sizes_ok(B, T, n_cap)) return CSA2_EINVAL;
   if (!aligned16(src) || !aligned16(n_vis) || !aligned16(pool)) return CSA2_EINVAL;
   const size_t need = csa2_workspace_bytes(CSA2_OP_BUILD_POOL, 0, B, T, n_cap);
-  if (!aligned16(ws)) return ws ? CSA2_EINVAL : CSA2_EWORKSPACE;
-  if (ws_bytes < need) return CSA2_EWORKSPACE;
-  const int Q = B * T;
-  const int64_t n_blk = (n_cap + CSA2_BLOCK - 1) / CSA2_BLOCK;
-  hipStream_t st = as_stream(stream);
-  const float* bm = src;
-  if (!is_bmax) {
-    float* tmp = static_cast<float*>(ws);
-    hipError_t e = csa2::launch_block_max(src, n_vis, Q, n_cap, tmp, st);
-    if (e != hipSuccess) return CSA2_EHIP;
-    bm = tmp;
+  if (need > 0) {
+    if (!aligned16(ws)) return ws ? CSA2_EINVAL : CSA2_EWORKSPACE;
+    if (ws_bytes < need) return CSA2_EWORKSPACE;
   }
-  void* sel_ws = static_cast<uint8_t*>(ws) + pool_bmax_bytes(Q, n_cap);
-  return status_of(csa2::launch_select(csa2::kSelPool, bm, n_vis, nullptr, Q, n_blk, n_cap,
-                                       CSA2_POOL_BLOCKS, pool, sel_ws, st));
+  return status_of(csa2::launch_build_pool(src, is_bmax, n_vis, B * T, n_cap, pool, ws,
+                                           as_stream(stream)));
 }
 
-int csa2_topk(int mode, const float* scores, const int32_t* n_vis, const int32_t* pool,
-              const int32_t* src_idx, int B, int T, int64_t n_cap, int32_t* idx, void* ws,
-              size_t ws_bytes, void* stream) {
+int csa2_topk(int mode, const float* scores, const float* bmax, const int32_t* n_vis,
+              const int32_t* pool, const int32_t* src_idx, int B, int T, int64_t n_cap,
+              int32_t* idx, void* ws, size_t ws_bytes, void* stream) {
   if (!sizes_ok(B, T, n_cap)) return CSA2_EINVAL;
   if (!aligned16(idx)) return CSA2_EINVAL;
   const int Q = B * T;
@@ -150,14 +135,17 @@ int csa2_topk(int mode, const float* scores, const int32_t* n_vis, const int32_t
   }
   if (mode != CSA2_FULL && mode != CSA2_REINDEX) return CSA2_EINVAL;
   if (!aligned16(scores) || !aligned16(n_vis)) return CSA2_EINVAL;
-  if (mode == CSA2_REINDEX && !aligned16(pool)) return CSA2_EINVAL;
+  if (mode == CSA2_REINDEX) {
+    if (!aligned16(pool) || bmax) return CSA2_EINVAL;
+    return status_of(csa2::launch_topk_reindex(scores, pool, n_vis, Q, n_cap, idx, st));
+  }
+  if (!opt_aligned16(bmax) || !opt_aligned16(pool)) return CSA2_EINVAL;
   const size_t need = csa2_workspace_bytes(CSA2_OP_TOPK, mode, B, T, n_cap);
-  if (!aligned16(ws)) return ws ? CSA2_EINVAL : CSA2_EWORKSPACE;
-  if (ws_bytes < need) return CSA2_EWORKSPACE;
-  const int kind = mode == CSA2_FULL ? csa2::kSelFull : csa2::kSelReindex;
-  const int64_t n_items = mode == CSA2_FULL ? n_cap : (int64_t)CSA2_POOL_CAND;
-  return status_of(
-      csa2::launch_select(kind, scores, n_vis, pool, Q, n_items, n_cap, CSA2_TOPK, idx, ws, st));
+  if (need > 0) {
+    if (!aligned16(ws)) return ws ? CSA2_EINVAL : CSA2_EWORKSPACE;
+    if (ws_bytes < need) return CSA2_EWORKSPACE;
+  }
+  return status_of(csa2::launch_topk_full(scores, bmax, pool, n_vis, Q, n_cap, idx, ws, st));
 }
 
 int csa2_sparse_attn(const void* q_bf16, const uint8_t* cache, const int32_t* idx,

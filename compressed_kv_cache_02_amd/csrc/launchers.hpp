@@ -22,12 +22,17 @@ hipError_t launch_index_score_prefill(const uint8_t* q_idx, const float* w, cons
                                       const int32_t* n_vis, int B, int T, int64_t n_cap,
                                       float* scores, float* bmax, hipStream_t st);
 
-// Exact Top-K selection.
+// Exact Top-K selection (hierarchical; see select.hip).
 enum SelectKind { kSelFull = 0, kSelReindex = 1, kSelPool = 2 };
-size_t select_workspace_bytes(int Q, int K);
-hipError_t launch_select(int kind, const float* values, const int32_t* n_vis, const int32_t* pool,
-                         int Q, int64_t n_items, int64_t n_cap, int K, int32_t* out, void* ws,
-                         hipStream_t st);
+size_t topk_workspace_bytes(int Q, int64_t n_cap);
+size_t pool_workspace_bytes(int Q, int64_t n_cap);
+hipError_t launch_topk_full(const float* scores, const float* bmax, const int32_t* pool,
+                            const int32_t* n_vis, int Q, int64_t n_cap, int32_t* out, void* ws,
+                            hipStream_t st);
+hipError_t launch_topk_reindex(const float* scores_pool, const int32_t* pool, const int32_t* n_vis,
+                               int Q, int64_t n_cap, int32_t* out, hipStream_t st);
+hipError_t launch_build_pool(const float* src, int is_bmax, const int32_t* n_vis, int Q,
+                             int64_t n_cap, int32_t* pool, void* ws, hipStream_t st);
 hipError_t launch_block_max(const float* scores, const int32_t* n_vis, int Q, int64_t n_cap,
                             float* bmax, hipStream_t st);
 hipError_t launch_copy_i32(const int32_t* src, int32_t* dst, int64_t n, hipStream_t st);

@@ -9,17 +9,29 @@
 // 890 B/token", 第二刀 and Fig. 5). Ties go to the lower position and the result
 // is emitted in ascending order (the reading stated in csa2.h).
 //
-// Items are visited in position order (Full: item = position; Reindex: the
-// pool is ascending, so item order is position order; pool: item = block id).
+// Selection is exact at every step and hierarchical where inputs are large. A
+// position among the best 512 lies in one of the best 512 blocks of 8 (ranked
+// by block maximum, ties to the lower block): every block ranked ahead of its
+// block holds, as its maximum, a distinct position ranked ahead of it. The same
+// holds one level up for blocks inside super-blocks of 8 blocks. Hence
+//   Full Top-512 = the best 512 positions inside the best 512 blocks, found
+//                  inside the best 512 super-blocks (after the first, each
+//                  selection sees at most 4,096 candidates); or, when the group
+//                  has built the pool from the same scores, the best 512 of the
+//                  pool's 16,384 positions;
+//   pool         = the best 2,048 blocks inside the best 2,048 super-blocks.
+// It is the pages' hierarchical indexer applied once more, one level up.
 //
-// Small inputs (<= 16,384 items per query, e.g. every Reindex layer): one
-// work-group of 1,024 threads per query holds 16 consecutive items per thread
-// in registers, runs three histogram levels (bits 31..21, 20..10, 9..0) in LDS
-// to find the exact K-th key, takes the ties lowest-position first with a block
-// prefix sum, and writes the selection ascending with a second prefix sum (the
-// items are already in position order, so no sort is needed).
+// One selection = one work-group per query that holds up to 16 items per
+// thread in registers, in item order (= id order). It finds the exact K-th key
+// by radix select on order-preserving 32-bit keys; the digits are taken from
+// the offset to the smallest valid key, so the first level spreads values of
+// any range over its 2,048 bins and few LDS atomics collide. Ties are taken
+// lowest id first with a block prefix sum, and the selected ids are written
+// ascending with a second prefix sum (no sort).
 //
-// Large inputs: a grid over (chunk, query) per pass --
+// Inputs beyond 2^20 positions per query use a multi-pass radix path over the
+// raw values instead (a grid over chunks x queries):
 //   zero   -- clear the per-query histograms and counters (a fill kernel, safe
 //             to capture in a HIP graph);
 //   hist1  -- 2,048-bin histogram of key bits 31..21, then one work-group per
@@ -44,8 +56,6 @@ constexpr int kCandCap = 4096;
 constexpr int kThreads = 256;
 constexpr int kItemsPerThread = 16;
 constexpr int kChunk = kThreads * kItemsPerThread;   // 4096 items per work-group
-constexpr int kSmallThreads = 1024;
-constexpr int kSmallMax = kSmallThreads * kItemsPerThread;   // 16,384
 constexpr int kFinalThreads = 1024;
 
 // Per-query thresholds derived after each histogram pass.
@@ -176,63 +186,261 @@ __device__ __forceinline__ void hist_add(uint32_t* lh, uint32_t bin, bool pred) 
   if (pred) atomicAdd(&lh[bin], 1u);
 }
 
-// ------------------------------------------------------------ small inputs --
+// ------------------------------------------------- one query per work-group --
 
-__global__ __launch_bounds__(kSmallThreads) void k_sel_small(Items it, int K, int32_t* out) {
-  __shared__ uint32_t lh[kBins];
-  __shared__ uint32_t sh[kSmallThreads / 64 + 2];
-  const int q = blockIdx.x;
-  const int t = threadIdx.x;
-  const int64_t nv = it.visible(q);
-  const int32_t* pl = it.kind == kSelReindex ? it.pool + (size_t)q * kPoolBlocks : nullptr;
-  uint32_t key[kItemsPerThread], pos[kItemsPerThread];
+// Where one selection stage takes its items from.
+//   kDirect: item i is id i of a value row (visible while i < the limit);
+//   kChild:  item i is child (i % 8) of parent sel[i / 8] (ids ascending,
+//            -1 padded): id = 8 * parent + i % 8, visible while below the limit;
+//            its value is indexed by the item (Reindex scores) or by the id.
+enum SrcKind { kDirect = 0, kChild = 2 };
+
+struct Src {
+  const float* vals;     // value rows, vstride floats per query
+  int64_t vstride;
+  const int32_t* sel;    // kChild: parent ids [Q][sel_stride]
+  int sel_stride;
+  int by_item;           // kChild: value indexed by item (1) or by child id (0)
+  int unit;              // positions per id: 1 (positions), 8 (blocks), 64 (super-blocks)
+  const int32_t* n_vis;
+  int64_t n_cap;
+  int64_t n_items;       // items per query
+  int vec;               // value rows start 16-byte aligned (vstride % 4 == 0)
+
+  // ids below this limit are visible
+  __device__ __forceinline__ int64_t limit(int q) const {
+    int64_t nv = n_vis[q];
+    nv = nv < 0 ? 0 : (nv > n_cap ? n_cap : nv);
+    return (nv + unit - 1) / unit;
+  }
+};
+
+// Items t*IPT .. t*IPT+IPT-1 of query q. Every load is issued before any is
+// used (indices are clamped into the row instead of branching), so a thread's
+// loads are in flight together: parents first (kChild), then values, 16 bytes
+// at a time where the row allows it.
+template <int KIND, int IPT>
+__device__ __forceinline__ uint32_t load_items(const Src& src, int q, int t, int64_t lim,
+                                               uint32_t* key, uint32_t* id) {
+  static_assert(IPT % kBlock == 0, "whole groups of 8 per thread");
+  const float* row = src.vals + (size_t)q * (size_t)src.vstride;
+  const int64_t i0 = (int64_t)t * IPT;
+  float v[IPT];
+  int64_t c[IPT];
+  bool ok[IPT];
+  // 8 consecutive values starting at `base` (clamped element-wise at the row end)
+  auto load8 = [&](int64_t base, float* dst) __attribute__((always_inline)) {
+    if (src.vec && base + kBlock <= src.vstride) {
+      const float4* r4 = reinterpret_cast<const float4*>(row + base);
+      const float4 a = r4[0], b = r4[1];
+      dst[0] = a.x; dst[1] = a.y; dst[2] = a.z; dst[3] = a.w;
+      dst[4] = b.x; dst[5] = b.y; dst[6] = b.z; dst[7] = b.w;
+    } else {
+#pragma unroll
+      for (int r = 0; r < kBlock; ++r) {
+        const int64_t k = base + r;
+        dst[r] = row[k < src.vstride ? k : src.vstride - 1];
+      }
+    }
+  };
+  if (KIND == kDirect) {
+#pragma unroll
+    for (int g = 0; g < IPT / kBlock; ++g) load8(i0 + g * kBlock, v + g * kBlock);
+#pragma unroll
+    for (int j = 0; j < IPT; ++j) {
+      c[j] = i0 + j;
+      ok[j] = c[j] < src.n_items && c[j] < lim;
+    }
+  } else {
+    int32_t par[IPT / kBlock];
+#pragma unroll
+    for (int p = 0; p < IPT / kBlock; ++p) {
+      const int64_t i = i0 + p * kBlock;
+      par[p] = i < src.n_items ? src.sel[(size_t)q * src.sel_stride + (i >> 3)] : -1;
+    }
+#pragma unroll
+    for (int p = 0; p < IPT / kBlock; ++p) {
+      const int64_t pa = par[p];
+      const int64_t cb = pa * kBlock;
+      const bool in = pa >= 0 && cb < lim;
+      load8(src.by_item ? i0 + p * kBlock : (in ? cb : 0), v + p * kBlock);
+#pragma unroll
+      for (int r = 0; r < kBlock; ++r) {
+        c[p * kBlock + r] = cb + r;
+        ok[p * kBlock + r] = pa >= 0 && cb + r < lim;
+      }
+    }
+  }
   uint32_t valid = 0;
 #pragma unroll
-  for (int j = 0; j < kItemsPerThread; ++j) {
-    const int64_t i = (int64_t)t * kItemsPerThread + j;
-    key[j] = 0;
-    pos[j] = 0;
-    if (it.get(q, i, nv, pl, key[j], pos[j])) valid |= 1u << j;
+  for (int j = 0; j < IPT; ++j) {
+    key[j] = float_key(v[j]);
+    id[j] = (uint32_t)c[j];
+    valid |= (ok[j] ? 1u : 0u) << j;
   }
-  uint32_t total;
-  block_excl_scan<kSmallThreads>(__popc(valid), sh, total);
+  return valid;
+}
+
+// --- wave / block primitives without LDS round trips where possible --------
+
+// Maximum over each row of 16 lanes with DPP moves, then over the four rows
+// with lane reads (scalar).
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0xB1, 0xF, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x4E, 0xF, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x141, 0xF, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x140, 0xF, 0xF, false));
+  const uint32_t a = (uint32_t)__builtin_amdgcn_readlane((int)v, 15);
+  const uint32_t b = (uint32_t)__builtin_amdgcn_readlane((int)v, 31);
+  const uint32_t c = (uint32_t)__builtin_amdgcn_readlane((int)v, 47);
+  const uint32_t d = (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+  return max(max(a, b), max(c, d));
+}
+
+// Inclusive prefix sum over the wave with DPP: shifts of 1, 2, 4, 8 inside
+// each row of 16 lanes, then the row totals carried across rows (lane 15 to
+// rows 1 and 3, lane 31 to rows 2 and 3).
+__device__ __forceinline__ uint32_t wave_incl_scan_dpp(uint32_t v) {
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xF, 0xF, false);
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xF, 0xF, false);
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xF, 0xF, false);
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xF, 0xF, false);
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xA, 0xF, false);
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xC, 0xF, false);
+  return v;
+}
+
+// Exclusive prefix over the block. `sh` holds NT/64 words and must alternate
+// between regions on consecutive calls (so no trailing barrier is needed).
+template <int NT>
+__device__ __forceinline__ uint32_t block_prefix(uint32_t v, uint32_t* sh, uint32_t& total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const uint32_t incl = wave_incl_scan_dpp(v);
+  if (lane == 63) sh[wave] = incl;
+  __syncthreads();
+  uint32_t base = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < NT / 64; ++w) {
+    const uint32_t x = sh[w];
+    base += w < wave ? x : 0u;
+    tot += x;
+  }
+  total = tot;
+  return base + incl - v;
+}
+
+constexpr int kSelBins = 4096;       // 12-bit digits: two levels cover 24 bits
+constexpr int kSelDigit = 12;
+
+// One work-group per query: exact selection of the K best items (NT threads x
+// IPT items). Writes ids ascending to out[q * out_stride + r], -1 padded to K.
+template <int KIND, int NT, int IPT>
+__global__ __launch_bounds__(NT) void k_select(Src src, int K, int32_t* __restrict__ out,
+                                               int out_stride) {
+  constexpr int NW = NT / 64;
+  constexpr int PER = kSelBins / NT;                 // bins per thread in the threshold search
+  __shared__ __align__(16) uint32_t lh[kSelBins];
+  __shared__ uint32_t sh[6][NW];   // regions: 0-2 count/range, 0/3 levels, 4 ties, 5 output
+  __shared__ uint32_t res[2];
+  const int q = blockIdx.x;
+  const int t = threadIdx.x;
+  const int lane = t & 63, wave = t >> 6;
+  const int64_t lim = src.limit(q);
+  uint32_t key[IPT], id[IPT];
+  const uint32_t valid = load_items<KIND, IPT>(src, q, t, lim, key, id);
+  // one exchange for the count of valid items and their key range
+  uint32_t mx = 0, cmn = 0;
+#pragma unroll
+  for (int j = 0; j < IPT; ++j)
+    if ((valid >> j) & 1u) {
+      mx = max(mx, key[j]);
+      cmn = max(cmn, ~key[j]);   // min as the max of complements
+    }
+  {
+    const uint32_t cnt = wave_incl_scan_dpp(__popc(valid));
+    mx = wave_max_u32(mx);
+    cmn = wave_max_u32(cmn);
+    if (lane == 63) {
+      sh[0][wave] = cnt;
+      sh[1][wave] = mx;
+      sh[2][wave] = cmn;
+    }
+  }
+  __syncthreads();
+  uint32_t total = 0, kmax = 0, kcmn = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    total += sh[0][w];
+    kmax = max(kmax, sh[1][w]);
+    kcmn = max(kcmn, sh[2][w]);
+  }
+  const uint32_t kmin = ~kcmn;
   const uint32_t kk = total < (uint32_t)K ? total : (uint32_t)K;
-  uint32_t kth = 0, ties_needed = 0;   // select key > kth, plus the first ties_needed == kth
   const bool all = total <= (uint32_t)K;
+  uint32_t kth = 0, ties_needed = 0;   // select key > kth, plus the first ties_needed == kth
   if (!all) {
+    // radix select on d = key - kmin, digits of up to 12 bits from the top
+    const uint32_t range = kmax - kmin;
+    int nb = range ? 32 - __clz(range) : 0;
     uint32_t prefix = 0, above = 0;
-    // three levels: bits 31..21, 20..10, 9..0
-#pragma unroll
-    for (int level = 0; level < 3; ++level) {
-      const int shift = level == 0 ? 21 : (level == 1 ? 10 : 0);
-      const uint32_t mask = level == 2 ? 0x3FFu : 0x7FFu;
-      for (int i = t; i < kBins; i += kSmallThreads) lh[i] = 0;
-      __syncthreads();
-#pragma unroll
-      for (int j = 0; j < kItemsPerThread; ++j) {
-        const bool in = ((valid >> j) & 1u) &&
-                        (level == 0 || (key[j] >> (shift + (level == 1 ? 11 : 10))) == prefix);
-        hist_add(lh, (key[j] >> shift) & mask, in);
+    int reg = 3;
+    while (nb > 0) {                       // uniform across the block
+      const int lo = nb > kSelDigit ? nb - kSelDigit : 0;
+      const uint32_t mask = (1u << (nb - lo)) - 1u;
+      {
+        uint4* l4 = reinterpret_cast<uint4*>(lh);
+        for (int i = t; i < kSelBins / 4; i += NT) l4[i] = make_uint4(0, 0, 0, 0);
       }
       __syncthreads();
-      uint32_t bin, ab;
-      find_threshold<kSmallThreads>(lh, (uint32_t)K - above, sh, bin, ab);
-      above += ab;
-      // prefix after level 0: bits 31..21; level 1: bits 31..10; level 2: the key
-      prefix = level == 0 ? bin : ((prefix << (level == 1 ? 11 : 10)) | bin);
+#pragma unroll
+      for (int j = 0; j < IPT; ++j) {
+        const uint32_t d = key[j] - kmin;
+        if (((valid >> j) & 1u) && ((uint64_t)d >> nb) == prefix) atomicAdd(&lh[(d >> lo) & mask], 1u);
+      }
+      __syncthreads();
+      // thread t owns bins [hi - PER, hi), counted from the top bin down
+      const int hi = kSelBins - PER * t;
+      uint32_t c[PER];
+      uint32_t s = 0;
+#pragma unroll
+      for (int j = 0; j < PER; ++j) {
+        c[j] = lh[hi - 1 - j];
+        s += c[j];
+      }
+      uint32_t tot;
+      reg = reg == 3 ? 0 : 3;
+      const uint32_t before = block_prefix<NT>(s, sh[reg], tot);
+      const uint32_t need = (uint32_t)K - above;
+      if (before < need && before + s >= need) {
+        uint32_t run = before;
+#pragma unroll
+        for (int j = 0; j < PER; ++j) {
+          if (run + c[j] >= need) {
+            res[0] = (uint32_t)(hi - 1 - j);
+            res[1] = run;
+            break;
+          }
+          run += c[j];
+        }
+      }
+      __syncthreads();
+      const uint32_t bin = res[0];
+      above += res[1];
+      prefix = (prefix << (nb - lo)) | bin;
+      nb = lo;
     }
-    kth = prefix;
+    kth = kmin + prefix;
     ties_needed = (uint32_t)K - above;
   }
   // ties: the first `ties_needed` items equal to kth, in item order
   uint32_t nt = 0;
 #pragma unroll
-  for (int j = 0; j < kItemsPerThread; ++j) nt += (((valid >> j) & 1u) && !all && key[j] == kth);
+  for (int j = 0; j < IPT; ++j) nt += (((valid >> j) & 1u) && !all && key[j] == kth);
   uint32_t tie_tot;
-  uint32_t tie_rank = block_excl_scan<kSmallThreads>(nt, sh, tie_tot);
+  uint32_t tie_rank = block_prefix<NT>(nt, sh[4], tie_tot);
   uint32_t sel = 0;
 #pragma unroll
-  for (int j = 0; j < kItemsPerThread; ++j) {
+  for (int j = 0; j < IPT; ++j) {
     if (!((valid >> j) & 1u)) continue;
     bool s = all || key[j] > kth;
     if (!all && key[j] == kth) {
@@ -242,12 +450,12 @@ __global__ __launch_bounds__(kSmallThreads) void k_sel_small(Items it, int K, in
     if (s) sel |= 1u << j;
   }
   uint32_t sel_tot;
-  uint32_t rank = block_excl_scan<kSmallThreads>(__popc(sel), sh, sel_tot);
-  int32_t* o = out + (size_t)q * K;
+  uint32_t rank = block_prefix<NT>(__popc(sel), sh[5], sel_tot);
+  int32_t* o = out + (size_t)q * out_stride;
 #pragma unroll
-  for (int j = 0; j < kItemsPerThread; ++j)
-    if ((sel >> j) & 1u) o[rank++] = (int32_t)pos[j];
-  for (int i = (int)kk + t; i < K; i += kSmallThreads) o[i] = -1;
+  for (int j = 0; j < IPT; ++j)
+    if ((sel >> j) & 1u) o[rank++] = (int32_t)id[j];
+  for (int i = (int)kk + t; i < K; i += NT) o[i] = -1;
 }
 
 // ------------------------------------------------------------ large inputs --
@@ -494,6 +702,25 @@ __global__ __launch_bounds__(kFinalThreads) void k_sel_final(Items it, void* ws,
   for (int i = threadIdx.x; i < K; i += kFinalThreads) o[i] = i < (int)kk ? (int32_t)fin[i] : -1;
 }
 
+// Maxima of super-blocks of 8 consecutive blocks (-inf where none is finite).
+__global__ void k_super_max(const float* __restrict__ bmax, int64_t n_blk, int64_t n_sb,
+                            float* __restrict__ smax) {
+  const int q = blockIdx.y;
+  const int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (j >= n_sb) return;
+  const float* b = bmax + (size_t)q * (size_t)n_blk;
+  float v[kBlock];
+#pragma unroll
+  for (int r = 0; r < kBlock; ++r) {
+    const int64_t k = j * kBlock + r;
+    v[r] = k < n_blk ? b[k] : -INFINITY;
+  }
+  float m = v[0];
+#pragma unroll
+  for (int r = 1; r < kBlock; ++r) m = fmaxf(m, v[r]);
+  smax[(size_t)q * (size_t)n_sb + j] = m;
+}
+
 __global__ void k_block_max(const float* __restrict__ scores, const int32_t* __restrict__ n_vis,
                             int64_t n_cap, float* __restrict__ bmax) {
   const int q = blockIdx.y;
@@ -518,23 +745,86 @@ __global__ void k_copy_i32(const int32_t* __restrict__ src, int32_t* __restrict_
 
 }  // namespace
 
-size_t select_workspace_bytes(int Q, int K) { return (size_t)Q * sel_stride(K); }
+// ------------------------------------------------------------ launchers --
 
-hipError_t launch_select(int kind, const float* values, const int32_t* n_vis, const int32_t* pool,
-                         int Q, int64_t n_items, int64_t n_cap, int K, int32_t* out, void* ws,
-                         hipStream_t st) {
+namespace {
+
+constexpr int64_t kOneWgMax = 16384;                 // items one work-group selects over
+constexpr size_t kWsAlign = 256;
+inline size_t up(size_t v) { return (v + kWsAlign - 1) / kWsAlign * kWsAlign; }
+
+inline int64_t n_blocks(int64_t n) { return (n + kBlock - 1) / kBlock; }
+
+// One per-query selection stage over up to 16,384 items.
+template <int KIND>
+hipError_t run_stage_k(const Src& s, int Q, int K, int32_t* out, int out_stride, hipStream_t st) {
+  if (s.n_items <= 4096)
+    hipLaunchKernelGGL((k_select<KIND, 256, 16>), dim3(Q), dim3(256), 0, st, s, K, out,
+                       out_stride);
+  else
+    hipLaunchKernelGGL((k_select<KIND, 1024, 16>), dim3(Q), dim3(1024), 0, st, s, K, out,
+                       out_stride);
+  return hipGetLastError();
+}
+
+struct Stage {
+  int kind;
+  Src src;
+};
+
+hipError_t run_stage(const Stage& g, int Q, int K, int32_t* out, int out_stride, hipStream_t st) {
+  return g.kind == kDirect ? run_stage_k<kDirect>(g.src, Q, K, out, out_stride, st)
+                           : run_stage_k<kChild>(g.src, Q, K, out, out_stride, st);
+}
+
+Stage direct(const float* vals, int64_t vstride, int unit, const int32_t* n_vis, int64_t n_cap,
+             int64_t n_items) {
+  Stage g;
+  g.kind = kDirect;
+  g.src.vals = vals;
+  g.src.vstride = vstride;
+  g.src.sel = nullptr;
+  g.src.sel_stride = 0;
+  g.src.by_item = 0;
+  g.src.unit = unit;
+  g.src.n_vis = n_vis;
+  g.src.n_cap = n_cap;
+  g.src.n_items = n_items;
+  g.src.vec = vstride % 4 == 0 && (reinterpret_cast<uintptr_t>(vals) & 15u) == 0;
+  return g;
+}
+
+Stage child(const float* vals, int64_t vstride, int unit, const int32_t* sel, int sel_stride,
+            int by_item, const int32_t* n_vis, int64_t n_cap) {
+  Stage g = direct(vals, vstride, unit, n_vis, n_cap, (int64_t)sel_stride * kBlock);
+  g.kind = kChild;
+  g.src.sel = sel;
+  g.src.sel_stride = sel_stride;
+  g.src.by_item = by_item;
+  return g;
+}
+
+hipError_t launch_super_max(const float* bmax, int Q, int64_t n_blk, float* smax, hipStream_t st) {
+  const int64_t n_sb = (n_blk + kBlock - 1) / kBlock;
+  hipLaunchKernelGGL(k_super_max, dim3((unsigned)((n_sb + 255) / 256), Q), dim3(256), 0, st, bmax,
+                     n_blk, n_sb, smax);
+  return hipGetLastError();
+}
+
+Items large_items(int kind, const float* values, const int32_t* n_vis, int64_t n_items,
+                  int64_t n_cap) {
   Items it;
   it.kind = kind;
   it.values = values;
   it.n_vis = n_vis;
-  it.pool = pool;
+  it.pool = nullptr;
   it.n_items = n_items;
   it.n_cap = n_cap;
-  if (n_items <= kSmallMax) {
-    hipLaunchKernelGGL(k_sel_small, dim3(Q), dim3(kSmallThreads), 0, st, it, K, out);
-    return hipGetLastError();
-  }
-  const unsigned gx = (unsigned)((n_items + kChunk - 1) / kChunk);
+  return it;
+}
+
+hipError_t run_large(const Items& it, int Q, int K, int32_t* out, void* ws, hipStream_t st) {
+  const unsigned gx = (unsigned)((it.n_items + kChunk - 1) / kChunk);
   hipLaunchKernelGGL(k_sel_zero, dim3(Q), dim3(kThreads), 0, st, ws, K);
   hipLaunchKernelGGL(k_sel_hist<1>, dim3(gx, Q), dim3(kThreads), 0, st, it, ws, K);
   hipLaunchKernelGGL(k_sel_thresh<1>, dim3(Q), dim3(kThreads), 0, st, ws, K);
@@ -543,6 +833,109 @@ hipError_t launch_select(int kind, const float* values, const int32_t* n_vis, co
   hipLaunchKernelGGL(k_sel_filter, dim3(gx, Q), dim3(kThreads), 0, st, it, ws, K);
   hipLaunchKernelGGL(k_sel_final, dim3(Q), dim3(kFinalThreads), 0, st, it, ws, K, out);
   return hipGetLastError();
+}
+
+// Workspace layout shared by the Full Top-K and the pool:
+//   [block maxima, when computed here][super-block maxima][parent ids Q x 2048]
+//   [block ids Q x 512][large path]
+struct WsLayout {
+  size_t bmax, smax, sel_a, sel_b, large, total;
+};
+
+WsLayout layout(int Q, int64_t n_cap, int K) {
+  WsLayout l;
+  const int64_t n_blk = n_blocks(n_cap);
+  l.bmax = 0;
+  l.smax = up((size_t)Q * n_blk * sizeof(float));
+  l.sel_a = l.smax + up((size_t)Q * n_blocks(n_blk) * sizeof(float));
+  l.sel_b = l.sel_a + up((size_t)Q * kPoolBlocks * sizeof(int32_t));
+  l.large = l.sel_b + up((size_t)Q * kTopK * sizeof(int32_t));
+  const bool need_large = n_blocks(n_blk) > kOneWgMax;
+  l.total = l.large + (need_large ? up((size_t)Q * sel_stride(K)) : 0);
+  return l;
+}
+
+template <typename T>
+T* at(void* ws, size_t off) {
+  return reinterpret_cast<T*>(static_cast<uint8_t*>(ws) + off);
+}
+
+}  // namespace
+
+size_t topk_workspace_bytes(int Q, int64_t n_cap) {
+  if (n_cap <= kOneWgMax) return 0;
+  return layout(Q, n_cap, kTopK).total;
+}
+
+size_t pool_workspace_bytes(int Q, int64_t n_cap) { return layout(Q, n_cap, kPoolBlocks).total; }
+
+hipError_t launch_topk_full(const float* scores, const float* bmax, const int32_t* pool,
+                            const int32_t* n_vis, int Q, int64_t n_cap, int32_t* out, void* ws,
+                            hipStream_t st) {
+  if (n_cap <= kOneWgMax)
+    return run_stage(direct(scores, n_cap, 1, n_vis, n_cap, n_cap), Q, kTopK, out, kTopK, st);
+  if (pool)   // the best 512 positions of the pool built from these scores
+    return run_stage(child(scores, n_cap, 1, pool, kPoolBlocks, 0, n_vis, n_cap), Q, kTopK, out,
+                     kTopK, st);
+  const int64_t n_blk = n_blocks(n_cap);
+  const int64_t n_sb = n_blocks(n_blk);
+  const WsLayout l = layout(Q, n_cap, kTopK);
+  if (n_sb > kOneWgMax)
+    return run_large(large_items(kSelFull, scores, n_vis, n_cap, n_cap), Q, kTopK, out,
+                     at<void>(ws, l.large), st);
+  hipError_t e;
+  if (!bmax) {
+    e = launch_block_max(scores, n_vis, Q, n_cap, at<float>(ws, l.bmax), st);
+    if (e != hipSuccess) return e;
+    bmax = at<float>(ws, l.bmax);
+  }
+  float* smax = at<float>(ws, l.smax);
+  int32_t* sel_sb = at<int32_t>(ws, l.sel_a);
+  int32_t* sel_blk = at<int32_t>(ws, l.sel_b);
+  // best 512 super-blocks, then the best 512 of their blocks, then of their positions
+  if ((e = launch_super_max(bmax, Q, n_blk, smax, st)) != hipSuccess) return e;
+  e = run_stage(direct(smax, n_sb, 64, n_vis, n_cap, n_sb), Q, kTopK, sel_sb, kTopK, st);
+  if (e != hipSuccess) return e;
+  e = run_stage(child(bmax, n_blk, 8, sel_sb, kTopK, 0, n_vis, n_cap), Q, kTopK, sel_blk, kTopK,
+                st);
+  if (e != hipSuccess) return e;
+  return run_stage(child(scores, n_cap, 1, sel_blk, kTopK, 0, n_vis, n_cap), Q, kTopK, out, kTopK,
+                   st);
+}
+
+hipError_t launch_topk_reindex(const float* scores_pool, const int32_t* pool, const int32_t* n_vis,
+                               int Q, int64_t n_cap, int32_t* out, hipStream_t st) {
+  return run_stage(child(scores_pool, kPoolCand, 1, pool, kPoolBlocks, 1, n_vis, n_cap), Q, kTopK,
+                   out, kTopK, st);
+}
+
+hipError_t launch_build_pool(const float* src, int is_bmax, const int32_t* n_vis, int Q,
+                             int64_t n_cap, int32_t* pool, void* ws, hipStream_t st) {
+  const int64_t n_blk = n_blocks(n_cap);
+  const int64_t n_sb = n_blocks(n_blk);
+  const WsLayout l = layout(Q, n_cap, kPoolBlocks);
+  const float* bm = src;
+  hipError_t e;
+  if (!is_bmax) {
+    e = launch_block_max(src, n_vis, Q, n_cap, at<float>(ws, l.bmax), st);
+    if (e != hipSuccess) return e;
+    bm = at<float>(ws, l.bmax);
+  }
+  if (n_blk <= kOneWgMax)
+    return run_stage(direct(bm, n_blk, 8, n_vis, n_cap, n_blk), Q, kPoolBlocks, pool, kPoolBlocks,
+                     st);
+  if (n_sb > kOneWgMax)
+    return run_large(large_items(kSelPool, bm, n_vis, n_blk, n_cap), Q, kPoolBlocks, pool,
+                     at<void>(ws, l.large), st);
+  // best 2,048 super-blocks, then the best 2,048 of their 16,384 blocks
+  float* smax = at<float>(ws, l.smax);
+  int32_t* sel_sb = at<int32_t>(ws, l.sel_a);
+  if ((e = launch_super_max(bm, Q, n_blk, smax, st)) != hipSuccess) return e;
+  e = run_stage(direct(smax, n_sb, 64, n_vis, n_cap, n_sb), Q, kPoolBlocks, sel_sb, kPoolBlocks,
+                st);
+  if (e != hipSuccess) return e;
+  return run_stage(child(bm, n_blk, 8, sel_sb, kPoolBlocks, 0, n_vis, n_cap), Q, kPoolBlocks, pool,
+                   kPoolBlocks, st);
 }
 
 hipError_t launch_block_max(const float* scores, const int32_t* n_vis, int Q, int64_t n_cap,

@@ -56,7 +56,8 @@ class LayerGroup:
         n_blk = (n_cap + BLOCK - 1) // BLOCK
         need_pool = any(m == REINDEX for m, _ in self.sched)
         self.scores = torch.empty((B, T, n_cap), dtype=torch.float32, device=dev)
-        self.bmax = torch.empty((B, T, n_blk), dtype=torch.float32, device=dev) if need_pool else None
+        # block maxima come with the scan and drive the hierarchical selections
+        self.bmax = torch.empty((B, T, n_blk), dtype=torch.float32, device=dev)
         self.pool = torch.empty((B, T, POOL_BLOCKS), dtype=torch.int32, device=dev) if need_pool else None
         self.scores_pool = (torch.empty((B, T, POOL_CAND), dtype=torch.float32, device=dev)
                             if need_pool else None)
@@ -102,8 +103,7 @@ class LayerGroup:
             csa2_quantize_kv(kv, cs, slot, cache, stream=stream)
 
     def scan(self, k_idx, n_vis, q_idx, w, stream=None):
-        """The Full layer's scan of every visible position (with block maxima
-        when the group has Reindex layers)."""
+        """The Full layer's scan of every visible position, with block maxima."""
         li = [i for i, (m, _) in enumerate(self.sched) if m == FULL][0]
         csa2_index_score(CSA2_FULL, q_idx[li], w[li], k_idx, n_vis, None, self.scores, self.bmax,
                          stream=stream)
@@ -116,8 +116,9 @@ class LayerGroup:
                 if self.pool is not None:
                     csa2_build_pool(self.bmax, True, n_vis, self.n_cap, self.pool, self.ws,
                                     stream=stream)
-                csa2_topk(CSA2_FULL, self.scores, n_vis, None, None, self.n_cap, self.idx[li],
-                          self.ws, stream=stream)
+                # with a pool the Full Top-K searches its 16,384 positions
+                csa2_topk(CSA2_FULL, self.scores, n_vis, self.pool, None, self.n_cap,
+                          self.idx[li], self.ws, stream=stream, bmax=self.bmax)
                 if self.keep_scores:
                     self.saved_scores[li] = self.scores.clone()
             elif mode == REINDEX:

@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define CSA2_ABI_VERSION 1
+#define CSA2_ABI_VERSION 2
 
 #define CSA2_IDX_HEADS 32
 #define CSA2_IDX_DIM 128
@@ -138,25 +138,35 @@ int csa2_index_score(int mode, const uint8_t* q_idx, const float* w, const uint8
  *   src    [B][T][ceil(n_cap/8)] block maxima when is_bmax != 0 (as written by
  *          csa2_index_score), else [B][T][n_cap] FULL scores (device);
  *   pool   [B][T][2048] int32 (device, written);
- *   ws     device workspace of at least csa2_workspace_bytes(CSA2_OP_BUILD_POOL, ...).
+ *   ws     device workspace of at least csa2_workspace_bytes(CSA2_OP_BUILD_POOL, ...)
+ *          bytes (may be NULL when that is 0).
  * Errors: CSA2_EINVAL (pointers, sizes), CSA2_EWORKSPACE. */
 int csa2_build_pool(const float* src, int is_bmax, const int32_t* n_vis, int B, int T,
                     int64_t n_cap, int32_t* pool, void* ws, size_t ws_bytes, void* stream);
 
 /* DEVICE. Top-512 per query ([P1] §二 mode table and layer layout; [P2] 黑科技之二).
- *   FULL:    the 512 highest of scores[b][t][0 .. n_vis) ([B][T][n_cap]);
+ *   FULL:    the 512 highest of scores[b][t][0 .. n_vis) ([B][T][n_cap]).
+ *            Optional helpers, both computed from these same scores and n_vis:
+ *            `bmax` [B][T][ceil(n_cap/8)] block maxima as csa2_index_score
+ *            writes them (NULL: computed into the workspace), and `pool`
+ *            [B][T][2048] as csa2_build_pool writes it (NULL: not used). With a
+ *            pool the search runs over its 16,384 positions; this is exact
+ *            because the 512 best positions always lie inside the 2,048 best
+ *            blocks of 8 ([P1] §二 hierarchical sparse indexer).
  *   REINDEX: the 512 highest of the pool candidates scores[b][t][i], i < 16384
  *            ([B][T][16384], from csa2_index_score REINDEX with the same pool);
+ *            `bmax` must be NULL.
  *   REUSE:   idx = src_idx byte for byte (a device copy; nothing when idx == src_idx).
  * Ranking is by (score descending, position ascending); the selected positions
  * are written to idx [B][T][512] int32 in ascending order, padded with -1 when
- * fewer than 512 candidates exist. Scores must not be NaN. FULL/REINDEX need a
- * workspace of csa2_workspace_bytes(CSA2_OP_TOPK, mode, ...) bytes.
- * Errors: CSA2_EINVAL (pointers, sizes, REINDEX without pool, REUSE without
- * src_idx), CSA2_EWORKSPACE. */
-int csa2_topk(int mode, const float* scores, const int32_t* n_vis, const int32_t* pool,
-              const int32_t* src_idx, int B, int T, int64_t n_cap, int32_t* idx, void* ws,
-              size_t ws_bytes, void* stream);
+ * fewer than 512 candidates exist. Scores must not be NaN. FULL needs a
+ * workspace of csa2_workspace_bytes(CSA2_OP_TOPK, CSA2_FULL, ...) bytes (0 when
+ * n_cap <= 16384; then `ws` may be NULL); REINDEX and REUSE need none.
+ * Errors: CSA2_EINVAL (pointers, sizes, REINDEX without pool or with bmax,
+ * REUSE without src_idx), CSA2_EWORKSPACE. */
+int csa2_topk(int mode, const float* scores, const float* bmax, const int32_t* n_vis,
+              const int32_t* pool, const int32_t* src_idx, int B, int T, int64_t n_cap,
+              int32_t* idx, void* ws, size_t ws_bytes, void* stream);
 
 /* DEVICE. Sparse MQA attention over the selected FP4 main-KV rows plus the
  * 128-token FP8 window ([P1] §二 layer layout, §三; [P3] 第三刀: dequantise

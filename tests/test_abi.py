@@ -37,7 +37,7 @@ def test_header_functions_are_exported():
     L = C.lib()
     for n in names:
         assert hasattr(L, n), n
-    assert C.csa2_abi_version() == 1
+    assert C.csa2_abi_version() == 2
 
 
 def test_status_strings():
@@ -58,6 +58,8 @@ def test_workspace_sizes():
     ws = C.csa2_workspace_bytes
     assert ws(C.CSA2_OP_INDEX_SCORE, 0, 8, 1, 1 << 20) == 0
     assert ws(C.CSA2_OP_TOPK, C.CSA2_REUSE, 8, 1, 1 << 20) == 0
+    assert ws(C.CSA2_OP_TOPK, C.CSA2_REINDEX, 8, 1, 1 << 20) == 0
+    assert ws(C.CSA2_OP_TOPK, C.CSA2_FULL, 8, 1, 16384) == 0
     assert ws(C.CSA2_OP_TOPK, C.CSA2_FULL, 8, 1, 1 << 20) > 0
     assert ws(C.CSA2_OP_BUILD_POOL, 0, 8, 1, 1 << 20) > 0
     assert ws(C.CSA2_OP_TOPK, C.CSA2_FULL, 0, 1, 100) == 0         # invalid sizes
@@ -94,18 +96,25 @@ def test_index_score_rejects_bad_arguments():
 
 
 def test_topk_and_pool_reject_bad_arguments():
+    # csa2_topk(mode, scores, bmax, n_vis, pool, src_idx, B, T, n_cap, idx, ws, ws_bytes, stream)
     f = C.lib().csa2_topk
-    assert f(0, _p(FAKE), _p(FAKE), None, None, 1, 1, 100, _p(FAKE), None, 0, None) == C.CSA2_EWORKSPACE
-    assert f(0, _p(FAKE), _p(FAKE), None, None, 1, 1, 100, _p(FAKE), _p(FAKE), 16, None) == C.CSA2_EWORKSPACE
-    assert f(1, _p(FAKE), _p(FAKE), None, None, 1, 1, 100, _p(FAKE), _p(FAKE), 1 << 30, None) == C.CSA2_EINVAL
-    assert f(2, None, None, None, None, 1, 1, 100, _p(FAKE), None, 0, None) == C.CSA2_EINVAL
-    assert f(5, _p(FAKE), _p(FAKE), None, None, 1, 1, 100, _p(FAKE), _p(FAKE), 1 << 30, None) == C.CSA2_EINVAL
-    assert f(0, _p(FAKE), _p(FAKE), None, None, 1, 1, 100, _p(FAKE_MIS), _p(FAKE), 1 << 30, None) == C.CSA2_EINVAL
+    N = 1 << 20          # large enough that FULL needs a workspace
+    F, M = _p(FAKE), _p(FAKE_MIS)
+    assert f(0, F, None, F, None, None, 1, 1, N, F, None, 0, None) == C.CSA2_EWORKSPACE
+    assert f(0, F, None, F, None, None, 1, 1, N, F, F, 16, None) == C.CSA2_EWORKSPACE
+    assert f(1, F, None, F, None, None, 1, 1, 100, F, F, 1 << 30, None) == C.CSA2_EINVAL  # no pool
+    assert f(1, F, F, F, F, None, 1, 1, 100, F, F, 1 << 30, None) == C.CSA2_EINVAL       # bmax
+    assert f(2, None, None, None, None, None, 1, 1, 100, F, None, 0, None) == C.CSA2_EINVAL
+    assert f(5, F, None, F, None, None, 1, 1, 100, F, F, 1 << 30, None) == C.CSA2_EINVAL
+    assert f(0, F, None, F, None, None, 1, 1, 100, M, F, 1 << 30, None) == C.CSA2_EINVAL
+    assert f(0, F, M, F, None, None, 1, 1, 100, F, F, 1 << 30, None) == C.CSA2_EINVAL
+    assert f(0, F, None, F, M, None, 1, 1, 100, F, F, 1 << 30, None) == C.CSA2_EINVAL
+    assert f(0, None, None, F, None, None, 1, 1, 100, F, F, 1 << 30, None) == C.CSA2_EINVAL
     g = C.lib().csa2_build_pool
-    assert g(_p(FAKE), 1, _p(FAKE), 1, 1, 100, _p(FAKE), None, 0, None) == C.CSA2_EWORKSPACE
-    assert g(_p(FAKE), 1, _p(FAKE), 1, 1, 100, _p(FAKE), _p(FAKE), 8, None) == C.CSA2_EWORKSPACE
-    assert g(None, 1, _p(FAKE), 1, 1, 100, _p(FAKE), _p(FAKE), 1 << 30, None) == C.CSA2_EINVAL
-    assert g(_p(FAKE), 1, _p(FAKE), 1, 0, 100, _p(FAKE), _p(FAKE), 1 << 30, None) == C.CSA2_EINVAL
+    assert g(F, 1, F, 1, 1, N, F, None, 0, None) == C.CSA2_EWORKSPACE
+    assert g(F, 1, F, 1, 1, N, F, F, 8, None) == C.CSA2_EWORKSPACE
+    assert g(None, 1, F, 1, 1, N, F, F, 1 << 30, None) == C.CSA2_EINVAL
+    assert g(F, 1, F, 1, 0, N, F, F, 1 << 30, None) == C.CSA2_EINVAL
 
 
 def test_attn_and_quantize_reject_bad_arguments():

@@ -203,8 +203,10 @@ def _score_sets(n, seed):
     yield "signed", x
 
 
-@pytest.mark.parametrize("n_cap", [100, 512, 513, 5000, 70001])
+@pytest.mark.parametrize("n_cap", [100, 512, 513, 5000, 16384, 16385, 70001, 1100000])
 def test_topk_full_bitexact(n_cap):
+    """Direct selection up to 16,384 positions, the block / super-block
+    hierarchy above, the multi-pass path beyond 2^20 positions."""
     for name, vals in _score_sets(2 * n_cap, n_cap):
         _stage("topk full", n_cap, name)
         B, T = 2, 1
@@ -223,6 +225,46 @@ def test_topk_full_bitexact(n_cap):
             v = int(nv[b, 0])
             want = OS.topk_positions(s[b, 0, :v], np.arange(v))
             assert np.array_equal(got[b, 0], want), (name, b)
+
+
+def _masked_block_max(s, nv):
+    m = s.copy()
+    m[nv:] = -np.inf
+    return OI.block_max(m, nv)
+
+
+@pytest.mark.parametrize("n_cap", [70001, 300007])
+def test_topk_full_with_block_max_and_pool(n_cap):
+    """FULL with the optional helpers: caller-supplied block maxima, the pool
+    built from the same scores, or both, must give the same exact Top-512."""
+    B, T = 2, 2
+    nv = np.array([[n_cap, n_cap - 5], [4000, 777]], dtype=np.int32)
+    for name, vals in _score_sets(B * T * n_cap, n_cap + 3):
+        _stage("topk full helpers", n_cap, name)
+        s = vals.reshape(B, T, n_cap)
+        bm = np.stack([np.stack([_masked_block_max(s[b, t], nv[b, t]) for t in range(T)])
+                       for b in range(B)])
+        pool = np.stack([np.stack([OS.build_pool(bm[b, t], nv[b, t]) for t in range(T)])
+                         for b in range(B)]).astype(np.int32)
+        scores = torch.from_numpy(s).to(DEV)
+        n_vis = torch.from_numpy(nv).to(DEV)
+        bm_d = torch.from_numpy(bm).to(DEV)
+        pool_d = torch.from_numpy(pool).to(DEV)
+        ws = torch.empty(max(256, C.csa2_workspace_bytes(C.CSA2_OP_TOPK, C.CSA2_FULL, B, T, n_cap)),
+                         dtype=torch.uint8, device=DEV)
+        outs = []
+        for kw in ({"bmax": bm_d}, {"pool": pool_d}, {"bmax": bm_d, "pool": pool_d}):
+            idx = torch.empty((B, T, 512), dtype=torch.int32, device=DEV)
+            C.csa2_topk(C.CSA2_FULL, scores, n_vis, kw.get("pool"), None, n_cap, idx, ws,
+                        bmax=kw.get("bmax"))
+            outs.append(idx)
+        torch.cuda.synchronize()
+        for b in range(B):
+            for t in range(T):
+                v = int(nv[b, t])
+                want = OS.topk_positions(s[b, t, :v], np.arange(v))
+                for k, idx in enumerate(outs):
+                    assert np.array_equal(to_np(idx)[b, t], want), (name, k, b, t)
 
 
 def test_topk_reindex_and_reuse():
@@ -259,10 +301,12 @@ def test_topk_reindex_and_reuse():
     assert to_np(dst).tobytes() == got.tobytes() and to_np(idx).tobytes() == got.tobytes()
 
 
-@pytest.mark.parametrize("n_cap", [9000, 100001, 200003])
+@pytest.mark.parametrize("n_cap", [9000, 100001, 200003, 1048576, 8500000])
 def test_build_pool_bitexact(n_cap):
-    B, T = 2, 2
-    nv = np.array([[n_cap, n_cap - 3], [1, 16385]], dtype=np.int32)
+    """Direct selection up to 16,384 blocks, the super-block hierarchy above,
+    the multi-pass path beyond 16,384 super-blocks."""
+    B, T = (2, 2) if n_cap < 2000000 else (1, 2)
+    nv = np.array([[n_cap, n_cap - 3], [1, 16385]], dtype=np.int32)[:B]
     for name, vals in _score_sets(B * T * n_cap, n_cap + 1):
         _stage("build_pool", n_cap, name)
         s = np.abs(vals).reshape(B, T, n_cap)
