@@ -162,3 +162,38 @@ def test_small_context_pool_is_every_block():
 def test_reindex_candidates_respect_visibility():
     pool = np.array([0, 2, 5, -1], dtype=np.int32)
     assert S.reindex_candidates(pool, 43).tolist() == list(range(8)) + list(range(16, 24)) + list(range(40, 43))
+
+
+@pytest.mark.parametrize("seed", range(300))
+def test_two_level_containment(seed):
+    """The reading behind the device's hierarchical selection, pinned by brute
+    force on tie-heavy inputs: with ties to the lower index at every level, the
+    k best positions lie in the k best blocks of 8, and the k best blocks lie
+    in the k best super-blocks of 8 blocks; so selecting inside those children
+    reproduces the plain selection exactly."""
+    rng = np.random.default_rng(5000 + seed)
+    n_cap = int(rng.integers(1, 900))
+    n_vis = int(rng.integers(1, n_cap + 1))
+    k = int(rng.integers(1, 12))
+    sc = rng.integers(0, 3, n_cap).astype(np.float32)
+    masked = sc.copy()
+    masked[n_vis:] = -np.inf
+    top = S.topk_positions(sc[:n_vis], np.arange(n_vis), k=k)
+    bm = I.block_max(masked, n_vis)
+    n_blk = -(-n_vis // 8)
+    best_blk = S.topk_positions(bm[:n_blk], np.arange(n_blk), k=k)
+    # super-block maxima over blocks (a block max is -inf when invisible)
+    n_sb = -(-n_blk // 8)
+    pad = np.full(n_sb * 8, -np.inf, dtype=np.float32)
+    pad[:n_blk] = bm[:n_blk]
+    sm = pad.reshape(n_sb, 8).max(axis=1)
+    best_sb = S.topk_positions(sm, np.arange(n_sb), k=k)
+    assert set(int(p) // 8 for p in top if p >= 0) <= set(int(b) for b in best_blk if b >= 0)
+    assert set(int(b) // 8 for b in best_blk if b >= 0) <= set(int(s) for s in best_sb if s >= 0)
+    # selecting inside the children of the chosen parents gives the same result
+    child_blk = np.array([8 * s + r for s in best_sb if s >= 0 for r in range(8)
+                          if 8 * s + r < n_blk], dtype=np.int64)
+    assert S.topk_positions(bm[child_blk], child_blk, k=k).tolist() == best_blk.tolist()
+    child_pos = np.array([8 * b + r for b in best_blk if b >= 0 for r in range(8)
+                          if 8 * b + r < n_vis], dtype=np.int64)
+    assert S.topk_positions(sc[child_pos], child_pos, k=k).tolist() == top.tolist()
