@@ -24,9 +24,15 @@ namespace csa2 {
 namespace {
 
 constexpr int kTilePos = 32;       // positions per MFMA tile
-constexpr int kTilesPerWave = 8;
-constexpr int kWaves = 4;
-constexpr int kItemsPerWG = kTilePos * kTilesPerWave * kWaves;   // 1024
+constexpr int kWaves = 4;          // waves per work-group of the decode scan
+// Tiles per wave: 8 for the Full scan (long rows, many work-groups anyway);
+// 2 inside the pool, where each query has only 16,384 candidates and more,
+// shorter work-groups spread a Reindex scan over more of the chip.
+template <int MODE>
+constexpr int tiles_per_wave() { return MODE == 0 ? 8 : 2; }
+template <int MODE>
+constexpr int items_per_wg() { return kTilePos * tiles_per_wave<MODE>() * kWaves; }
+constexpr int kPrefetch = 3;       // tiles in registers per wave (one scored, the rest in flight)
 
 // Row (head) of accumulator register r in lane `lane` of a 32x32 MFMA result.
 __device__ __forceinline__ int acc32_row(int lane, int r) {
@@ -100,16 +106,28 @@ __global__ __launch_bounds__(256) void k_index_score_decode(
   const uint4* q4 = reinterpret_cast<const uint4*>(qp);
   const v8i a0 = as_v8i(q4[0], q4[1]);
   const v8i a1 = as_v8i(q4[2], q4[3]);
+  // head weights of this lane's 16 accumulator rows: 4 runs of 4 consecutive heads
   float wr[16];
+  {
+    const float4* w4 = reinterpret_cast<const float4*>(w + (size_t)qi * kIdxHeads);
 #pragma unroll
-  for (int r = 0; r < 16; ++r) wr[r] = w[(size_t)qi * kIdxHeads + acc32_row(lane, r)];
+    for (int j = 0; j < 4; ++j) {
+      const float4 v = w4[2 * j + half];   // heads 8j + 4*half .. +3
+      wr[4 * j + 0] = v.x;
+      wr[4 * j + 1] = v.y;
+      wr[4 * j + 2] = v.z;
+      wr[4 * j + 3] = v.w;
+    }
+  }
 
   const uint8_t* kbase = k_idx + (size_t)b * (size_t)n_cap * kIdxDim + half * 64;
   const int32_t* pl = MODE == 1 ? pool + (size_t)qi * kPoolBlocks : nullptr;
   float* srow = scores + (size_t)qi * (size_t)n_items;
   float* brow = bmax ? bmax + (size_t)qi * (size_t)n_blk : nullptr;
 
-  const int64_t wave_base = (int64_t)blockIdx.x * kItemsPerWG + (int64_t)wave * kTilePos * kTilesPerWave;
+  constexpr int kTilesPerWave = tiles_per_wave<MODE>();
+  const int64_t wave_base = (int64_t)blockIdx.x * items_per_wg<MODE>() +
+                            (int64_t)wave * kTilePos * kTilesPerWave;
 
   // Reindex: the pool entries of all of this wave's tiles are fetched first, so
   // a tile's key loads never wait on a pool lookup.
@@ -131,21 +149,26 @@ __global__ __launch_bounds__(256) void k_index_score_decode(
     return ok ? pos : 0;
   };
 
-  KTile cur, nxt;
-  bool cur_ok;
-  {
-    const int64_t pos = position_of(0, cur_ok);
-    load_tile(cur, kbase + pos * kIdxDim, cur_ok);
+  // Tiles are loaded kPrefetch - 1 ahead of the one being scored.
+  KTile buf[kPrefetch];
+  bool okb[kPrefetch];
+#pragma unroll
+  for (int i = 0; i < kPrefetch - 1; ++i) {
+    const int64_t pos = position_of(i, okb[i]);
+    load_tile(buf[i], kbase + pos * kIdxDim, okb[i]);
   }
 #pragma unroll
   for (int it = 0; it < kTilesPerWave; ++it) {
     const int64_t tile0 = wave_base + (int64_t)it * kTilePos;
     if (tile0 >= n_items) break;
-    bool nxt_ok = false;
-    if (it + 1 < kTilesPerWave) {
-      const int64_t pos = position_of(it + 1, nxt_ok);
-      load_tile(nxt, kbase + pos * kIdxDim, nxt_ok);
+    constexpr int kAhead = kPrefetch - 1;
+    if (it + kAhead < kTilesPerWave) {
+      const int nb = (it + kAhead) % kPrefetch;
+      const int64_t pos = position_of(it + kAhead, okb[nb]);
+      load_tile(buf[nb], kbase + pos * kIdxDim, okb[nb]);
     }
+    const KTile& cur = buf[it % kPrefetch];
+    const bool cur_ok = okb[it % kPrefetch];
     float s = -INFINITY;
     // Skip the MFMA when no lane of the wave holds a visible position.
     if (__any(cur_ok)) {
@@ -154,9 +177,12 @@ __global__ __launch_bounds__(256) void k_index_score_decode(
                                                             0, 0, 0, 0, 0, 0);
       acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a1, as_v8i(cur.v[2], cur.v[3]), acc,
                                                             0, 0, 0, 0, 0, 0);
-      float part = weighted_relu_sum(acc, wr);
-      part += wave_shfl_xor(part, 32);
-      if (cur_ok) s = part;
+      const float part = weighted_relu_sum(acc, wr);
+      // lo-half + hi-half row sums, in every lane
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(part), __float_as_uint(part),
+                                                       false, false);
+      const float tot = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+      if (cur_ok) s = tot;
     }
     const int64_t item = tile0 + col;
     if (half == 0 && item < n_items) srow[item] = s;
@@ -164,8 +190,6 @@ __global__ __launch_bounds__(256) void k_index_score_decode(
       const float m = max_over_8_lanes(s);
       if (half == 0 && (col & 7) == 0 && item < n_items) brow[item >> 3] = m;
     }
-    cur = nxt;
-    cur_ok = nxt_ok;
   }
 }
 
@@ -399,7 +423,8 @@ hipError_t launch_index_score_decode(int mode, const uint8_t* q_idx, const float
                                      float* scores, float* bmax, hipStream_t st) {
   const int Q = B * T;
   const int64_t n_items = mode == 0 ? n_cap : (int64_t)kPoolCand;
-  const int64_t gx = (n_items + kItemsPerWG - 1) / kItemsPerWG;
+  const int64_t per_wg = mode == 0 ? items_per_wg<0>() : items_per_wg<1>();
+  const int64_t gx = (n_items + per_wg - 1) / per_wg;
   const dim3 grid((unsigned)gx, (unsigned)Q);
   if (mode == 0) {
     hipLaunchKernelGGL(k_index_score_decode<0>, grid, dim3(256), 0, st, q_idx, w, k_idx, n_vis,

@@ -550,6 +550,331 @@ __global__ __launch_bounds__(kThreads) void k_sparse_attn_decode(AttnArgs a) {
   }
 }
 
+// ------------------------------------------------ decode kernel, 8 waves --
+
+typedef _Float16 v4h __attribute__((ext_vector_type(4)));
+
+// Gather for the 8-wave decode work-group: thread t of wave w owns channels
+// 8p..8p+7 with p = 16*(w%4) + t%16, and keys 4g..4g+3 of the chunk with
+// g = 4*(w/4) + (t%64)/16 (wave w serves key half w/4 and channel quarter w%4).
+struct Gather8 {
+  const uint8_t* cache_b;
+  const uint8_t* swa_b;
+  const int32_t* idx_q;
+  int64_t n_cap, tq, pos0;
+  int S, piece, g4;
+
+  __device__ void init(const AttnArgs& a, int qi) {
+    const int b = qi / a.T;
+    cache_b = a.cache + (size_t)b * (size_t)a.n_cap * kRowBytes;
+    swa_b = a.swa + (size_t)b * (size_t)a.S * kDim;
+    idx_q = a.idx + (size_t)qi * kTopK;
+    n_cap = a.n_cap;
+    tq = a.q_pos[qi];
+    pos0 = a.swa_pos0[b];
+    S = a.S;
+    const int t = threadIdx.x, w = t >> 6;
+    piece = 16 * (w & 3) + (t & 15);
+    g4 = 4 * (w >> 2) + ((t & 63) >> 4);
+  }
+
+  // Raw bytes of this thread's 4 keys; bit j marks key j present. Row loads are
+  // unconditional (an absent key reads row 0) so none waits on another.
+  __device__ __forceinline__ uint32_t load(int chunk, int chunk0, const int32_t* sidx,
+                                           uint2 (&r)[4]) const {
+    const int slot0 = chunk * kChunkKeys + g4 * 4;
+    uint32_t ok = 0;
+    if (slot0 < kTopK) {
+      const int4 i4 = *reinterpret_cast<const int4*>(sidx + (slot0 - chunk0 * kChunkKeys));
+      const int32_t pj[4] = {i4.x, i4.y, i4.z, i4.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const bool v = pj[j] >= 0 && (int64_t)pj[j] < n_cap;
+        ok |= (v ? 1u : 0u) << j;
+        const uint8_t* row = cache_b + (size_t)(v ? pj[j] : 0) * kRowBytes;
+        r[j].x = *reinterpret_cast<const uint32_t*>(row + piece * 4);
+        r[j].y = row[kCodeBytes + (piece >> 1)];
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int64_t tok = tq - (kWindow - 1) + (slot0 + j - kTopK);
+        const int64_t rr = tok - pos0;
+        const bool v = tok >= 0 && rr >= 0 && rr < S;
+        ok |= (v ? 1u : 0u) << j;
+        r[j] = *reinterpret_cast<const uint2*>(swa_b + (size_t)(v ? rr : 0) * kDim + piece * 8);
+      }
+    }
+    return ok;
+  }
+
+  __device__ __forceinline__ void stage_idx(int chunk0, int n, int32_t* sidx) const {
+    const int s0 = chunk0 * kChunkKeys;
+    const int cnt = min(n * kChunkKeys, kTopK - s0);
+    for (int i = threadIdx.x; i < cnt; i += blockDim.x) sidx[i] = idx_q[s0 + i];
+  }
+
+  // Dequantise (as Gather::store) and store into krow / vt; flags presence.
+  __device__ __forceinline__ void store(bool is_main, const uint2 (&r)[4], uint32_t ok,
+                                        uint16_t* krow, uint16_t* vt, int* kvalid) const {
+    uint32_t pr[4][4];   // [key][channel pair]
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (is_main) {
+        const uint32_t c = r[j].y;
+        const uint32_t E = (c >> 3) & 15u, M = c & 7u;
+        const float hw = __uint_as_float(E ? (E + 120u) << 23 : 118u << 23);
+        const _Float16 mf = E ? __builtin_bit_cast(_Float16, (uint16_t)(0x3C00u | (M << 7)))
+                              : (_Float16)(float)M;
+        const v2h m2 = {mf, mf};
+        pr[j][0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(r[j].x, hw, 0) * m2);
+        pr[j][1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(r[j].x, hw, 1) * m2);
+        pr[j][2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(r[j].x, hw, 2) * m2);
+        pr[j][3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(r[j].x, hw, 3) * m2);
+      } else {
+        pr[j][0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(r[j].x, 1.0f, false));
+        pr[j][1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(r[j].x, 1.0f, true));
+        pr[j][2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(r[j].y, 1.0f, false));
+        pr[j][3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(r[j].y, 1.0f, true));
+      }
+      if (!((ok >> j) & 1u)) pr[j][0] = pr[j][1] = pr[j][2] = pr[j][3] = 0u;
+      const int key = g4 * 4 + j;
+      if ((threadIdx.x & 15) == 0 && ((threadIdx.x >> 6) & 3) == 0) kvalid[key] = (ok >> j) & 1u;
+      *reinterpret_cast<uint4*>(&krow[key * kKrowStride + piece * 8]) =
+          make_uint4(pr[j][0], pr[j][1], pr[j][2], pr[j][3]);
+    }
+    // transpose 4 keys x 8 channels into 8 channel rows of 4 keys (8 bytes each)
+    const int off = (g4 & 1) * 4;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const uint2 lo = make_uint2(__builtin_amdgcn_perm(pr[1][b], pr[0][b], 0x05040100u),
+                                  __builtin_amdgcn_perm(pr[3][b], pr[2][b], 0x05040100u));
+      const uint2 hi = make_uint2(__builtin_amdgcn_perm(pr[1][b], pr[0][b], 0x07060302u),
+                                  __builtin_amdgcn_perm(pr[3][b], pr[2][b], 0x07060302u));
+      const int d0 = piece * 8 + 2 * b;
+      *reinterpret_cast<uint2*>(&vt[vt_off(d0, g4 >> 1) + off]) = lo;
+      *reinterpret_cast<uint2*>(&vt[vt_off(d0 + 1, g4 >> 1) + off]) = hi;
+    }
+  }
+};
+
+// Reductions over the four 16-lane rows of a wave (lanes with the same lane %
+// 16), in VALU: v_permlane16_swap pairs rows 0/1 and 2/3, v_permlane32_swap
+// pairs the halves; every lane ends with (r0 op r1) op (r2 op r3).
+__device__ __forceinline__ float rows_max(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float rows_sum(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+// Online softmax step over 16 keys: z = this lane's 4 logits (head = column).
+__device__ __forceinline__ float softmax_step16(const float (&z)[4], float& m_run, float& l_run,
+                                                v4h& p_hi, v4h& p_lo) {
+  const float mx = rows_max(fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3])));
+  const float m_new = fmaxf(m_run, mx);
+  float alpha = 1.0f, psum = 0.0f;
+  float p[4];
+  if (m_new == -INFINITY) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) p[i] = 0.0f;
+  } else {
+    alpha = __expf(m_run - m_new);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      p[i] = __expf(z[i] - m_new);
+      psum += p[i];
+    }
+  }
+  psum = rows_sum(psum);
+  l_run = l_run * alpha + psum;
+  m_run = m_new;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const _Float16 h = (_Float16)p[i];
+    p_hi[i] = h;
+    p_lo[i] = (_Float16)(p[i] - (float)h);
+  }
+  return alpha;
+}
+
+// One work-group of 8 waves per (query, 16-head group, slice of CPS chunks).
+// Wave w takes key half w/4 of every chunk and channel quarter w%4: the four
+// waves of a half exchange partial Q.K sums through LDS (one barrier per
+// chunk), keep their own online-softmax state and P.V accumulators, and the two
+// halves are combined at the end. Two waves per SIMD hide each other's LDS and
+// MFMA latencies.
+template <int CPS>
+__global__ __launch_bounds__(512) void k_sparse_attn_decode8(AttnArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t krow[kChunkKeys * kKrowStride];
+  __shared__ __attribute__((aligned(16))) uint16_t vt[kDim * kVtRowHalves];
+  __shared__ float spart[2][2][4][16][kHG + 1];
+  __shared__ int kvalid[2][kChunkKeys];
+  __shared__ float qmax[4][kHG];
+  __shared__ __attribute__((aligned(16))) int32_t sidx[CPS * kChunkKeys];
+
+  const int qi = blockIdx.y;
+  const int hg = blockIdx.x % kHeadGroups;
+  const int split = blockIdx.x / kHeadGroups;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int cq = wave & 3, kh = wave >> 2;
+  const int col = lane & 15, grp = lane >> 4;
+  Gather8 g;
+  g.init(a, qi);
+  const int chunk0 = split * CPS;
+
+  v4f acc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc[i] = v4f{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.0f;
+  v8h qreg[4];
+  float zscale = 1.0f;
+
+  auto chunk = [&](int c, const uint2 (&r)[4], uint32_t ok) __attribute__((always_inline)) {
+    const int buf = c & 1;
+    g.store((chunk0 + c) * kChunkKeys < kTopK, r, ok, krow, vt, kvalid[buf]);
+    {
+      v4f s = {0.f, 0.f, 0.f, 0.f};
+      const uint16_t* kr = &krow[(kh * 16 + col) * kKrowStride + cq * 128 + grp * 8];
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        const uint4 v = *reinterpret_cast<const uint4*>(kr + kb * 32);
+        s = __builtin_amdgcn_mfma_f32_16x16x32_f16(*reinterpret_cast<const v8h*>(&v), qreg[kb], s,
+                                                   0, 0, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) spart[buf][kh][cq][4 * grp + i][col] = s[i];
+    }
+    __syncthreads();
+    float z[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int k = 4 * grp + i;
+      const float sv = ((spart[buf][kh][0][k][col] + spart[buf][kh][1][k][col]) +
+                        spart[buf][kh][2][k][col]) + spart[buf][kh][3][k][col];
+      z[i] = kvalid[buf][kh * 16 + k] ? sv * zscale : -INFINITY;
+    }
+    v4h p_hi, p_lo;
+    const float alpha = softmax_step16(z, m_run, l_run, p_hi, p_lo);
+    if (__any(alpha != 1.0f)) {
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) acc[dt] *= alpha;
+    }
+    const int g4 = kh * 4 + grp;   // this lane's 4 keys in the chunk
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+      const int row = cq * 128 + dt * 16 + col;
+      const uint2 vv = *reinterpret_cast<const uint2*>(&vt[vt_off(row, g4 >> 1) + (g4 & 1) * 4]);
+      const v4h v = __builtin_bit_cast(v4h, vv);
+      acc[dt] = __builtin_amdgcn_mfma_f32_16x16x16f16(v, p_hi, acc[dt], 0, 0, 0);
+      acc[dt] = __builtin_amdgcn_mfma_f32_16x16x16f16(v, p_lo, acc[dt], 0, 0, 0);
+    }
+  };
+  // The quarter cq of the 16 heads' query in fp16 after the head's shift.
+  auto load_q = [&]() __attribute__((always_inline)) {
+    const uint16_t* qp = a.q + ((size_t)qi * kHeads + hg * kHG + col) * kDim + cq * 128 + grp * 8;
+    uint4 raw[4];
+    float amax = 0.0f;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      raw[kb] = *reinterpret_cast<const uint4*>(qp + kb * 32);
+      amax = fmaxf(amax, bf16x8_absmax(raw[kb]));
+    }
+    amax = rows_max(amax);
+    if (grp == 0 && kh == 0) qmax[cq][col] = amax;
+    __syncthreads();
+    amax = fmaxf(fmaxf(qmax[0][col], qmax[1][col]), fmaxf(qmax[2][col], qmax[3][col]));
+    const int sh = q_shift(amax);
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) qreg[kb] = q_to_f16(raw[kb], sh);
+    zscale = ldexpf(a.scale, -sh);
+  };
+
+  g.stage_idx(chunk0, CPS, sidx);
+  load_q();   // ends with a barrier, which also publishes sidx
+  constexpr int PF = CPS < 4 ? CPS : 4;
+  {
+    uint2 raw[PF][4];
+    uint32_t okm[PF];
+    static_for<PF>([&](auto ii) __attribute__((always_inline)) {
+      constexpr int i = decltype(ii)::value;
+      if (i < CPS) okm[i] = g.load(chunk0 + i, chunk0, sidx, raw[i]);
+    });
+    for (int c0 = 0; c0 < CPS; c0 += PF) {
+      static_for<PF>([&](auto ii) __attribute__((always_inline)) {
+        constexpr int i = decltype(ii)::value;
+        const int c = c0 + i;
+        if (c < CPS) {
+          uint2 cur[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) cur[j] = raw[i][j];
+          const uint32_t cok = okm[i];
+          if (c + PF < CPS) okm[i] = g.load(chunk0 + c + PF, chunk0, sidx, raw[i]);
+          chunk(c, cur, cok);
+        }
+      });
+    }
+  }
+
+  // Combine the two key halves: half 1 hands its state to half 0 through LDS
+  // (reusing the key buffers once every wave is done with them).
+  __syncthreads();
+  float* xs = reinterpret_cast<float*>(vt);   // [4 waves][64 lanes][8 tiles x 4 + 2]
+  constexpr int XS = 8 * 4 + 2;
+  if (kh == 1) {
+    float* d = xs + ((size_t)cq * 64 + lane) * XS;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) d[dt * 4 + i] = acc[dt][i];
+    d[32] = m_run;
+    d[33] = l_run;
+  }
+  __syncthreads();
+  if (kh == 1) return;
+  {
+    const float* d = xs + ((size_t)cq * 64 + lane) * XS;
+    const float m1 = d[32], l1 = d[33];
+    const float M = fmaxf(m_run, m1);
+    const float w0 = m_run == -INFINITY ? 0.0f : __expf(m_run - M);
+    const float w1 = m1 == -INFINITY ? 0.0f : __expf(m1 - M);
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[dt][i] = acc[dt][i] * w0 + d[dt * 4 + i] * w1;
+    l_run = l_run * w0 + l1 * w1;
+    m_run = M;
+  }
+
+  // lane holds head 16*hg + col, channels 128*cq + 16*dt + 4*grp .. +3
+  const int head = hg * kHG + col;
+  const int splits = gridDim.x / kHeadGroups;
+  if (splits == 1) {
+    const float inv = l_run > 0.0f ? 1.0f / l_run : 0.0f;
+    float* o = a.out + ((size_t)qi * kHeads + head) * kDim + cq * 128 + 4 * grp;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt)
+      *reinterpret_cast<float4*>(o + dt * 16) =
+          make_float4(acc[dt][0] * inv, acc[dt][1] * inv, acc[dt][2] * inv, acc[dt][3] * inv);
+  } else {
+    const size_t ps = (size_t)qi * splits + split;
+    float* o = a.part + (ps * kHeads + head) * kDim + cq * 128 + 4 * grp;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt)
+      *reinterpret_cast<float4*>(o + dt * 16) = make_float4(acc[dt][0], acc[dt][1], acc[dt][2], acc[dt][3]);
+    if (grp == 0 && cq == 0) {
+      a.part_ml[(ps * kHeads + head) * 2 + 0] = m_run;
+      a.part_ml[(ps * kHeads + head) * 2 + 1] = l_run;
+    }
+  }
+}
+
 // One work-group per (query, head); 128 threads x 4 channels.
 __global__ __launch_bounds__(128) void k_attn_merge(const float* __restrict__ part,
                                                     const float* __restrict__ part_ml, int splits,
@@ -650,12 +975,12 @@ hipError_t launch_sparse_attn(const uint16_t* q, const uint8_t* cache, const int
   } else {
     const dim3 grid(a.splits * kHeadGroups, Q);
     switch (kChunks / a.splits) {
-      case 1: hipLaunchKernelGGL(k_sparse_attn_decode<1>, grid, dim3(kThreads), 0, st, a); break;
-      case 2: hipLaunchKernelGGL(k_sparse_attn_decode<2>, grid, dim3(kThreads), 0, st, a); break;
-      case 4: hipLaunchKernelGGL(k_sparse_attn_decode<4>, grid, dim3(kThreads), 0, st, a); break;
-      case 5: hipLaunchKernelGGL(k_sparse_attn_decode<5>, grid, dim3(kThreads), 0, st, a); break;
-      case 10: hipLaunchKernelGGL(k_sparse_attn_decode<10>, grid, dim3(kThreads), 0, st, a); break;
-      default: hipLaunchKernelGGL(k_sparse_attn_decode<20>, grid, dim3(kThreads), 0, st, a); break;
+      case 1: hipLaunchKernelGGL(k_sparse_attn_decode8<1>, grid, dim3(512), 0, st, a); break;
+      case 2: hipLaunchKernelGGL(k_sparse_attn_decode8<2>, grid, dim3(512), 0, st, a); break;
+      case 4: hipLaunchKernelGGL(k_sparse_attn_decode8<4>, grid, dim3(512), 0, st, a); break;
+      case 5: hipLaunchKernelGGL(k_sparse_attn_decode8<5>, grid, dim3(512), 0, st, a); break;
+      case 10: hipLaunchKernelGGL(k_sparse_attn_decode8<10>, grid, dim3(512), 0, st, a); break;
+      default: hipLaunchKernelGGL(k_sparse_attn_decode8<20>, grid, dim3(512), 0, st, a); break;
     }
   }
   if (a.splits > 1)
