@@ -28,15 +28,20 @@
 // channels.
 //
 // Two work shapes:
-//   wide   (>= 512 queries): one work-group per query, wave w owns heads
-//          16w..16w+15 and all 512 output channels, every gathered row serves all
-//          64 heads;
-//   decode (fewer queries): one work-group per (query, 16-head group, slice of
-//          the 640 key slots); wave w forms the partial Q.K over its own 128
-//          gathered channels, the four partials are summed through LDS in a
-//          fixed order, and wave w accumulates P.V for its 128 output channels.
-//          A slice's rows are requested before its first chunk is computed.
-//          Slices are merged by log-sum-exp in a second kernel.
+//   wide   (more than 16 queries): one work-group of 4 waves per (query, slice
+//          of the key slots); wave w owns heads 16w..16w+15 and all 512 output
+//          channels, so every gathered row serves all 64 heads;
+//   decode (up to 16 queries): one work-group of 8 waves per (query, 16-head
+//          group, slice). Wave w takes key half w/4 of each 32-key chunk and
+//          channel quarter w%4: it dequantises only that quarter of its keys
+//          into the row-major buffer, forms partial Q.K sums that the four
+//          waves of its half add up through LDS in a fixed order, and
+//          accumulates P.V for its 128 channels. Its P.V operand comes straight
+//          from the row-major buffer through the gfx950 transposing LDS read
+//          (ds_read_b64_tr_b16), so no transposed copy is stored. The two key
+//          halves are combined at the end; two waves per SIMD hide each other's
+//          LDS and MFMA latencies.
+//   Slices are merged by log-sum-exp in a second kernel.
 #include "device_common.hpp"
 #include "launchers.hpp"
 
@@ -424,132 +429,6 @@ __global__ __launch_bounds__(kThreads) void k_sparse_attn_wide(AttnArgs a) {
   }
 }
 
-// ---------------------------------------------------------- decode kernel --
-
-template <int CPS>
-__global__ __launch_bounds__(kThreads) void k_sparse_attn_decode(AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t krow[kChunkKeys * kKrowStride];
-  __shared__ __attribute__((aligned(16))) uint16_t vt[kDim * kVtRowHalves];
-  __shared__ float spart[2][4][kChunkKeys][kHG + 1];
-  __shared__ int kvalid[2][kChunkKeys];
-  __shared__ float qmax[4][kHG];
-  __shared__ __attribute__((aligned(16))) int32_t sidx[CPS * kChunkKeys];
-
-  const int qi = blockIdx.y;
-  const int hg = blockIdx.x % kHeadGroups;
-  const int split = blockIdx.x / kHeadGroups;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int col = lane & 15, grp = lane >> 4;
-  Gather g;
-  g.init(a, qi);
-  const int chunk0 = split * CPS;
-
-  v4f acc[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) acc[i] = v4f{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY, l_run = 0.0f;
-  v8h qreg[4];
-  float zscale = 1.0f;
-
-  // One chunk: gather this wave's channel quarter, partial Q.K, exchange the
-  // partials, softmax, P.V on this wave's 128 output channels. The krow / vt
-  // regions a wave writes are the ones it reads, so only the partials need a
-  // work-group barrier (double-buffered, one barrier per chunk).
-  auto chunk = [&](int c, const uint2 (&r)[8], uint32_t ok) __attribute__((always_inline)) {
-    const int buf = c & 1;
-    g.store((chunk0 + c) * kChunkKeys < kTopK, r, ok, krow, vt, kvalid[buf]);
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-      v4f s = {0.f, 0.f, 0.f, 0.f};
-      const uint16_t* kr = &krow[(mt * 16 + col) * kKrowStride + wave * 128 + grp * 8];
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-        const uint4 v = *reinterpret_cast<const uint4*>(kr + kb * 32);
-        s = __builtin_amdgcn_mfma_f32_16x16x32_f16(*reinterpret_cast<const v8h*>(&v), qreg[kb], s,
-                                                   0, 0, 0);
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) spart[buf][wave][mt * 16 + 4 * grp + i][col] = s[i];
-    }
-    __syncthreads();
-    float z[8];
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int key = mt * 16 + 4 * grp + i;
-        const float sv = ((spart[buf][0][key][col] + spart[buf][1][key][col]) +
-                          spart[buf][2][key][col]) + spart[buf][3][key][col];
-        z[mt * 4 + i] = kvalid[buf][key] ? sv * zscale : -INFINITY;
-      }
-    v8h p_hi, p_lo;
-    const float alpha = softmax_step(z, m_run, l_run, p_hi, p_lo);
-    if (__any(alpha != 1.0f)) {
-#pragma unroll
-      for (int dt = 0; dt < 8; ++dt) acc[dt] *= alpha;
-    }
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt) {
-      const v8h v = vt_operand(vt, wave * 128 + dt * 16 + col, grp);
-      acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(v, p_hi, acc[dt], 0, 0, 0);
-      acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(v, p_lo, acc[dt], 0, 0, 0);
-    }
-  };
-  // The wave's quarter of its 16 heads' query (channels 128*wave + kb*32 +
-  // grp*8 .. +7) in fp16 after the head's shift; the four waves agree on the
-  // per-head maximum through LDS.
-  auto load_q = [&]() __attribute__((always_inline)) {
-    const uint16_t* qp = a.q + ((size_t)qi * kHeads + hg * kHG + col) * kDim + wave * 128 + grp * 8;
-    uint4 raw[4];
-    float amax = 0.0f;
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      raw[kb] = *reinterpret_cast<const uint4*>(qp + kb * 32);
-      amax = fmaxf(amax, bf16x8_absmax(raw[kb]));
-    }
-    amax = fmaxf(amax, wave_shfl_xor(amax, 16));
-    amax = fmaxf(amax, wave_shfl_xor(amax, 32));
-    if (grp == 0) qmax[wave][col] = amax;
-    __syncthreads();
-    amax = fmaxf(fmaxf(qmax[0][col], qmax[1][col]), fmaxf(qmax[2][col], qmax[3][col]));
-    const int sh = q_shift(amax);
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb) qreg[kb] = q_to_f16(raw[kb], sh);
-    zscale = ldexpf(a.scale, -sh);
-  };
-
-  g.stage_idx(chunk0, CPS, sidx);
-  load_q();   // ends with a barrier, which also publishes sidx
-  constexpr int PF = CPS < 4 ? CPS : 4;
-  pipeline<CPS, PF>(
-      [&](int c, uint2 (&r)[8]) __attribute__((always_inline)) {
-        return g.load(chunk0 + c, chunk0, sidx, r);
-      },
-      chunk);
-
-  // lane holds head 16*hg + col, channels 128*wave + 16*dt + 4*grp .. +3
-  const int head = hg * kHG + col;
-  const int splits = gridDim.x / kHeadGroups;
-  if (splits == 1) {
-    const float inv = l_run > 0.0f ? 1.0f / l_run : 0.0f;
-    float* o = a.out + ((size_t)qi * kHeads + head) * kDim + wave * 128 + 4 * grp;
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt)
-      *reinterpret_cast<float4*>(o + dt * 16) =
-          make_float4(acc[dt][0] * inv, acc[dt][1] * inv, acc[dt][2] * inv, acc[dt][3] * inv);
-  } else {
-    const size_t ps = (size_t)qi * splits + split;
-    float* o = a.part + (ps * kHeads + head) * kDim + wave * 128 + 4 * grp;
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt)
-      *reinterpret_cast<float4*>(o + dt * 16) = make_float4(acc[dt][0], acc[dt][1], acc[dt][2], acc[dt][3]);
-    if (grp == 0 && wave == 0) {
-      a.part_ml[(ps * kHeads + head) * 2 + 0] = m_run;
-      a.part_ml[(ps * kHeads + head) * 2 + 1] = l_run;
-    }
-  }
-}
-
 // ------------------------------------------------ decode kernel, 8 waves --
 
 typedef _Float16 v4h __attribute__((ext_vector_type(4)));
@@ -614,12 +493,12 @@ struct Gather8 {
     for (int i = threadIdx.x; i < cnt; i += blockDim.x) sidx[i] = idx_q[s0 + i];
   }
 
-  // Dequantise (as Gather::store) and store into krow / vt; flags presence.
+  // Dequantise (as Gather::store) into krow; flags presence.
   __device__ __forceinline__ void store(bool is_main, const uint2 (&r)[4], uint32_t ok,
-                                        uint16_t* krow, uint16_t* vt, int* kvalid) const {
-    uint32_t pr[4][4];   // [key][channel pair]
+                                        uint16_t* krow, int* kvalid) const {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
+      uint32_t pr[4];   // fp16 pairs of channels 8p+2b, 8p+2b+1
       if (is_main) {
         const uint32_t c = r[j].y;
         const uint32_t E = (c >> 3) & 15u, M = c & 7u;
@@ -627,33 +506,21 @@ struct Gather8 {
         const _Float16 mf = E ? __builtin_bit_cast(_Float16, (uint16_t)(0x3C00u | (M << 7)))
                               : (_Float16)(float)M;
         const v2h m2 = {mf, mf};
-        pr[j][0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(r[j].x, hw, 0) * m2);
-        pr[j][1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(r[j].x, hw, 1) * m2);
-        pr[j][2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(r[j].x, hw, 2) * m2);
-        pr[j][3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(r[j].x, hw, 3) * m2);
+        pr[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(r[j].x, hw, 0) * m2);
+        pr[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(r[j].x, hw, 1) * m2);
+        pr[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(r[j].x, hw, 2) * m2);
+        pr[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(r[j].x, hw, 3) * m2);
       } else {
-        pr[j][0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(r[j].x, 1.0f, false));
-        pr[j][1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(r[j].x, 1.0f, true));
-        pr[j][2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(r[j].y, 1.0f, false));
-        pr[j][3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(r[j].y, 1.0f, true));
+        pr[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(r[j].x, 1.0f, false));
+        pr[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(r[j].x, 1.0f, true));
+        pr[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(r[j].y, 1.0f, false));
+        pr[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(r[j].y, 1.0f, true));
       }
-      if (!((ok >> j) & 1u)) pr[j][0] = pr[j][1] = pr[j][2] = pr[j][3] = 0u;
+      if (!((ok >> j) & 1u)) pr[0] = pr[1] = pr[2] = pr[3] = 0u;
       const int key = g4 * 4 + j;
       if ((threadIdx.x & 15) == 0 && ((threadIdx.x >> 6) & 3) == 0) kvalid[key] = (ok >> j) & 1u;
       *reinterpret_cast<uint4*>(&krow[key * kKrowStride + piece * 8]) =
-          make_uint4(pr[j][0], pr[j][1], pr[j][2], pr[j][3]);
-    }
-    // transpose 4 keys x 8 channels into 8 channel rows of 4 keys (8 bytes each)
-    const int off = (g4 & 1) * 4;
-#pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      const uint2 lo = make_uint2(__builtin_amdgcn_perm(pr[1][b], pr[0][b], 0x05040100u),
-                                  __builtin_amdgcn_perm(pr[3][b], pr[2][b], 0x05040100u));
-      const uint2 hi = make_uint2(__builtin_amdgcn_perm(pr[1][b], pr[0][b], 0x07060302u),
-                                  __builtin_amdgcn_perm(pr[3][b], pr[2][b], 0x07060302u));
-      const int d0 = piece * 8 + 2 * b;
-      *reinterpret_cast<uint2*>(&vt[vt_off(d0, g4 >> 1) + off]) = lo;
-      *reinterpret_cast<uint2*>(&vt[vt_off(d0 + 1, g4 >> 1) + off]) = hi;
+          make_uint4(pr[0], pr[1], pr[2], pr[3]);
     }
   }
 };
@@ -713,8 +580,7 @@ __device__ __forceinline__ float softmax_step16(const float (&z)[4], float& m_ru
 template <int CPS>
 __global__ __launch_bounds__(512) void k_sparse_attn_decode8(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t krow[kChunkKeys * kKrowStride];
-  __shared__ __attribute__((aligned(16))) uint16_t vt[kDim * kVtRowHalves];
-  __shared__ float spart[2][2][4][16][kHG + 1];
+  __shared__ float spart[2][2][4][16][kHG];
   __shared__ int kvalid[2][kChunkKeys];
   __shared__ float qmax[4][kHG];
   __shared__ __attribute__((aligned(16))) int32_t sidx[CPS * kChunkKeys];
@@ -738,7 +604,7 @@ __global__ __launch_bounds__(512) void k_sparse_attn_decode8(AttnArgs a) {
 
   auto chunk = [&](int c, const uint2 (&r)[4], uint32_t ok) __attribute__((always_inline)) {
     const int buf = c & 1;
-    g.store((chunk0 + c) * kChunkKeys < kTopK, r, ok, krow, vt, kvalid[buf]);
+    g.store((chunk0 + c) * kChunkKeys < kTopK, r, ok, krow, kvalid[buf]);
     {
       v4f s = {0.f, 0.f, 0.f, 0.f};
       const uint16_t* kr = &krow[(kh * 16 + col) * kKrowStride + cq * 128 + grp * 8];
@@ -766,12 +632,17 @@ __global__ __launch_bounds__(512) void k_sparse_attn_decode8(AttnArgs a) {
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt) acc[dt] *= alpha;
     }
-    const int g4 = kh * 4 + grp;   // this lane's 4 keys in the chunk
+    // P.V operand: the transposing LDS read hands lane (grp, i) the values of
+    // channel ch0 + i for keys 16*kh + 4*grp .. +3, when lane (grp, m) points
+    // at key 16*kh + 4*grp + m/4, channels ch0 + 4*(m%4) .. +3.
+    const uint16_t* vsrc = &krow[(kh * 16 + 4 * grp + (col >> 2)) * kKrowStride + cq * 128 +
+                                 4 * (col & 3)];
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) {
-      const int row = cq * 128 + dt * 16 + col;
-      const uint2 vv = *reinterpret_cast<const uint2*>(&vt[vt_off(row, g4 >> 1) + (g4 & 1) * 4]);
-      const v4h v = __builtin_bit_cast(v4h, vv);
+      typedef short v4s __attribute__((ext_vector_type(4)));
+      const v4s raw = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) v4s*)(vsrc + dt * 16));
+      const v4h v = __builtin_bit_cast(v4h, raw);
       acc[dt] = __builtin_amdgcn_mfma_f32_16x16x16f16(v, p_hi, acc[dt], 0, 0, 0);
       acc[dt] = __builtin_amdgcn_mfma_f32_16x16x16f16(v, p_lo, acc[dt], 0, 0, 0);
     }
@@ -823,31 +694,34 @@ __global__ __launch_bounds__(512) void k_sparse_attn_decode8(AttnArgs a) {
   }
 
   // Combine the two key halves: half 1 hands its state to half 0 through LDS
-  // (reusing the key buffers once every wave is done with them).
+  // (reusing the key buffer and the partial sums once every wave is done).
   __syncthreads();
-  float* xs = reinterpret_cast<float*>(vt);   // [4 waves][64 lanes][8 tiles x 4 + 2]
-  constexpr int XS = 8 * 4 + 2;
+  float* xs = reinterpret_cast<float*>(krow);        // [4][64 lanes][32]
+  float* xml = &spart[0][0][0][0][0];                // [4][64 lanes][2]
   if (kh == 1) {
-    float* d = xs + ((size_t)cq * 64 + lane) * XS;
+    float* d = xs + ((size_t)cq * 64 + lane) * 32;
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) d[dt * 4 + i] = acc[dt][i];
-    d[32] = m_run;
-    d[33] = l_run;
+      *reinterpret_cast<float4*>(d + dt * 4) = make_float4(acc[dt][0], acc[dt][1], acc[dt][2], acc[dt][3]);
+    xml[(cq * 64 + lane) * 2 + 0] = m_run;
+    xml[(cq * 64 + lane) * 2 + 1] = l_run;
   }
   __syncthreads();
   if (kh == 1) return;
   {
-    const float* d = xs + ((size_t)cq * 64 + lane) * XS;
-    const float m1 = d[32], l1 = d[33];
+    const float* d = xs + ((size_t)cq * 64 + lane) * 32;
+    const float m1 = xml[(cq * 64 + lane) * 2 + 0], l1 = xml[(cq * 64 + lane) * 2 + 1];
     const float M = fmaxf(m_run, m1);
     const float w0 = m_run == -INFINITY ? 0.0f : __expf(m_run - M);
     const float w1 = m1 == -INFINITY ? 0.0f : __expf(m1 - M);
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) acc[dt][i] = acc[dt][i] * w0 + d[dt * 4 + i] * w1;
+    for (int dt = 0; dt < 8; ++dt) {
+      const float4 o = *reinterpret_cast<const float4*>(d + dt * 4);
+      acc[dt][0] = acc[dt][0] * w0 + o.x * w1;
+      acc[dt][1] = acc[dt][1] * w0 + o.y * w1;
+      acc[dt][2] = acc[dt][2] * w0 + o.z * w1;
+      acc[dt][3] = acc[dt][3] * w0 + o.w * w1;
+    }
     l_run = l_run * w0 + l1 * w1;
     m_run = M;
   }
@@ -875,28 +749,41 @@ __global__ __launch_bounds__(512) void k_sparse_attn_decode8(AttnArgs a) {
   }
 }
 
-// One work-group per (query, head); 128 threads x 4 channels.
+// One work-group per (query, head); 128 threads x 4 channels. Every load is
+// independent of the others (one round trip), then the slices are combined.
+constexpr int kMaxSplits = 8;
 __global__ __launch_bounds__(128) void k_attn_merge(const float* __restrict__ part,
                                                     const float* __restrict__ part_ml, int splits,
                                                     float* __restrict__ out) {
   const int qi = blockIdx.y, head = blockIdx.x;
+  float m[kMaxSplits], l[kMaxSplits];
+  float4 v[kMaxSplits];
+#pragma unroll
+  for (int s = 0; s < kMaxSplits; ++s) {
+    if (s < splits) {
+      const size_t ps = (size_t)qi * splits + s;
+      m[s] = part_ml[(ps * kHeads + head) * 2];
+      l[s] = part_ml[(ps * kHeads + head) * 2 + 1];
+      v[s] = *reinterpret_cast<const float4*>(part + (ps * kHeads + head) * kDim + threadIdx.x * 4);
+    }
+  }
   float M = -INFINITY;
-  for (int s = 0; s < splits; ++s)
-    M = fmaxf(M, part_ml[(((size_t)qi * splits + s) * kHeads + head) * 2]);
+#pragma unroll
+  for (int s = 0; s < kMaxSplits; ++s)
+    if (s < splits) M = fmaxf(M, m[s]);
   float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
   float L = 0.0f;
   if (M != -INFINITY) {
-    for (int s = 0; s < splits; ++s) {
-      const size_t ps = (size_t)qi * splits + s;
-      const float m = part_ml[(ps * kHeads + head) * 2];
-      const float l = part_ml[(ps * kHeads + head) * 2 + 1];
-      const float wgt = m == -INFINITY ? 0.0f : __expf(m - M);
-      L += wgt * l;
-      const float4 v = *reinterpret_cast<const float4*>(part + (ps * kHeads + head) * kDim + threadIdx.x * 4);
-      o.x += wgt * v.x;
-      o.y += wgt * v.y;
-      o.z += wgt * v.z;
-      o.w += wgt * v.w;
+#pragma unroll
+    for (int s = 0; s < kMaxSplits; ++s) {
+      if (s < splits) {
+        const float wgt = m[s] == -INFINITY ? 0.0f : __expf(m[s] - M);
+        L += wgt * l[s];
+        o.x += wgt * v[s].x;
+        o.y += wgt * v[s].y;
+        o.z += wgt * v[s].z;
+        o.w += wgt * v[s].w;
+      }
     }
   }
   const float inv = L > 0.0f ? 1.0f / L : 0.0f;
@@ -957,6 +844,7 @@ hipError_t launch_sparse_attn(const uint16_t* q, const uint8_t* cache, const int
   a.part = nullptr;
   a.part_ml = nullptr;
   const Shape sh = attn_shape(Q);
+  if (sh.splits > kMaxSplits) return hipErrorInvalidValue;
   a.splits = sh.splits;
   if (a.splits > 1) {
     a.part = reinterpret_cast<float*>(ws);
