@@ -192,8 +192,10 @@ __device__ __forceinline__ void hist_add(uint32_t* lh, uint32_t bin, bool pred) 
 //   kDirect: item i is id i of a value row (visible while i < the limit);
 //   kChild:  item i is child (i % 8) of parent sel[i / 8] (ids ascending,
 //            -1 padded): id = 8 * parent + i % 8, visible while below the limit;
-//            its value is indexed by the item (Reindex scores) or by the id.
-enum SrcKind { kDirect = 0, kChild = 2 };
+//            its value is indexed by the id;
+//   kChildItem: as kChild, but the value is indexed by the item (Reindex
+//            scores), so value loads do not wait for the parents.
+enum SrcKind { kDirect = 0, kChild = 2, kChildItem = 3 };
 
 struct Src {
   const float* vals;     // value rows, vstride floats per query
@@ -258,12 +260,16 @@ __device__ __forceinline__ uint32_t load_items(const Src& src, int q, int t, int
       const int64_t i = i0 + p * kBlock;
       par[p] = i < src.n_items ? src.sel[(size_t)q * src.sel_stride + (i >> 3)] : -1;
     }
+    if (KIND == kChildItem) {
+#pragma unroll
+      for (int p = 0; p < IPT / kBlock; ++p) load8(i0 + p * kBlock, v + p * kBlock);
+    }
 #pragma unroll
     for (int p = 0; p < IPT / kBlock; ++p) {
       const int64_t pa = par[p];
       const int64_t cb = pa * kBlock;
       const bool in = pa >= 0 && cb < lim;
-      load8(src.by_item ? i0 + p * kBlock : (in ? cb : 0), v + p * kBlock);
+      if (KIND == kChild) load8(in ? cb : 0, v + p * kBlock);
 #pragma unroll
       for (int r = 0; r < kBlock; ++r) {
         c[p * kBlock + r] = cb + r;
@@ -341,7 +347,7 @@ __global__ __launch_bounds__(NT) void k_select(Src src, int K, int32_t* __restri
   constexpr int PER = kSelBins / NT;                 // bins per thread in the threshold search
   __shared__ __align__(16) uint32_t lh[kSelBins];
   __shared__ uint32_t sh[6][NW];   // regions: 0-2 count/range, 0/3 levels, 4 ties, 5 output
-  __shared__ uint32_t res[2];
+  __shared__ uint32_t res[3];
   const int q = blockIdx.x;
   const int t = threadIdx.x;
   const int lane = t & 63, wave = t >> 6;
@@ -378,6 +384,7 @@ __global__ __launch_bounds__(NT) void k_select(Src src, int K, int32_t* __restri
   const uint32_t kk = total < (uint32_t)K ? total : (uint32_t)K;
   const bool all = total <= (uint32_t)K;
   uint32_t kth = 0, ties_needed = 0;   // select key > kth, plus the first ties_needed == kth
+  uint32_t eq_count = total;           // items equal to kth (all of them if the range is 0)
   if (!all) {
     // radix select on d = key - kmin, digits of up to 12 bits from the top
     const uint32_t range = kmax - kmin;
@@ -418,6 +425,7 @@ __global__ __launch_bounds__(NT) void k_select(Src src, int K, int32_t* __restri
           if (run + c[j] >= need) {
             res[0] = (uint32_t)(hi - 1 - j);
             res[1] = run;
+            res[2] = c[j];
             break;
           }
           run += c[j];
@@ -426,28 +434,36 @@ __global__ __launch_bounds__(NT) void k_select(Src src, int K, int32_t* __restri
       __syncthreads();
       const uint32_t bin = res[0];
       above += res[1];
+      eq_count = res[2];   // after the last level: the items equal to the K-th key
       prefix = (prefix << (nb - lo)) | bin;
       nb = lo;
     }
     kth = kmin + prefix;
     ties_needed = (uint32_t)K - above;
   }
-  // ties: the first `ties_needed` items equal to kth, in item order
-  uint32_t nt = 0;
-#pragma unroll
-  for (int j = 0; j < IPT; ++j) nt += (((valid >> j) & 1u) && !all && key[j] == kth);
-  uint32_t tie_tot;
-  uint32_t tie_rank = block_prefix<NT>(nt, sh[4], tie_tot);
   uint32_t sel = 0;
+  if (!all && ties_needed < eq_count) {
+    // ties: the first `ties_needed` items equal to kth, in item order
+    uint32_t nt = 0;
 #pragma unroll
-  for (int j = 0; j < IPT; ++j) {
-    if (!((valid >> j) & 1u)) continue;
-    bool s = all || key[j] > kth;
-    if (!all && key[j] == kth) {
-      s = tie_rank < ties_needed;
-      ++tie_rank;
+    for (int j = 0; j < IPT; ++j) nt += (((valid >> j) & 1u) && key[j] == kth);
+    uint32_t tie_tot;
+    uint32_t tie_rank = block_prefix<NT>(nt, sh[4], tie_tot);
+#pragma unroll
+    for (int j = 0; j < IPT; ++j) {
+      if (!((valid >> j) & 1u)) continue;
+      bool s = key[j] > kth;
+      if (key[j] == kth) {
+        s = tie_rank < ties_needed;
+        ++tie_rank;
+      }
+      if (s) sel |= 1u << j;
     }
-    if (s) sel |= 1u << j;
+  } else {
+    // every item equal to the K-th key is taken: no tie ranking needed
+#pragma unroll
+    for (int j = 0; j < IPT; ++j)
+      if (((valid >> j) & 1u) && (all || key[j] >= kth)) sel |= 1u << j;
   }
   uint32_t sel_tot;
   uint32_t rank = block_prefix<NT>(__popc(sel), sh[5], sel_tot);
@@ -773,8 +789,9 @@ struct Stage {
 };
 
 hipError_t run_stage(const Stage& g, int Q, int K, int32_t* out, int out_stride, hipStream_t st) {
-  return g.kind == kDirect ? run_stage_k<kDirect>(g.src, Q, K, out, out_stride, st)
-                           : run_stage_k<kChild>(g.src, Q, K, out, out_stride, st);
+  if (g.kind == kDirect) return run_stage_k<kDirect>(g.src, Q, K, out, out_stride, st);
+  if (g.kind == kChildItem) return run_stage_k<kChildItem>(g.src, Q, K, out, out_stride, st);
+  return run_stage_k<kChild>(g.src, Q, K, out, out_stride, st);
 }
 
 Stage direct(const float* vals, int64_t vstride, int unit, const int32_t* n_vis, int64_t n_cap,
@@ -797,7 +814,7 @@ Stage direct(const float* vals, int64_t vstride, int unit, const int32_t* n_vis,
 Stage child(const float* vals, int64_t vstride, int unit, const int32_t* sel, int sel_stride,
             int by_item, const int32_t* n_vis, int64_t n_cap) {
   Stage g = direct(vals, vstride, unit, n_vis, n_cap, (int64_t)sel_stride * kBlock);
-  g.kind = kChild;
+  g.kind = by_item ? kChildItem : kChild;
   g.src.sel = sel;
   g.src.sel_stride = sel_stride;
   g.src.by_item = by_item;
