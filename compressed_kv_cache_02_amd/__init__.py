@@ -149,7 +149,8 @@ def csa2_quantize_kv(kv_bf16, cos_sin, dst_slot, cache, stream=None):
 def csa2_index_score(mode, q_idx, w, k_idx, n_vis, pool, scores, bmax=None, stream=None):
     """q_idx [B,T,32,128] uint8, w [B,T,32] f32, k_idx [B,n_cap,128] uint8,
     n_vis [B,T] int32, pool [B,T,2048] int32 (REINDEX), scores f32
-    ([B,T,n_cap] FULL / [B,T,16384] REINDEX), bmax [B,T,ceil(n_cap/8)] f32 or None."""
+    ([B,T,n_cap] FULL / [B,T,16384] REINDEX; None in FULL mode writes only
+    the block maxima), bmax [B,T,ceil(n_cap/8)] f32 or None."""
     import torch
     B, T = q_idx.shape[0], q_idx.shape[1]
     n_cap = k_idx.shape[1]
@@ -158,7 +159,8 @@ def csa2_index_score(mode, q_idx, w, k_idx, n_vis, pool, scores, bmax=None, stre
     _expect(k_idx, "k_idx", torch.uint8, (B, n_cap, IDX_DIM))
     _expect(n_vis, "n_vis", torch.int32, (B, T))
     n_items = n_cap if mode == CSA2_FULL else POOL_CAND
-    _expect(scores, "scores", torch.float32, (B, T, n_items))
+    if scores is not None or mode != CSA2_FULL:
+        _expect(scores, "scores", torch.float32, (B, T, n_items))
     if pool is not None:
         _expect(pool, "pool", torch.int32, (B, T, POOL_BLOCKS))
     if bmax is not None:

@@ -95,8 +95,9 @@ int csa2_index_score(int mode, const uint8_t* q_idx, const float* w, const uint8
   if (mode != CSA2_FULL && mode != CSA2_REINDEX) return CSA2_EINVAL;
   if (!sizes_ok(B, T, n_cap)) return CSA2_EINVAL;
   if (!aligned16(q_idx) || !aligned16(w) || !aligned16(k_idx) || !aligned16(n_vis) ||
-      !aligned16(scores) || !opt_aligned16(bmax))
+      !opt_aligned16(scores) || !opt_aligned16(bmax))
     return CSA2_EINVAL;
+  if (!scores && (mode != CSA2_FULL || !bmax)) return CSA2_EINVAL;   // something to write
   if (mode == CSA2_REINDEX && (!aligned16(pool) || bmax)) return CSA2_EINVAL;
   hipError_t e;
   if (mode == CSA2_FULL && T >= 64)

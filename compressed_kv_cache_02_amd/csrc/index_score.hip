@@ -122,7 +122,7 @@ __global__ __launch_bounds__(256) void k_index_score_decode(
 
   const uint8_t* kbase = k_idx + (size_t)b * (size_t)n_cap * kIdxDim + half * 64;
   const int32_t* pl = MODE == 1 ? pool + (size_t)qi * kPoolBlocks : nullptr;
-  float* srow = scores + (size_t)qi * (size_t)n_items;
+  float* srow = scores ? scores + (size_t)qi * (size_t)n_items : nullptr;
   float* brow = bmax ? bmax + (size_t)qi * (size_t)n_blk : nullptr;
 
   constexpr int kTilesPerWave = tiles_per_wave<MODE>();
@@ -185,7 +185,7 @@ __global__ __launch_bounds__(256) void k_index_score_decode(
       if (cur_ok) s = tot;
     }
     const int64_t item = tile0 + col;
-    if (half == 0 && item < n_items) srow[item] = s;
+    if (srow && half == 0 && item < n_items) srow[item] = s;
     if (brow) {
       const float m = max_over_8_lanes(s);
       if (half == 0 && (col & 7) == 0 && item < n_items) brow[item >> 3] = m;
@@ -312,7 +312,7 @@ __global__ __launch_bounds__(kPfThreads) void k_index_score_prefill(
       if (key >= nvq) s = -INFINITY;
       const bool store = tqq < T && key < n_cap;
       const size_t qi = (size_t)b * T + (size_t)tqq;
-      if (store) scores[qi * (size_t)n_cap + key] = s;
+      if (store && scores) scores[qi * (size_t)n_cap + key] = s;
       if (BMAX) {
         const float m = max_over_8_lanes(s);
         if (store && (col & 7) == 0) bmax[qi * (size_t)n_blk + (key >> 3)] = m;
@@ -334,7 +334,7 @@ __global__ __launch_bounds__(kPfThreads) void k_index_score_prefill(
       const int64_t nvq = half ? nv[2 * qp + 1] : nv[2 * qp];
       const int tqq = half ? tq[2 * qp + 1] : tq[2 * qp];
       const size_t qi = (size_t)b * T + (size_t)tqq;
-      sp[qp] = scores + qi * (size_t)n_cap + chunk0 + col;
+      sp[qp] = scores ? scores + qi * (size_t)n_cap + chunk0 + col : nullptr;
       if (BMAX) bp[qp] = bmax + qi * (size_t)n_blk + ((chunk0 + col) >> 3);
       int64_t l = nvq - chunk0 - col;
       lim[qp] = (int)(l < -1 ? -1 : (l > kPfChunk ? kPfChunk : l));
@@ -347,7 +347,7 @@ __global__ __launch_bounds__(kPfThreads) void k_index_score_prefill(
                                                         __float_as_uint(p[2 * qp + 1]), false, false);
       float s = __uint_as_float(sw2[0]) + __uint_as_float(sw2[1]);
       s = t * kTilePos < lim[qp] ? s : -INFINITY;
-      sp[qp][t * kTilePos] = s;
+      if (scores) sp[qp][t * kTilePos] = s;
       if (BMAX) {
         const float m = max_over_8_lanes(s);
         if ((col & 7) == 0) bp[qp][t * (kTilePos / kBlock)] = m;

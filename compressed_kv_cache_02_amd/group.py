@@ -55,10 +55,17 @@ class LayerGroup:
         L = len(self.sched)
         n_blk = (n_cap + BLOCK - 1) // BLOCK
         need_pool = any(m == REINDEX for m, _ in self.sched)
-        self.scores = torch.empty((B, T, n_cap), dtype=torch.float32, device=dev)
-        # block maxima come with the scan and drive the hierarchical selections
+        # Block maxima come with the scan and drive the hierarchical selections.
+        # A group with a pool writes no full score rows: its Full layer
+        # re-scores the pool's 16,384 positions (bit-identical to the scan) and
+        # takes its Top-K there, exact because the 512 best positions always
+        # lie inside the 2,048 best blocks.
         self.bmax = torch.empty((B, T, n_blk), dtype=torch.float32, device=dev)
+        self.scores = None if need_pool else torch.empty((B, T, n_cap), dtype=torch.float32,
+                                                         device=dev)
         self.pool = torch.empty((B, T, POOL_BLOCKS), dtype=torch.int32, device=dev) if need_pool else None
+        self.scores_full_pool = (torch.empty((B, T, POOL_CAND), dtype=torch.float32, device=dev)
+                                 if need_pool else None)
         self.scores_pool = (torch.empty((B, T, POOL_CAND), dtype=torch.float32, device=dev)
                             if need_pool else None)
         self.idx = [None] * L
@@ -106,7 +113,7 @@ class LayerGroup:
         """The Full layer's scan of every visible position, with block maxima."""
         li = [i for i, (m, _) in enumerate(self.sched) if m == FULL][0]
         csa2_index_score(CSA2_FULL, q_idx[li], w[li], k_idx, n_vis, None, self.scores, self.bmax,
-                         stream=stream)
+                         stream=stream)   # scores is None when the group has a pool
 
     def rest(self, k_idx, cache, n_vis, q_pos, swa_pos0, q_idx, w, q, swa, scale=1.0,
              stream=None):
@@ -116,11 +123,16 @@ class LayerGroup:
                 if self.pool is not None:
                     csa2_build_pool(self.bmax, True, n_vis, self.n_cap, self.pool, self.ws,
                                     stream=stream)
-                # with a pool the Full Top-K searches its 16,384 positions
-                csa2_topk(CSA2_FULL, self.scores, n_vis, self.pool, None, self.n_cap,
-                          self.idx[li], self.ws, stream=stream, bmax=self.bmax)
+                    csa2_index_score(CSA2_REINDEX, q_idx[li], w[li], k_idx, n_vis, self.pool,
+                                     self.scores_full_pool, None, stream=stream)
+                    csa2_topk(CSA2_REINDEX, self.scores_full_pool, n_vis, self.pool, None,
+                              self.n_cap, self.idx[li], self.ws, stream=stream)
+                else:
+                    csa2_topk(CSA2_FULL, self.scores, n_vis, None, None, self.n_cap,
+                              self.idx[li], self.ws, stream=stream, bmax=self.bmax)
                 if self.keep_scores:
-                    self.saved_scores[li] = self.scores.clone()
+                    self.saved_scores[li] = (self.scores if self.scores is not None
+                                             else self.scores_full_pool).clone()
             elif mode == REINDEX:
                 csa2_index_score(CSA2_REINDEX, q_idx[li], w[li], k_idx, n_vis, self.pool,
                                  self.scores_pool, None, stream=stream)

@@ -117,6 +117,10 @@ int csa2_quantize_kv(const void* kv_bf16, const float* cos_sin, const int64_t* d
  *   mode FULL:    scores[b][t][n] for every n < n_cap; n >= n_vis[b][t] gets -inf.
  *                 If `bmax` is not NULL, bmax[b][t][j] = max of scores over
  *                 positions 8j..8j+7 (visible ones; -inf if none), j < ceil(n_cap/8).
+ *                 `scores` may be NULL when `bmax` is not: only the block maxima
+ *                 are written (scores of chosen positions can be recomputed
+ *                 bit for bit with REINDEX, which evaluates each position the
+ *                 same way).
  *   mode REINDEX: scores[b][t][i] for i < 16384 at position 8*pool[b][t][i/8] + i%8;
  *                 -inf where the pool entry is -1 or the position is >= n_vis.
  *                 `bmax` must be NULL.
@@ -126,7 +130,7 @@ int csa2_quantize_kv(const void* kv_bf16, const float* cos_sin, const int64_t* d
  *         treated as -1).
  * Products are exact; sums are float32 (MFMA accumulation order).
  * Errors: CSA2_EINVAL for REUSE, NULL/misaligned pointers, REINDEX without a
- * pool, B < 1, T < 1, n_cap < 1 or n_cap >= 2^31. */
+ * pool, nothing to write, B < 1, T < 1, n_cap < 1 or n_cap >= 2^31. */
 int csa2_index_score(int mode, const uint8_t* q_idx, const float* w, const uint8_t* k_idx,
                      const int32_t* n_vis, const int32_t* pool, int B, int T, int64_t n_cap,
                      float* scores, float* bmax, void* stream);

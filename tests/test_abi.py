@@ -88,6 +88,9 @@ def test_index_score_rejects_bad_arguments():
     assert call(k=FAKE_MIS) == C.CSA2_EINVAL
     assert call(mode=1, pool=0) == C.CSA2_EINVAL                # REINDEX needs a pool
     assert call(mode=1, bm=FAKE) == C.CSA2_EINVAL               # no block max in REINDEX
+    assert call(s=0) == C.CSA2_EINVAL                           # FULL: nothing to write
+    assert call(mode=1, s=0) == C.CSA2_EINVAL                   # REINDEX needs scores
+    assert call(s=0, bm=FAKE_MIS) == C.CSA2_EINVAL
     assert call(B=0) == C.CSA2_EINVAL
     assert call(T=0) == C.CSA2_EINVAL
     assert call(n_cap=0) == C.CSA2_EINVAL

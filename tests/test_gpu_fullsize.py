@@ -132,48 +132,62 @@ def check_selection(idx, vals, n_items_vis, what, k=K):
     assert not bool(tie_out.any()), what + ": tie not resolved to the lower id"
 
 
+def check_pool_topk(idx, sp, pool, nv, n_cap, what):
+    """idx must be the exact Top-K of the pool candidates' scores sp (slot i is
+    position 8 * pool[i // 8] + i % 8), written as ascending positions."""
+    Q = idx.shape[0]
+    pool = pool.long()
+    cand = (pool[:, :, None] * 8 + torch.arange(8, device=DEV)).reshape(Q, -1)
+    cand = torch.where((pool[:, :, None] >= 0).expand(-1, -1, 8).reshape(Q, -1), cand,
+                       torch.full_like(cand, -1))
+    ok = (cand >= 0) & (cand < nv[:, None])
+    assert bool(torch.isneginf(sp[~ok]).all()), what + ": non-candidates must be -inf"
+    # map selected positions back to candidate slots and check there
+    slot_of = torch.full((Q, n_cap), -1, dtype=torch.long, device=DEV)
+    q_ids = torch.arange(Q, device=DEV)[:, None].expand_as(cand)
+    slot_of[q_ids[ok], cand[ok]] = torch.arange(cand.shape[1], device=DEV).expand_as(cand)[ok]
+    v = idx >= 0
+    sidx = torch.where(v, slot_of.gather(1, torch.where(v, idx, 0).long()), -1)
+    assert bool((sidx[v] >= 0).all()), what + ": a position outside the pool"
+    # candidate slots ascend with positions, so the plain check applies
+    check_selection(sidx.to(torch.int32), sp, None, what)
+
+
 def check_properties(w, g, n_vis):
     Q = w.B * w.T
     nv = n_vis.reshape(Q).long()
-    scores = g.scores.reshape(Q, w.n_cap)
-    ids = torch.arange(w.n_cap, device=DEV)
-    vis = ids[None, :] < nv[:, None]
-    assert bool(torch.isneginf(scores[~vis]).all()), "invisible positions must score -inf"
-    assert bool(torch.isfinite(scores[vis]).all()), "visible scores must be finite"
+    n_blk = (w.n_cap + 7) // 8
+    bmax = g.bmax.reshape(Q, n_blk)
+    nb = (nv + 7) // 8
+    blk_vis = torch.arange(n_blk, device=DEV)[None, :] < nb[:, None]
+    assert bool(torch.isneginf(bmax[~blk_vis]).all()), "invisible blocks must have -inf maxima"
+    assert bool(torch.isfinite(bmax[blk_vis]).all()), "visible blocks must have finite maxima"
+    if g.scores is not None:
+        scores = g.scores.reshape(Q, w.n_cap)
+        ids = torch.arange(w.n_cap, device=DEV)
+        vis = ids[None, :] < nv[:, None]
+        assert bool(torch.isneginf(scores[~vis]).all()), "invisible positions must score -inf"
+        assert bool(torch.isfinite(scores[vis]).all()), "visible scores must be finite"
+        pad = torch.full((Q, n_blk * 8), -float("inf"), device=DEV)
+        pad[:, :w.n_cap] = scores
+        assert torch.equal(bmax, pad.reshape(Q, n_blk, 8).max(dim=2).values), "block maxima"
     last_x = max([li for li, (mode, _) in enumerate(g.sched) if mode == "X"], default=-1)
     for li, (mode, src) in enumerate(g.sched):
         idx = g.idx[li].reshape(Q, K)
-        if mode == "F":
-            check_selection(idx, scores, nv, "Full Top-K")
+        if mode == "F" and g.scores is not None:
+            check_selection(idx, g.scores.reshape(Q, w.n_cap), nv, "Full Top-K")
+        elif mode == "F":
+            # Full Top-K taken inside the pool from the re-scored candidates
+            check_pool_topk(idx, g.scores_full_pool.reshape(Q, -1), g.pool.reshape(Q, -1), nv,
+                            w.n_cap, "Full Top-K in the pool")
         elif mode == "X" and li == last_x:
             # (the Reindex layers share one score buffer: the last one's remains)
-            # the pool's candidate list, -inf where not a visible pooled position
-            sp = g.scores_pool.reshape(Q, -1)
-            pool = g.pool.reshape(Q, -1).long()
-            cand = (pool[:, :, None] * 8 + torch.arange(8, device=DEV)).reshape(Q, -1)
-            cand = torch.where((pool[:, :, None] >= 0).expand(-1, -1, 8).reshape(Q, -1), cand,
-                               torch.full_like(cand, -1))
-            ok = (cand >= 0) & (cand < nv[:, None])
-            assert bool(torch.isneginf(sp[~ok]).all()), "Reindex: non-candidates must be -inf"
-            # map selected positions back to candidate slots and check there
-            slot_of = torch.full((Q, w.n_cap), -1, dtype=torch.long, device=DEV)
-            q_ids = torch.arange(Q, device=DEV)[:, None].expand_as(cand)
-            slot_of[q_ids[ok], cand[ok]] = torch.arange(cand.shape[1], device=DEV).expand_as(cand)[ok]
-            v = idx >= 0
-            sidx = torch.where(v, slot_of.gather(1, torch.where(v, idx, 0).long()), -1)
-            assert bool((sidx[v] >= 0).all()), "Reindex picked a position outside the pool"
-            # candidate slots ascend with positions, so the same check applies
-            check_selection(sidx.to(torch.int32), sp, None, "Reindex Top-K")
+            check_pool_topk(idx, g.scores_pool.reshape(Q, -1), g.pool.reshape(Q, -1), nv,
+                            w.n_cap, "Reindex Top-K")
         elif mode == "U":
             assert torch.equal(idx, g.idx[src].reshape(Q, K)), "Reuse differs from its source"
         assert bool(torch.isfinite(g.out[li]).all()), "attention output not finite (layer %d)" % li
     if g.pool is not None:
-        n_blk = (w.n_cap + 7) // 8
-        bmax = g.bmax.reshape(Q, n_blk)
-        pad = torch.full((Q, n_blk * 8), -float("inf"), device=DEV)
-        pad[:, :w.n_cap] = scores
-        assert torch.equal(bmax, pad.reshape(Q, n_blk, 8).max(dim=2).values), "block maxima"
-        nb = (nv + 7) // 8
         check_selection(g.pool.reshape(Q, -1), bmax, nb, "pool", k=C.POOL_BLOCKS)
 
 

@@ -163,6 +163,44 @@ def test_index_score_prefill_shape(B, T, n_cap):
                                 "b%d t%d" % (b, t))
 
 
+@pytest.mark.parametrize("T", [1, 70])
+def test_full_scan_block_maxima_only_and_rescoring(T):
+    """A FULL scan that writes only block maxima gives the same maxima bit for
+    bit, and REINDEX over a pool reproduces the FULL scores of its positions bit
+    for bit (so a Top-K over re-scored pool positions is the Full Top-K)."""
+    B, n_cap = 2, 40003
+    _stage("scan bmax-only + rescoring", B, T, n_cap)
+    q, w, k = _idx_inputs(B, T, n_cap, 11)
+    rng = np.random.default_rng(T)
+    nv = rng.integers(n_cap // 2, n_cap + 1, (B, T)).astype(np.int32)
+    nv.flat[0] = n_cap
+    n_vis = torch.from_numpy(nv).to(DEV)
+    nb = (n_cap + 7) // 8
+    scores = torch.empty((B, T, n_cap), dtype=torch.float32, device=DEV)
+    bmax = torch.empty((B, T, nb), dtype=torch.float32, device=DEV)
+    bmax2 = torch.full_like(bmax, 7.0)
+    C.csa2_index_score(C.CSA2_FULL, q, w, k, n_vis, None, scores, bmax)
+    C.csa2_index_score(C.CSA2_FULL, q, w, k, n_vis, None, None, bmax2)
+    pool = torch.empty((B, T, 2048), dtype=torch.int32, device=DEV)
+    ws = torch.empty(C.csa2_workspace_bytes(C.CSA2_OP_BUILD_POOL, 0, B, T, n_cap),
+                     dtype=torch.uint8, device=DEV)
+    C.csa2_build_pool(bmax2, True, n_vis, n_cap, pool, ws)
+    sp = torch.empty((B, T, 16384), dtype=torch.float32, device=DEV)
+    C.csa2_index_score(C.CSA2_REINDEX, q, w, k, n_vis, pool, sp, None)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_np(bmax).view(np.uint32), to_np(bmax2).view(np.uint32))
+    sn, spn, pn = to_np(scores), to_np(sp), to_np(pool)
+    for b in range(B):
+        for t in range(T):
+            cand = OS.reindex_candidates(pn[b, t], nv[b, t])
+            p = pn[b, t]
+            pos_all = (np.maximum(p, 0)[:, None] * 8 + np.arange(8)[None, :]).reshape(-1)
+            valid = np.repeat(p >= 0, 8) & (pos_all < nv[b, t])
+            assert np.array_equal(pos_all[valid], cand)
+            assert np.array_equal(spn[b, t][valid].view(np.uint32), sn[b, t][cand].view(np.uint32))
+            assert np.all(np.isneginf(spn[b, t][~valid]))
+
+
 def test_index_score_reindex():
     _stage("index_score reindex")
     B, T, n_cap = 2, 2, 30000
