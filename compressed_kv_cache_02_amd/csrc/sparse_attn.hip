@@ -457,14 +457,18 @@ struct Gather8 {
     g4 = 4 * (w >> 2) + ((t & 63) >> 4);
   }
 
+  // This thread's 4 selected positions of `chunk` (unused for window chunks).
+  __device__ __forceinline__ int4 load_idx(int chunk) const {
+    const int slot0 = chunk * kChunkKeys + g4 * 4;
+    return slot0 < kTopK ? *reinterpret_cast<const int4*>(idx_q + slot0) : make_int4(-1, -1, -1, -1);
+  }
+
   // Raw bytes of this thread's 4 keys; bit j marks key j present. Row loads are
   // unconditional (an absent key reads row 0) so none waits on another.
-  __device__ __forceinline__ uint32_t load(int chunk, int chunk0, const int32_t* sidx,
-                                           uint2 (&r)[4]) const {
+  __device__ __forceinline__ uint32_t load(int chunk, const int4& i4, uint2 (&r)[4]) const {
     const int slot0 = chunk * kChunkKeys + g4 * 4;
     uint32_t ok = 0;
     if (slot0 < kTopK) {
-      const int4 i4 = *reinterpret_cast<const int4*>(sidx + (slot0 - chunk0 * kChunkKeys));
       const int32_t pj[4] = {i4.x, i4.y, i4.z, i4.w};
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -485,12 +489,6 @@ struct Gather8 {
       }
     }
     return ok;
-  }
-
-  __device__ __forceinline__ void stage_idx(int chunk0, int n, int32_t* sidx) const {
-    const int s0 = chunk0 * kChunkKeys;
-    const int cnt = min(n * kChunkKeys, kTopK - s0);
-    for (int i = threadIdx.x; i < cnt; i += blockDim.x) sidx[i] = idx_q[s0 + i];
   }
 
   // Dequantise (as Gather::store) into krow; flags presence.
@@ -583,7 +581,6 @@ __global__ __launch_bounds__(512) void k_sparse_attn_decode8(AttnArgs a) {
   __shared__ float spart[2][2][4][16][kHG];
   __shared__ int kvalid[2][kChunkKeys];
   __shared__ float qmax[4][kHG];
-  __shared__ __attribute__((aligned(16))) int32_t sidx[CPS * kChunkKeys];
 
   const int qi = blockIdx.y;
   const int hg = blockIdx.x % kHeadGroups;
@@ -667,56 +664,64 @@ __global__ __launch_bounds__(512) void k_sparse_attn_decode8(AttnArgs a) {
     zscale = ldexpf(a.scale, -sh);
   };
 
-  g.stage_idx(chunk0, CPS, sidx);
-  load_q();   // ends with a barrier, which also publishes sidx
+  // Every index this thread needs is requested first, then the first rows,
+  // so the index -> row chain overlaps the query set-up.
+  int4 ix[CPS];
+  static_for<CPS>([&](auto ii) __attribute__((always_inline)) {
+    constexpr int i = decltype(ii)::value;
+    ix[i] = g.load_idx(chunk0 + i);
+  });
   constexpr int PF = CPS < 4 ? CPS : 4;
-  {
-    uint2 raw[PF][4];
-    uint32_t okm[PF];
+  uint2 raw[PF][4];
+  uint32_t okm[PF];
+  static_for<PF>([&](auto ii) __attribute__((always_inline)) {
+    constexpr int i = decltype(ii)::value;
+    if (i < CPS) okm[i] = g.load(chunk0 + i, ix[i], raw[i]);
+  });
+  load_q();   // ends with a barrier
+  for (int c0 = 0; c0 < CPS; c0 += PF) {
     static_for<PF>([&](auto ii) __attribute__((always_inline)) {
       constexpr int i = decltype(ii)::value;
-      if (i < CPS) okm[i] = g.load(chunk0 + i, chunk0, sidx, raw[i]);
-    });
-    for (int c0 = 0; c0 < CPS; c0 += PF) {
-      static_for<PF>([&](auto ii) __attribute__((always_inline)) {
-        constexpr int i = decltype(ii)::value;
-        const int c = c0 + i;
-        if (c < CPS) {
-          uint2 cur[4];
+      const int c = c0 + i;
+      if (c < CPS) {
+        uint2 cur[4];
 #pragma unroll
-          for (int j = 0; j < 4; ++j) cur[j] = raw[i][j];
-          const uint32_t cok = okm[i];
-          if (c + PF < CPS) okm[i] = g.load(chunk0 + c + PF, chunk0, sidx, raw[i]);
-          chunk(c, cur, cok);
+        for (int j = 0; j < 4; ++j) cur[j] = raw[i][j];
+        const uint32_t cok = okm[i];
+        if (c + PF < CPS) {
+          static_for<CPS>([&](auto jj) __attribute__((always_inline)) {
+            constexpr int cc = decltype(jj)::value;
+            if (cc == c + PF) okm[i] = g.load(chunk0 + cc, ix[cc], raw[i]);
+          });
         }
-      });
-    }
+        chunk(c, cur, cok);
+      }
+    });
   }
 
   // Combine the two key halves: half 1 hands its state to half 0 through LDS
   // (reusing the key buffer and the partial sums once every wave is done).
   __syncthreads();
-  float* xs = reinterpret_cast<float*>(krow);        // [4][64 lanes][32]
+  float* xs = reinterpret_cast<float*>(krow);        // [4 quarters][8 tiles][64 lanes][4]
   float* xml = &spart[0][0][0][0][0];                // [4][64 lanes][2]
   if (kh == 1) {
-    float* d = xs + ((size_t)cq * 64 + lane) * 32;
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt)
-      *reinterpret_cast<float4*>(d + dt * 4) = make_float4(acc[dt][0], acc[dt][1], acc[dt][2], acc[dt][3]);
+      *reinterpret_cast<float4*>(xs + (((size_t)cq * 8 + dt) * 64 + lane) * 4) =
+          make_float4(acc[dt][0], acc[dt][1], acc[dt][2], acc[dt][3]);
     xml[(cq * 64 + lane) * 2 + 0] = m_run;
     xml[(cq * 64 + lane) * 2 + 1] = l_run;
   }
   __syncthreads();
   if (kh == 1) return;
   {
-    const float* d = xs + ((size_t)cq * 64 + lane) * 32;
     const float m1 = xml[(cq * 64 + lane) * 2 + 0], l1 = xml[(cq * 64 + lane) * 2 + 1];
     const float M = fmaxf(m_run, m1);
     const float w0 = m_run == -INFINITY ? 0.0f : __expf(m_run - M);
     const float w1 = m1 == -INFINITY ? 0.0f : __expf(m1 - M);
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) {
-      const float4 o = *reinterpret_cast<const float4*>(d + dt * 4);
+      const float4 o = *reinterpret_cast<const float4*>(xs + (((size_t)cq * 8 + dt) * 64 + lane) * 4);
       acc[dt][0] = acc[dt][0] * w0 + o.x * w1;
       acc[dt][1] = acc[dt][1] * w0 + o.y * w1;
       acc[dt][2] = acc[dt][2] * w0 + o.z * w1;
@@ -844,7 +849,7 @@ hipError_t launch_sparse_attn(const uint16_t* q, const uint8_t* cache, const int
   a.part = nullptr;
   a.part_ml = nullptr;
   const Shape sh = attn_shape(Q);
-  if (sh.splits > kMaxSplits) return hipErrorInvalidValue;
+  if (sh.splits > kMaxSplits || (!sh.wide && sh.splits != 5)) return hipErrorInvalidValue;
   a.splits = sh.splits;
   if (a.splits > 1) {
     a.part = reinterpret_cast<float*>(ws);
@@ -861,15 +866,9 @@ hipError_t launch_sparse_attn(const uint16_t* q, const uint8_t* cache, const int
       default: hipLaunchKernelGGL(k_sparse_attn_wide<20>, grid, dim3(kThreads), 0, st, a); break;
     }
   } else {
+    // the decode shape always runs 5 slices of 4 chunks
     const dim3 grid(a.splits * kHeadGroups, Q);
-    switch (kChunks / a.splits) {
-      case 1: hipLaunchKernelGGL(k_sparse_attn_decode8<1>, grid, dim3(512), 0, st, a); break;
-      case 2: hipLaunchKernelGGL(k_sparse_attn_decode8<2>, grid, dim3(512), 0, st, a); break;
-      case 4: hipLaunchKernelGGL(k_sparse_attn_decode8<4>, grid, dim3(512), 0, st, a); break;
-      case 5: hipLaunchKernelGGL(k_sparse_attn_decode8<5>, grid, dim3(512), 0, st, a); break;
-      case 10: hipLaunchKernelGGL(k_sparse_attn_decode8<10>, grid, dim3(512), 0, st, a); break;
-      default: hipLaunchKernelGGL(k_sparse_attn_decode8<20>, grid, dim3(512), 0, st, a); break;
-    }
+    hipLaunchKernelGGL(k_sparse_attn_decode8<kChunks / 5>, grid, dim3(512), 0, st, a);
   }
   if (a.splits > 1)
     hipLaunchKernelGGL(k_attn_merge, dim3(kHeads, Q), dim3(128), 0, st, a.part, a.part_ml,
