@@ -13,7 +13,11 @@ kernel (the Full-mode scan; its duration is measured with HIP events around
 its launches inside the timed region, on the stream it is launched on), and
 the oracle's throughput on the host cores for a bounded sample.
 
-Usage: python bench.py [--steps K] [--warmup W] [--gpus 1] [--workload c2|c4|c1]
+Usage: python bench.py [--steps K] [--warmup W] [--gpus 1] [--workload c2|c4|c1|c3]
+
+The default workload is the 1M-context decoder group. `--workload c3` times the
+4,096-query prefill chunk instead (no write path; its scan is an FP8 MFMA
+contraction, so its roofline is reported against the FP8 MFMA peak).
 """
 
 import argparse
@@ -27,6 +31,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, HERE)
 
 HBM_PEAK_GBS = 8000.0
+FP8_MFMA_PEAK_TFLOPS = 5000.0      # dense FP8 MFMA, MI355X
 SCAN_KERNEL = "k_index_score_decode"
 TRAFFIC_FILE = os.path.join(HERE, "profiles", "traffic_index_score_full_c2.json")
 SCAN_SOURCE = os.path.join(HERE, "compressed_kv_cache_02_amd", "csrc", "index_score.hip")
@@ -41,7 +46,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=10)
-    p.add_argument("--workload", default="c2", choices=["c1", "c2", "c4"])
+    p.add_argument("--workload", default="c2", choices=["c1", "c2", "c3", "c4"])
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--graph", dest="graph", action="store_true", default=True,
                    help="replay each step segment as a HIP graph (default)")
@@ -75,13 +80,16 @@ def source_sha(path):
 
 def read_traffic(n_launch_bytes):
     """HBM traffic per scan launch from the committed rocprofv3 counter summary,
-    or None if missing or taken on another version of the kernel."""
+    or None if missing, taken on another version of the kernel or on another
+    workload (another number of algorithmic bytes per launch)."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
     if t.get("source_sha") != source_sha(SCAN_SOURCE):
+        return None
+    if t.get("algorithmic_bytes_per_launch") != n_launch_bytes:
         return None
     return t.get("traffic_bytes_per_launch")
 
@@ -111,7 +119,8 @@ def cpu_baseline(w, inp, seed, new_rows, budget_s=10.0):
         for b in range(w.B):
             main_b = synth.pooled_main_rows(n_cap, m, "cuda", seed, w.name, "main", b,
                                             outliers=w.outliers)
-            main_b[n_cap - 1] = new_rows[b]
+            if new_rows is not None:
+                main_b[n_cap - 1] = new_rows[b]
 
             class Cache:
                 def __getitem__(self, sel, _rows=main_b):
@@ -137,8 +146,10 @@ def cpu_baseline(w, inp, seed, new_rows, budget_s=10.0):
             if spent >= budget_s:
                 break
     return {"value": done / spent, "unit": "queries/s", "cores": 1, "kind": "oracle",
-            "sample": "%d of %d queries, each through all %d layers incl. the write-path row; "
-                      "%.1f s of single-threaded oracle time" % (done, w.B * w.T, len(sched), spent)}
+            "sample": "%d of %d queries, each through all %d layers%s; "
+                      "%.1f s of single-threaded oracle time" % (
+                          done, w.B * w.T, len(sched),
+                          " incl. the write-path row" if new_rows is not None else "", spent)}
 
 
 def main():
@@ -169,15 +180,21 @@ def main():
     inp["main_rows_per_seq"] = None
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
-    # per-step write path: one new row per sequence into the newest slot
-    if "write_bf16" in inp:
-        new_rows = inp["write_bf16"]
+    # per-step write path of a decode step: one new row per sequence into the
+    # newest slot (the prefill chunk has none)
+    prefill = T > 1
+    if prefill:
+        new_rows, write = None, None
     else:
-        import synth
-        new_rows = synth.token_rows_bf16(B, dev, seed, w.name, "write")
-    slot = torch.arange(B, dtype=torch.int64, device=dev) * n_cap + (n_cap - 1)
-    cs_new = torch.from_numpy(C.csa2_rope_table(np.full(B, (n_cap - 1) * m, dtype=np.int64))).to(dev)
-    write = (new_rows, cs_new, slot)
+        if "write_bf16" in inp:
+            new_rows = inp["write_bf16"]
+        else:
+            import synth
+            new_rows = synth.token_rows_bf16(B, dev, seed, w.name, "write")
+        slot = torch.arange(B, dtype=torch.int64, device=dev) * n_cap + (n_cap - 1)
+        cs_new = torch.from_numpy(C.csa2_rope_table(np.full(B, (n_cap - 1) * m,
+                                                            dtype=np.int64))).to(dev)
+        write = (new_rows, cs_new, slot)
 
     n_vis = visible_entries(inp["q_pos"], m).to(torch.int32)
     n_vis_total = int(n_vis.sum().item())
@@ -188,7 +205,8 @@ def main():
                  inp["w"], inp["q"], inp["swa"])
 
     def seg_write():
-        g.write(cache, write)
+        if write is not None:
+            g.write(cache, write)
 
     def seg_scan():
         g.scan(inp["k_idx"], n_vis, inp["q_idx"], inp["w"])
@@ -214,13 +232,16 @@ def main():
                 f()
         torch.cuda.current_stream().wait_stream(side)
         torch.cuda.synchronize()
-        for f in segs:
+        for k, f in enumerate(segs):
+            if k == 0 and write is None:
+                graphs.append(None)          # nothing to capture
+                continue
             gr = torch.cuda.CUDAGraph()
             with torch.cuda.graph(gr):
                 f()
             graphs.append(gr)
         torch.cuda.synchronize()
-        segs = [gr.replay for gr in graphs]
+        segs = [gr.replay if gr is not None else (lambda: None) for gr in graphs]
         for _ in range(max(1, args.warmup)):
             for f in segs:
                 f()
@@ -249,11 +270,29 @@ def main():
     qps = B * T * args.steps / el
     scan_ms = float(np.mean([s.elapsed_time(e) for s, e in ev]))
     scan_bytes = scan_algorithmic_bytes(B, T, n_vis_total)
-    achieved = scan_bytes / (scan_ms * 1e-3) / 1e9
-    traffic = read_traffic(scan_bytes)
-    step_bytes = step_algorithmic_bytes(w, n_vis_total)
+    if prefill:
+        # a dense FP8 contraction: 32 heads x 128 channels x 2 FLOP per visible pair
+        scan_flop = 8192 * n_vis_total
+        achieved = scan_flop / (scan_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": FP8_MFMA_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / FP8_MFMA_PEAK_TFLOPS, 4),
+                "traffic": None, "kernel": "k_index_score_prefill",
+                "kernel_ms": round(scan_ms, 4), "algorithmic_flop_per_launch": scan_flop}
+        step_roof = None
+    else:
+        achieved = scan_bytes / (scan_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": read_traffic(scan_bytes), "kernel": SCAN_KERNEL,
+                "kernel_ms": round(scan_ms, 4), "algorithmic_bytes_per_launch": scan_bytes}
+        step_bytes = step_algorithmic_bytes(w, n_vis_total)
+        step_roof = {"algorithmic_bytes": step_bytes,
+                     "achieved_GBps": round(step_bytes / (ms * 1e-3) / 1e9, 1),
+                     "frac": round(step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
     res = {
-        "metric": "CSA2 decode queries/s at 1M ctx (Top-512 + SWA-128); % HBM/MFMA roofline",
+        "metric": ("CSA2 prefill queries/s, 4,096-query chunk after 262,144 tokens; % MFMA roofline"
+                   if prefill else
+                   "CSA2 decode queries/s at 1M ctx (Top-512 + SWA-128); % HBM/MFMA roofline"),
         "value": round(qps, 2),
         "unit": "queries/s",
         "n_gpus": 1,
@@ -268,16 +307,12 @@ def main():
         "config": {"workload": "%s: %s" % (w.name, {
             "c2": "decoder layer group [F,X,U,X,U,X,U] at 1,048,576 positions (m=1), batch 8 decode, + write path",
             "c4": "encoder group [F,U x5] at 1,048,576 tokens (m=2, 524,288 entries), batch 64 decode, write path, outliers",
-            "c1": "Full-mode decode, batch 32, 131,072 tokens (m=2, 65,536 entries)"}[w.name]),
+            "c1": "Full-mode decode, batch 32, 131,072 tokens (m=2, 65,536 entries)",
+            "c3": "Full-mode prefill of 4,096 queries after 262,144 tokens (m=2, 131,072-133,120 visible entries)"}[w.name]),
             "batch": B, "queries_per_seq": T, "n_cap": n_cap, "layers": len(g.sched),
             "topk": 512, "window": 128, "timing": "HIP graph replay" if args.graph else "eager"},
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic, "kernel": SCAN_KERNEL,
-                     "kernel_ms": round(scan_ms, 4), "algorithmic_bytes_per_launch": scan_bytes},
-        "step_roofline": {"algorithmic_bytes": step_bytes,
-                          "achieved_GBps": round(step_bytes / (ms * 1e-3) / 1e9, 1),
-                          "frac": round(step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
+        "roofline": roof,
+        "step_roofline": step_roof,
     }
     log("timed %d steps: %.3f ms/step; running the oracle sample" % (args.steps, ms))
     if not args.no_cpu_baseline:
