@@ -9,9 +9,11 @@ Reindex scans inside the pool, Reuse, and sparse attention in every layer.
 Inputs are seeded synthetic tensors already resident in HBM.
 
 Prints ONE JSON line (rank 0) with the queries/s, the roofline of the dominant
-kernel (the Full-mode scan; its duration is measured with HIP events around
-its launches inside the timed region, on the stream it is launched on), and
-the oracle's throughput on the host cores for a bounded sample.
+kernel (the Full-mode scan) and the oracle's throughput on the host cores for a
+bounded sample. With graph replay (the default) each step is one HIP graph and
+the scan's duration comes from HIP events around a graph of `--steps`
+back-to-back scan launches on the same stream; with --eager the events bracket
+the scan inside every timed step.
 
 Usage: python bench.py [--steps K] [--warmup W] [--gpus 1] [--workload c2|c4|c1|c3]
 
@@ -220,45 +222,65 @@ def main():
         seg_scan()
         seg_rest()
     torch.cuda.synchronize()
-    segs = [seg_write, seg_scan, seg_rest]
+    stream = torch.cuda.current_stream()
+
+    def step():
+        seg_write()
+        seg_scan()
+        seg_rest()
+
     if args.graph:
-        # One HIP graph per segment, so HIP events can bracket the scan's graph
-        # on the stream it runs on; every call inside only launches kernels.
-        graphs = []
+        # The whole step is one HIP graph (every call inside only launches
+        # kernels); the scan's own duration is taken from a second graph that
+        # launches the scan R times back to back, bracketed by HIP events on the
+        # stream it runs on (events between graphs would add launch gaps to
+        # the step).
+        R = args.steps
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(side):
-            for f in segs:
-                f()
+            step()
         torch.cuda.current_stream().wait_stream(side)
         torch.cuda.synchronize()
-        for k, f in enumerate(segs):
-            if k == 0 and write is None:
-                graphs.append(None)          # nothing to capture
-                continue
-            gr = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(gr):
-                f()
-            graphs.append(gr)
+        step_graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(step_graph):
+            step()
+        scan_graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(scan_graph):
+            for _ in range(R):
+                seg_scan()
         torch.cuda.synchronize()
-        segs = [gr.replay if gr is not None else (lambda: None) for gr in graphs]
         for _ in range(max(1, args.warmup)):
-            for f in segs:
-                f()
+            step_graph.replay()
         torch.cuda.synchronize()
-    stream = torch.cuda.current_stream()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        segs[0]()
-        ev[i][0].record(stream)
-        segs[1]()
-        ev[i][1].record(stream)
-        segs[2]()
-    torch.cuda.synchronize()
-    el = time.perf_counter() - t0
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            step_graph.replay()
+        torch.cuda.synchronize()
+        el = time.perf_counter() - t0
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        scan_graph.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        scan_ms = e0.elapsed_time(e1) / R
+        step()                       # leave the buffers of a plain step behind
+        torch.cuda.synchronize()
+    else:
+        # eager: events bracket the scan inside every timed step
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            seg_write()
+            ev[i][0].record(stream)
+            seg_scan()
+            ev[i][1].record(stream)
+            seg_rest()
+        torch.cuda.synchronize()
+        el = time.perf_counter() - t0
+        scan_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
     if args.copy_calibration:
         a = torch.empty(1 << 28, dtype=torch.float32, device=dev)
         b2 = torch.empty_like(a)
@@ -268,7 +290,6 @@ def main():
 
     ms = el * 1e3 / args.steps
     qps = B * T * args.steps / el
-    scan_ms = float(np.mean([s.elapsed_time(e) for s, e in ev]))
     scan_bytes = scan_algorithmic_bytes(B, T, n_vis_total)
     if prefill:
         # a dense FP8 contraction: 32 heads x 128 channels x 2 FLOP per visible pair
@@ -310,7 +331,8 @@ def main():
             "c1": "Full-mode decode, batch 32, 131,072 tokens (m=2, 65,536 entries)",
             "c3": "Full-mode prefill of 4,096 queries after 262,144 tokens (m=2, 131,072-133,120 visible entries)"}[w.name]),
             "batch": B, "queries_per_seq": T, "n_cap": n_cap, "layers": len(g.sched),
-            "topk": 512, "window": 128, "timing": "HIP graph replay" if args.graph else "eager"},
+            "topk": 512, "window": 128, "timing": ("one HIP graph per step; scan timed over back-to-back launches"
+                       if args.graph else "eager")},
         "roofline": roof,
         "step_roofline": step_roof,
     }
