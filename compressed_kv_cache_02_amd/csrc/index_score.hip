@@ -79,6 +79,20 @@ __device__ __forceinline__ float max_over_8_lanes(float m) {
 }
 
 // sum over the lane's 16 accumulator rows of w_r * relu(acc_r), in row order
+// One 16-byte global -> LDS copy per lane, with no registers on the way: the
+// wave's 64 pieces land in 64 consecutive 16-byte slots starting at `dst`
+// (wave-uniform). Written as assembly so that the compiler does not make
+// every later LDS read wait for the copy: the reads of the other buffer may
+// proceed while it is in flight. wait_lds_dma() waits for all of them.
+__device__ __forceinline__ void lds_dma16(const uint4* src, uint4* dst) {
+  const uint32_t lds_addr = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint4*)dst;
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :: "v"(src), "s"(lds_addr) : "memory", "m0");
+}
+__device__ __forceinline__ void wait_lds_dma() {
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
 __device__ __forceinline__ float weighted_relu_sum(const v16f& acc, const float* wr) {
   float part = 0.0f;
 #pragma unroll
@@ -216,7 +230,8 @@ constexpr int kPfChunk = 256;                        // keys per LDS chunk
 constexpr int kPfChunksPerWG = 16;
 constexpr int kPfKeysPerWG = kPfChunk * kPfChunksPerWG;   // 4096
 constexpr int kPfPieces = kPfChunk * (kIdxDim / 16);      // 2048 16-byte pieces
-constexpr int kPfLoads = (kPfPieces + kPfThreads - 1) / kPfThreads;
+constexpr int kPfLoads = kPfPieces / kPfThreads;            // 4 per thread
+static_assert(kPfPieces % kPfThreads == 0, "a chunk is a whole number of loads per thread");
 
 template <bool BMAX>
 __global__ __launch_bounds__(kPfThreads) void k_index_score_prefill(
@@ -264,30 +279,31 @@ __global__ __launch_bounds__(kPfThreads) void k_index_score_prefill(
   const int n_chunks = (int)((span + kPfChunk - 1) / kPfChunk);
   const uint8_t* kseq = k_idx + (size_t)b * (size_t)n_cap * kIdxDim;
 
-  uint4 pre[kPfLoads];
-  auto load_chunk = [&](int c) __attribute__((always_inline)) {
+  // K rows of chunk c go straight from global memory into LDS buffer `buf`
+  // (no registers on the way): LDS slot s = row*8 + j holds piece
+  // j ^ ((row/8) & 7) of the chunk's row `row`. Each wave's load fills 64
+  // consecutive slots. Rows past n_cap repeat the last row; their scores are
+  // masked to -inf.
+  auto load_chunk = [&](int c, int buf) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < kPfLoads; ++i) {
-      const int p = tid + i * kPfThreads;
-      const int64_t row = key0 + (int64_t)c * kPfChunk + (p >> 3);
-      pre[i] = (p < kPfPieces && row < n_cap)
-                   ? *reinterpret_cast<const uint4*>(kseq + row * kIdxDim + (p & 7) * 16)
-                   : make_uint4(0, 0, 0, 0);
-    }
-  };
-  auto store_chunk = [&](int buf) __attribute__((always_inline)) {
-#pragma unroll
-    for (int i = 0; i < kPfLoads; ++i) {
-      const int p = tid + i * kPfThreads;
-      const int row = p >> 3;
-      if (p < kPfPieces) lds[buf][row * 8 + ((p & 7) ^ (row & 7))] = pre[i];
+      const int slot = tid + i * kPfThreads;
+      const int row = slot >> 3;
+      int64_t krow = key0 + (int64_t)c * kPfChunk + row;
+      krow = krow < n_cap ? krow : n_cap - 1;
+      const int piece = (slot & 7) ^ ((row >> 3) & 7);
+      lds_dma16(reinterpret_cast<const uint4*>(kseq + krow * kIdxDim) + piece,
+                &lds[buf][i * kPfThreads + wave * 64]);
     }
   };
 
-  // B operand of tile tt of an LDS chunk (32 keys; this lane's 64 bytes)
+  // B operand of tile tt of an LDS chunk: column `col` of tile tt is key
+  // 8*col + tt of the chunk, so over the chunk's 8 tiles a lane sees one whole
+  // block of 8 positions (its block maximum stays in a register). Pieces are
+  // swizzled by row/8, which differs across 8 consecutive lanes.
   auto load_b = [&](const uint4* L, int tt, v8i& b0, v8i& b1) __attribute__((always_inline)) {
-    const int row = tt * kTilePos + col;
-    const int sw = row & 7;
+    const int row = kBlock * col + tt;
+    const int sw = col & 7;
     b0 = as_v8i(L[row * 8 + ((half * 4 + 0) ^ sw)], L[row * 8 + ((half * 4 + 1) ^ sw)]);
     b1 = as_v8i(L[row * 8 + ((half * 4 + 2) ^ sw)], L[row * 8 + ((half * 4 + 3) ^ sw)]);
   };
@@ -297,13 +313,15 @@ __global__ __launch_bounds__(kPfThreads) void k_index_score_prefill(
     acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a1[q], b1, acc, 0, 0, 0, 0, 0, 0);
     return acc;
   };
-  // Combine the four queries' half sums of one tile and store them (with the
-  // block maxima when requested). Lanes 0..31 take query 2qp, 32..63 query
-  // 2qp+1 after the swap.
-  auto emit = [&](int64_t tile0, const float* p) __attribute__((always_inline)) {
-    const int64_t key = tile0 + col;
+  constexpr int kPairs = kPfQPerWave / 2;
+  // Lanes 0..31 take query 2qp, lanes 32..63 query 2qp+1 of each pair after
+  // the swap; bm[qp] is the running maximum of this lane's block.
+  float bm[kPairs];
+  // Slow path (ragged chunk or partial wave): every check per key.
+  auto emit = [&](int64_t chunk0, int tt, const float* p) __attribute__((always_inline)) {
+    const int64_t key = chunk0 + kBlock * col + tt;
 #pragma unroll
-    for (int qp = 0; qp < kPfQPerWave / 2; ++qp) {
+    for (int qp = 0; qp < kPairs; ++qp) {
       const auto sw2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(p[2 * qp]),
                                                         __float_as_uint(p[2 * qp + 1]), false, false);
       float s = __uint_as_float(sw2[0]) + __uint_as_float(sw2[1]);
@@ -313,20 +331,26 @@ __global__ __launch_bounds__(kPfThreads) void k_index_score_prefill(
       const bool store = tqq < T && key < n_cap;
       const size_t qi = (size_t)b * T + (size_t)tqq;
       if (store && scores) scores[qi * (size_t)n_cap + key] = s;
-      if (BMAX) {
-        const float m = max_over_8_lanes(s);
-        if (store && (col & 7) == 0) bmax[qi * (size_t)n_blk + (key >> 3)] = m;
-      }
+      bm[qp] = fmaxf(bm[qp], s);
+    }
+  };
+  // Block maxima of the chunk: lane col holds block chunk0/8 + col.
+  auto emit_bmax = [&](int64_t chunk0) __attribute__((always_inline)) {
+    if (!BMAX) return;
+    const int64_t blk = (chunk0 >> 3) + col;
+#pragma unroll
+    for (int qp = 0; qp < kPairs; ++qp) {
+      const int tqq = half ? tq[2 * qp + 1] : tq[2 * qp];
+      const size_t qi = (size_t)b * T + (size_t)tqq;
+      if (tqq < T && blk < n_blk) bmax[qi * (size_t)n_blk + blk] = bm[qp];
     }
   };
 
   // Stores of a fast-path tile: every query of the wave is real and every key
   // below n_cap, so the chunk's code is one basic block (no exec branches).
-  // Per chunk each lane keeps one score pointer and one visibility limit per
-  // query pair; tile t then stores at a constant offset.
-  constexpr int kPairs = kPfQPerWave / 2;
+  // Per chunk each lane keeps one score pointer (its block's first position)
+  // and one visibility limit per query pair.
   float* sp[kPairs];
-  float* bp[kPairs];
   int lim[kPairs];
   auto chunk_setup = [&](int64_t chunk0) __attribute__((always_inline)) {
 #pragma unroll
@@ -334,10 +358,10 @@ __global__ __launch_bounds__(kPfThreads) void k_index_score_prefill(
       const int64_t nvq = half ? nv[2 * qp + 1] : nv[2 * qp];
       const int tqq = half ? tq[2 * qp + 1] : tq[2 * qp];
       const size_t qi = (size_t)b * T + (size_t)tqq;
-      sp[qp] = scores ? scores + qi * (size_t)n_cap + chunk0 + col : nullptr;
-      if (BMAX) bp[qp] = bmax + qi * (size_t)n_blk + ((chunk0 + col) >> 3);
-      int64_t l = nvq - chunk0 - col;
-      lim[qp] = (int)(l < -1 ? -1 : (l > kPfChunk ? kPfChunk : l));
+      sp[qp] = scores ? scores + qi * (size_t)n_cap + chunk0 + kBlock * col : nullptr;
+      int64_t l = nvq - chunk0 - kBlock * col;
+      lim[qp] = (int)(l < -1 ? -1 : (l > kBlock ? kBlock : l));
+      bm[qp] = -INFINITY;
     }
   };
   auto emit_fast = [&](int t, const float* p) __attribute__((always_inline)) {
@@ -346,22 +370,19 @@ __global__ __launch_bounds__(kPfThreads) void k_index_score_prefill(
       const auto sw2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(p[2 * qp]),
                                                         __float_as_uint(p[2 * qp + 1]), false, false);
       float s = __uint_as_float(sw2[0]) + __uint_as_float(sw2[1]);
-      s = t * kTilePos < lim[qp] ? s : -INFINITY;
-      if (scores) sp[qp][t * kTilePos] = s;
-      if (BMAX) {
-        const float m = max_over_8_lanes(s);
-        if ((col & 7) == 0) bp[qp][t * (kTilePos / kBlock)] = m;
-      }
+      s = t < lim[qp] ? s : -INFINITY;
+      if (scores) sp[qp][t] = s;
+      if (BMAX) bm[qp] = fmaxf(bm[qp], s);
     }
   };
   const bool wave_full = tq[kPfQPerWave - 1] < T;
 
   constexpr int kTiles = kPfChunk / kTilePos;     // 8
-  load_chunk(0);
-  store_chunk(0);
+  load_chunk(0, 0);
+  wait_lds_dma();
   __syncthreads();
   for (int c = 0; c < n_chunks; ++c) {
-    if (c + 1 < n_chunks) load_chunk(c + 1);
+    if (c + 1 < n_chunks) load_chunk(c + 1, (c + 1) & 1);
     const uint4* L = lds[c & 1];
     const int64_t chunk0 = key0 + (int64_t)c * kPfChunk;
     if (wave_full && chunk0 + kPfChunk <= n_cap && chunk0 < nv_max) {
@@ -380,7 +401,11 @@ __global__ __launch_bounds__(kPfThreads) void k_index_score_prefill(
         const int t = j / kPfQPerWave, q = j % kPfQPerWave;
         if (j + 1 < kTiles * kPfQPerWave) {
           const int t1 = (j + 1) / kPfQPerWave, q1 = (j + 1) % kPfQPerWave;
+          // raised wave priority while issuing: the matrix core is kept fed
+          // when the other wave on this SIMD is also ready to issue
+          __builtin_amdgcn_s_setprio(1);
           acc[(j + 1) & 1] = mfma2(q1, bb0, bb1);
+          __builtin_amdgcn_s_setprio(0);
           // the last MFMA on tile t1 is issued: fetch the next tile's operand
           if (q1 == kPfQPerWave - 1 && t1 + 1 < kTiles) load_b(L, t1 + 1, bb0, bb1);
         }
@@ -392,13 +417,17 @@ __global__ __launch_bounds__(kPfThreads) void k_index_score_prefill(
         if (q == kPfQPerWave - 1) emit_fast(t, p);
         __builtin_amdgcn_sched_barrier(0);
       }
+      emit_bmax(chunk0);
     } else {
-      // Ragged last chunk, or nothing visible to this wave's queries.
+      // Ragged last chunk, a partial wave, or nothing visible to this wave's
+      // queries (rows past n_cap repeat the last row; keys checked one by one).
+#pragma unroll
+      for (int qp = 0; qp < kPairs; ++qp) bm[qp] = -INFINITY;
+      const bool any_vis = chunk0 < nv_max;
+#pragma unroll 1
       for (int tt = 0; tt < kTiles; ++tt) {
-        const int64_t tile0 = chunk0 + tt * kTilePos;
-        if (tile0 >= n_cap) break;
         float p[kPfQPerWave];
-        if (tile0 < nv_max) {
+        if (any_vis) {
           v8i b0, b1;
           load_b(L, tt, b0, b1);
 #pragma unroll
@@ -407,10 +436,11 @@ __global__ __launch_bounds__(kPfThreads) void k_index_score_prefill(
 #pragma unroll
           for (int q = 0; q < kPfQPerWave; ++q) p[q] = 0.0f;
         }
-        emit(tile0, p);
+        emit(chunk0, tt, p);
       }
+      emit_bmax(chunk0);
     }
-    if (c + 1 < n_chunks) store_chunk((c + 1) & 1);
+    wait_lds_dma();   // the next chunk has landed in LDS
     __syncthreads();
   }
 }
