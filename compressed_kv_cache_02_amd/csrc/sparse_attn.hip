@@ -32,15 +32,15 @@
 //          of the key slots); wave w owns heads 16w..16w+15 and all 512 output
 //          channels, so every gathered row serves all 64 heads;
 //   decode (up to 16 queries): one work-group of 8 waves per (query, 16-head
-//          group, slice). Wave w takes key half w/4 of each 32-key chunk and
-//          channel quarter w%4: it dequantises only that quarter of its keys
-//          into the row-major buffer, forms partial Q.K sums that the four
-//          waves of its half add up through LDS in a fixed order, and
-//          accumulates P.V for its 128 channels. Its P.V operand comes straight
-//          from the row-major buffer through the gfx950 transposing LDS read
-//          (ds_read_b64_tr_b16), so no transposed copy is stored. The two key
-//          halves are combined at the end; two waves per SIMD hide each other's
-//          LDS and MFMA latencies.
+//          group, slice of 128 key slots). Each lane dequantises 128 channels
+//          of one key straight into its Q.K operand registers (both operands
+//          use the same permuted channel order) and into a row-major fp16 copy
+//          in LDS; wave w forms the logits of its 16 keys, the work-group
+//          agrees on the slice maximum, and wave w accumulates P.V for output
+//          channels 64w..64w+63, reading V through the gfx950 transposing LDS
+//          read (ds_read_b64_tr_b16) so no transposed copy is stored. The query
+//          is converted once per work-group (two heads per wave) and shared
+//          through LDS.
 //   Slices are merged by log-sum-exp in a second kernel.
 #include "device_common.hpp"
 #include "launchers.hpp"
@@ -429,99 +429,30 @@ __global__ __launch_bounds__(kThreads) void k_sparse_attn_wide(AttnArgs a) {
   }
 }
 
-// ------------------------------------------------ decode kernel, 8 waves --
+// ------------------------------------------------------- decode kernel --
+
+// Decode shape: 5 slices of 128 key slots (slices 0-3 hold the selected rows,
+// slice 4 the window), one work-group of 8 waves per (query, 16-head group,
+// slice). Three phases separated by two barriers:
+//   1. every thread dequantises 4 keys x 32 channels into a row-major fp16
+//      buffer of all 128 keys;
+//   2. wave w forms the logits of keys 16w..16w+15 for the 16 heads over all
+//      512 channels and publishes its per-head maximum; with the slice maximum
+//      it writes p = exp(z - max) of its keys (fp16 hi + lo) and their sum;
+//   3. wave w accumulates P.V for output channels 64w..64w+63 over the 128 keys,
+//      reading V through the transposing LDS read (ds_read_b64_tr_b16).
+// The slices are merged by log-sum-exp in a second kernel.
+constexpr int kDecSplits = 5;
+constexpr int kDecKeys = kSlots / kDecSplits;     // 128 key slots per work-group
+constexpr int kDecWaves = 8;
+constexpr int kDecThreads = kDecWaves * 64;
+constexpr int kPRow = kDecKeys + 8;               // fp16 elements per LDS row of P
+static_assert(kDecKeys == 16 * kDecWaves, "one 16-key tile per wave");
+static_assert(kTopK % kDecKeys == 0, "a slice holds only selected rows or only window rows");
+static_assert(kDecThreads / 16 * 4 == kDecKeys, "4 keys x 32 channels per thread");
 
 typedef _Float16 v4h __attribute__((ext_vector_type(4)));
-
-// Gather for the 8-wave decode work-group: thread t of wave w owns channels
-// 8p..8p+7 with p = 16*(w%4) + t%16, and keys 4g..4g+3 of the chunk with
-// g = 4*(w/4) + (t%64)/16 (wave w serves key half w/4 and channel quarter w%4).
-struct Gather8 {
-  const uint8_t* cache_b;
-  const uint8_t* swa_b;
-  const int32_t* idx_q;
-  int64_t n_cap, tq, pos0;
-  int S, piece, g4;
-
-  __device__ void init(const AttnArgs& a, int qi) {
-    const int b = qi / a.T;
-    cache_b = a.cache + (size_t)b * (size_t)a.n_cap * kRowBytes;
-    swa_b = a.swa + (size_t)b * (size_t)a.S * kDim;
-    idx_q = a.idx + (size_t)qi * kTopK;
-    n_cap = a.n_cap;
-    tq = a.q_pos[qi];
-    pos0 = a.swa_pos0[b];
-    S = a.S;
-    const int t = threadIdx.x, w = t >> 6;
-    piece = 16 * (w & 3) + (t & 15);
-    g4 = 4 * (w >> 2) + ((t & 63) >> 4);
-  }
-
-  // This thread's 4 selected positions of `chunk` (unused for window chunks).
-  __device__ __forceinline__ int4 load_idx(int chunk) const {
-    const int slot0 = chunk * kChunkKeys + g4 * 4;
-    return slot0 < kTopK ? *reinterpret_cast<const int4*>(idx_q + slot0) : make_int4(-1, -1, -1, -1);
-  }
-
-  // Raw bytes of this thread's 4 keys; bit j marks key j present. Row loads are
-  // unconditional (an absent key reads row 0) so none waits on another.
-  __device__ __forceinline__ uint32_t load(int chunk, const int4& i4, uint2 (&r)[4]) const {
-    const int slot0 = chunk * kChunkKeys + g4 * 4;
-    uint32_t ok = 0;
-    if (slot0 < kTopK) {
-      const int32_t pj[4] = {i4.x, i4.y, i4.z, i4.w};
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const bool v = pj[j] >= 0 && (int64_t)pj[j] < n_cap;
-        ok |= (v ? 1u : 0u) << j;
-        const uint8_t* row = cache_b + (size_t)(v ? pj[j] : 0) * kRowBytes;
-        r[j].x = *reinterpret_cast<const uint32_t*>(row + piece * 4);
-        r[j].y = row[kCodeBytes + (piece >> 1)];
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int64_t tok = tq - (kWindow - 1) + (slot0 + j - kTopK);
-        const int64_t rr = tok - pos0;
-        const bool v = tok >= 0 && rr >= 0 && rr < S;
-        ok |= (v ? 1u : 0u) << j;
-        r[j] = *reinterpret_cast<const uint2*>(swa_b + (size_t)(v ? rr : 0) * kDim + piece * 8);
-      }
-    }
-    return ok;
-  }
-
-  // Dequantise (as Gather::store) into krow; flags presence.
-  __device__ __forceinline__ void store(bool is_main, const uint2 (&r)[4], uint32_t ok,
-                                        uint16_t* krow, int* kvalid) const {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      uint32_t pr[4];   // fp16 pairs of channels 8p+2b, 8p+2b+1
-      if (is_main) {
-        const uint32_t c = r[j].y;
-        const uint32_t E = (c >> 3) & 15u, M = c & 7u;
-        const float hw = __uint_as_float(E ? (E + 120u) << 23 : 118u << 23);
-        const _Float16 mf = E ? __builtin_bit_cast(_Float16, (uint16_t)(0x3C00u | (M << 7)))
-                              : (_Float16)(float)M;
-        const v2h m2 = {mf, mf};
-        pr[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(r[j].x, hw, 0) * m2);
-        pr[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(r[j].x, hw, 1) * m2);
-        pr[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(r[j].x, hw, 2) * m2);
-        pr[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(r[j].x, hw, 3) * m2);
-      } else {
-        pr[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(r[j].x, 1.0f, false));
-        pr[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(r[j].x, 1.0f, true));
-        pr[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(r[j].y, 1.0f, false));
-        pr[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(r[j].y, 1.0f, true));
-      }
-      if (!((ok >> j) & 1u)) pr[0] = pr[1] = pr[2] = pr[3] = 0u;
-      const int key = g4 * 4 + j;
-      if ((threadIdx.x & 15) == 0 && ((threadIdx.x >> 6) & 3) == 0) kvalid[key] = (ok >> j) & 1u;
-      *reinterpret_cast<uint4*>(&krow[key * kKrowStride + piece * 8]) =
-          make_uint4(pr[0], pr[1], pr[2], pr[3]);
-    }
-  }
-};
+typedef short v4s __attribute__((ext_vector_type(4)));
 
 // Reductions over the four 16-lane rows of a wave (lanes with the same lane %
 // 16), in VALU: v_permlane16_swap pairs rows 0/1 and 2/3, v_permlane32_swap
@@ -539,218 +470,237 @@ __device__ __forceinline__ float rows_sum(float v) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
-// Online softmax step over 16 keys: z = this lane's 4 logits (head = column).
-__device__ __forceinline__ float softmax_step16(const float (&z)[4], float& m_run, float& l_run,
-                                                v4h& p_hi, v4h& p_lo) {
-  const float mx = rows_max(fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3])));
-  const float m_new = fmaxf(m_run, mx);
-  float alpha = 1.0f, psum = 0.0f;
-  float p[4];
-  if (m_new == -INFINITY) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) p[i] = 0.0f;
-  } else {
-    alpha = __expf(m_run - m_new);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      p[i] = __expf(z[i] - m_new);
-      psum += p[i];
-    }
-  }
-  psum = rows_sum(psum);
-  l_run = l_run * alpha + psum;
-  m_run = m_new;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const _Float16 h = (_Float16)p[i];
-    p_hi[i] = h;
-    p_lo[i] = (_Float16)(p[i] - (float)h);
-  }
-  return alpha;
+// 16 FP4 codes (two 32-bit words, channels 2b, 2b+1 in byte b) with the E4M3
+// scale byte c -> 8 fp16 pairs, exactly as Gather::store dequantises them.
+__device__ __forceinline__ void fp4x16_to_f16(uint32_t w0, uint32_t w1, uint32_t c, uint32_t* pr) {
+  const uint32_t E = (c >> 3) & 15u, M = c & 7u;
+  const float hw = __uint_as_float(E ? (E + 120u) << 23 : 118u << 23);
+  const _Float16 mf = E ? __builtin_bit_cast(_Float16, (uint16_t)(0x3C00u | (M << 7)))
+                        : (_Float16)(float)M;
+  const v2h m2 = {mf, mf};
+  pr[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w0, hw, 0) * m2);
+  pr[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w0, hw, 1) * m2);
+  pr[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w0, hw, 2) * m2);
+  pr[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w0, hw, 3) * m2);
+  pr[4] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w1, hw, 0) * m2);
+  pr[5] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w1, hw, 1) * m2);
+  pr[6] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w1, hw, 2) * m2);
+  pr[7] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w1, hw, 3) * m2);
+}
+// 4 E4M3 bytes -> 2 fp16 pairs (exact).
+__device__ __forceinline__ void fp8x4_to_f16(uint32_t w, uint32_t* pr) {
+  pr[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false));
+  pr[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, true));
 }
 
-// One work-group of 8 waves per (query, 16-head group, slice of CPS chunks).
-// Wave w takes key half w/4 of every chunk and channel quarter w%4: the four
-// waves of a half exchange partial Q.K sums through LDS (one barrier per
-// chunk), keep their own online-softmax state and P.V accumulators, and the two
-// halves are combined at the end. Two waves per SIMD hide each other's LDS and
-// MFMA latencies.
-template <int CPS>
-__global__ __launch_bounds__(512) void k_sparse_attn_decode8(AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t krow[kChunkKeys * kKrowStride];
-  __shared__ float spart[2][2][4][16][kHG];
-  __shared__ int kvalid[2][kChunkKeys];
-  __shared__ float qmax[4][kHG];
+// Maximum over each 32-lane half of a wave (DPP within 16-lane rows, then
+// v_permlane16_swap across the two rows of the half).
+__device__ __forceinline__ float half_max(float m) {
+  m = fmaxf(m, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(m), 0xB1, 0xF, 0xF, false)));
+  m = fmaxf(m, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(m), 0x4E, 0xF, 0xF, false)));
+  m = fmaxf(m, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(m), 0x141, 0xF, 0xF, false)));
+  m = fmaxf(m, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(m), 0x140, 0xF, 0xF, false)));
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+  return fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+}
+
+__global__ __launch_bounds__(kDecThreads) void k_sparse_attn_decode(AttnArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t krow[kDecKeys * kKrowStride];
+  // fp16 query [16 heads][kKrowStride] until the logits are formed, then P
+  // (hi, lo) [16 heads][kPRow] each
+  constexpr int kQP = kHG * kKrowStride > 2 * kHG * kPRow ? kHG * kKrowStride : 2 * kHG * kPRow;
+  __shared__ __attribute__((aligned(16))) uint16_t qp_buf[kQP];
+  __shared__ float wmax[kDecWaves][kHG];
+  __shared__ float wsum[kDecWaves][kHG];
+  __shared__ int qsh[kHG];
+  uint16_t* const qf = qp_buf;
+  uint16_t* const pbuf = qp_buf;   // P hi at [0, kHG*kPRow), lo after it
 
   const int qi = blockIdx.y;
   const int hg = blockIdx.x % kHeadGroups;
   const int split = blockIdx.x / kHeadGroups;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int cq = wave & 3, kh = wave >> 2;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
   const int col = lane & 15, grp = lane >> 4;
-  Gather8 g;
-  g.init(a, qi);
-  const int chunk0 = split * CPS;
+  const int b = qi / a.T;
+  const int slot0 = split * kDecKeys;
+  const bool is_main = slot0 < kTopK;
 
-  v4f acc[8];
+  // ---- loads. Lane (grp, col) of wave w loads key 16w + col of the slice:
+  // channels 128grp .. 128grp+127 of its row. Q.K runs over a permuted channel
+  // order that both operands share: MFMA step kb takes channels
+  // 128grp + 8kb .. +7 in lane group grp, so each lane's key operand is its own
+  // dequantised row slice and needs no LDS round trip.
+  const int kk = wave * 16 + col;           // this lane's key in the slice
+  int32_t pj = 0;
+  if (is_main) pj = a.idx[(size_t)qi * kTopK + slot0 + kk];
+  // query staging: wave w converts heads 2w, 2w+1 (lane: head 2w + lane/32,
+  // channels 16*(lane%32) .. +15)
+  const int qh = 2 * wave + (lane >> 5), qc = 16 * (lane & 31);
+  const uint4* qsrc = reinterpret_cast<const uint4*>(
+      a.q + ((size_t)qi * kHeads + hg * kHG + qh) * kDim + qc);
+  const uint4 qr0 = qsrc[0], qr1 = qsrc[1];
+  uint4 raw[8];          // FP4: raw[0..3] codes, raw[4].xy scales; FP8: raw[0..7]
+  bool ok;
+  if (is_main) {
+    ok = pj >= 0 && (int64_t)pj < a.n_cap;
+    const uint8_t* row = a.cache + ((size_t)b * (size_t)a.n_cap + (size_t)(ok ? pj : 0)) * kRowBytes;
+    const uint4* c4 = reinterpret_cast<const uint4*>(row + 64 * grp);
 #pragma unroll
-  for (int i = 0; i < 8; ++i) acc[i] = v4f{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY, l_run = 0.0f;
-  v8h qreg[4];
-  float zscale = 1.0f;
-
-  auto chunk = [&](int c, const uint2 (&r)[4], uint32_t ok) __attribute__((always_inline)) {
-    const int buf = c & 1;
-    g.store((chunk0 + c) * kChunkKeys < kTopK, r, ok, krow, kvalid[buf]);
-    {
-      v4f s = {0.f, 0.f, 0.f, 0.f};
-      const uint16_t* kr = &krow[(kh * 16 + col) * kKrowStride + cq * 128 + grp * 8];
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-        const uint4 v = *reinterpret_cast<const uint4*>(kr + kb * 32);
-        s = __builtin_amdgcn_mfma_f32_16x16x32_f16(*reinterpret_cast<const v8h*>(&v), qreg[kb], s,
-                                                   0, 0, 0);
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) spart[buf][kh][cq][4 * grp + i][col] = s[i];
-    }
-    __syncthreads();
-    float z[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int k = 4 * grp + i;
-      const float sv = ((spart[buf][kh][0][k][col] + spart[buf][kh][1][k][col]) +
-                        spart[buf][kh][2][k][col]) + spart[buf][kh][3][k][col];
-      z[i] = kvalid[buf][kh * 16 + k] ? sv * zscale : -INFINITY;
-    }
-    v4h p_hi, p_lo;
-    const float alpha = softmax_step16(z, m_run, l_run, p_hi, p_lo);
-    if (__any(alpha != 1.0f)) {
-#pragma unroll
-      for (int dt = 0; dt < 8; ++dt) acc[dt] *= alpha;
-    }
-    // P.V operand: the transposing LDS read hands lane (grp, i) the values of
-    // channel ch0 + i for keys 16*kh + 4*grp .. +3, when lane (grp, m) points
-    // at key 16*kh + 4*grp + m/4, channels ch0 + 4*(m%4) .. +3.
-    const uint16_t* vsrc = &krow[(kh * 16 + 4 * grp + (col >> 2)) * kKrowStride + cq * 128 +
-                                 4 * (col & 3)];
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt) {
-      typedef short v4s __attribute__((ext_vector_type(4)));
-      const v4s raw = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (__attribute__((address_space(3))) v4s*)(vsrc + dt * 16));
-      const v4h v = __builtin_bit_cast(v4h, raw);
-      acc[dt] = __builtin_amdgcn_mfma_f32_16x16x16f16(v, p_hi, acc[dt], 0, 0, 0);
-      acc[dt] = __builtin_amdgcn_mfma_f32_16x16x16f16(v, p_lo, acc[dt], 0, 0, 0);
-    }
-  };
-  // The quarter cq of the 16 heads' query in fp16 after the head's shift.
-  auto load_q = [&]() __attribute__((always_inline)) {
-    const uint16_t* qp = a.q + ((size_t)qi * kHeads + hg * kHG + col) * kDim + cq * 128 + grp * 8;
-    uint4 raw[4];
-    float amax = 0.0f;
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      raw[kb] = *reinterpret_cast<const uint4*>(qp + kb * 32);
-      amax = fmaxf(amax, bf16x8_absmax(raw[kb]));
-    }
-    amax = rows_max(amax);
-    if (grp == 0 && kh == 0) qmax[cq][col] = amax;
-    __syncthreads();
-    amax = fmaxf(fmaxf(qmax[0][col], qmax[1][col]), fmaxf(qmax[2][col], qmax[3][col]));
-    const int sh = q_shift(amax);
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb) qreg[kb] = q_to_f16(raw[kb], sh);
-    zscale = ldexpf(a.scale, -sh);
-  };
-
-  // Every index this thread needs is requested first, then the first rows,
-  // so the index -> row chain overlaps the query set-up.
-  int4 ix[CPS];
-  static_for<CPS>([&](auto ii) __attribute__((always_inline)) {
-    constexpr int i = decltype(ii)::value;
-    ix[i] = g.load_idx(chunk0 + i);
-  });
-  constexpr int PF = CPS < 4 ? CPS : 4;
-  uint2 raw[PF][4];
-  uint32_t okm[PF];
-  static_for<PF>([&](auto ii) __attribute__((always_inline)) {
-    constexpr int i = decltype(ii)::value;
-    if (i < CPS) okm[i] = g.load(chunk0 + i, ix[i], raw[i]);
-  });
-  load_q();   // ends with a barrier
-  for (int c0 = 0; c0 < CPS; c0 += PF) {
-    static_for<PF>([&](auto ii) __attribute__((always_inline)) {
-      constexpr int i = decltype(ii)::value;
-      const int c = c0 + i;
-      if (c < CPS) {
-        uint2 cur[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) cur[j] = raw[i][j];
-        const uint32_t cok = okm[i];
-        if (c + PF < CPS) {
-          static_for<CPS>([&](auto jj) __attribute__((always_inline)) {
-            constexpr int cc = decltype(jj)::value;
-            if (cc == c + PF) okm[i] = g.load(chunk0 + cc, ix[cc], raw[i]);
-          });
-        }
-        chunk(c, cur, cok);
-      }
-    });
-  }
-
-  // Combine the two key halves: half 1 hands its state to half 0 through LDS
-  // (reusing the key buffer and the partial sums once every wave is done).
-  __syncthreads();
-  float* xs = reinterpret_cast<float*>(krow);        // [4 quarters][8 tiles][64 lanes][4]
-  float* xml = &spart[0][0][0][0][0];                // [4][64 lanes][2]
-  if (kh == 1) {
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt)
-      *reinterpret_cast<float4*>(xs + (((size_t)cq * 8 + dt) * 64 + lane) * 4) =
-          make_float4(acc[dt][0], acc[dt][1], acc[dt][2], acc[dt][3]);
-    xml[(cq * 64 + lane) * 2 + 0] = m_run;
-    xml[(cq * 64 + lane) * 2 + 1] = l_run;
-  }
-  __syncthreads();
-  if (kh == 1) return;
-  {
-    const float m1 = xml[(cq * 64 + lane) * 2 + 0], l1 = xml[(cq * 64 + lane) * 2 + 1];
-    const float M = fmaxf(m_run, m1);
-    const float w0 = m_run == -INFINITY ? 0.0f : __expf(m_run - M);
-    const float w1 = m1 == -INFINITY ? 0.0f : __expf(m1 - M);
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt) {
-      const float4 o = *reinterpret_cast<const float4*>(xs + (((size_t)cq * 8 + dt) * 64 + lane) * 4);
-      acc[dt][0] = acc[dt][0] * w0 + o.x * w1;
-      acc[dt][1] = acc[dt][1] * w0 + o.y * w1;
-      acc[dt][2] = acc[dt][2] * w0 + o.z * w1;
-      acc[dt][3] = acc[dt][3] * w0 + o.w * w1;
-    }
-    l_run = l_run * w0 + l1 * w1;
-    m_run = M;
-  }
-
-  // lane holds head 16*hg + col, channels 128*cq + 16*dt + 4*grp .. +3
-  const int head = hg * kHG + col;
-  const int splits = gridDim.x / kHeadGroups;
-  if (splits == 1) {
-    const float inv = l_run > 0.0f ? 1.0f / l_run : 0.0f;
-    float* o = a.out + ((size_t)qi * kHeads + head) * kDim + cq * 128 + 4 * grp;
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt)
-      *reinterpret_cast<float4*>(o + dt * 16) =
-          make_float4(acc[dt][0] * inv, acc[dt][1] * inv, acc[dt][2] * inv, acc[dt][3] * inv);
+    for (int i = 0; i < 4; ++i) raw[i] = c4[i];
+    const uint2 sc = *reinterpret_cast<const uint2*>(row + kCodeBytes + 8 * grp);
+    raw[4] = make_uint4(sc.x, sc.y, 0u, 0u);
   } else {
-    const size_t ps = (size_t)qi * splits + split;
-    float* o = a.part + (ps * kHeads + head) * kDim + cq * 128 + 4 * grp;
+    const int64_t tq = a.q_pos[qi], pos0 = a.swa_pos0[b];
+    const int64_t tok = tq - (kWindow - 1) + (slot0 + kk - kTopK);
+    const int64_t rr = tok - pos0;
+    ok = tok >= 0 && rr >= 0 && rr < a.S;
+    const uint4* r4 = reinterpret_cast<const uint4*>(
+        a.swa + ((size_t)b * (size_t)a.S + (size_t)(ok ? rr : 0)) * kDim + 128 * grp);
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt)
-      *reinterpret_cast<float4*>(o + dt * 16) = make_float4(acc[dt][0], acc[dt][1], acc[dt][2], acc[dt][3]);
-    if (grp == 0 && cq == 0) {
-      a.part_ml[(ps * kHeads + head) * 2 + 0] = m_run;
-      a.part_ml[(ps * kHeads + head) * 2 + 1] = l_run;
+    for (int i = 0; i < 8; ++i) raw[i] = r4[i];
+  }
+
+  // ---- the query in fp16, each head shifted by a power of two (q_shift)
+  {
+    const float amax = half_max(fmaxf(bf16x8_absmax(qr0), bf16x8_absmax(qr1)));
+    const int sh = q_shift(amax);
+    const v8h h0 = q_to_f16(qr0, sh), h1 = q_to_f16(qr1, sh);
+    *reinterpret_cast<v8h*>(&qf[qh * kKrowStride + qc]) = h0;
+    *reinterpret_cast<v8h*>(&qf[qh * kKrowStride + qc + 8]) = h1;
+    if ((lane & 31) == 0) qsh[qh] = sh;
+  }
+  __syncthreads();
+  v8h qreg[16];
+#pragma unroll
+  for (int kb = 0; kb < 16; ++kb)
+    qreg[kb] = *reinterpret_cast<const v8h*>(&qf[col * kKrowStride + 128 * grp + 8 * kb]);
+  const float zscale = ldexpf(a.scale, -qsh[col]);
+
+  // ---- dequantise this lane's 128 channels: the Q.K operand in registers and
+  // the row-major copy in LDS for P.V
+  v8h kreg[16];
+  {
+    const uint32_t* w = reinterpret_cast<const uint32_t*>(raw);
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+      uint32_t pr[8];
+      if (is_main) {
+        fp4x16_to_f16(w[2 * m], w[2 * m + 1], (w[16 + m / 4] >> (8 * (m % 4))) & 0xFFu, pr);
+      } else {
+        fp8x4_to_f16(w[4 * m + 0], pr + 0);
+        fp8x4_to_f16(w[4 * m + 1], pr + 2);
+        fp8x4_to_f16(w[4 * m + 2], pr + 4);
+        fp8x4_to_f16(w[4 * m + 3], pr + 6);
+      }
+      const uint4 lo = ok ? make_uint4(pr[0], pr[1], pr[2], pr[3]) : make_uint4(0u, 0u, 0u, 0u);
+      const uint4 hi = ok ? make_uint4(pr[4], pr[5], pr[6], pr[7]) : make_uint4(0u, 0u, 0u, 0u);
+      kreg[2 * m] = __builtin_bit_cast(v8h, lo);
+      kreg[2 * m + 1] = __builtin_bit_cast(v8h, hi);
+      uint4* dst = reinterpret_cast<uint4*>(&krow[kk * kKrowStride + 128 * grp + 16 * m]);
+      dst[0] = lo;
+      dst[1] = hi;
     }
+  }
+  // presence of keys 16w .. 16w+15 (lanes 0..15 hold them), wave-uniform
+  const uint32_t kmask = (uint32_t)__ballot(ok) & 0xFFFFu;
+
+  // ---- phase 2: logits of keys 16w..16w+15 (lane: keys 4grp+r, head col),
+  // four independent accumulation chains
+  v4f s;
+  {
+    v4f sc[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) sc[c] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb < 16; ++kb)
+      sc[kb & 3] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kreg[kb], qreg[kb], sc[kb & 3], 0, 0, 0);
+    s = (sc[0] + sc[1]) + (sc[2] + sc[3]);
+  }
+  float z[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) z[r] = ((kmask >> (4 * grp + r)) & 1u) ? s[r] * zscale : -INFINITY;
+  const float mloc = rows_max(fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3])));
+  if (grp == 0) wmax[wave][col] = mloc;
+  __syncthreads();
+  float M = wmax[0][col];
+#pragma unroll
+  for (int w = 1; w < kDecWaves; ++w) M = fmaxf(M, wmax[w][col]);
+  {
+    float p[4], psum = 0.0f;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      p[r] = M == -INFINITY ? 0.0f : __expf(z[r] - M);
+      psum += p[r];
+    }
+    psum = rows_sum(psum);
+    if (grp == 0) wsum[wave][col] = psum;
+    v4h ph, pl;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const _Float16 h = (_Float16)p[r];
+      ph[r] = h;
+      pl[r] = (_Float16)(p[r] - (float)h);
+    }
+    // (every wave has read the query from this buffer before the barrier above)
+    *reinterpret_cast<v4h*>(&pbuf[col * kPRow + wave * 16 + 4 * grp]) = ph;
+    *reinterpret_cast<v4h*>(&pbuf[kHG * kPRow + col * kPRow + wave * 16 + 4 * grp]) = pl;
+  }
+  __syncthreads();
+  float l = 0.0f;
+#pragma unroll
+  for (int w = 0; w < kDecWaves; ++w) l += wsum[w][col];
+
+  // ---- phase 3: P.V for channels 64w..64w+63 (lane: channels 4grp+r of each
+  // 16-channel tile, head col). The transposing read hands lane (grp, i) the
+  // values of channel c0 + i for keys k0 + 4grp .. +3 when lane (grp, m)
+  // points at key k0 + 4grp + m/4, channels c0 + 4(m%4) .. +3.
+  // 32 keys per MFMA (v_mfma_f32_16x16x32_f16): lane (grp, i) takes keys
+  // 32ks + 8grp .. +7 of channel i, as two transposing reads of 4 keys each.
+  // Operands are requested two key steps ahead of their MFMAs.
+  constexpr int kKs = kDecKeys / 32;
+  v8h ph[kKs], pl[kKs], vv[kKs][4];
+  auto fetch = [&](int ks) __attribute__((always_inline)) {
+    ph[ks] = *reinterpret_cast<const v8h*>(&pbuf[col * kPRow + ks * 32 + 8 * grp]);
+    pl[ks] = *reinterpret_cast<const v8h*>(&pbuf[kHG * kPRow + col * kPRow + ks * 32 + 8 * grp]);
+    const uint16_t* vsrc =
+        &krow[(ks * 32 + 8 * grp + (col >> 2)) * kKrowStride + wave * 64 + 4 * (col & 3)];
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) {
+      const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) v4s*)(vsrc + dt * 16));
+      const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) v4s*)(vsrc + 4 * kKrowStride + dt * 16));
+      vv[ks][dt] = __builtin_bit_cast(v8h, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    }
+  };
+  v4f acc[4];
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt) acc[dt] = v4f{0.f, 0.f, 0.f, 0.f};
+  fetch(0);
+  fetch(1);
+#pragma unroll
+  for (int ks = 0; ks < kKs; ++ks) {
+    if (ks + 2 < kKs) fetch(ks + 2);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) {
+      acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vv[ks][dt], ph[ks], acc[dt], 0, 0, 0);
+      acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vv[ks][dt], pl[ks], acc[dt], 0, 0, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+
+  // lane holds head 16hg + col, channels 64w + 16dt + 4grp .. +3
+  const int head = hg * kHG + col;
+  const size_t ps = (size_t)qi * kDecSplits + split;
+  float* o = a.part + (ps * kHeads + head) * kDim + wave * 64 + 4 * grp;
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+    *reinterpret_cast<float4*>(o + dt * 16) = make_float4(acc[dt][0], acc[dt][1], acc[dt][2], acc[dt][3]);
+  if (wave == 0 && grp == 0) {
+    a.part_ml[(ps * kHeads + head) * 2 + 0] = M;
+    a.part_ml[(ps * kHeads + head) * 2 + 1] = l;
   }
 }
 
@@ -810,7 +760,7 @@ Shape attn_shape(int Q) {
   Shape sh;
   if (Q <= 16) {
     sh.wide = false;
-    sh.splits = 5;
+    sh.splits = kDecSplits;
   } else if (Q < kWideMinQueries) {
     sh.wide = true;
     sh.splits = 4;
@@ -849,7 +799,7 @@ hipError_t launch_sparse_attn(const uint16_t* q, const uint8_t* cache, const int
   a.part = nullptr;
   a.part_ml = nullptr;
   const Shape sh = attn_shape(Q);
-  if (sh.splits > kMaxSplits || (!sh.wide && sh.splits != 5)) return hipErrorInvalidValue;
+  if (sh.splits > kMaxSplits || (!sh.wide && sh.splits != kDecSplits)) return hipErrorInvalidValue;
   a.splits = sh.splits;
   if (a.splits > 1) {
     a.part = reinterpret_cast<float*>(ws);
@@ -866,9 +816,8 @@ hipError_t launch_sparse_attn(const uint16_t* q, const uint8_t* cache, const int
       default: hipLaunchKernelGGL(k_sparse_attn_wide<20>, grid, dim3(kThreads), 0, st, a); break;
     }
   } else {
-    // the decode shape always runs 5 slices of 4 chunks
-    const dim3 grid(a.splits * kHeadGroups, Q);
-    hipLaunchKernelGGL(k_sparse_attn_decode8<kChunks / 5>, grid, dim3(512), 0, st, a);
+    const dim3 grid(kDecSplits * kHeadGroups, Q);
+    hipLaunchKernelGGL(k_sparse_attn_decode, grid, dim3(kDecThreads), 0, st, a);
   }
   if (a.splits > 1)
     hipLaunchKernelGGL(k_attn_merge, dim3(kHeads, Q), dim3(128), 0, st, a.part, a.part_ml,
