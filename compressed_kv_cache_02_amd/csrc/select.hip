@@ -343,6 +343,7 @@ constexpr int kSelDigit = 12;
 template <int KIND, int NT, int IPT>
 __global__ __launch_bounds__(NT) void k_select(Src src, int K, int32_t* __restrict__ out,
                                                int out_stride) {
+  static_assert(IPT <= 32, "item masks are 32-bit");
   constexpr int NW = NT / 64;
   constexpr int PER = kSelBins / NT;                 // bins per thread in the threshold search
   __shared__ __align__(16) uint32_t lh[kSelBins];

@@ -235,6 +235,8 @@ def _score_sets(n, seed):
     yield "ties", rng.integers(0, 6, n).astype(np.float32)
     yield "normal", np.abs(rng.standard_normal(n)).astype(np.float32)
     yield "all-equal", np.ones(n, dtype=np.float32)
+    # tens of copies of each value near the K-th: ties inside small radix bins
+    yield "rounded", (np.round(rng.standard_normal(n) * 64) / 64).astype(np.float32)
     x = rng.standard_normal(n).astype(np.float32)     # signed, with zeros of both signs
     x[::7] = 0.0
     x[3::7] = -0.0
