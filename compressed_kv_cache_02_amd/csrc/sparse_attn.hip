@@ -28,10 +28,10 @@
 // channels.
 //
 // Two work shapes:
-//   wide   (more than 16 queries): one work-group of 4 waves per (query, slice
-//          of the key slots); wave w owns heads 16w..16w+15 and all 512 output
+//   wide   (512 queries or more): one work-group of 4 waves per query over all
+//          640 key slots; wave w owns heads 16w..16w+15 and all 512 output
 //          channels, so every gathered row serves all 64 heads;
-//   decode (up to 16 queries): one work-group of 8 waves per (query, 16-head
+//   decode (fewer than 512 queries): one work-group of 8 waves per (query, 16-head
 //          group, slice of 128 key slots). Each lane dequantises 128 channels
 //          of one key straight into its Q.K operand registers (both operands
 //          use the same permuted channel order) and into a row-major fp16 copy
@@ -317,10 +317,9 @@ __device__ __forceinline__ void pipeline(Load&& load, Chunk&& chunk) {
 
 // ------------------------------------------------------------ wide kernel --
 
-// One work-group per (query, slice of CPS chunks); wave w owns heads
-// 16w..16w+15 and all 512 output channels, so every gathered row serves the 64
-// heads. With one slice per query the output is written directly, otherwise
-// the partial state goes to the workspace for the merge kernel.
+// One work-group per query (CPS = all chunks of its key slots); wave w owns
+// heads 16w..16w+15 and all 512 output channels, so every gathered row serves
+// the 64 heads. The output is written directly.
 template <int CPS>
 __global__ __launch_bounds__(kThreads) void k_sparse_attn_wide(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t krow[kChunkKeys * kKrowStride];
@@ -409,24 +408,12 @@ __global__ __launch_bounds__(kThreads) void k_sparse_attn_wide(AttnArgs a) {
 
   // lane holds head 16*wave + col, channels 16*dt + 4*grp .. +3
   const int head = wave * 16 + col;
-  if (a.splits == 1) {
-    const float inv = l_run > 0.0f ? 1.0f / l_run : 0.0f;
-    float* o = a.out + ((size_t)qi * kHeads + head) * kDim + 4 * grp;
+  const float inv = l_run > 0.0f ? 1.0f / l_run : 0.0f;
+  float* o = a.out + ((size_t)qi * kHeads + head) * kDim + 4 * grp;
 #pragma unroll
-    for (int dt = 0; dt < 32; ++dt)
-      *reinterpret_cast<float4*>(o + dt * 16) =
-          make_float4(acc[dt][0] * inv, acc[dt][1] * inv, acc[dt][2] * inv, acc[dt][3] * inv);
-  } else {
-    const size_t ps = (size_t)qi * a.splits + split;
-    float* o = a.part + (ps * kHeads + head) * kDim + 4 * grp;
-#pragma unroll
-    for (int dt = 0; dt < 32; ++dt)
-      *reinterpret_cast<float4*>(o + dt * 16) = make_float4(acc[dt][0], acc[dt][1], acc[dt][2], acc[dt][3]);
-    if (grp == 0) {
-      a.part_ml[(ps * kHeads + head) * 2 + 0] = m_run;
-      a.part_ml[(ps * kHeads + head) * 2 + 1] = l_run;
-    }
-  }
+  for (int dt = 0; dt < 32; ++dt)
+    *reinterpret_cast<float4*>(o + dt * 16) =
+        make_float4(acc[dt][0] * inv, acc[dt][1] * inv, acc[dt][2] * inv, acc[dt][3] * inv);
 }
 
 // ------------------------------------------------------- decode kernel --
@@ -753,17 +740,15 @@ struct Shape {
 };
 
 Shape attn_shape(int Q) {
-  // Measured on MI355X (graph-replayed, 1M-entry caches): up to 16 queries the
-  // 16-head work-groups over 5 slices are fastest (8 queries: 22 us vs 25 us
-  // for the best 64-head shape); up to 512 queries the 64-head work-groups over
-  // 4 slices (64 queries: 49 us vs 67 us); beyond that one slice per query.
+  // Measured on MI355X (graph-replayed, 256K-entry caches, random selections):
+  // below 512 queries the 16-head work-groups over 5 slices are fastest
+  // (32 queries: 28 us vs 46 us for the 64-head work-groups over 4 slices;
+  // 128 queries: 84 us vs 91 us); from 512 queries on, one 64-head work-group
+  // per query, which writes its output directly.
   Shape sh;
-  if (Q <= 16) {
+  if (Q < kWideMinQueries) {
     sh.wide = false;
     sh.splits = kDecSplits;
-  } else if (Q < kWideMinQueries) {
-    sh.wide = true;
-    sh.splits = 4;
   } else {
     sh.wide = true;
     sh.splits = 1;
@@ -799,7 +784,7 @@ hipError_t launch_sparse_attn(const uint16_t* q, const uint8_t* cache, const int
   a.part = nullptr;
   a.part_ml = nullptr;
   const Shape sh = attn_shape(Q);
-  if (sh.splits > kMaxSplits || (!sh.wide && sh.splits != kDecSplits)) return hipErrorInvalidValue;
+  if (sh.wide ? sh.splits != 1 : sh.splits != kDecSplits) return hipErrorInvalidValue;
   a.splits = sh.splits;
   if (a.splits > 1) {
     a.part = reinterpret_cast<float*>(ws);
@@ -807,14 +792,7 @@ hipError_t launch_sparse_attn(const uint16_t* q, const uint8_t* cache, const int
   }
   if (sh.wide) {
     const dim3 grid(a.splits, Q);
-    switch (kChunks / a.splits) {
-      case 1: hipLaunchKernelGGL(k_sparse_attn_wide<1>, grid, dim3(kThreads), 0, st, a); break;
-      case 2: hipLaunchKernelGGL(k_sparse_attn_wide<2>, grid, dim3(kThreads), 0, st, a); break;
-      case 4: hipLaunchKernelGGL(k_sparse_attn_wide<4>, grid, dim3(kThreads), 0, st, a); break;
-      case 5: hipLaunchKernelGGL(k_sparse_attn_wide<5>, grid, dim3(kThreads), 0, st, a); break;
-      case 10: hipLaunchKernelGGL(k_sparse_attn_wide<10>, grid, dim3(kThreads), 0, st, a); break;
-      default: hipLaunchKernelGGL(k_sparse_attn_wide<20>, grid, dim3(kThreads), 0, st, a); break;
-    }
+    hipLaunchKernelGGL(k_sparse_attn_wide<kChunks>, grid, dim3(kThreads), 0, st, a);
   } else {
     const dim3 grid(kDecSplits * kHeadGroups, Q);
     hipLaunchKernelGGL(k_sparse_attn_decode, grid, dim3(kDecThreads), 0, st, a);
