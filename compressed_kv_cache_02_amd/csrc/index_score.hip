@@ -78,7 +78,6 @@ __device__ __forceinline__ float max_over_8_lanes(float m) {
   return m;
 }
 
-// sum over the lane's 16 accumulator rows of w_r * relu(acc_r), in row order
 // One 16-byte global -> LDS copy per lane, with no registers on the way: the
 // wave's 64 pieces land in 64 consecutive 16-byte slots starting at `dst`
 // (wave-uniform). Written as assembly so that the compiler does not make
@@ -93,6 +92,7 @@ __device__ __forceinline__ void wait_lds_dma() {
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
+// sum over the lane's 16 accumulator rows of w_r * relu(acc_r), in row order
 __device__ __forceinline__ float weighted_relu_sum(const v16f& acc, const float* wr) {
   float part = 0.0f;
 #pragma unroll

@@ -720,6 +720,9 @@ __global__ __launch_bounds__(kFinalThreads) void k_sel_final(Items it, void* ws,
 }
 
 // Maxima of super-blocks of 8 consecutive blocks (-inf where none is finite).
+// VEC: rows start 16-byte aligned, so a super-block's 8 maxima are two float4
+// loads.
+template <bool VEC>
 __global__ void k_super_max(const float* __restrict__ bmax, int64_t n_blk, int64_t n_sb,
                             float* __restrict__ smax) {
   const int q = blockIdx.y;
@@ -727,10 +730,17 @@ __global__ void k_super_max(const float* __restrict__ bmax, int64_t n_blk, int64
   if (j >= n_sb) return;
   const float* b = bmax + (size_t)q * (size_t)n_blk;
   float v[kBlock];
+  if (VEC && (j + 1) * kBlock <= n_blk) {
+    const float4* b4 = reinterpret_cast<const float4*>(b + j * kBlock);
+    const float4 x = b4[0], y = b4[1];
+    v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
+    v[4] = y.x; v[5] = y.y; v[6] = y.z; v[7] = y.w;
+  } else {
 #pragma unroll
-  for (int r = 0; r < kBlock; ++r) {
-    const int64_t k = j * kBlock + r;
-    v[r] = k < n_blk ? b[k] : -INFINITY;
+    for (int r = 0; r < kBlock; ++r) {
+      const int64_t k = j * kBlock + r;
+      v[r] = k < n_blk ? b[k] : -INFINITY;
+    }
   }
   float m = v[0];
 #pragma unroll
@@ -824,8 +834,11 @@ Stage child(const float* vals, int64_t vstride, int unit, const int32_t* sel, in
 
 hipError_t launch_super_max(const float* bmax, int Q, int64_t n_blk, float* smax, hipStream_t st) {
   const int64_t n_sb = (n_blk + kBlock - 1) / kBlock;
-  hipLaunchKernelGGL(k_super_max, dim3((unsigned)((n_sb + 255) / 256), Q), dim3(256), 0, st, bmax,
-                     n_blk, n_sb, smax);
+  const dim3 grid((unsigned)((n_sb + 255) / 256), Q);
+  if ((n_blk & 3) == 0 && (reinterpret_cast<uintptr_t>(bmax) & 15) == 0)
+    hipLaunchKernelGGL(k_super_max<true>, grid, dim3(256), 0, st, bmax, n_blk, n_sb, smax);
+  else
+    hipLaunchKernelGGL(k_super_max<false>, grid, dim3(256), 0, st, bmax, n_blk, n_sb, smax);
   return hipGetLastError();
 }
 
