@@ -85,8 +85,11 @@ __device__ __forceinline__ float max_over_8_lanes(float m) {
 // proceed while it is in flight. wait_lds_dma() waits for all of them.
 __device__ __forceinline__ void lds_dma16(const uint4* src, uint4* dst) {
   const uint32_t lds_addr = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint4*)dst;
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-               :: "v"(src), "s"(lds_addr) : "memory", "m0");
+  // m0 is saved and restored around the copy (the compiler reserves it)
+  uint32_t saved;
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\t"
+               "global_load_lds_dwordx4 %1, off\n\ts_mov_b32 m0, %0"
+               : "=&s"(saved) : "v"(src), "s"(lds_addr) : "memory");
 }
 __device__ __forceinline__ void wait_lds_dma() {
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");

@@ -8,74 +8,44 @@
 // every layer has its own query and window ("DeepSeek V4.1 Flash vs V4 Pro",
 // 黑科技之二). Key = value = the dequantised 512-wide row (reading in csa2.h).
 //
-// Keys are processed 32 at a time. Gather: thread t of the 256 owns channels
-// 8p..8p+7 with p = 16*(t/64) + (t%16) -- so wave w owns channels
-// 128w..128w+127 -- and keys 8g..8g+7 of the chunk with g = (t%64)/16. It loads
-// the FP4 codes (4 bytes) and E4M3 scale of each of its keys, or 8 E4M3 bytes of
-// a window row, dequantises them to fp16 (exact) with the gfx950 FP4/FP8
-// converts and stores them in LDS twice:
-//   krow -- row-major fp16 [key][channel], the A operand of Q.K;
-//   vt   -- transposed fp16 [channel][key], the A operand of P.V. Its rows are
-//           80 bytes (5 slots of 16 bytes for 4 chunks of 8 keys) and chunk c of
-//           row d sits in slot (c + d/8) % 5, which spreads the 16-byte stores
-//           of a wave over the LDS banks.
-// Q.K: v_mfma_f32_16x16x32_f16 with keys as A and 16 query heads as B (kept in
-// registers, each head scaled by a power of two into fp16 range; the logits are
-// scaled back). Online softmax per head (one lane column of the 16x16 result).
-// P.V: v_mfma_f32_16x16x32_f16 with the transposed keys as A and P as B. P is
-// split as P = hi + lo with both parts in fp16 (two MFMAs per tile), which keeps
-// the product accurate to about 2^-22 of P even when rows carry large outlier
-// channels.
+// Common to both work shapes: rows are dequantised to fp16 exactly with the
+// gfx950 converts (v_cvt_scalef32_pk_f16_fp4 with the power-of-two part of the
+// E4M3 scale, then one v_pk_mul_f16 by its mantissa part; window rows with
+// v_cvt_scalef32_pk_f16_fp8). Q.K: v_mfma_f32_16x16x32_f16 with 16 keys as A
+// and 16 query heads as B (each head scaled by a power of two into fp16 range;
+// the logits are scaled back). P.V: v_mfma_f32_16x16x32_f16 with V^T as A,
+// read from a row-major fp16 LDS copy by the transposing LDS read
+// ds_read_b64_tr_b16, and P as B. P is split as P = hi + lo with both parts in
+// fp16 (two MFMAs per tile), which keeps the product accurate to about 2^-22
+// of P even when rows carry large outlier channels.
 //
 // Two work shapes:
-//   wide   (512 queries or more): one work-group of 4 waves per query over all
-//          640 key slots; wave w owns heads 16w..16w+15 and all 512 output
-//          channels, so every gathered row serves all 64 heads;
+//   prefill (512 queries or more): one work-group of 8 waves per query over
+//          its 640 key slots in chunks of 64 with an online softmax; wave w
+//          serves 16 heads (w % 4), and the 4 head groups share each
+//          dequantised chunk through LDS.
 //   decode (fewer than 512 queries): one work-group of 8 waves per (query, 16-head
 //          group, slice of 128 key slots). Each lane dequantises 128 channels
 //          of one key straight into its Q.K operand registers (both operands
-//          use the same permuted channel order) and into a row-major fp16 copy
-//          in LDS; wave w forms the logits of its 16 keys, the work-group
-//          agrees on the slice maximum, and wave w accumulates P.V for output
-//          channels 64w..64w+63, reading V through the gfx950 transposing LDS
-//          read (ds_read_b64_tr_b16) so no transposed copy is stored. The query
-//          is converted once per work-group (two heads per wave) and shared
-//          through LDS.
-//   Slices are merged by log-sum-exp in a second kernel.
+//          use the same permuted channel order) and into the row-major LDS
+//          copy; wave w forms the logits of its 16 keys, the work-group agrees
+//          on the slice maximum, and wave w accumulates P.V for output channels
+//          64w..64w+63. The query is converted once per work-group (two heads
+//          per wave) and shared through LDS. Slices are merged by log-sum-exp
+//          in a second kernel.
 #include "device_common.hpp"
 #include "launchers.hpp"
-
-#include <utility>
 
 namespace csa2 {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kChunkKeys = 32;
 constexpr int kSlots = kTopK + kWindow;           // 640 key slots per query
-constexpr int kChunks = kSlots / kChunkKeys;      // 20
 constexpr int kKrowStride = kDim + 8;             // fp16 elements per LDS key row
-constexpr int kVtRowHalves = 40;                  // fp16 elements per LDS channel row (80 B)
-constexpr int kHG = 16;                           // heads per decode work-group
+constexpr int kHG = 16;                           // heads per head group
 constexpr int kHeadGroups = kHeads / kHG;
-constexpr int kWideMinQueries = 512;
+constexpr int kPrefillMinQueries = 512;
 
 typedef _Float16 v2h __attribute__((ext_vector_type(2)));
-
-template <typename F, int... I>
-__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
-  (f(std::integral_constant<int, I>{}), ...);
-}
-// Calls f(integral_constant<int, i>) for i = 0..N-1, fully unrolled.
-template <int N, typename F>
-__device__ __forceinline__ void static_for(F&& f) {
-  static_for_impl(f, std::make_integer_sequence<int, N>{});
-}
-
-// fp16 element offset of (channel row d, 16-byte key chunk c) in vt.
-__device__ __forceinline__ int vt_off(int d, int c) {
-  return d * kVtRowHalves + ((c + (d >> 3)) % 5) * 8;
-}
 
 struct AttnArgs {
   const uint16_t* q;
@@ -92,125 +62,6 @@ struct AttnArgs {
   float* part;     // [Q][splits][64][512] unnormalised outputs
   float* part_ml;  // [Q][splits][64][2] running max and sum
   int splits;
-};
-
-struct Gather {
-  const uint8_t* cache_b;
-  const uint8_t* swa_b;
-  const int32_t* idx_q;
-  int64_t n_cap, tq, pos0;
-  int S, piece, kgrp;
-
-  __device__ void init(const AttnArgs& a, int qi) {
-    const int b = qi / a.T;
-    cache_b = a.cache + (size_t)b * (size_t)a.n_cap * kRowBytes;
-    swa_b = a.swa + (size_t)b * (size_t)a.S * kDim;
-    idx_q = a.idx + (size_t)qi * kTopK;
-    n_cap = a.n_cap;
-    tq = a.q_pos[qi];
-    pos0 = a.swa_pos0[b];
-    S = a.S;
-    const int t = threadIdx.x;
-    piece = 16 * (t >> 6) + (t & 15);
-    kgrp = (t & 63) >> 4;
-  }
-
-  // Raw bytes of this thread's 8 keys (8 channels each) of chunk `chunk`; bit j
-  // of the result marks key j present. The selected positions come from `sidx`
-  // (this work-group's slice of the index list, staged in LDS by stage_idx), so
-  // no global load waits on another; every row load is issued unconditionally
-  // (an absent key reads row 0, which exists, and is masked afterwards).
-  __device__ __forceinline__ uint32_t load(int chunk, int chunk0, const int32_t* sidx,
-                                           uint2 (&r)[8]) const {
-    const int slot0 = chunk * kChunkKeys + kgrp * 8;
-    uint32_t ok = 0;
-    if (slot0 < kTopK) {
-      const int4 i0 = *reinterpret_cast<const int4*>(sidx + (slot0 - chunk0 * kChunkKeys));
-      const int4 i1 = *reinterpret_cast<const int4*>(sidx + (slot0 - chunk0 * kChunkKeys) + 4);
-      const int32_t pj[8] = {i0.x, i0.y, i0.z, i0.w, i1.x, i1.y, i1.z, i1.w};
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const bool v = pj[j] >= 0 && (int64_t)pj[j] < n_cap;
-        ok |= (v ? 1u : 0u) << j;
-        const uint8_t* row = cache_b + (size_t)(v ? pj[j] : 0) * kRowBytes;
-        r[j].x = *reinterpret_cast<const uint32_t*>(row + piece * 4);
-        r[j].y = row[kCodeBytes + (piece >> 1)];
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int64_t tok = tq - (kWindow - 1) + (slot0 + j - kTopK);
-        const int64_t rr = tok - pos0;
-        const bool v = tok >= 0 && rr >= 0 && rr < S;
-        ok |= (v ? 1u : 0u) << j;
-        r[j] = *reinterpret_cast<const uint2*>(swa_b + (size_t)(v ? rr : 0) * kDim + piece * 8);
-      }
-    }
-    return ok;
-  }
-
-  // Copies the selected positions of chunks [chunk0, chunk0 + n) into LDS.
-  __device__ __forceinline__ void stage_idx(int chunk0, int n, int32_t* sidx) const {
-    const int s0 = chunk0 * kChunkKeys;
-    const int cnt = min(n * kChunkKeys, kTopK - s0);
-    for (int i = threadIdx.x; i < cnt; i += kThreads) sidx[i] = idx_q[s0 + i];
-  }
-
-  // Dequantise and store into krow / vt; flags the keys' presence in kvalid.
-  // FP4: v_cvt_scalef32_pk_f16_fp4 applies the power-of-two part of the E4M3
-  // scale (2^(E-7), or 2^-9 for a subnormal scale), then one v_pk_mul_f16
-  // multiplies by its mantissa part (1 + M/8, or M): every step is exact
-  // because the products have at most 6 significant bits and lie in
-  // [2^-10, 2688]. FP8 window rows: v_cvt_scalef32_pk_f16_fp8 with scale 1.
-  __device__ __forceinline__ void store(bool is_main, const uint2 (&r)[8], uint32_t ok,
-                                        uint16_t* krow, uint16_t* vt, int* kvalid) const {
-    uint32_t pr[8][4];   // [key][channel pair]: fp16 pairs of channels 8p+2b, 8p+2b+1
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      if (is_main) {
-        const uint32_t c = r[j].y;
-        const uint32_t E = (c >> 3) & 15u, M = c & 7u;
-        const float hw = __uint_as_float(E ? (E + 120u) << 23 : 118u << 23);
-        const _Float16 mf = E ? __builtin_bit_cast(_Float16, (uint16_t)(0x3C00u | (M << 7)))
-                              : (_Float16)(float)M;
-        const v2h m2 = {mf, mf};
-        v2h h0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(r[j].x, hw, 0) * m2;
-        v2h h1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(r[j].x, hw, 1) * m2;
-        v2h h2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(r[j].x, hw, 2) * m2;
-        v2h h3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(r[j].x, hw, 3) * m2;
-        pr[j][0] = __builtin_bit_cast(uint32_t, h0);
-        pr[j][1] = __builtin_bit_cast(uint32_t, h1);
-        pr[j][2] = __builtin_bit_cast(uint32_t, h2);
-        pr[j][3] = __builtin_bit_cast(uint32_t, h3);
-      } else {
-        pr[j][0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(r[j].x, 1.0f, false));
-        pr[j][1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(r[j].x, 1.0f, true));
-        pr[j][2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(r[j].y, 1.0f, false));
-        pr[j][3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(r[j].y, 1.0f, true));
-      }
-      if (!((ok >> j) & 1u)) pr[j][0] = pr[j][1] = pr[j][2] = pr[j][3] = 0u;
-      const int key = kgrp * 8 + j;
-      if ((threadIdx.x & 15) == 0 && (threadIdx.x >> 6) == 0) kvalid[key] = (ok >> j) & 1u;
-      *reinterpret_cast<uint4*>(&krow[key * kKrowStride + piece * 8]) =
-          make_uint4(pr[j][0], pr[j][1], pr[j][2], pr[j][3]);
-    }
-    // transpose 8 keys x 8 channels: row 8p + 2b takes the low halves of the
-    // pairs, row 8p + 2b + 1 the high halves
-    const int slot = ((kgrp + piece) % 5) * 8;
-#pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      const uint4 lo = make_uint4(__builtin_amdgcn_perm(pr[1][b], pr[0][b], 0x05040100u),
-                                  __builtin_amdgcn_perm(pr[3][b], pr[2][b], 0x05040100u),
-                                  __builtin_amdgcn_perm(pr[5][b], pr[4][b], 0x05040100u),
-                                  __builtin_amdgcn_perm(pr[7][b], pr[6][b], 0x05040100u));
-      const uint4 hi = make_uint4(__builtin_amdgcn_perm(pr[1][b], pr[0][b], 0x07060302u),
-                                  __builtin_amdgcn_perm(pr[3][b], pr[2][b], 0x07060302u),
-                                  __builtin_amdgcn_perm(pr[5][b], pr[4][b], 0x07060302u),
-                                  __builtin_amdgcn_perm(pr[7][b], pr[6][b], 0x07060302u));
-      *reinterpret_cast<uint4*>(&vt[(piece * 8 + 2 * b) * kVtRowHalves + slot]) = lo;
-      *reinterpret_cast<uint4*>(&vt[(piece * 8 + 2 * b + 1) * kVtRowHalves + slot]) = hi;
-    }
-  }
 };
 
 // Exponent shift that brings a per-head maximum |q| into [2^14, 2^15): q * 2^s
@@ -242,178 +93,6 @@ __device__ __forceinline__ float bf16x8_absmax(const uint4& raw) {
     m = fmaxf(m, fabsf(bf16_bits_to_f32(w[i] >> 16)));
   }
   return m;
-}
-
-// P.V operand for one 16-channel tile: channel row `row`, keys
-// {4*grp..+3, 16+4*grp..+3}, matching the Q.K result layout of P.
-__device__ __forceinline__ v8h vt_operand(const uint16_t* vt, int row, int grp) {
-  const uint2 lo = *reinterpret_cast<const uint2*>(&vt[vt_off(row, grp >> 1) + (grp & 1) * 4]);
-  const uint2 hi = *reinterpret_cast<const uint2*>(&vt[vt_off(row, 2 + (grp >> 1)) + (grp & 1) * 4]);
-  const uint4 v = make_uint4(lo.x, lo.y, hi.x, hi.y);
-  return *reinterpret_cast<const v8h*>(&v);
-}
-
-// Online softmax step for one chunk. z: this lane's 8 logits (head = column,
-// -inf for absent keys). Returns alpha and writes P as hi/lo fp16 operands.
-__device__ __forceinline__ float softmax_step(const float (&z)[8], float& m_run, float& l_run,
-                                              v8h& p_hi, v8h& p_lo) {
-  float mx = -INFINITY;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) mx = fmaxf(mx, z[i]);
-  mx = fmaxf(mx, wave_shfl_xor(mx, 16));
-  mx = fmaxf(mx, wave_shfl_xor(mx, 32));
-  const float m_new = fmaxf(m_run, mx);
-  float alpha = 1.0f, psum = 0.0f;
-  float p[8];
-  if (m_new == -INFINITY) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) p[i] = 0.0f;
-  } else {
-    alpha = __expf(m_run - m_new);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      p[i] = __expf(z[i] - m_new);
-      psum += p[i];
-    }
-  }
-  psum += wave_shfl_xor(psum, 16);
-  psum += wave_shfl_xor(psum, 32);
-  l_run = l_run * alpha + psum;
-  m_run = m_new;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const _Float16 h = (_Float16)p[i];
-    p_hi[i] = h;
-    p_lo[i] = (_Float16)(p[i] - (float)h);
-  }
-  return alpha;
-}
-
-// Runs chunk(c, raw, ok) for c = 0..CPS-1 of the slice with row loads issued PF
-// chunks ahead (register slots are indexed statically).
-template <int CPS, int PF, typename Load, typename Chunk>
-__device__ __forceinline__ void pipeline(Load&& load, Chunk&& chunk) {
-  uint2 raw[PF][8];
-  uint32_t ok[PF];
-  static_for<PF>([&](auto ii) __attribute__((always_inline)) {
-    constexpr int i = decltype(ii)::value;
-    if (i < CPS) ok[i] = load(i, raw[i]);
-  });
-  for (int c0 = 0; c0 < CPS; c0 += PF) {
-    static_for<PF>([&](auto ii) __attribute__((always_inline)) {
-      constexpr int i = decltype(ii)::value;
-      const int c = c0 + i;
-      if (c < CPS) {
-        uint2 cur[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) cur[j] = raw[i][j];
-        const uint32_t cok = ok[i];
-        if (c + PF < CPS) ok[i] = load(c + PF, raw[i]);
-        chunk(c, cur, cok);
-      }
-    });
-  }
-}
-
-// ------------------------------------------------------------ wide kernel --
-
-// One work-group per query (CPS = all chunks of its key slots); wave w owns
-// heads 16w..16w+15 and all 512 output channels, so every gathered row serves
-// the 64 heads. The output is written directly.
-template <int CPS>
-__global__ __launch_bounds__(kThreads) void k_sparse_attn_wide(AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t krow[kChunkKeys * kKrowStride];
-  __shared__ __attribute__((aligned(16))) uint16_t vt[kDim * kVtRowHalves];
-  __shared__ int kvalid[kChunkKeys];
-  __shared__ __attribute__((aligned(16))) int32_t sidx[CPS * kChunkKeys];
-
-  const int qi = blockIdx.y;
-  const int split = blockIdx.x;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int col = lane & 15, grp = lane >> 4;
-  Gather g;
-  g.init(a, qi);
-  const int chunk0 = split * CPS;
-
-  v4f acc[32];
-#pragma unroll
-  for (int i = 0; i < 32; ++i) acc[i] = v4f{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY, l_run = 0.0f;
-  v8h qreg[16];
-  float zscale;
-
-  // This wave's 16 heads as the B operand of Q.K: head 16*wave + col,
-  // channels kb*32 + grp*8 .. +7 for kb = 0..15, in fp16 after the head's shift.
-  auto load_q = [&]() __attribute__((always_inline)) {
-    const uint16_t* qp = a.q + ((size_t)qi * kHeads + wave * 16 + col) * kDim + grp * 8;
-    uint4 raw[16];
-    float amax = 0.0f;
-#pragma unroll
-    for (int kb = 0; kb < 16; ++kb) {
-      raw[kb] = *reinterpret_cast<const uint4*>(qp + kb * 32);
-      amax = fmaxf(amax, bf16x8_absmax(raw[kb]));
-    }
-    amax = fmaxf(amax, wave_shfl_xor(amax, 16));
-    amax = fmaxf(amax, wave_shfl_xor(amax, 32));
-    const int sh = q_shift(amax);
-#pragma unroll
-    for (int kb = 0; kb < 16; ++kb) qreg[kb] = q_to_f16(raw[kb], sh);
-    zscale = ldexpf(a.scale, -sh);
-  };
-
-  auto chunk = [&](int c, const uint2 (&r)[8], uint32_t ok) __attribute__((always_inline)) {
-    g.store((chunk0 + c) * kChunkKeys < kTopK, r, ok, krow, vt, kvalid);
-    __syncthreads();
-    float z[8];
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-      v4f s = {0.f, 0.f, 0.f, 0.f};
-      const uint16_t* kr = &krow[(mt * 16 + col) * kKrowStride + grp * 8];
-#pragma unroll
-      for (int kb = 0; kb < 16; ++kb) {
-        const uint4 v = *reinterpret_cast<const uint4*>(kr + kb * 32);
-        s = __builtin_amdgcn_mfma_f32_16x16x32_f16(*reinterpret_cast<const v8h*>(&v), qreg[kb], s,
-                                                   0, 0, 0);
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int key = mt * 16 + 4 * grp + i;
-        z[mt * 4 + i] = kvalid[key] ? s[i] * zscale : -INFINITY;
-      }
-    }
-    v8h p_hi, p_lo;
-    const float alpha = softmax_step(z, m_run, l_run, p_hi, p_lo);
-    if (__any(alpha != 1.0f)) {
-#pragma unroll
-      for (int dt = 0; dt < 32; ++dt) acc[dt] *= alpha;
-    }
-#pragma unroll
-    for (int dt = 0; dt < 32; ++dt) {
-      const v8h v = vt_operand(vt, dt * 16 + col, grp);
-      acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(v, p_hi, acc[dt], 0, 0, 0);
-      acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(v, p_lo, acc[dt], 0, 0, 0);
-    }
-    __syncthreads();
-  };
-
-  g.stage_idx(chunk0, CPS, sidx);
-  load_q();
-  __syncthreads();
-  constexpr int PF = CPS < 2 ? CPS : 2;
-  pipeline<CPS, PF>(
-      [&](int c, uint2 (&r)[8]) __attribute__((always_inline)) {
-        return g.load(chunk0 + c, chunk0, sidx, r);
-      },
-      chunk);
-
-  // lane holds head 16*wave + col, channels 16*dt + 4*grp .. +3
-  const int head = wave * 16 + col;
-  const float inv = l_run > 0.0f ? 1.0f / l_run : 0.0f;
-  float* o = a.out + ((size_t)qi * kHeads + head) * kDim + 4 * grp;
-#pragma unroll
-  for (int dt = 0; dt < 32; ++dt)
-    *reinterpret_cast<float4*>(o + dt * 16) =
-        make_float4(acc[dt][0] * inv, acc[dt][1] * inv, acc[dt][2] * inv, acc[dt][3] * inv);
 }
 
 // ------------------------------------------------------- decode kernel --
@@ -458,7 +137,10 @@ __device__ __forceinline__ float rows_sum(float v) {
 }
 
 // 16 FP4 codes (two 32-bit words, channels 2b, 2b+1 in byte b) with the E4M3
-// scale byte c -> 8 fp16 pairs, exactly as Gather::store dequantises them.
+// scale byte c -> 8 fp16 pairs: the power-of-two part of the scale in the
+// convert, its mantissa part (1 + M/8, or M for a subnormal scale) in one
+// v_pk_mul_f16; exact, as the products have at most 6 significant bits and lie
+// in [2^-10, 2688].
 __device__ __forceinline__ void fp4x16_to_f16(uint32_t w0, uint32_t w1, uint32_t c, uint32_t* pr) {
   const uint32_t E = (c >> 3) & 15u, M = c & 7u;
   const float hw = __uint_as_float(E ? (E + 120u) << 23 : 118u << 23);
@@ -691,6 +373,205 @@ __global__ __launch_bounds__(kDecThreads) void k_sparse_attn_decode(AttnArgs a) 
   }
 }
 
+// ------------------------------------------------------ prefill kernel --
+
+// 512 queries or more: one 8-wave work-group per query over its 640 key slots
+// in 10 chunks of 64 (chunks 0-7 selected rows, 8-9 the window), online
+// softmax across chunks. Wave w serves heads 16(w%4)..+15: for Q.K it takes
+// 32 of the chunk's keys (w/4 picks the half), for P.V output channels
+// 256(w/4)..+255 over all 64 keys. Per chunk: the 512 threads dequantise the
+// chunk (8 threads per key, 64 channels each) into one of two row-major fp16
+// LDS buffers (the next chunk's rows are loaded meanwhile); barrier; Q.K with
+// the keys read from LDS and the query in registers; the two waves of a head
+// group exchange their maxima; barrier; p (fp16 hi + lo) into LDS; barrier;
+// P.V with V read by ds_read_b64_tr_b16.
+constexpr int kPfKeys = 64;                       // keys per chunk
+constexpr int kPfChunks = kSlots / kPfKeys;       // 10
+constexpr int kPfWavesA = 8;
+constexpr int kPfThreadsA = kPfWavesA * 64;
+constexpr int kPRowPf = kPfKeys + 8;              // fp16 per LDS row of P
+static_assert(kTopK % kPfKeys == 0, "a chunk holds only selected rows or only window rows");
+static_assert(kPfThreadsA == kPfKeys * 8, "8 threads per key in the dequantisation");
+
+__global__ __launch_bounds__(kPfThreadsA) void k_sparse_attn_prefill(AttnArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t krow[2][kPfKeys * kKrowStride];
+  __shared__ __attribute__((aligned(16))) uint16_t pbuf[2][kHeads * kPRowPf];   // hi, lo
+  __shared__ float cmax[kPfWavesA][kHG];
+  __shared__ float csum[kPfWavesA][kHG];
+  __shared__ int kvalid[2][kPfKeys];
+
+  const int qi = blockIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+  const int hg = wave & 3, half = wave >> 2;
+  const int col = lane & 15, grp = lane >> 4;
+  const int b = qi / a.T;
+  const int64_t tq = a.q_pos[qi], pos0 = a.swa_pos0[b];
+
+  // ---- dequantisation role: key dk of each chunk, channels 64*dc .. +63
+  const int dk = (int)threadIdx.x >> 3, dc = (int)threadIdx.x & 7;
+  int32_t pj[kTopK / kPfKeys];
+#pragma unroll
+  for (int c = 0; c < kTopK / kPfKeys; ++c) pj[c] = a.idx[(size_t)qi * kTopK + c * kPfKeys + dk];
+  const uint8_t* cache_b = a.cache + (size_t)b * (size_t)a.n_cap * kRowBytes;
+  const uint8_t* swa_b = a.swa + (size_t)b * (size_t)a.S * kDim;
+  // raw bytes of this thread's piece of chunk c: FP4 r[0..1] codes, r[2].x
+  // scales; FP8 r[0..3]
+  auto load = [&](int c, uint4 (&r)[4]) __attribute__((always_inline)) -> bool {
+    bool v;
+    if (c * kPfKeys < kTopK) {
+      int32_t p = pj[0];
+#pragma unroll
+      for (int i = 1; i < kTopK / kPfKeys; ++i) p = c == i ? pj[i] : p;
+      v = p >= 0 && (int64_t)p < a.n_cap;
+      const uint8_t* row = cache_b + (size_t)(v ? p : 0) * kRowBytes;
+      const uint4* c4 = reinterpret_cast<const uint4*>(row + 32 * dc);
+      r[0] = c4[0];
+      r[1] = c4[1];
+      r[2].x = *reinterpret_cast<const uint32_t*>(row + kCodeBytes + 4 * dc);
+    } else {
+      const int64_t tok = tq - (kWindow - 1) + (c * kPfKeys + dk - kTopK);
+      const int64_t rr = tok - pos0;
+      v = tok >= 0 && rr >= 0 && rr < a.S;
+      const uint4* r4 = reinterpret_cast<const uint4*>(swa_b + (size_t)(v ? rr : 0) * kDim + 64 * dc);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) r[i] = r4[i];
+    }
+    return v;
+  };
+  auto store = [&](int c, const uint4 (&r)[4], bool v) __attribute__((always_inline)) {
+    uint32_t pr[32];
+    if (c * kPfKeys < kTopK) {
+      const uint32_t* w = reinterpret_cast<const uint32_t*>(r);
+#pragma unroll
+      for (int m = 0; m < 4; ++m) fp4x16_to_f16(w[2 * m], w[2 * m + 1], (r[2].x >> (8 * m)) & 0xFFu, pr + 8 * m);
+    } else {
+      const uint32_t* w = reinterpret_cast<const uint32_t*>(r);
+#pragma unroll
+      for (int m = 0; m < 16; ++m) fp8x4_to_f16(w[m], pr + 2 * m);
+    }
+    uint4* dst = reinterpret_cast<uint4*>(&krow[c & 1][dk * kKrowStride + 64 * dc]);
+#pragma unroll
+    for (int m = 0; m < 8; ++m)
+      dst[m] = v ? make_uint4(pr[4 * m], pr[4 * m + 1], pr[4 * m + 2], pr[4 * m + 3])
+                 : make_uint4(0u, 0u, 0u, 0u);
+    if (dc == 0) kvalid[c & 1][dk] = v;
+  };
+
+  uint4 raw[4];
+  bool rv = load(0, raw);
+
+  // ---- the query of heads 16hg..+15 (lane: head col, channels kb*32+8grp..+7)
+  v8h qreg[16];
+  float zscale;
+  {
+    const uint16_t* qp = a.q + ((size_t)qi * kHeads + hg * kHG + col) * kDim + grp * 8;
+    uint4 qr[16];
+#pragma unroll
+    for (int kb = 0; kb < 16; ++kb) qr[kb] = *reinterpret_cast<const uint4*>(qp + kb * 32);
+    float amax = 0.0f;
+#pragma unroll
+    for (int kb = 0; kb < 16; ++kb) amax = fmaxf(amax, bf16x8_absmax(qr[kb]));
+    const int sh = q_shift(rows_max(amax));
+#pragma unroll
+    for (int kb = 0; kb < 16; ++kb) qreg[kb] = q_to_f16(qr[kb], sh);
+    zscale = ldexpf(a.scale, -sh);
+  }
+
+  v4f acc[16];
+#pragma unroll
+  for (int dt = 0; dt < 16; ++dt) acc[dt] = v4f{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.0f;
+
+  for (int c = 0; c < kPfChunks; ++c) {
+    const int buf = c & 1;
+    store(c, raw, rv);
+    if (c + 1 < kPfChunks) rv = load(c + 1, raw);
+    __syncthreads();   // chunk c is in krow[buf]
+
+    // Q.K: keys 32*half + 16kt + 4grp + r, head col
+    float z[2][4];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      v4f sc[2] = {v4f{0.f, 0.f, 0.f, 0.f}, v4f{0.f, 0.f, 0.f, 0.f}};
+      const uint16_t* kr = &krow[buf][(32 * half + 16 * kt + col) * kKrowStride + grp * 8];
+#pragma unroll
+      for (int kb = 0; kb < 16; ++kb) {
+        const v8h kv = *reinterpret_cast<const v8h*>(kr + kb * 32);
+        sc[kb & 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kv, qreg[kb], sc[kb & 1], 0, 0, 0);
+      }
+      const v4f s = sc[0] + sc[1];
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        z[kt][r] = kvalid[buf][32 * half + 16 * kt + 4 * grp + r] ? s[r] * zscale : -INFINITY;
+    }
+    float mloc = -INFINITY;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) mloc = fmaxf(mloc, z[kt][r]);
+    mloc = rows_max(mloc);
+    if (grp == 0) cmax[wave][col] = mloc;
+    __syncthreads();
+    const float mc = fmaxf(cmax[hg][col], cmax[hg + 4][col]);
+    const float m_new = fmaxf(m_run, mc);
+    const float alpha = m_new == -INFINITY ? 1.0f : __expf(m_run - m_new);
+    float psum = 0.0f;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      v4h ph, pl;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float p = m_new == -INFINITY ? 0.0f : __expf(z[kt][r] - m_new);
+        psum += p;
+        const _Float16 h = (_Float16)p;
+        ph[r] = h;
+        pl[r] = (_Float16)(p - (float)h);
+      }
+      const int off = (hg * kHG + col) * kPRowPf + 32 * half + 16 * kt + 4 * grp;
+      *reinterpret_cast<v4h*>(&pbuf[0][off]) = ph;
+      *reinterpret_cast<v4h*>(&pbuf[1][off]) = pl;
+    }
+    psum = rows_sum(psum);
+    if (grp == 0) csum[wave][col] = psum;
+    m_run = m_new;
+    if (__any(alpha != 1.0f)) {
+#pragma unroll
+      for (int dt = 0; dt < 16; ++dt) acc[dt] *= alpha;
+    }
+    __syncthreads();   // P of chunk c is complete
+    l_run = l_run * alpha + (csum[hg][col] + csum[hg + 4][col]);
+
+    // P.V: channels 256*half + 16dt + 4grp + r, head col
+#pragma unroll
+    for (int ks = 0; ks < kPfKeys / 32; ++ks) {
+      const int poff = (hg * kHG + col) * kPRowPf + ks * 32 + 8 * grp;
+      const v8h ph = *reinterpret_cast<const v8h*>(&pbuf[0][poff]);
+      const v8h pl = *reinterpret_cast<const v8h*>(&pbuf[1][poff]);
+      const uint16_t* vsrc =
+          &krow[buf][(ks * 32 + 8 * grp + (col >> 2)) * kKrowStride + 256 * half + 4 * (col & 3)];
+#pragma unroll
+      for (int dt = 0; dt < 16; ++dt) {
+        const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) v4s*)(vsrc + dt * 16));
+        const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) v4s*)(vsrc + 4 * kKrowStride + dt * 16));
+        const v8h v = __builtin_bit_cast(v8h, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(v, ph, acc[dt], 0, 0, 0);
+        acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(v, pl, acc[dt], 0, 0, 0);
+      }
+    }
+  }
+
+  // lane holds head 16hg + col, channels 256*half + 16dt + 4grp .. +3
+  const float inv = l_run > 0.0f ? 1.0f / l_run : 0.0f;
+  float* o = a.out + ((size_t)qi * kHeads + hg * kHG + col) * kDim + 256 * half + 4 * grp;
+#pragma unroll
+  for (int dt = 0; dt < 16; ++dt)
+    *reinterpret_cast<float4*>(o + dt * 16) =
+        make_float4(acc[dt][0] * inv, acc[dt][1] * inv, acc[dt][2] * inv, acc[dt][3] * inv);
+}
+
 // One work-group per (query, head); 128 threads x 4 channels. Every load is
 // independent of the others (one round trip), then the slices are combined.
 constexpr int kMaxSplits = 8;
@@ -746,7 +627,7 @@ Shape attn_shape(int Q) {
   // 128 queries: 84 us vs 91 us); from 512 queries on, one 64-head work-group
   // per query, which writes its output directly.
   Shape sh;
-  if (Q < kWideMinQueries) {
+  if (Q < kPrefillMinQueries) {
     sh.wide = false;
     sh.splits = kDecSplits;
   } else {
@@ -791,8 +672,7 @@ hipError_t launch_sparse_attn(const uint16_t* q, const uint8_t* cache, const int
     a.part_ml = a.part + (size_t)Q * a.splits * kHeads * kDim;
   }
   if (sh.wide) {
-    const dim3 grid(a.splits, Q);
-    hipLaunchKernelGGL(k_sparse_attn_wide<kChunks>, grid, dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL(k_sparse_attn_prefill, dim3(Q), dim3(kPfThreadsA), 0, st, a);
   } else {
     const dim3 grid(kDecSplits * kHeadGroups, Q);
     hipLaunchKernelGGL(k_sparse_attn_decode, grid, dim3(kDecThreads), 0, st, a);
