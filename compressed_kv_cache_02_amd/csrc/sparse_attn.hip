@@ -120,6 +120,13 @@ static_assert(kDecThreads / 16 * 4 == kDecKeys, "4 keys x 32 channels per thread
 typedef _Float16 v4h __attribute__((ext_vector_type(4)));
 typedef short v4s __attribute__((ext_vector_type(4)));
 
+// Work-group barrier that orders LDS accesses only: it waits for this wave's
+// LDS operations, not for its global loads in flight (__syncthreads waits for
+// those too, which would expose the latency of rows loaded ahead of use).
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 // Reductions over the four 16-lane rows of a wave (lanes with the same lane %
 // 16), in VALU: v_permlane16_swap pairs rows 0/1 and 2/3, v_permlane32_swap
 // pairs the halves; every lane ends with (r0 op r1) op (r2 op r3).
@@ -239,7 +246,7 @@ __global__ __launch_bounds__(kDecThreads) void k_sparse_attn_decode(AttnArgs a) 
     *reinterpret_cast<v8h*>(&qf[qh * kKrowStride + qc + 8]) = h1;
     if ((lane & 31) == 0) qsh[qh] = sh;
   }
-  __syncthreads();
+  lds_barrier();
   v8h qreg[16];
 #pragma unroll
   for (int kb = 0; kb < 16; ++kb)
@@ -291,7 +298,7 @@ __global__ __launch_bounds__(kDecThreads) void k_sparse_attn_decode(AttnArgs a) 
   for (int r = 0; r < 4; ++r) z[r] = ((kmask >> (4 * grp + r)) & 1u) ? s[r] * zscale : -INFINITY;
   const float mloc = rows_max(fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3])));
   if (grp == 0) wmax[wave][col] = mloc;
-  __syncthreads();
+  lds_barrier();
   float M = wmax[0][col];
 #pragma unroll
   for (int w = 1; w < kDecWaves; ++w) M = fmaxf(M, wmax[w][col]);
@@ -315,7 +322,7 @@ __global__ __launch_bounds__(kDecThreads) void k_sparse_attn_decode(AttnArgs a) 
     *reinterpret_cast<v4h*>(&pbuf[col * kPRow + wave * 16 + 4 * grp]) = ph;
     *reinterpret_cast<v4h*>(&pbuf[kHG * kPRow + col * kPRow + wave * 16 + 4 * grp]) = pl;
   }
-  __syncthreads();
+  lds_barrier();
   float l = 0.0f;
 #pragma unroll
   for (int w = 0; w < kDecWaves; ++w) l += wsum[w][col];
@@ -379,12 +386,13 @@ __global__ __launch_bounds__(kDecThreads) void k_sparse_attn_decode(AttnArgs a) 
 // in 10 chunks of 64 (chunks 0-7 selected rows, 8-9 the window), online
 // softmax across chunks. Wave w serves heads 16(w%4)..+15: for Q.K it takes
 // 32 of the chunk's keys (w/4 picks the half), for P.V output channels
-// 256(w/4)..+255 over all 64 keys. Per chunk: the 512 threads dequantise the
-// chunk (8 threads per key, 64 channels each) into one of two row-major fp16
-// LDS buffers (the next chunk's rows are loaded meanwhile); barrier; Q.K with
-// the keys read from LDS and the query in registers; the two waves of a head
-// group exchange their maxima; barrier; p (fp16 hi + lo) into LDS; barrier;
-// P.V with V read by ds_read_b64_tr_b16.
+// 256(w/4)..+255 over all 64 keys. Per chunk: the next chunk's rows are
+// requested; barrier (this chunk is in one of two row-major fp16 LDS buffers);
+// Q.K with the keys read from LDS and the query in registers; the two waves of
+// a head group exchange their maxima; barrier; p (fp16 hi + lo) into LDS;
+// barrier; the 512 threads dequantise the next chunk (8 threads per key, 64
+// channels each) into the other buffer while P.V runs with V read by
+// ds_read_b64_tr_b16.
 constexpr int kPfKeys = 64;                       // keys per chunk
 constexpr int kPfChunks = kSlots / kPfKeys;       // 10
 constexpr int kPfWavesA = 8;
@@ -483,11 +491,11 @@ __global__ __launch_bounds__(kPfThreadsA) void k_sparse_attn_prefill(AttnArgs a)
   for (int dt = 0; dt < 16; ++dt) acc[dt] = v4f{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.0f;
 
+  store(0, raw, rv);
   for (int c = 0; c < kPfChunks; ++c) {
     const int buf = c & 1;
-    store(c, raw, rv);
     if (c + 1 < kPfChunks) rv = load(c + 1, raw);
-    __syncthreads();   // chunk c is in krow[buf]
+    lds_barrier();   // chunk c is in krow[buf]
 
     // Q.K: keys 32*half + 16kt + 4grp + r, head col
     float z[2][4];
@@ -512,7 +520,7 @@ __global__ __launch_bounds__(kPfThreadsA) void k_sparse_attn_prefill(AttnArgs a)
       for (int r = 0; r < 4; ++r) mloc = fmaxf(mloc, z[kt][r]);
     mloc = rows_max(mloc);
     if (grp == 0) cmax[wave][col] = mloc;
-    __syncthreads();
+    lds_barrier();
     const float mc = fmaxf(cmax[hg][col], cmax[hg + 4][col]);
     const float m_new = fmaxf(m_run, mc);
     const float alpha = m_new == -INFINITY ? 1.0f : __expf(m_run - m_new);
@@ -539,8 +547,11 @@ __global__ __launch_bounds__(kPfThreadsA) void k_sparse_attn_prefill(AttnArgs a)
 #pragma unroll
       for (int dt = 0; dt < 16; ++dt) acc[dt] *= alpha;
     }
-    __syncthreads();   // P of chunk c is complete
+    lds_barrier();   // P of chunk c is complete
     l_run = l_run * alpha + (csum[hg][col] + csum[hg + 4][col]);
+    // the next chunk is dequantised into the other buffer here, so its vector
+    // work overlaps this chunk's P.V
+    if (c + 1 < kPfChunks) store(c + 1, raw, rv);
 
     // P.V: channels 256*half + 16dt + 4grp + r, head col
 #pragma unroll
