@@ -42,6 +42,7 @@ from .formats import (  # noqa: F401
 from .rope import rope_cos_sin, apply_rope  # noqa: F401
 from .compress import compress_mean, n_entries, n_visible  # noqa: F401
 from .indexer import index_scores, block_max  # noqa: F401
+from .mxfp4 import quantize_index_keys, dequantize_index_keys  # noqa: F401
 from .select import topk_positions, build_pool, reindex_candidates  # noqa: F401
 from .attention import sparse_attention, swa_tokens  # noqa: F401
 from .group import layer_schedule, run_group  # noqa: F401

@@ -68,20 +68,21 @@ def layer_schedule(kind):
 
 
 def run_group(schedule, q_idx, w, q, swa, k_codes, cache_rows, n_vis, t,
-              swa_pos0, scale=1.0, with_pool=True):
+              swa_pos0, scale=1.0, with_pool=True, k_scales=None):
     """One query through a layer group.
 
     q_idx / w: dict layer -> indexer query [32,128] E4M3 codes / weights [32]
     (only index-producing layers need them); q / swa: dict layer -> main query
     [64,512] (bf16 values as floats) / window rows [S,512] E4M3 codes;
     k_codes [n_cap,128] and cache_rows [n_cap,288] are the group's shared
-    indexer keys and packed main KV. Returns (idx per layer, out per layer,
+    indexer keys and packed main KV (with ``k_scales`` [n_cap,4], k_codes are
+    [n_cap,64] packed FP4 keys; see ``mxfp4``). Returns (idx per layer, out per layer,
     pool, scores per index-producing layer)."""
     idx_of, out_of, scores_of = {}, {}, {}
     pool = None
     for li, (mode, src) in enumerate(schedule):
         if mode == FULL:
-            s = index_scores(q_idx[li], w[li], k_codes, n_vis)
+            s = index_scores(q_idx[li], w[li], k_codes, n_vis, k_scales=k_scales)
             nv = min(int(n_vis), s.shape[0])
             idx_of[li] = topk_positions(s[:nv], np.arange(nv))
             if with_pool and pool is None:
@@ -89,7 +90,8 @@ def run_group(schedule, q_idx, w, q, swa, k_codes, cache_rows, n_vis, t,
             scores_of[li] = s
         elif mode == REINDEX:
             cand = reindex_candidates(pool, n_vis)
-            s = index_scores(q_idx[li], w[li], k_codes, n_vis, positions=cand)
+            s = index_scores(q_idx[li], w[li], k_codes, n_vis, positions=cand,
+                             k_scales=k_scales)
             idx_of[li] = topk_positions(s, cand)
             scores_of[li] = (cand, s)
         elif mode == REUSE:

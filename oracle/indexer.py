@@ -13,22 +13,27 @@ every causally visible compressed position [P1 §二 hierarchical indexer; P3
     most 43 bits). The weighted head sum runs in float64 in ascending h and is
     rounded once to float32.
   * Positions n >= n_vis are not visible and score -inf.
+  * With FP4 keys (E2M1 codes plus one power-of-two scale per 32 channels, see
+    ``mxfp4``) the dequantised key takes the place of the E4M3 key; nothing
+    else changes.
 """
 
 import numpy as np
 
 from .formats import e4m3_decode
+from .mxfp4 import dequantize_index_keys
 
 N_IDX_HEADS = 32
 D_IDX = 128
 BLOCK = 8          # positions per pool block [P1 §二 hierarchical indexer]
 
 
-def index_scores(q_codes, w, k_codes, n_vis, positions=None, chunk=65536):
+def index_scores(q_codes, w, k_codes, n_vis, positions=None, chunk=65536, k_scales=None):
     """Scores of one query.
 
     q_codes: uint8 [32, 128] E4M3 indexer query; w: float32 [32];
-    k_codes: uint8 [n_cap, 128] E4M3 indexer keys; n_vis: visible count;
+    k_codes: uint8 [n_cap, 128] E4M3 indexer keys, or, with ``k_scales``
+    (uint8 [n_cap, 4] E8M0), uint8 [n_cap, 64] packed FP4 keys; n_vis: visible count;
     positions: int array of positions to score (default: all 0..n_cap-1).
     Returns float32 scores for ``positions`` (-inf where position >= n_vis).
     """
@@ -43,7 +48,10 @@ def index_scores(q_codes, w, k_codes, n_vis, positions=None, chunk=65536):
     vis = np.nonzero(positions < int(n_vis))[0]
     for c0 in range(0, vis.shape[0], chunk):
         sel = vis[c0:c0 + chunk]
-        k = e4m3_decode(k_codes[positions[sel]])                        # [c,128]
+        if k_scales is None:
+            k = e4m3_decode(k_codes[positions[sel]])                    # [c,128]
+        else:
+            k = dequantize_index_keys(k_codes[positions[sel]], k_scales[positions[sel]])
         d = k @ q.T                                                     # exact
         acc = np.zeros(sel.shape[0], dtype=np.float64)
         for h in range(N_IDX_HEADS):
