@@ -16,10 +16,14 @@ back-to-back scan launches on the same stream; with --eager the events bracket
 the scan inside every timed step.
 
 Usage: python bench.py [--steps K] [--warmup W] [--gpus 1] [--workload c2|c4|c1|c3]
+                       [--index-k fp8|fp4]
 
 The default workload is the 1M-context decoder group. `--workload c3` times the
 4,096-query prefill chunk instead (no write path; its scan is an FP8 MFMA
 contraction, so its roofline is reported against the FP8 MFMA peak).
+`--index-k fp4` runs a decode workload with FP4 indexer keys (E2M1 codes plus
+one E8M0 scale per 32 channels, 68 bytes per key instead of 128) drawn from the
+same N(0,1) keys; the default line uses the workloads' FP8 keys.
 """
 
 import argparse
@@ -49,6 +53,9 @@ def parse():
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--workload", default="c2", choices=["c1", "c2", "c3", "c4"])
+    p.add_argument("--index-k", default="fp8", choices=["fp8", "fp4"],
+                   help="indexer-key format: FP8 E4M3 (the workloads' format) or FP4 "
+                        "E2M1 with one E8M0 scale per 32 channels (decode workloads)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--graph", dest="graph", action="store_true", default=True,
                    help="replay each step segment as a HIP graph (default)")
@@ -59,17 +66,24 @@ def parse():
     return p.parse_args()
 
 
-def scan_algorithmic_bytes(B, T, n_vis_total):
-    """Bytes the Full-mode scan must move per launch: 128 B of indexer key per
+def key_bytes(index_k):
+    """Bytes of one indexer key: 128 E4M3 codes, or 64 bytes of E2M1 codes plus
+    four E8M0 scales."""
+    return 68 if index_k == "fp4" else 128
+
+
+def scan_algorithmic_bytes(B, T, n_vis_total, index_k="fp8"):
+    """Bytes the Full-mode scan must move per launch: one indexer key per
     visible position plus each query's 32x128 E4M3 query and 32 float weights."""
-    return 128 * n_vis_total + (32 * 128 + 32 * 4) * B * T
+    return key_bytes(index_k) * n_vis_total + (32 * 128 + 32 * 4) * B * T
 
 
-def step_algorithmic_bytes(w, n_vis_total):
+def step_algorithmic_bytes(w, n_vis_total, index_k="fp8"):
     """Whole-step bytes per the path's definition: scans, attention, write path."""
     q = w.B * w.T
-    full = 128 * n_vis_total + (4096 + 128 + 2048) * q
-    reindex = (2097152 + 4224 + 8192 + 2048) * q
+    kb = key_bytes(index_k)
+    full = kb * n_vis_total + (4096 + 128 + 2048) * q
+    reindex = (16384 * kb + 4224 + 8192 + 2048) * q
     attn = 411648 * q
     n_x = {"decoder": 3}.get(w.kind, 0)
     return full + n_x * reindex + w.n_layers * attn + 1568 * w.B
@@ -96,7 +110,7 @@ def read_traffic(n_launch_bytes):
     return t.get("traffic_bytes_per_launch")
 
 
-def cpu_baseline(w, inp, seed, new_rows, budget_s=10.0):
+def cpu_baseline(w, inp, seed, new_rows, budget_s=10.0, index_k="fp8"):
     """The oracle, single-threaded, on whole queries through the whole group
     (write-path row included), one sequence after another until about
     `budget_s` seconds of oracle time have accumulated (at least one query).
@@ -113,8 +127,10 @@ def cpu_baseline(w, inp, seed, new_rows, budget_s=10.0):
     from oracle.compress import n_visible
     import synth
 
+    from oracle import mxfp4 as OM
     n_cap, m = w.n_cap, w.m
     sched = OG.layer_schedule(w.kind)
+    wall0 = time.perf_counter()
     limit = threadpool_limits(limits=1) if threadpool_limits is not None else contextlib.nullcontext()
     spent, done = 0.0, 0
     with limit:
@@ -130,7 +146,11 @@ def cpu_baseline(w, inp, seed, new_rows, budget_s=10.0):
                     x = _rows[torch.from_numpy(sel).to(_rows.device)].float().cpu().numpy()
                     return OF.quantize_rows(OR.apply_rope(x, sel * m))
 
-            kn = inp["k_idx"][b].cpu().numpy()
+            if index_k == "fp4":
+                # the oracle quantises the bf16 keys itself (staging, not timed)
+                kn, ks = OM.quantize_index_keys(inp["k_bf16"][b].float().cpu().numpy())
+            else:
+                kn, ks = inp["k_idx"][b].cpu().numpy(), None
             for t in range(w.T):
                 qi = {li: inp["q_idx"][li][b, t].cpu().numpy() for li in inp["q_idx"]}
                 wi = {li: inp["w"][li][b, t].cpu().numpy() for li in inp["w"]}
@@ -139,13 +159,15 @@ def cpu_baseline(w, inp, seed, new_rows, budget_s=10.0):
                 tq = w.q_positions[t]
                 nv = int(n_visible(tq, m))
                 t0 = time.perf_counter()
-                OG.run_group(sched, qi, wi, q, swa, kn, Cache(), nv, tq, w.swa_pos0)
+                OG.run_group(sched, qi, wi, q, swa, kn, Cache(), nv, tq, w.swa_pos0, k_scales=ks)
                 spent += time.perf_counter() - t0
                 done += 1
                 if spent >= budget_s:
                     break
             del main_b
-            if spent >= budget_s:
+            # staging (input copies, FP4 key quantisation) is not timed, but the
+            # whole sample stays within a few budgets of wall time
+            if spent >= budget_s or time.perf_counter() - wall0 >= 4 * budget_s:
                 break
     return {"value": done / spent, "unit": "queries/s", "cores": 1, "kind": "oracle",
             "sample": "%d of %d queries, each through all %d layers%s; "
@@ -171,8 +193,18 @@ def main():
     torch.cuda.set_device(0)
     seed = 0
     log("generating inputs for %s" % w.name)
-    inp = make_inputs(w, dev, seed=seed)
+    inp = make_inputs(w, dev, seed=seed, index_k=args.index_k)
     B, T, n_cap, m = w.B, w.T, w.n_cap, w.m
+    if args.index_k == "fp4":
+        if T > 1:
+            print("--index-k fp4 covers the decode workloads (c1, c2, c4)", file=sys.stderr)
+            sys.exit(2)
+        codes = torch.empty((B, n_cap, 64), dtype=torch.uint8, device=dev)
+        scales = torch.empty((B, n_cap, 4), dtype=torch.uint8, device=dev)
+        C.csa2_quantize_index_k(inp["k_bf16"].reshape(B * n_cap, 128), None, codes, scales)
+        keys = (codes, scales)
+    else:
+        keys = inp["k_idx"]
     # cache build: every sequence's rows through the write-path kernel
     cache = torch.empty((B, n_cap, 288), dtype=torch.uint8, device=dev)
     cs_all = torch.from_numpy(C.csa2_rope_table(np.arange(n_cap, dtype=np.int64) * m)).to(dev)
@@ -203,7 +235,7 @@ def main():
     g = LayerGroup(w.kind, B, T, n_cap, device=dev)
     stream = torch.cuda.current_stream()
 
-    args_rest = (inp["k_idx"], cache, n_vis, inp["q_pos"], inp["swa_pos0"], inp["q_idx"],
+    args_rest = (keys, cache, n_vis, inp["q_pos"], inp["swa_pos0"], inp["q_idx"],
                  inp["w"], inp["q"], inp["swa"])
 
     def seg_write():
@@ -211,7 +243,7 @@ def main():
             g.write(cache, write)
 
     def seg_scan():
-        g.scan(inp["k_idx"], n_vis, inp["q_idx"], inp["w"])
+        g.scan(keys, n_vis, inp["q_idx"], inp["w"])
 
     def seg_rest():
         g.rest(*args_rest)
@@ -290,7 +322,7 @@ def main():
 
     ms = el * 1e3 / args.steps
     qps = B * T * args.steps / el
-    scan_bytes = scan_algorithmic_bytes(B, T, n_vis_total)
+    scan_bytes = scan_algorithmic_bytes(B, T, n_vis_total, args.index_k)
     if prefill:
         # a dense FP8 contraction: 32 heads x 128 channels x 2 FLOP per visible pair
         scan_flop = 8192 * n_vis_total
@@ -306,7 +338,7 @@ def main():
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": read_traffic(scan_bytes), "kernel": SCAN_KERNEL,
                 "kernel_ms": round(scan_ms, 4), "algorithmic_bytes_per_launch": scan_bytes}
-        step_bytes = step_algorithmic_bytes(w, n_vis_total)
+        step_bytes = step_algorithmic_bytes(w, n_vis_total, args.index_k)
         step_roof = {"algorithmic_bytes": step_bytes,
                      "achieved_GBps": round(step_bytes / (ms * 1e-3) / 1e9, 1),
                      "frac": round(step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
@@ -331,14 +363,17 @@ def main():
             "c1": "Full-mode decode, batch 32, 131,072 tokens (m=2, 65,536 entries)",
             "c3": "Full-mode prefill of 4,096 queries after 262,144 tokens (m=2, 131,072-133,120 visible entries)"}[w.name]),
             "batch": B, "queries_per_seq": T, "n_cap": n_cap, "layers": len(g.sched),
-            "topk": 512, "window": 128, "timing": ("one HIP graph per step; scan timed over back-to-back launches"
+            "topk": 512, "window": 128,
+            "index_k": {"fp8": "FP8 E4M3 indexer keys (128 B)",
+                        "fp4": "FP4 E2M1 indexer keys + E8M0 per 32 channels (68 B)"}[args.index_k],
+            "timing": ("one HIP graph per step; scan timed over back-to-back launches"
                        if args.graph else "eager")},
         "roofline": roof,
         "step_roofline": step_roof,
     }
     log("timed %d steps: %.3f ms/step; running the oracle sample" % (args.steps, ms))
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(w, inp, seed, new_rows)
+        res["cpu_baseline"] = cpu_baseline(w, inp, seed, new_rows, index_k=args.index_k)
     else:
         res["cpu_baseline"] = None
     print(json.dumps(res), flush=True)

@@ -17,7 +17,7 @@ __all__ = [
     "CSA2_OP_TOPK", "CSA2_OP_SPARSE_ATTN", "Csa2Error", "lib", "lib_path",
     "csa2_abi_version", "csa2_status_string", "csa2_workspace_bytes", "csa2_rope_table",
     "csa2_quantize_kv", "csa2_index_score", "csa2_build_pool", "csa2_topk",
-    "csa2_sparse_attn",
+    "csa2_sparse_attn", "csa2_quantize_index_k", "csa2_index_score_fp4k",
 ]
 
 CSA2_FULL, CSA2_REINDEX, CSA2_REUSE = 0, 1, 2
@@ -26,6 +26,7 @@ CSA2_OK, CSA2_EINVAL, CSA2_EUNSUPPORTED, CSA2_EWORKSPACE, CSA2_EHIP = 0, -1, -2,
 
 IDX_HEADS, IDX_DIM, HEADS, DIM = 32, 128, 64, 512
 ROW_BYTES, TOPK, POOL_BLOCKS, BLOCK, POOL_CAND, WINDOW = 288, 512, 2048, 8, 16384, 128
+IDX_FP4_CODE_BYTES, IDX_FP4_SCALES = 64, 4
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB = None
@@ -43,6 +44,9 @@ _SIGS = {
     "csa2_rope_table": (_i32, [_vp, _i64, _vp]),
     "csa2_quantize_kv": (_i32, [_vp, _vp, _vp, _i64, _vp, _i64, _vp]),
     "csa2_index_score": (_i32, [_i32, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i64, _vp, _vp, _vp]),
+    "csa2_quantize_index_k": (_i32, [_vp, _vp, _i64, _vp, _vp, _i64, _vp]),
+    "csa2_index_score_fp4k": (_i32, [_i32, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i64, _vp, _vp,
+                                     _vp]),
     "csa2_build_pool": (_i32, [_vp, _i32, _vp, _i32, _i32, _i64, _vp, _vp, _sz, _vp]),
     "csa2_topk": (_i32, [_i32, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i64, _vp, _vp, _sz, _vp]),
     "csa2_sparse_attn": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i64, _i32, _f32,
@@ -168,6 +172,49 @@ def csa2_index_score(mode, q_idx, w, k_idx, n_vis, pool, scores, bmax=None, stre
     _check("csa2_index_score", lib().csa2_index_score(mode, _p(q_idx), _p(w), _p(k_idx),
                                                       _p(n_vis), _p(pool), B, T, n_cap,
                                                       _p(scores), _p(bmax), _stream(stream)))
+
+
+def csa2_quantize_index_k(k_bf16, dst_slot, codes, scales, stream=None):
+    """k_bf16 [n,128] bf16, dst_slot [n] int64 or None, codes [rows,64] uint8,
+    scales [rows,4] uint8 (any leading dims of codes/scales flattened)."""
+    import torch
+    n = k_bf16.shape[0]
+    _expect(k_bf16, "k_bf16", torch.bfloat16, (n, IDX_DIM))
+    if dst_slot is not None:
+        _expect(dst_slot, "dst_slot", torch.int64, (n,))
+    _expect(codes, "codes", torch.uint8)
+    _expect(scales, "scales", torch.uint8)
+    rows = codes.numel() // IDX_FP4_CODE_BYTES
+    if codes.shape[-1] != IDX_FP4_CODE_BYTES or scales.shape[-1] != IDX_FP4_SCALES or \
+            scales.numel() // IDX_FP4_SCALES != rows:
+        raise ValueError("codes must be [..., 64] and scales [..., 4] with the same rows")
+    _check("csa2_quantize_index_k", lib().csa2_quantize_index_k(_p(k_bf16), _p(dst_slot), n,
+                                                                _p(codes), _p(scales), rows,
+                                                                _stream(stream)))
+
+
+def csa2_index_score_fp4k(mode, q_idx, w, k_codes, k_scales, n_vis, pool, scores, bmax=None,
+                          stream=None):
+    """As csa2_index_score with FP4 indexer keys: k_codes [B,n_cap,64] uint8,
+    k_scales [B,n_cap,4] uint8."""
+    import torch
+    B, T = q_idx.shape[0], q_idx.shape[1]
+    n_cap = k_codes.shape[1]
+    _expect(q_idx, "q_idx", torch.uint8, (B, T, IDX_HEADS, IDX_DIM))
+    _expect(w, "w", torch.float32, (B, T, IDX_HEADS))
+    _expect(k_codes, "k_codes", torch.uint8, (B, n_cap, IDX_FP4_CODE_BYTES))
+    _expect(k_scales, "k_scales", torch.uint8, (B, n_cap, IDX_FP4_SCALES))
+    _expect(n_vis, "n_vis", torch.int32, (B, T))
+    n_items = n_cap if mode == CSA2_FULL else POOL_CAND
+    if scores is not None or mode != CSA2_FULL:
+        _expect(scores, "scores", torch.float32, (B, T, n_items))
+    if pool is not None:
+        _expect(pool, "pool", torch.int32, (B, T, POOL_BLOCKS))
+    if bmax is not None:
+        _expect(bmax, "bmax", torch.float32, (B, T, (n_cap + BLOCK - 1) // BLOCK))
+    _check("csa2_index_score_fp4k", lib().csa2_index_score_fp4k(
+        mode, _p(q_idx), _p(w), _p(k_codes), _p(k_scales), _p(n_vis), _p(pool), B, T, n_cap,
+        _p(scores), _p(bmax), _stream(stream)))
 
 
 def csa2_build_pool(src, is_bmax, n_vis, n_cap, pool, ws, stream=None):

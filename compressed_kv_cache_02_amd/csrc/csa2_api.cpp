@@ -109,6 +109,32 @@ int csa2_index_score(int mode, const uint8_t* q_idx, const float* w, const uint8
   return status_of(e);
 }
 
+int csa2_quantize_index_k(const void* k_bf16, const int64_t* dst_slot, int64_t n,
+                          uint8_t* codes, uint8_t* scales, int64_t rows, void* stream) {
+  if (n < 0 || rows < 1) return CSA2_EINVAL;
+  if (n == 0) return CSA2_OK;
+  if (!aligned16(k_bf16) || !aligned16(codes) || !aligned16(scales) || !opt_aligned16(dst_slot))
+    return CSA2_EINVAL;
+  if (!dst_slot && n > rows) return CSA2_EINVAL;
+  return status_of(csa2::launch_quantize_index_k(static_cast<const uint16_t*>(k_bf16), dst_slot, n,
+                                                 codes, scales, rows, as_stream(stream)));
+}
+
+int csa2_index_score_fp4k(int mode, const uint8_t* q_idx, const float* w, const uint8_t* k_codes,
+                          const uint8_t* k_scales, const int32_t* n_vis, const int32_t* pool,
+                          int B, int T, int64_t n_cap, float* scores, float* bmax, void* stream) {
+  if (mode != CSA2_FULL && mode != CSA2_REINDEX) return CSA2_EINVAL;
+  if (!sizes_ok(B, T, n_cap)) return CSA2_EINVAL;
+  if (!aligned16(q_idx) || !aligned16(w) || !aligned16(k_codes) || !aligned16(k_scales) ||
+      !aligned16(n_vis) || !opt_aligned16(scores) || !opt_aligned16(bmax))
+    return CSA2_EINVAL;
+  if (!scores && (mode != CSA2_FULL || !bmax)) return CSA2_EINVAL;
+  if (mode == CSA2_REINDEX && (!aligned16(pool) || bmax)) return CSA2_EINVAL;
+  return status_of(csa2::launch_index_score_decode_fp4k(mode, q_idx, w, k_codes, k_scales, n_vis,
+                                                        pool, B, T, n_cap, scores, bmax,
+                                                        as_stream(stream)));
+}
+
 int csa2_build_pool(const float* src, int is_bmax, const int32_t* n_vis, int B, int T,
                     int64_t n_cap, int32_t* pool, void* ws, size_t ws_bytes, void* stream) {
   if (!sizes_ok(B, T, n_cap)) return CSA2_EINVAL;

@@ -17,6 +17,8 @@
 // position; the epilogue applies ReLU and the head weights and adds the other
 // half with one cross-half shuffle. The scan is HBM-bound (64 FLOP per byte);
 // the MFMA only keeps the 4096 MACs per key off the vector ALU.
+#include <type_traits>
+
 #include "device_common.hpp"
 #include "launchers.hpp"
 
@@ -103,10 +105,44 @@ __device__ __forceinline__ float weighted_relu_sum(const v16f& acc, const float*
   return part;
 }
 
-template <int MODE>
+// FP4 indexer keys (KF = 1): one key is 64 bytes of E2M1 codes plus 4 E8M0
+// scales, one per 32 channels. The scaled FP8 x FP4 MFMA applies them itself:
+// in v_mfma_scale_f32_32x32x64_f8f6f4 an FP4 B lane (column, half h) holds K
+// values 32h..32h+31 in nibble order and its scale byte covers exactly those
+// 32, while an FP8 A lane of half h holds K values 16h..16h+15 (bytes 0..15)
+// and 32+16h..32+16h+15 (bytes 16..31) (measured with in-bounds impulse
+// probes on gfx950). So MFMA j (channels 64j..64j+63) takes from a key lane
+// code bytes 32j+16h..+15 with scale byte 2j+h, and from a query lane the
+// 16-byte pieces 4j+h and 4j+2+h.
+struct KTile4 {
+  uint4 c[2];      // code bytes 16h..16h+15 and 32+16h..32+16h+15 of the key
+  uint32_t sc;     // the key's four scale bytes shifted right by 8h
+};
+
+__device__ __forceinline__ void load_tile4(KTile4& t, const uint8_t* codes, const uint8_t* scales,
+                                           int half, bool ok) {
+  if (ok) {
+    t.c[0] = *reinterpret_cast<const uint4*>(codes);
+    t.c[1] = *reinterpret_cast<const uint4*>(codes + 32);
+    t.sc = *reinterpret_cast<const uint32_t*>(scales) >> (8 * half);
+  } else {
+    t.c[0] = t.c[1] = make_uint4(0, 0, 0, 0);
+    t.sc = 0;
+  }
+}
+
+__device__ __forceinline__ v8i fp4_operand(const uint4& a) {
+  v8i r;
+  r[0] = (int)a.x; r[1] = (int)a.y; r[2] = (int)a.z; r[3] = (int)a.w;
+  r[4] = r[5] = r[6] = r[7] = 0;   // an FP4 operand uses the first four registers
+  return r;
+}
+
+template <int MODE, int KF>
 __global__ __launch_bounds__(256) void k_index_score_decode(
     const uint8_t* __restrict__ q_idx, const float* __restrict__ w,
-    const uint8_t* __restrict__ k_idx, const int32_t* __restrict__ n_vis,
+    const uint8_t* __restrict__ k_idx, const uint8_t* __restrict__ k_scales,
+    const int32_t* __restrict__ n_vis,
     const int32_t* __restrict__ pool, int T, int64_t n_cap, int64_t n_items,
     float* __restrict__ scores, float* __restrict__ bmax) {
   const int qi = blockIdx.y;
@@ -119,10 +155,12 @@ __global__ __launch_bounds__(256) void k_index_score_decode(
   nv = nv < 0 ? 0 : (nv > n_cap ? n_cap : nv);
   const int64_t n_blk = (n_cap + kBlock - 1) / kBlock;
 
-  const uint8_t* qp = q_idx + (size_t)qi * (kIdxHeads * kIdxDim) + col * kIdxDim + half * 64;
-  const uint4* q4 = reinterpret_cast<const uint4*>(qp);
-  const v8i a0 = as_v8i(q4[0], q4[1]);
-  const v8i a1 = as_v8i(q4[2], q4[3]);
+  // A operands: FP8 keys pair a query lane's channels with the key lane's in
+  // the same order (64h..64h+63); FP4 keys need the FP8 x FP4 order above.
+  const uint4* q4 = reinterpret_cast<const uint4*>(q_idx + (size_t)qi * (kIdxHeads * kIdxDim) +
+                                                   col * kIdxDim);
+  const v8i a0 = KF ? as_v8i(q4[half], q4[2 + half]) : as_v8i(q4[4 * half], q4[4 * half + 1]);
+  const v8i a1 = KF ? as_v8i(q4[4 + half], q4[6 + half]) : as_v8i(q4[4 * half + 2], q4[4 * half + 3]);
   // head weights of this lane's 16 accumulator rows: 4 runs of 4 consecutive heads
   float wr[16];
   {
@@ -137,7 +175,9 @@ __global__ __launch_bounds__(256) void k_index_score_decode(
     }
   }
 
-  const uint8_t* kbase = k_idx + (size_t)b * (size_t)n_cap * kIdxDim + half * 64;
+  constexpr int kKeyBytes = KF ? kIdxDim / 2 : kIdxDim;
+  const uint8_t* kbase = k_idx + (size_t)b * (size_t)n_cap * kKeyBytes + half * (KF ? 16 : 64);
+  const uint8_t* sbase = KF ? k_scales + (size_t)b * (size_t)n_cap * 4 : nullptr;
   const int32_t* pl = MODE == 1 ? pool + (size_t)qi * kPoolBlocks : nullptr;
   float* srow = scores ? scores + (size_t)qi * (size_t)n_items : nullptr;
   float* brow = bmax ? bmax + (size_t)qi * (size_t)n_blk : nullptr;
@@ -167,12 +207,19 @@ __global__ __launch_bounds__(256) void k_index_score_decode(
   };
 
   // Tiles are loaded kPrefetch - 1 ahead of the one being scored.
-  KTile buf[kPrefetch];
+  using Tile = typename std::conditional<KF == 1, KTile4, KTile>::type;
+  Tile buf[kPrefetch];
   bool okb[kPrefetch];
+  auto load = [&](Tile& t, int64_t pos, bool ok) __attribute__((always_inline)) {
+    if constexpr (KF == 1)
+      load_tile4(t, kbase + pos * kKeyBytes, sbase + pos * 4, half, ok);
+    else
+      load_tile(t, kbase + pos * kKeyBytes, ok);
+  };
 #pragma unroll
   for (int i = 0; i < kPrefetch - 1; ++i) {
     const int64_t pos = position_of(i, okb[i]);
-    load_tile(buf[i], kbase + pos * kIdxDim, okb[i]);
+    load(buf[i], pos, okb[i]);
   }
 #pragma unroll
   for (int it = 0; it < kTilesPerWave; ++it) {
@@ -182,18 +229,28 @@ __global__ __launch_bounds__(256) void k_index_score_decode(
     if (it + kAhead < kTilesPerWave) {
       const int nb = (it + kAhead) % kPrefetch;
       const int64_t pos = position_of(it + kAhead, okb[nb]);
-      load_tile(buf[nb], kbase + pos * kIdxDim, okb[nb]);
+      load(buf[nb], pos, okb[nb]);
     }
-    const KTile& cur = buf[it % kPrefetch];
+    const Tile& cur = buf[it % kPrefetch];
     const bool cur_ok = okb[it % kPrefetch];
     float s = -INFINITY;
     // Skip the MFMA when no lane of the wave holds a visible position.
     if (__any(cur_ok)) {
       v16f acc = {};
-      acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a0, as_v8i(cur.v[0], cur.v[1]), acc,
-                                                            0, 0, 0, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a1, as_v8i(cur.v[2], cur.v[3]), acc,
-                                                            0, 0, 0, 0, 0, 0);
+      if constexpr (KF == 1) {
+        // A: E4M3 (format 0) with scale 2^0 (E8M0 127); B: E2M1 (format 4)
+        // with the key's block scales (bytes 0 and 2 of the shifted word,
+        // each taken from byte 0 of the scale register)
+        acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a0, fp4_operand(cur.c[0]), acc, 0, 4,
+                                                              0, 127, 0, (int)cur.sc);
+        acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a1, fp4_operand(cur.c[1]), acc, 0, 4,
+                                                              0, 127, 0, (int)(cur.sc >> 16));
+      } else {
+        acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a0, as_v8i(cur.v[0], cur.v[1]), acc,
+                                                              0, 0, 0, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a1, as_v8i(cur.v[2], cur.v[3]), acc,
+                                                              0, 0, 0, 0, 0, 0);
+      }
       const float part = weighted_relu_sum(acc, wr);
       // lo-half + hi-half row sums, in every lane
       const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(part), __float_as_uint(part),
@@ -460,11 +517,31 @@ hipError_t launch_index_score_decode(int mode, const uint8_t* q_idx, const float
   const int64_t gx = (n_items + per_wg - 1) / per_wg;
   const dim3 grid((unsigned)gx, (unsigned)Q);
   if (mode == 0) {
-    hipLaunchKernelGGL(k_index_score_decode<0>, grid, dim3(256), 0, st, q_idx, w, k_idx, n_vis,
-                       pool, T, n_cap, n_items, scores, bmax);
+    hipLaunchKernelGGL((k_index_score_decode<0, 0>), grid, dim3(256), 0, st, q_idx, w, k_idx,
+                       nullptr, n_vis, pool, T, n_cap, n_items, scores, bmax);
   } else {
-    hipLaunchKernelGGL(k_index_score_decode<1>, grid, dim3(256), 0, st, q_idx, w, k_idx, n_vis,
-                       pool, T, n_cap, n_items, scores, nullptr);
+    hipLaunchKernelGGL((k_index_score_decode<1, 0>), grid, dim3(256), 0, st, q_idx, w, k_idx,
+                       nullptr, n_vis, pool, T, n_cap, n_items, scores, nullptr);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_index_score_decode_fp4k(int mode, const uint8_t* q_idx, const float* w,
+                                          const uint8_t* k_codes, const uint8_t* k_scales,
+                                          const int32_t* n_vis, const int32_t* pool, int B, int T,
+                                          int64_t n_cap, float* scores, float* bmax,
+                                          hipStream_t st) {
+  const int Q = B * T;
+  const int64_t n_items = mode == 0 ? n_cap : (int64_t)kPoolCand;
+  const int64_t per_wg = mode == 0 ? items_per_wg<0>() : items_per_wg<1>();
+  const int64_t gx = (n_items + per_wg - 1) / per_wg;
+  const dim3 grid((unsigned)gx, (unsigned)Q);
+  if (mode == 0) {
+    hipLaunchKernelGGL((k_index_score_decode<0, 1>), grid, dim3(256), 0, st, q_idx, w, k_codes,
+                       k_scales, n_vis, pool, T, n_cap, n_items, scores, bmax);
+  } else {
+    hipLaunchKernelGGL((k_index_score_decode<1, 1>), grid, dim3(256), 0, st, q_idx, w, k_codes,
+                       k_scales, n_vis, pool, T, n_cap, n_items, scores, nullptr);
   }
   return hipGetLastError();
 }

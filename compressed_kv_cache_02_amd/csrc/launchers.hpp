@@ -11,11 +11,22 @@ namespace csa2 {
 hipError_t launch_quantize_kv(const uint16_t* kv, const float* cos_sin, const int64_t* slot,
                               int64_t n, uint8_t* cache, int64_t cache_rows, hipStream_t st);
 
+// FP4 indexer keys (E2M1 codes [rows][64] + E8M0 scales [rows][4]) from bf16 keys.
+hipError_t launch_quantize_index_k(const uint16_t* k, const int64_t* slot, int64_t n,
+                                   uint8_t* codes, uint8_t* scales, int64_t rows, hipStream_t st);
+
 // Decode-shaped scan: one query per grid row, positions split over work-groups.
 hipError_t launch_index_score_decode(int mode, const uint8_t* q_idx, const float* w,
                                      const uint8_t* k_idx, const int32_t* n_vis,
                                      const int32_t* pool, int B, int T, int64_t n_cap,
                                      float* scores, float* bmax, hipStream_t st);
+
+// Decode-shaped scan over FP4 indexer keys (codes [B][n_cap][64], scales [B][n_cap][4]).
+hipError_t launch_index_score_decode_fp4k(int mode, const uint8_t* q_idx, const float* w,
+                                          const uint8_t* k_codes, const uint8_t* k_scales,
+                                          const int32_t* n_vis, const int32_t* pool, int B, int T,
+                                          int64_t n_cap, float* scores, float* bmax,
+                                          hipStream_t st);
 
 // Prefill-shaped scan: a dense FP8 contraction over (queries x 32 heads) x positions.
 hipError_t launch_index_score_prefill(const uint8_t* q_idx, const float* w, const uint8_t* k_idx,

@@ -97,7 +97,63 @@ __global__ __launch_bounds__(256) void k_quantize_kv(const uint16_t* __restrict_
   if ((lane & 1) == 0) dstp[kCodeBytes + (lane >> 1)] = (uint8_t)sc;
 }
 
+// ---------------------------------------------------------------------------
+// FP4 indexer keys: E2M1 codes with one E8M0 (power-of-two) scale per 32
+// channels. The earlier model generation trained its indexer keys in FP4
+// ("DeepSeek V4.1 Flash vs V4 Pro", 黑科技之三); the pages' FP4 is of the MXFP4
+// family ("DeepSeek V4.1-Flash 为什么这么强？CED 与 CSA2 架构全拆解", §三), and
+// the block scale follows the OCP Microscaling (MX) v1.0 conversion rule:
+// exponent floor(log2(amax)) - 2, stored with bias 127, clamped to 0..254.
+//
+// One wave per key, lane l owns channels 2l and 2l+1 (one 4-byte bf16 load,
+// one byte of codes); a 32-channel block is a row of 16 lanes. For a normal
+// amax with biased exponent E, floor(log2(amax)) - 2 + 127 = E - 2, so the
+// scale code is max(E - 2, 0) (zero and subnormal maxima give 0). Dividing by
+// the scale is a multiplication by 2^(127 - code), exact for every value whose
+// code can be nonzero; the element code then comes from exact comparisons with
+// the E2M1 midpoints, ties to the even code, saturating at 6.
+__device__ __forceinline__ uint32_t e2m1_code_of_scaled(float x, float inv_scale) {
+  const float y = __fmul_rn(fabsf(x), inv_scale);
+  uint32_t m = (y > 0.25f) + (y >= 0.75f) + (y > 1.25f) + (y >= 1.75f) + (y > 2.5f) +
+               (y >= 3.5f) + (y > 5.0f);
+  return m | ((__float_as_uint(x) >> 28) & 8u);
+}
+
+__global__ __launch_bounds__(256) void k_quantize_index_k(const uint16_t* __restrict__ k,
+                                                          const int64_t* __restrict__ slot,
+                                                          int64_t n, uint8_t* __restrict__ codes,
+                                                          uint8_t* __restrict__ scales,
+                                                          int64_t rows) {
+  const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (r >= n) return;
+  const int64_t dst = slot ? slot[r] : r;
+  if (dst < 0 || dst >= rows) return;
+  const uint32_t pair = *reinterpret_cast<const uint32_t*>(k + r * kIdxDim + 2 * lane);
+  const float x0 = bf16_bits_to_f32(pair & 0xFFFFu), x1 = bf16_bits_to_f32(pair >> 16);
+  uint32_t amax = max(__float_as_uint(x0) & 0x7FFFFFFFu, __float_as_uint(x1) & 0x7FFFFFFFu);
+  amax = max(amax, (uint32_t)wave_shfl_xor((int)amax, 1));
+  amax = max(amax, (uint32_t)wave_shfl_xor((int)amax, 2));
+  amax = max(amax, (uint32_t)wave_shfl_xor((int)amax, 4));
+  amax = max(amax, (uint32_t)wave_shfl_xor((int)amax, 8));   // max over the 16-lane row
+  const uint32_t E = amax >> 23;
+  const uint32_t code = E >= 2u ? E - 2u : 0u;
+  const float inv = __uint_as_float((254u - code) << 23);       // 2^(127 - code)
+  codes[dst * (kIdxDim / 2) + lane] =
+      (uint8_t)(e2m1_code_of_scaled(x0, inv) | (e2m1_code_of_scaled(x1, inv) << 4));
+  if ((lane & 15) == 0) scales[dst * 4 + (lane >> 4)] = (uint8_t)code;
+}
+
 }  // namespace
+
+hipError_t launch_quantize_index_k(const uint16_t* k, const int64_t* slot, int64_t n,
+                                   uint8_t* codes, uint8_t* scales, int64_t rows, hipStream_t st) {
+  if (n == 0) return hipSuccess;
+  const int64_t blocks = (n + 3) / 4;
+  hipLaunchKernelGGL(k_quantize_index_k, dim3((unsigned)blocks), dim3(256), 0, st, k, slot, n,
+                     codes, scales, rows);
+  return hipGetLastError();
+}
 
 hipError_t launch_quantize_kv(const uint16_t* kv, const float* cos_sin, const int64_t* slot,
                               int64_t n, uint8_t* cache, int64_t cache_rows, hipStream_t st) {

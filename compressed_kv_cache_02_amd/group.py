@@ -17,8 +17,8 @@ import torch
 
 from . import (CSA2_FULL, CSA2_REINDEX, CSA2_REUSE, CSA2_OP_BUILD_POOL, CSA2_OP_SPARSE_ATTN,
                CSA2_OP_TOPK, POOL_BLOCKS, POOL_CAND, TOPK, HEADS, DIM, BLOCK,
-               csa2_build_pool, csa2_index_score, csa2_quantize_kv, csa2_sparse_attn,
-               csa2_topk, csa2_workspace_bytes)
+               csa2_build_pool, csa2_index_score, csa2_index_score_fp4k, csa2_quantize_kv,
+               csa2_sparse_attn, csa2_topk, csa2_workspace_bytes)
 
 FULL, REINDEX, REUSE = "F", "X", "U"
 
@@ -38,6 +38,18 @@ def schedule(kind):
             s.append((REUSE, len(s) - 1))
         return s
     raise ValueError(kind)
+
+
+def index_score(mode, q_idx, w, keys, n_vis, pool, scores, bmax=None, stream=None):
+    """csa2_index_score over FP8 keys (a [B, n_cap, 128] uint8 tensor) or
+    csa2_index_score_fp4k over FP4 keys (a (codes [B, n_cap, 64],
+    scales [B, n_cap, 4]) pair)."""
+    if isinstance(keys, tuple):
+        codes, scales = keys
+        csa2_index_score_fp4k(mode, q_idx, w, codes, scales, n_vis, pool, scores, bmax,
+                              stream=stream)
+    else:
+        csa2_index_score(mode, q_idx, w, keys, n_vis, pool, scores, bmax, stream=stream)
 
 
 def visible_entries(t, m):
@@ -87,8 +99,9 @@ class LayerGroup:
              write=None, stream=None, hooks=None):
         """One pass of the whole group.
 
-        k_idx [B,n_cap,128], cache [B,n_cap,288]: the group's shared keys and
-        packed main KV; n_vis [B,T] int32; q_pos [B,T] int64; swa_pos0 [B] int64;
+        k_idx [B,n_cap,128] FP8 keys, or a (codes [B,n_cap,64], scales
+        [B,n_cap,4]) pair of FP4 keys; cache [B,n_cap,288]: the group's shared
+        keys and packed main KV; n_vis [B,T] int32; q_pos [B,T] int64; swa_pos0 [B] int64;
         q_idx / w: per index-producing layer (dict or list indexed by layer);
         q / swa: per layer. write = (kv_bf16 [n,512], cos_sin [n,32,2],
         dst_slot [n]) runs the write path first. hooks: optional dict of
@@ -112,8 +125,8 @@ class LayerGroup:
     def scan(self, k_idx, n_vis, q_idx, w, stream=None):
         """The Full layer's scan of every visible position, with block maxima."""
         li = [i for i, (m, _) in enumerate(self.sched) if m == FULL][0]
-        csa2_index_score(CSA2_FULL, q_idx[li], w[li], k_idx, n_vis, None, self.scores, self.bmax,
-                         stream=stream)   # scores is None when the group has a pool
+        index_score(CSA2_FULL, q_idx[li], w[li], k_idx, n_vis, None, self.scores, self.bmax,
+                    stream=stream)   # scores is None when the group has a pool
 
     def rest(self, k_idx, cache, n_vis, q_pos, swa_pos0, q_idx, w, q, swa, scale=1.0,
              stream=None):
@@ -123,8 +136,8 @@ class LayerGroup:
                 if self.pool is not None:
                     csa2_build_pool(self.bmax, True, n_vis, self.n_cap, self.pool, self.ws,
                                     stream=stream)
-                    csa2_index_score(CSA2_REINDEX, q_idx[li], w[li], k_idx, n_vis, self.pool,
-                                     self.scores_full_pool, None, stream=stream)
+                    index_score(CSA2_REINDEX, q_idx[li], w[li], k_idx, n_vis, self.pool,
+                                self.scores_full_pool, None, stream=stream)
                     csa2_topk(CSA2_REINDEX, self.scores_full_pool, n_vis, self.pool, None,
                               self.n_cap, self.idx[li], self.ws, stream=stream)
                 else:
@@ -134,8 +147,8 @@ class LayerGroup:
                     self.saved_scores[li] = (self.scores if self.scores is not None
                                              else self.scores_full_pool).clone()
             elif mode == REINDEX:
-                csa2_index_score(CSA2_REINDEX, q_idx[li], w[li], k_idx, n_vis, self.pool,
-                                 self.scores_pool, None, stream=stream)
+                index_score(CSA2_REINDEX, q_idx[li], w[li], k_idx, n_vis, self.pool,
+                            self.scores_pool, None, stream=stream)
                 csa2_topk(CSA2_REINDEX, self.scores_pool, n_vis, self.pool, None, self.n_cap,
                           self.idx[li], self.ws, stream=stream)
                 if self.keep_scores:

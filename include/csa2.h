@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define CSA2_ABI_VERSION 2
+#define CSA2_ABI_VERSION 3
 
 #define CSA2_IDX_HEADS 32
 #define CSA2_IDX_DIM 128
@@ -56,6 +56,8 @@ extern "C" {
 #define CSA2_POOL_CAND 16384
 #define CSA2_WINDOW 128
 #define CSA2_ROPE_PAIRS 32      /* RoPE on channels 448..511, adjacent pairs */
+#define CSA2_IDX_FP4_CODE_BYTES 64   /* FP4 indexer key: 128 E2M1 codes ... */
+#define CSA2_IDX_FP4_SCALES 4        /* ... and one E8M0 scale per 32 channels */
 
 /* Layer mode ([P1] §二 mode table; [P2] 黑科技之二; [P3] 第二刀, Fig. 4):
  *   FULL    -- own indexer keys, own scores over every visible position, own Top-K;
@@ -134,6 +136,35 @@ int csa2_quantize_kv(const void* kv_bf16, const float* cos_sin, const int64_t* d
 int csa2_index_score(int mode, const uint8_t* q_idx, const float* w, const uint8_t* k_idx,
                      const int32_t* n_vis, const int32_t* pool, int B, int T, int64_t n_cap,
                      float* scores, float* bmax, void* stream);
+
+/* DEVICE. FP4 indexer keys. An earlier model generation already trained the
+ * indexer's keys in FP4 ([P2] 黑科技之三) and the pages' FP4 belongs to the MXFP4
+ * family ([P1] §三); they give no block size or scale type for the indexer, so
+ * this library takes the OCP Microscaling (MX) v1.0 layout and conversion rule:
+ *   k_bf16   [n][128] bf16 keys (device, finite values);
+ *   dst_slot [n] int64 destination row (device), or NULL for row r -> row r;
+ *            slots outside [0, rows) are skipped;
+ *   codes    [rows][64] (device, written): byte j = E2M1 code of channel 2j in the
+ *            low nibble, channel 2j+1 in the high nibble;
+ *   scales   [rows][4] (device, written): byte b = E8M0 scale of channels
+ *            32b..32b+31, max(E - 2, 0) for the biased exponent E of the block's
+ *            largest |value| (= floor(log2(amax)) - 2 + 127; 0 for a zero block).
+ * Each element is the E2M1 code nearest |v| / 2^(scale - 127) (ties to the even
+ * code, saturating at 6); its sign bit is the sign bit of v.
+ * Errors: CSA2_EINVAL for NULL/misaligned pointers, n < 0, rows < 1. */
+int csa2_quantize_index_k(const void* k_bf16, const int64_t* dst_slot, int64_t n,
+                          uint8_t* codes, uint8_t* scales, int64_t rows, void* stream);
+
+/* DEVICE. csa2_index_score over FP4 indexer keys (csa2_quantize_index_k's
+ * layout): k_codes [B][n_cap][64], k_scales [B][n_cap][4] (device) take the
+ * place of k_idx; the key value of channel c is E2M1(code) * 2^(scale - 127),
+ * multiplied exactly with the E4M3 query by the scaled FP8 x FP4 matrix
+ * instruction. Modes, outputs, masking and errors are those of
+ * csa2_index_score; every T runs the decode-shaped scan, and REINDEX
+ * re-scores a position to the same bits as FULL. */
+int csa2_index_score_fp4k(int mode, const uint8_t* q_idx, const float* w, const uint8_t* k_codes,
+                          const uint8_t* k_scales, const int32_t* n_vis, const int32_t* pool,
+                          int B, int T, int64_t n_cap, float* scores, float* bmax, void* stream);
 
 /* DEVICE. Hierarchical candidate pool ([P1] §二 hierarchical sparse indexer;
  * [P3] 第二刀, Fig. 5): per query, among blocks j < ceil(n_vis/8), the 2,048

@@ -62,11 +62,16 @@ def quantize_index_keys(k):
     k = np.asarray(k, dtype=np.float32)
     n = k.shape[0]
     assert k.shape == (n, D_IDX)
-    blocks = k.reshape(-1, MX_BLOCK)                        # [n*4, 32]
-    sc = mx_scale_codes(np.abs(blocks).max(axis=1))         # [n*4]
-    codes = e2m1_codes(blocks, mx_scale_values(sc)).reshape(n, D_IDX)
-    packed = (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
-    return packed, sc.reshape(n, MX_BLOCKS)
+    packed = np.empty((n, CODE_BYTES), dtype=np.uint8)
+    scales = np.empty((n, MX_BLOCKS), dtype=np.uint8)
+    step = 4096
+    for r0 in range(0, n, step):
+        blocks = k[r0:r0 + step].reshape(-1, MX_BLOCK)              # [rows*4, 32]
+        sc = mx_scale_codes(np.abs(blocks).max(axis=1))             # [rows*4]
+        codes = e2m1_codes(blocks, mx_scale_values(sc)).reshape(-1, D_IDX)
+        packed[r0:r0 + step] = codes[:, 0::2] | (codes[:, 1::2] << 4)
+        scales[r0:r0 + step] = sc.reshape(-1, MX_BLOCKS)
+    return packed, scales
 
 
 def unpack_index_codes(packed):

@@ -15,8 +15,8 @@ from dataclasses import dataclass
 
 import torch
 
-from . import (e4m3_rows, head_weights, main_queries, pooled_main_rows, token_rows_bf16,
-               outlier_channels)
+from . import (e4m3_rows, head_weights, main_queries, normal_rows, pooled_main_rows,
+               token_rows_bf16, outlier_channels)
 
 
 @dataclass(frozen=True)
@@ -76,8 +76,12 @@ def scaled(w, n_tokens, n_cap, name=None):
                     w.first_q - shift, n_cap, w.outliers, w.write_path)
 
 
-def make_inputs(w, device="cuda", seed=0, keep_main_bf16=False, B=None):
+def make_inputs(w, device="cuda", seed=0, keep_main_bf16=False, B=None, index_k="fp8"):
     """Device tensors for workload `w` (optionally with fewer sequences B).
+
+    index_k="fp4" draws the indexer keys as bf16 rows of the same N(0,1) draws
+    (k_bf16 [B, n_cap, 128]; k_idx is None) for the FP4 indexer-key format; the
+    caller quantises them.
 
     Returns a dict with: k_idx, main_bf16 (only if keep_main_bf16; else None),
     q_idx / w (per index-producing layer), q / swa (per layer), q_pos, swa_pos0,
@@ -86,8 +90,13 @@ def make_inputs(w, device="cuda", seed=0, keep_main_bf16=False, B=None):
     n_cap, T, L = w.n_cap, w.T, w.n_layers
     out = {"workload": w, "B": B}
     ok = w.outliers
-    out["k_idx"] = e4m3_rows(B * n_cap, 128, device, seed, w.name, "k_idx",
-                             outliers=ok).view(B, n_cap, 128)
+    if index_k == "fp4":
+        out["k_idx"] = None
+        out["k_bf16"] = normal_rows(B * n_cap, 128, device, seed, w.name, "k_idx",
+                                    outliers=ok).to(torch.bfloat16).view(B, n_cap, 128)
+    else:
+        out["k_idx"] = e4m3_rows(B * n_cap, 128, device, seed, w.name, "k_idx",
+                                 outliers=ok).view(B, n_cap, 128)
     main = []
     for b in range(B):
         main.append(pooled_main_rows(n_cap, w.m, device, seed, w.name, "main", b, outliers=ok))

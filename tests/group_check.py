@@ -11,6 +11,7 @@ import numpy as np
 
 from oracle import group as OG
 from oracle import indexer as OI
+from oracle import mxfp4 as OM
 from oracle.compress import n_visible
 from tests.helpers import NEAR_TIE, assert_attn_close, assert_topk_near, to_np
 
@@ -20,7 +21,8 @@ def check_queries(w, inp, g, samples, cache_of, log=print):
 
     w: the workload; inp: its device inputs; g: the LayerGroup after a step;
     cache_of(b): an object whose [sel] gives the oracle's packed rows of
-    sequence b. Returns (attention outputs checked, near-tie swaps)."""
+    sequence b. With FP4 indexer keys (inp["k_bf16"]) the oracle quantises the
+    bf16 keys itself. Returns (attention outputs checked, near-tie swaps)."""
     sched = OG.layer_schedule(w.kind)
     n_checked = n_swaps = 0
     idx_host = [to_np(x) for x in g.idx]
@@ -30,7 +32,10 @@ def check_queries(w, inp, g, samples, cache_of, log=print):
     for b, t in samples:
         by_seq.setdefault(b, []).append(t)
     for b, ts in sorted(by_seq.items()):
-        kn = to_np(inp["k_idx"][b])
+        if inp.get("k_bf16") is not None:
+            kn, ks = OM.quantize_index_keys(inp["k_bf16"][b].float().cpu().numpy())
+        else:
+            kn, ks = to_np(inp["k_idx"][b]), None
         oc = cache_of(b)
         for t in ts:
             tq = w.q_positions[t]
@@ -40,7 +45,7 @@ def check_queries(w, inp, g, samples, cache_of, log=print):
             q = {li: inp["q"][li][b, t].float().cpu().numpy() for li in range(len(sched))}
             swa = {li: to_np(inp["swa"][li][b]) for li in range(len(sched))}
             o_idx, o_out, o_pool, o_scores = OG.run_group(sched, qi, wi, q, swa, kn, oc, nv, tq,
-                                                          w.swa_pos0)
+                                                          w.swa_pos0, k_scales=ks)
             pool_diff = set()
             if pool_host is not None:
                 pg = pool_host[b, t]
@@ -65,7 +70,7 @@ def check_queries(w, inp, g, samples, cache_of, log=print):
                         # oracle score of any visible position, computed only
                         # when the sets differ
                         if "s" not in full:
-                            full["s"] = OI.index_scores(qi[li], wi[li], kn, nv)
+                            full["s"] = OI.index_scores(qi[li], wi[li], kn, nv, k_scales=ks)
                         return full["s"][p]
 
                     n_swaps += assert_topk_near(gi, o_idx[li], score,

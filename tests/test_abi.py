@@ -28,16 +28,16 @@ FAKE_MIS = 0x10004      # misaligned placeholder
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(csa2_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(csa2_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_header_functions_are_exported():
     names = declared_functions()
-    assert len(names) == 9, names
+    assert len(names) == 11, names
     L = C.lib()
     for n in names:
         assert hasattr(L, n), n
-    assert C.csa2_abi_version() == 2
+    assert C.csa2_abi_version() == 3
 
 
 def test_status_strings():
@@ -139,3 +139,31 @@ def test_attn_and_quantize_reject_bad_arguments():
     assert q(None, _p(FAKE), None, 4, _p(FAKE), 10, None) == C.CSA2_EINVAL
     assert q(_p(FAKE), _p(FAKE), _p(FAKE_MIS), 4, _p(FAKE), 10, None) == C.CSA2_EINVAL
     assert q(_p(FAKE), _p(FAKE), None, 0, _p(FAKE), 10, None) == C.CSA2_OK           # nothing to do
+
+
+def test_fp4_key_calls_reject_bad_arguments():
+    q = C.lib().csa2_quantize_index_k
+    F, M = _p(FAKE), _p(FAKE_MIS)
+    assert q(F, None, -1, F, F, 10, None) == C.CSA2_EINVAL
+    assert q(F, None, 11, F, F, 10, None) == C.CSA2_EINVAL      # rows beyond the buffers
+    assert q(F, None, 4, F, F, 0, None) == C.CSA2_EINVAL
+    assert q(None, None, 4, F, F, 10, None) == C.CSA2_EINVAL
+    assert q(F, None, 4, F, M, 10, None) == C.CSA2_EINVAL
+    assert q(F, M, 4, F, F, 10, None) == C.CSA2_EINVAL
+    assert q(F, None, 0, F, F, 10, None) == C.CSA2_OK            # nothing to do
+    f = C.lib().csa2_index_score_fp4k
+
+    def call(mode=0, B=1, T=1, n_cap=100, **kw):
+        a = dict(q=FAKE, w=FAKE, k=FAKE, ks=FAKE, nv=FAKE, pool=FAKE, s=FAKE, bm=None)
+        a.update(kw)
+        return f(mode, _p(a["q"]), _p(a["w"]), _p(a["k"]), _p(a["ks"]), _p(a["nv"]),
+                 _p(a["pool"]), B, T, n_cap, _p(a["s"]), _p(a["bm"]), None)
+
+    assert call(mode=2) == C.CSA2_EINVAL
+    assert call(ks=0) == C.CSA2_EINVAL                          # scales are required
+    assert call(ks=FAKE_MIS) == C.CSA2_EINVAL
+    assert call(mode=1, pool=0) == C.CSA2_EINVAL
+    assert call(mode=1, bm=FAKE) == C.CSA2_EINVAL
+    assert call(s=0) == C.CSA2_EINVAL
+    assert call(n_cap=0) == C.CSA2_EINVAL
+    assert call(B=300, T=300) == C.CSA2_EINVAL
