@@ -30,11 +30,13 @@ constexpr int kWaves = 4;          // waves per work-group of the decode scan
 // Tiles per wave: 8 for the Full scan (long rows, many work-groups anyway);
 // 2 inside the pool, where each query has only 16,384 candidates and more,
 // shorter work-groups spread a Reindex scan over more of the chip.
-template <int MODE>
+template <int MODE, int KF>
 constexpr int tiles_per_wave() { return MODE == 0 ? 8 : 2; }
-template <int MODE>
-constexpr int items_per_wg() { return kTilePos * tiles_per_wave<MODE>() * kWaves; }
-constexpr int kPrefetch = 3;       // tiles in registers per wave (one scored, the rest in flight)
+template <int MODE, int KF>
+constexpr int items_per_wg() { return kTilePos * tiles_per_wave<MODE, KF>() * kWaves; }
+// Tiles in registers per wave (one scored, the rest in flight).
+template <int KF>
+constexpr int prefetch_tiles() { return 3; }
 
 // Row (head) of accumulator register r in lane `lane` of a 32x32 MFMA result.
 __device__ __forceinline__ int acc32_row(int lane, int r) {
@@ -182,8 +184,9 @@ __global__ __launch_bounds__(256) void k_index_score_decode(
   float* srow = scores ? scores + (size_t)qi * (size_t)n_items : nullptr;
   float* brow = bmax ? bmax + (size_t)qi * (size_t)n_blk : nullptr;
 
-  constexpr int kTilesPerWave = tiles_per_wave<MODE>();
-  const int64_t wave_base = (int64_t)blockIdx.x * items_per_wg<MODE>() +
+  constexpr int kTilesPerWave = tiles_per_wave<MODE, KF>();
+  constexpr int kPrefetch = prefetch_tiles<KF>();
+  const int64_t wave_base = (int64_t)blockIdx.x * items_per_wg<MODE, KF>() +
                             (int64_t)wave * kTilePos * kTilesPerWave;
 
   // Reindex: the pool entries of all of this wave's tiles are fetched first, so
@@ -216,8 +219,9 @@ __global__ __launch_bounds__(256) void k_index_score_decode(
     else
       load_tile(t, kbase + pos * kKeyBytes, ok);
   };
+  // (never beyond this wave's own tiles: blk[] holds kTilesPerWave entries)
 #pragma unroll
-  for (int i = 0; i < kPrefetch - 1; ++i) {
+  for (int i = 0; i < kPrefetch - 1 && i < kTilesPerWave; ++i) {
     const int64_t pos = position_of(i, okb[i]);
     load(buf[i], pos, okb[i]);
   }
@@ -513,7 +517,7 @@ hipError_t launch_index_score_decode(int mode, const uint8_t* q_idx, const float
                                      float* scores, float* bmax, hipStream_t st) {
   const int Q = B * T;
   const int64_t n_items = mode == 0 ? n_cap : (int64_t)kPoolCand;
-  const int64_t per_wg = mode == 0 ? items_per_wg<0>() : items_per_wg<1>();
+  const int64_t per_wg = mode == 0 ? items_per_wg<0, 0>() : items_per_wg<1, 0>();
   const int64_t gx = (n_items + per_wg - 1) / per_wg;
   const dim3 grid((unsigned)gx, (unsigned)Q);
   if (mode == 0) {
@@ -533,7 +537,7 @@ hipError_t launch_index_score_decode_fp4k(int mode, const uint8_t* q_idx, const 
                                           hipStream_t st) {
   const int Q = B * T;
   const int64_t n_items = mode == 0 ? n_cap : (int64_t)kPoolCand;
-  const int64_t per_wg = mode == 0 ? items_per_wg<0>() : items_per_wg<1>();
+  const int64_t per_wg = mode == 0 ? items_per_wg<0, 1>() : items_per_wg<1, 1>();
   const int64_t gx = (n_items + per_wg - 1) / per_wg;
   const dim3 grid((unsigned)gx, (unsigned)Q);
   if (mode == 0) {
