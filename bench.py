@@ -95,19 +95,19 @@ def source_sha(path):
 
 
 def read_traffic(n_launch_bytes):
-    """HBM traffic per scan launch from the committed rocprofv3 counter summary,
-    or None if missing, taken on another version of the kernel or on another
-    workload (another number of algorithmic bytes per launch)."""
+    """HBM traffic per scan launch from the committed rocprofv3 counter summary
+    (one entry per key format), or None if no entry was taken on this version of
+    the kernel source with this many algorithmic bytes per launch."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    if t.get("source_sha") != source_sha(SCAN_SOURCE):
-        return None
-    if t.get("algorithmic_bytes_per_launch") != n_launch_bytes:
-        return None
-    return t.get("traffic_bytes_per_launch")
+    sha = source_sha(SCAN_SOURCE)
+    for e in t.get("entries", []):
+        if e.get("source_sha") == sha and e.get("algorithmic_bytes_per_launch") == n_launch_bytes:
+            return e.get("traffic_bytes_per_launch")
+    return None
 
 
 def cpu_baseline(w, inp, seed, new_rows, budget_s=10.0, index_k="fp8"):
@@ -336,7 +336,8 @@ def main():
         achieved = scan_bytes / (scan_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "traffic": read_traffic(scan_bytes), "kernel": SCAN_KERNEL,
+                "traffic": read_traffic(scan_bytes),
+                "kernel": "%s<0, %d>" % (SCAN_KERNEL, 1 if args.index_k == "fp4" else 0),
                 "kernel_ms": round(scan_ms, 4), "algorithmic_bytes_per_launch": scan_bytes}
         step_bytes = step_algorithmic_bytes(w, n_vis_total, args.index_k)
         step_roof = {"algorithmic_bytes": step_bytes,
