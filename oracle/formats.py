@@ -58,6 +58,24 @@ def e4m3_decode(codes):
     return _E4M3_TABLE[np.asarray(codes, dtype=np.uint8)]
 
 
+def e4m3_encode(x):
+    """OCP E4M3FN codes of float values: the finite E4M3 value nearest to x, ties
+    to the even code (mantissa LSB 0), saturating at +-448 (values beyond 448
+    take the largest finite code, as in the "satfinite" conversion of the OCP
+    8-bit floating point specification); the sign bit is x's sign bit (-0 ->
+    0x80). Finite inputs only. Used for the window rows and FP8 indexer keys
+    that the write path appends."""
+    x = np.asarray(x, dtype=np.float64)
+    shape = x.shape
+    # magnitudes above 480 are nearest to 448 as well; capping them keeps every
+    # distance below exact in float64 (a huge |x| would swamp the differences)
+    a = np.minimum(np.abs(x), 480.0).reshape(-1, 1)
+    dist = np.abs(_SCALE_VALUES[None, :] - a)                  # codes 0..126, exact
+    mag = _SCALE_CODES[_nearest_even(dist, _SCALE_CODES[None, :])]
+    sign = np.signbit(x).reshape(-1).astype(np.int64) << 7
+    return (mag | sign).astype(np.uint8).reshape(shape)
+
+
 def e2m1_decode(codes):
     """Vectorised E2M1 decode: bit 3 is the sign, bits 0..2 index E2M1_GRID."""
     codes = np.asarray(codes, dtype=np.uint8)

@@ -200,3 +200,37 @@ def test_quantize_is_nearest_over_whole_rows(seed):
     cand = F.E2M1_GRID[None, None, :] * s[:, :, None]
     best = np.abs(cand - np.abs(y.astype(np.float64))[:, :, None]).min(axis=2)
     assert np.array_equal(np.abs(np.abs(deq) - np.abs(y)), best)
+
+
+# ---- E4M3 encoding (window rows and FP8 indexer keys appended by the write path)
+
+def test_e4m3_encode_round_trips_every_finite_code():
+    codes = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], dtype=np.uint8)
+    assert np.array_equal(F.e4m3_encode(F.e4m3_decode(codes)), codes)
+
+
+def test_e4m3_encode_midpoints_ties_to_even_and_saturation():
+    for c in range(0, 126):
+        lo, hi = F.e4m3_value_of_code(c), F.e4m3_value_of_code(c + 1)
+        mid = (lo + hi) / 2.0                      # exact: at most 5 significant bits
+        want = c if c % 2 == 0 else c + 1
+        assert int(F.e4m3_encode(np.float32(mid))) == want, c
+        assert int(F.e4m3_encode(np.float32(-mid))) == want | 0x80, c
+        assert int(F.e4m3_encode(np.nextafter(np.float32(mid), np.float32(0)))) == c
+        assert int(F.e4m3_encode(np.nextafter(np.float32(mid), np.float32(1e9)))) == c + 1
+    for big in (448.5, 463.0, 464.0, 480.0, 1e6, 3e38):
+        assert int(F.e4m3_encode(np.float32(big))) == 0x7E
+        assert int(F.e4m3_encode(np.float32(-big))) == 0xFE
+    assert int(F.e4m3_encode(np.float32(-0.0))) == 0x80
+
+
+def test_e4m3_encode_matches_torch_float8_after_clamping():
+    """torch's float8_e4m3fn cast rounds to nearest even but gives NaN beyond the
+    range, so on values clamped to +-448 it must agree with the oracle."""
+    import torch
+    rng = np.random.default_rng(12)
+    x = np.concatenate([rng.standard_normal(20000) * 10.0 ** rng.uniform(-4, 3, 20000),
+                        rng.standard_normal(2000) * 600.0]).astype(np.float32)
+    x = torch.from_numpy(x).to(torch.bfloat16).float().numpy()     # bf16 values, as appended
+    t = torch.from_numpy(x).clamp(-448.0, 448.0).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(F.e4m3_encode(x), t)
