@@ -56,6 +56,12 @@ def parse():
     p.add_argument("--index-k", default="fp8", choices=["fp8", "fp4"],
                    help="indexer-key format: FP8 E4M3 (the workloads' format) or FP4 "
                         "E2M1 with one E8M0 scale per 32 channels (decode workloads)")
+    p.add_argument("--write-path", default="main", choices=["main", "full"],
+                   help="per-step write path of the decode workloads: 'main' packs one "
+                        "already-compressed main-KV row per sequence (the workloads' "
+                        "definition); 'full' also compresses each sequence's newest m "
+                        "tokens on the device, appends the compressed indexer key and "
+                        "appends the new token's window row in every layer")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--graph", dest="graph", action="store_true", default=True,
                    help="replay each step segment as a HIP graph (default)")
@@ -110,7 +116,7 @@ def read_traffic(n_launch_bytes):
     return None
 
 
-def cpu_baseline(w, inp, seed, new_rows, budget_s=10.0, index_k="fp8"):
+def cpu_baseline(w, inp, seed, new_rows, budget_s=10.0, index_k="fp8", oracle_rows=None):
     """The oracle, single-threaded, on whole queries through the whole group
     (write-path row included), one sequence after another until about
     `budget_s` seconds of oracle time have accumulated (at least one query).
@@ -150,12 +156,22 @@ def cpu_baseline(w, inp, seed, new_rows, budget_s=10.0, index_k="fp8"):
                 # the oracle quantises the bf16 keys itself (staging, not timed)
                 kn, ks = OM.quantize_index_keys(inp["k_bf16"][b].float().cpu().numpy())
             else:
-                kn, ks = inp["k_idx"][b].cpu().numpy(), None
+                kn, ks = inp["k_idx"][b].cpu().numpy().copy(), None
+            if oracle_rows is not None:
+                # the full write path's appended key, as the oracle computes it
+                if index_k == "fp4":
+                    kn[n_cap - 1], ks[n_cap - 1] = oracle_rows["k"][0][b], oracle_rows["k"][1][b]
+                else:
+                    kn[n_cap - 1] = oracle_rows["k"][b]
             for t in range(w.T):
                 qi = {li: inp["q_idx"][li][b, t].cpu().numpy() for li in inp["q_idx"]}
                 wi = {li: inp["w"][li][b, t].cpu().numpy() for li in inp["w"]}
                 q = {li: inp["q"][li][b, t].float().cpu().numpy() for li in range(len(sched))}
                 swa = {li: inp["swa"][li][b].cpu().numpy() for li in range(len(sched))}
+                if oracle_rows is not None:
+                    for li in range(len(sched)):
+                        swa[li] = swa[li].copy()
+                        swa[li][-1] = oracle_rows["win"][li][b]
                 tq = w.q_positions[t]
                 nv = int(n_visible(tq, m))
                 t0 = time.perf_counter()
@@ -229,6 +245,36 @@ def main():
         cs_new = torch.from_numpy(C.csa2_rope_table(np.full(B, (n_cap - 1) * m,
                                                             dtype=np.int64))).to(dev)
         write = (new_rows, cs_new, slot)
+    full_write = None
+    if args.write_path == "full" and not prefill:
+        import synth
+        from oracle import compress as OCm            # the oracle's rows for cpu_baseline only
+        from oracle import formats as OFm
+        from oracle import mxfp4 as OMm
+        # the newest group of m tokens of every sequence (main latent and indexer key),
+        # the new token's window row per layer; the compressed entry replaces new_rows
+        tok_main = synth.token_rows_bf16(B * m, dev, seed, w.name, "write_tok", outliers=w.outliers)
+        tok_k = synth.normal_rows(B * m, 128, dev, seed, w.name, "write_k",
+                                  outliers=w.outliers).to(torch.bfloat16)
+        win = [synth.normal_rows(B, 512, dev, seed, w.name, "write_win", li,
+                                 outliers=w.outliers).to(torch.bfloat16) for li in range(w.n_layers)]
+        entry = torch.empty((B, 512), dtype=torch.bfloat16, device=dev)
+        kentry = torch.empty((B, 128), dtype=torch.bfloat16, device=dev)
+        wslot = torch.arange(B, dtype=torch.int64, device=dev) * w.S + (w.S - 1)
+        full_write = (tok_main, tok_k, win, entry, kentry, wslot)
+        write = (entry, cs_new, slot)
+
+        def _bits(t):
+            return t.view(torch.int16).cpu().numpy().view(np.uint16)
+        # oracle-side rows for the cpu_baseline: compressed entry, appended key, window rows
+        new_rows = torch.from_numpy(OCm.bf16_bits_to_f32(OCm.compress_mean(_bits(tok_main), m))).to(
+            torch.bfloat16).to(dev)
+        k_new = OCm.bf16_bits_to_f32(OCm.compress_mean(_bits(tok_k), m))
+        oracle_rows = {"k": (OMm.quantize_index_keys(k_new) if args.index_k == "fp4"
+                             else OFm.e4m3_encode(k_new)),
+                       "win": [OFm.e4m3_encode(x.float().cpu().numpy()) for x in win]}
+    else:
+        oracle_rows = None
 
     n_vis = visible_entries(inp["q_pos"], m).to(torch.int32)
     n_vis_total = int(n_vis.sum().item())
@@ -239,6 +285,16 @@ def main():
                  inp["w"], inp["q"], inp["swa"])
 
     def seg_write():
+        if full_write is not None:
+            tok_main, tok_k, win, entry, kentry, wslot = full_write
+            C.csa2_compress_tokens(tok_main, m, entry)
+            C.csa2_compress_tokens(tok_k, m, kentry)
+            if args.index_k == "fp4":
+                C.csa2_quantize_index_k(kentry, slot, keys[0], keys[1])
+            else:
+                C.csa2_quantize_e4m3(kentry, slot, keys)
+            for li in range(w.n_layers):
+                C.csa2_quantize_e4m3(win[li], wslot, inp["swa"][li])
         if write is not None:
             g.write(cache, write)
 
@@ -365,6 +421,9 @@ def main():
             "c3": "Full-mode prefill of 4,096 queries after 262,144 tokens (m=2, 131,072-133,120 visible entries)"}[w.name]),
             "batch": B, "queries_per_seq": T, "n_cap": n_cap, "layers": len(g.sched),
             "topk": 512, "window": 128,
+            "write_path": {"main": "one compressed main-KV row per sequence (RoPE + FP4)",
+                           "full": "m tokens compressed on device, main row RoPE + FP4, indexer "
+                                   "key appended, window row appended in every layer"}[args.write_path],
             "index_k": {"fp8": "FP8 E4M3 indexer keys (128 B)",
                         "fp4": "FP4 E2M1 indexer keys + E8M0 per 32 channels (68 B)"}[args.index_k],
             "timing": ("one HIP graph per step; scan timed over back-to-back launches"
@@ -374,7 +433,8 @@ def main():
     }
     log("timed %d steps: %.3f ms/step; running the oracle sample" % (args.steps, ms))
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(w, inp, seed, new_rows, index_k=args.index_k)
+        res["cpu_baseline"] = cpu_baseline(w, inp, seed, new_rows, index_k=args.index_k,
+                                           oracle_rows=oracle_rows)
     else:
         res["cpu_baseline"] = None
     print(json.dumps(res), flush=True)

@@ -18,6 +18,7 @@ __all__ = [
     "csa2_abi_version", "csa2_status_string", "csa2_workspace_bytes", "csa2_rope_table",
     "csa2_quantize_kv", "csa2_index_score", "csa2_build_pool", "csa2_topk",
     "csa2_sparse_attn", "csa2_quantize_index_k", "csa2_index_score_fp4k",
+    "csa2_compress_tokens", "csa2_quantize_e4m3",
 ]
 
 CSA2_FULL, CSA2_REINDEX, CSA2_REUSE = 0, 1, 2
@@ -44,6 +45,8 @@ _SIGS = {
     "csa2_rope_table": (_i32, [_vp, _i64, _vp]),
     "csa2_quantize_kv": (_i32, [_vp, _vp, _vp, _i64, _vp, _i64, _vp]),
     "csa2_index_score": (_i32, [_i32, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i64, _vp, _vp, _vp]),
+    "csa2_compress_tokens": (_i32, [_vp, _i64, _i32, _i32, _vp, _vp]),
+    "csa2_quantize_e4m3": (_i32, [_vp, _i64, _i32, _vp, _vp, _i64, _vp]),
     "csa2_quantize_index_k": (_i32, [_vp, _vp, _i64, _vp, _vp, _i64, _vp]),
     "csa2_index_score_fp4k": (_i32, [_i32, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i64, _vp, _vp,
                                      _vp]),
@@ -172,6 +175,33 @@ def csa2_index_score(mode, q_idx, w, k_idx, n_vis, pool, scores, bmax=None, stre
     _check("csa2_index_score", lib().csa2_index_score(mode, _p(q_idx), _p(w), _p(k_idx),
                                                       _p(n_vis), _p(pool), B, T, n_cap,
                                                       _p(scores), _p(bmax), _stream(stream)))
+
+
+def csa2_compress_tokens(tokens_bf16, m, out_bf16, stream=None):
+    """tokens_bf16 [n_tok, width] bf16 -> out_bf16 [ceil(n_tok/m), width] bf16
+    (mean of every m consecutive rows)."""
+    import torch
+    n_tok, width = tokens_bf16.shape
+    _expect(tokens_bf16, "tokens_bf16", torch.bfloat16, (n_tok, width))
+    _expect(out_bf16, "out_bf16", torch.bfloat16, ((n_tok + m - 1) // m, width))
+    _check("csa2_compress_tokens", lib().csa2_compress_tokens(_p(tokens_bf16), n_tok, width, m,
+                                                              _p(out_bf16), _stream(stream)))
+
+
+def csa2_quantize_e4m3(rows_bf16, dst_slot, out, stream=None):
+    """rows_bf16 [n, width] bf16 -> E4M3 codes in out [rows, width] uint8 (any
+    leading dims of out flattened) at dst_slot [n] int64 (None: row r -> r)."""
+    import torch
+    n, width = rows_bf16.shape
+    _expect(rows_bf16, "rows_bf16", torch.bfloat16, (n, width))
+    if dst_slot is not None:
+        _expect(dst_slot, "dst_slot", torch.int64, (n,))
+    _expect(out, "out", torch.uint8)
+    if out.shape[-1] != width:
+        raise ValueError("out rows must be %d wide" % width)
+    _check("csa2_quantize_e4m3", lib().csa2_quantize_e4m3(_p(rows_bf16), n, width, _p(dst_slot),
+                                                          _p(out), out.numel() // width,
+                                                          _stream(stream)))
 
 
 def csa2_quantize_index_k(k_bf16, dst_slot, codes, scales, stream=None):

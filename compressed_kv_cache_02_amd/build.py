@@ -19,7 +19,8 @@ OUT_DIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libcsa2.so")
 
 ARCH = "gfx950"
-HIP_SOURCES = ["quantize_kv.hip", "index_score.hip", "select.hip", "sparse_attn.hip"]
+HIP_SOURCES = ["quantize_kv.hip", "write_path.hip", "index_score.hip", "select.hip",
+               "sparse_attn.hip"]
 HOST_SOURCES = ["csa2_api.cpp"]
 COMMON = ["-O3", "-fPIC", "-std=c++17", "-I", CSRC, "-I", INCLUDE, "-Wall",
           "-Wno-unused-function"]

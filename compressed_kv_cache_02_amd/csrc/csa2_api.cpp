@@ -109,6 +109,27 @@ int csa2_index_score(int mode, const uint8_t* q_idx, const float* w, const uint8
   return status_of(e);
 }
 
+int csa2_compress_tokens(const void* tokens_bf16, int64_t n_tok, int width, int m,
+                         void* out_bf16, void* stream) {
+  if (n_tok < 0 || m < 1 || m > CSA2_MAX_M || width < 8 || width > CSA2_MAX_WIDTH || width % 8)
+    return CSA2_EINVAL;
+  if (n_tok == 0) return CSA2_OK;
+  if (!aligned16(tokens_bf16) || !aligned16(out_bf16)) return CSA2_EINVAL;
+  return status_of(csa2::launch_compress_rows(static_cast<const uint16_t*>(tokens_bf16), n_tok,
+                                              width, m, static_cast<uint16_t*>(out_bf16),
+                                              as_stream(stream)));
+}
+
+int csa2_quantize_e4m3(const void* rows_bf16, int64_t n, int width, const int64_t* dst_slot,
+                       uint8_t* out, int64_t rows, void* stream) {
+  if (n < 0 || rows < 1 || width < 8 || width > CSA2_MAX_WIDTH || width % 8) return CSA2_EINVAL;
+  if (n == 0) return CSA2_OK;
+  if (!aligned16(rows_bf16) || !aligned16(out) || !opt_aligned16(dst_slot)) return CSA2_EINVAL;
+  if (!dst_slot && n > rows) return CSA2_EINVAL;
+  return status_of(csa2::launch_quantize_e4m3(static_cast<const uint16_t*>(rows_bf16), n, width,
+                                              dst_slot, out, rows, as_stream(stream)));
+}
+
 int csa2_quantize_index_k(const void* k_bf16, const int64_t* dst_slot, int64_t n,
                           uint8_t* codes, uint8_t* scales, int64_t rows, void* stream) {
   if (n < 0 || rows < 1) return CSA2_EINVAL;

@@ -11,6 +11,13 @@ namespace csa2 {
 hipError_t launch_quantize_kv(const uint16_t* kv, const float* cos_sin, const int64_t* slot,
                               int64_t n, uint8_t* cache, int64_t cache_rows, hipStream_t st);
 
+// Write path around the FP4 packer: m-token mean compressor (bf16 -> bf16) and
+// E4M3 append of bf16 rows (window rows, FP8 indexer keys).
+hipError_t launch_compress_rows(const uint16_t* tok, int64_t n_tok, int width, int m,
+                                uint16_t* out, hipStream_t st);
+hipError_t launch_quantize_e4m3(const uint16_t* x, int64_t n, int width, const int64_t* slot,
+                                uint8_t* out, int64_t rows, hipStream_t st);
+
 // FP4 indexer keys (E2M1 codes [rows][64] + E8M0 scales [rows][4]) from bf16 keys.
 hipError_t launch_quantize_index_k(const uint16_t* k, const int64_t* slot, int64_t n,
                                    uint8_t* codes, uint8_t* scales, int64_t rows, hipStream_t st);

@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define CSA2_ABI_VERSION 3
+#define CSA2_ABI_VERSION 4
 
 #define CSA2_IDX_HEADS 32
 #define CSA2_IDX_DIM 128
@@ -56,6 +56,8 @@ extern "C" {
 #define CSA2_POOL_CAND 16384
 #define CSA2_WINDOW 128
 #define CSA2_ROPE_PAIRS 32      /* RoPE on channels 448..511, adjacent pairs */
+#define CSA2_MAX_M 64                /* largest compression ratio csa2_compress_tokens accepts */
+#define CSA2_MAX_WIDTH 8192          /* widest row of the write-path helpers */
 #define CSA2_IDX_FP4_CODE_BYTES 64   /* FP4 indexer key: 128 E2M1 codes ... */
 #define CSA2_IDX_FP4_SCALES 4        /* ... and one E8M0 scale per 32 channels */
 
@@ -136,6 +138,36 @@ int csa2_quantize_kv(const void* kv_bf16, const float* cos_sin, const int64_t* d
 int csa2_index_score(int mode, const uint8_t* q_idx, const float* w, const uint8_t* k_idx,
                      const int32_t* n_vis, const int32_t* pool, int B, int T, int64_t n_cap,
                      float* scores, float* bmax, void* stream);
+
+/* DEVICE. Sequence compressor of the write path: every m tokens become one
+ * compressed entry ([P1] §二 layer layout: m = 2 in encoder groups, 1 in decoder
+ * groups; [P2] 黑科技之二). The learned compressor of the real model is not on the
+ * pages; this library takes the mean the workloads fix:
+ *   out[j][c] = bf16( (sum_{r = jm .. min(jm+m, n_tok)-1} tokens[r][c]) / count ),
+ * summed in float32 in token order, divided with a correctly rounded float32
+ * division, rounded to bf16 nearest-even. A trailing partial group is the mean of
+ * the rows present (a decode step re-compresses the open group when its second
+ * token arrives; only complete entries are visible to queries).
+ *   tokens_bf16 [n_tok][width] (device), out_bf16 [ceil(n_tok/m)][width] (device,
+ *   written), width a multiple of 8 up to CSA2_MAX_WIDTH, 1 <= m <= CSA2_MAX_M.
+ * Rows of several sequences compress in one call when each contributes a whole
+ * number of groups. Inputs must be finite.
+ * Errors: CSA2_EINVAL for NULL/misaligned pointers or bad sizes. */
+int csa2_compress_tokens(const void* tokens_bf16, int64_t n_tok, int width, int m,
+                         void* out_bf16, void* stream);
+
+/* DEVICE. E4M3 append of the write path: the sliding-window KV stays FP8 ([P1]
+ * §三; [P3] 第三刀) and every layer keeps its own window ([P2] 黑科技之二); FP8
+ * indexer keys are E4M3 as in every workload.
+ *   rows_bf16 [n][width] (device); dst_slot [n] int64 destination row (device) or
+ *   NULL for row r -> row r, slots outside [0, rows) skipped; out [rows][width]
+ *   E4M3 codes (device, written); width a multiple of 8 up to CSA2_MAX_WIDTH.
+ * Each value becomes the nearest E4M3 (OCP E4M3FN) value, ties to the even code,
+ * saturating at +-448, sign bit kept. Inputs must be finite.
+ * Errors: CSA2_EINVAL for NULL/misaligned pointers, bad sizes, n > rows without
+ * slots. */
+int csa2_quantize_e4m3(const void* rows_bf16, int64_t n, int width, const int64_t* dst_slot,
+                       uint8_t* out, int64_t rows, void* stream);
 
 /* DEVICE. FP4 indexer keys. An earlier model generation already trained the
  * indexer's keys in FP4 ([P2] 黑科技之三) and the pages' FP4 belongs to the MXFP4

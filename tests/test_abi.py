@@ -33,11 +33,11 @@ def declared_functions():
 
 def test_header_functions_are_exported():
     names = declared_functions()
-    assert len(names) == 11, names
+    assert len(names) == 13, names
     L = C.lib()
     for n in names:
         assert hasattr(L, n), n
-    assert C.csa2_abi_version() == 3
+    assert C.csa2_abi_version() == 4
 
 
 def test_status_strings():
@@ -167,3 +167,23 @@ def test_fp4_key_calls_reject_bad_arguments():
     assert call(s=0) == C.CSA2_EINVAL
     assert call(n_cap=0) == C.CSA2_EINVAL
     assert call(B=300, T=300) == C.CSA2_EINVAL
+
+
+def test_write_path_helpers_reject_bad_arguments():
+    F, M = _p(FAKE), _p(FAKE_MIS)
+    c = C.lib().csa2_compress_tokens
+    assert c(F, 4, 512, 0, F, None) == C.CSA2_EINVAL             # m < 1
+    assert c(F, 4, 512, 65, F, None) == C.CSA2_EINVAL            # m beyond the limit
+    assert c(F, 4, 500, 2, F, None) == C.CSA2_EINVAL             # width not a multiple of 8
+    assert c(F, 4, 16384, 2, F, None) == C.CSA2_EINVAL
+    assert c(F, -1, 512, 2, F, None) == C.CSA2_EINVAL
+    assert c(M, 4, 512, 2, F, None) == C.CSA2_EINVAL
+    assert c(F, 4, 512, 2, None, None) == C.CSA2_EINVAL
+    assert c(F, 0, 512, 2, F, None) == C.CSA2_OK                 # nothing to do
+    q = C.lib().csa2_quantize_e4m3
+    assert q(F, 4, 512, None, F, 3, None) == C.CSA2_EINVAL      # rows beyond the output
+    assert q(F, 4, 12, None, F, 10, None) == C.CSA2_EINVAL
+    assert q(F, 4, 512, M, F, 10, None) == C.CSA2_EINVAL
+    assert q(None, 4, 512, None, F, 10, None) == C.CSA2_EINVAL
+    assert q(F, 4, 512, None, F, 0, None) == C.CSA2_EINVAL
+    assert q(F, 0, 512, None, F, 10, None) == C.CSA2_OK
