@@ -62,6 +62,9 @@ def parse():
                         "definition); 'full' also compresses each sequence's newest m "
                         "tokens on the device, appends the compressed indexer key and "
                         "appends the new token's window row in every layer")
+    p.add_argument("--spec-tokens", type=int, default=1,
+                   help="query tokens per sequence of a decode workload (the last T "
+                        "positions, e.g. speculative decode); 1 = the workload as defined")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--graph", dest="graph", action="store_true", default=True,
                    help="replay each step segment as a HIP graph (default)")
@@ -78,17 +81,19 @@ def key_bytes(index_k):
     return 68 if index_k == "fp4" else 128
 
 
-def scan_algorithmic_bytes(B, T, n_vis_total, index_k="fp8"):
+def scan_algorithmic_bytes(B, T, n_keys, index_k="fp8"):
     """Bytes the Full-mode scan must move per launch: one indexer key per
-    visible position plus each query's 32x128 E4M3 query and 32 float weights."""
-    return key_bytes(index_k) * n_vis_total + (32 * 128 + 32 * 4) * B * T
+    position visible to some query of its sequence (n_keys, summed over the
+    sequences; the query tokens of a sequence share the key reads) plus each
+    query's 32x128 E4M3 query and 32 float weights."""
+    return key_bytes(index_k) * n_keys + (32 * 128 + 32 * 4) * B * T
 
 
-def step_algorithmic_bytes(w, n_vis_total, index_k="fp8"):
+def step_algorithmic_bytes(w, n_keys, index_k="fp8"):
     """Whole-step bytes per the path's definition: scans, attention, write path."""
     q = w.B * w.T
     kb = key_bytes(index_k)
-    full = kb * n_vis_total + (4096 + 128 + 2048) * q
+    full = kb * n_keys + (4096 + 128 + 2048) * q
     reindex = (16384 * kb + 4224 + 8192 + 2048) * q
     attn = 411648 * q
     n_x = {"decoder": 3}.get(w.kind, 0)
@@ -205,6 +210,13 @@ def main():
     from synth.configs import WORKLOADS, make_inputs
 
     w = WORKLOADS[args.workload]
+    if args.spec_tokens > 1:
+        import dataclasses
+        if w.T != 1 or args.spec_tokens >= 64:
+            print("--spec-tokens applies to the decode workloads, below 64", file=sys.stderr)
+            sys.exit(2)
+        w = dataclasses.replace(w, name=w.name, T=args.spec_tokens,
+                                first_q=w.first_q - (args.spec_tokens - 1))
     dev = "cuda"
     torch.cuda.set_device(0)
     seed = 0
@@ -212,7 +224,7 @@ def main():
     inp = make_inputs(w, dev, seed=seed, index_k=args.index_k)
     B, T, n_cap, m = w.B, w.T, w.n_cap, w.m
     if args.index_k == "fp4":
-        if T > 1:
+        if T >= 64:
             print("--index-k fp4 covers the decode workloads (c1, c2, c4)", file=sys.stderr)
             sys.exit(2)
         codes = torch.empty((B, n_cap, 64), dtype=torch.uint8, device=dev)
@@ -232,7 +244,7 @@ def main():
     torch.cuda.empty_cache()
     # per-step write path of a decode step: one new row per sequence into the
     # newest slot (the prefill chunk has none)
-    prefill = T > 1
+    prefill = T >= 64
     if prefill:
         new_rows, write = None, None
     else:
@@ -278,6 +290,9 @@ def main():
 
     n_vis = visible_entries(inp["q_pos"], m).to(torch.int32)
     n_vis_total = int(n_vis.sum().item())
+    # keys visible to some query of each sequence: what a scan that shares the
+    # key reads among a sequence's query tokens must move (decode shapes)
+    n_keys = int(n_vis.max(dim=1).values.sum().item())
     g = LayerGroup(w.kind, B, T, n_cap, device=dev)
     stream = torch.cuda.current_stream()
 
@@ -378,7 +393,7 @@ def main():
 
     ms = el * 1e3 / args.steps
     qps = B * T * args.steps / el
-    scan_bytes = scan_algorithmic_bytes(B, T, n_vis_total, args.index_k)
+    scan_bytes = scan_algorithmic_bytes(B, T, n_keys, args.index_k)
     if prefill:
         # a dense FP8 contraction: 32 heads x 128 channels x 2 FLOP per visible pair
         scan_flop = 8192 * n_vis_total
@@ -395,7 +410,7 @@ def main():
                 "traffic": read_traffic(scan_bytes),
                 "kernel": "%s<0, %d>" % (SCAN_KERNEL, 1 if args.index_k == "fp4" else 0),
                 "kernel_ms": round(scan_ms, 4), "algorithmic_bytes_per_launch": scan_bytes}
-        step_bytes = step_algorithmic_bytes(w, n_vis_total, args.index_k)
+        step_bytes = step_algorithmic_bytes(w, n_keys, args.index_k)
         step_roof = {"algorithmic_bytes": step_bytes,
                      "achieved_GBps": round(step_bytes / (ms * 1e-3) / 1e9, 1),
                      "frac": round(step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
@@ -421,6 +436,7 @@ def main():
             "c3": "Full-mode prefill of 4,096 queries after 262,144 tokens (m=2, 131,072-133,120 visible entries)"}[w.name]),
             "batch": B, "queries_per_seq": T, "n_cap": n_cap, "layers": len(g.sched),
             "topk": 512, "window": 128,
+            "spec_tokens": T if not prefill else None,
             "write_path": {"main": "one compressed main-KV row per sequence (RoPE + FP4)",
                            "full": "m tokens compressed on device, main row RoPE + FP4, indexer "
                                    "key appended, window row appended in every layer"}[args.write_path],

@@ -20,6 +20,8 @@ inline bool aligned16(const void* p) { return p && (reinterpret_cast<uintptr_t>(
 
 inline bool opt_aligned16(const void* p) { return !p || (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+inline bool aligned4(const void* p) { return p && (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
 inline bool sizes_ok(int B, int T, int64_t n_cap) {
   if (B < 1 || T < 1 || n_cap < 1 || n_cap >= (int64_t(1) << 31)) return false;
   if ((int64_t)B * T > 65535) return false;   // one grid row per query
@@ -134,7 +136,7 @@ int csa2_quantize_index_k(const void* k_bf16, const int64_t* dst_slot, int64_t n
                           uint8_t* codes, uint8_t* scales, int64_t rows, void* stream) {
   if (n < 0 || rows < 1) return CSA2_EINVAL;
   if (n == 0) return CSA2_OK;
-  if (!aligned16(k_bf16) || !aligned16(codes) || !aligned16(scales) || !opt_aligned16(dst_slot))
+  if (!aligned16(k_bf16) || !aligned16(codes) || !aligned4(scales) || !opt_aligned16(dst_slot))
     return CSA2_EINVAL;
   if (!dst_slot && n > rows) return CSA2_EINVAL;
   return status_of(csa2::launch_quantize_index_k(static_cast<const uint16_t*>(k_bf16), dst_slot, n,
@@ -146,7 +148,7 @@ int csa2_index_score_fp4k(int mode, const uint8_t* q_idx, const float* w, const 
                           int B, int T, int64_t n_cap, float* scores, float* bmax, void* stream) {
   if (mode != CSA2_FULL && mode != CSA2_REINDEX) return CSA2_EINVAL;
   if (!sizes_ok(B, T, n_cap)) return CSA2_EINVAL;
-  if (!aligned16(q_idx) || !aligned16(w) || !aligned16(k_codes) || !aligned16(k_scales) ||
+  if (!aligned16(q_idx) || !aligned16(w) || !aligned16(k_codes) || !aligned4(k_scales) ||
       !aligned16(n_vis) || !opt_aligned16(scores) || !opt_aligned16(bmax))
     return CSA2_EINVAL;
   if (!scores && (mode != CSA2_FULL || !bmax)) return CSA2_EINVAL;

@@ -140,49 +140,64 @@ __device__ __forceinline__ v8i fp4_operand(const uint4& a) {
   return r;
 }
 
-template <int MODE, int KF>
+// NQ > 1 (Full mode, several query tokens of one sequence, e.g. speculative
+// decode): a wave scores NQ consecutive queries of the sequence against each key
+// tile it loads, so a sequence's keys are read once per NQ queries. Every query
+// runs the same instruction sequence as with NQ = 1 (same bits); each keeps its
+// own visibility limit.
+template <int MODE, int KF, int NQ>
 __global__ __launch_bounds__(256) void k_index_score_decode(
     const uint8_t* __restrict__ q_idx, const float* __restrict__ w,
     const uint8_t* __restrict__ k_idx, const uint8_t* __restrict__ k_scales,
     const int32_t* __restrict__ n_vis,
     const int32_t* __restrict__ pool, int T, int64_t n_cap, int64_t n_items,
     float* __restrict__ scores, float* __restrict__ bmax) {
-  const int qi = blockIdx.y;
-  const int b = qi / T;
+  static_assert(MODE == 0 || NQ == 1, "query groups share keys only in the Full scan");
+  const int groups = (T + NQ - 1) / NQ;           // query groups per sequence
+  const int b = blockIdx.y / groups;
+  const int t0 = (blockIdx.y % groups) * NQ;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int half = lane >> 5;
   const int col = lane & 31;
-  int64_t nv = n_vis[qi];
-  nv = nv < 0 ? 0 : (nv > n_cap ? n_cap : nv);
   const int64_t n_blk = (n_cap + kBlock - 1) / kBlock;
 
-  // A operands: FP8 keys pair a query lane's channels with the key lane's in
-  // the same order (64h..64h+63); FP4 keys need the FP8 x FP4 order above.
-  const uint4* q4 = reinterpret_cast<const uint4*>(q_idx + (size_t)qi * (kIdxHeads * kIdxDim) +
-                                                   col * kIdxDim);
-  const v8i a0 = KF ? as_v8i(q4[half], q4[2 + half]) : as_v8i(q4[4 * half], q4[4 * half + 1]);
-  const v8i a1 = KF ? as_v8i(q4[4 + half], q4[6 + half]) : as_v8i(q4[4 * half + 2], q4[4 * half + 3]);
-  // head weights of this lane's 16 accumulator rows: 4 runs of 4 consecutive heads
-  float wr[16];
-  {
-    const float4* w4 = reinterpret_cast<const float4*>(w + (size_t)qi * kIdxHeads);
+  // per query of the group: index, visibility (0 past T), A operands, weights.
+  // FP8 keys pair a query lane's channels with the key lane's in the same
+  // order (64h..64h+63); FP4 keys need the FP8 x FP4 order above.
+  int qi[NQ];
+  bool real[NQ];
+  int64_t nv[NQ];
+  v8i a0[NQ], a1[NQ];
+  float wr[NQ][16];     // weights of the lane's 16 accumulator rows: 4 runs of 4 heads
+  int64_t nv_max = 0;
+#pragma unroll
+  for (int q = 0; q < NQ; ++q) {
+    real[q] = t0 + q < T;
+    qi[q] = b * T + (real[q] ? t0 + q : T - 1);
+    int64_t v = n_vis[qi[q]];
+    v = v < 0 ? 0 : (v > n_cap ? n_cap : v);
+    nv[q] = real[q] ? v : 0;
+    nv_max = nv[q] > nv_max ? nv[q] : nv_max;
+    const uint4* q4 = reinterpret_cast<const uint4*>(q_idx + (size_t)qi[q] * (kIdxHeads * kIdxDim) +
+                                                     col * kIdxDim);
+    a0[q] = KF ? as_v8i(q4[half], q4[2 + half]) : as_v8i(q4[4 * half], q4[4 * half + 1]);
+    a1[q] = KF ? as_v8i(q4[4 + half], q4[6 + half]) : as_v8i(q4[4 * half + 2], q4[4 * half + 3]);
+    const float4* w4 = reinterpret_cast<const float4*>(w + (size_t)qi[q] * kIdxHeads);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const float4 v = w4[2 * j + half];   // heads 8j + 4*half .. +3
-      wr[4 * j + 0] = v.x;
-      wr[4 * j + 1] = v.y;
-      wr[4 * j + 2] = v.z;
-      wr[4 * j + 3] = v.w;
+      const float4 x = w4[2 * j + half];   // heads 8j + 4*half .. +3
+      wr[q][4 * j + 0] = x.x;
+      wr[q][4 * j + 1] = x.y;
+      wr[q][4 * j + 2] = x.z;
+      wr[q][4 * j + 3] = x.w;
     }
   }
 
   constexpr int kKeyBytes = KF ? kIdxDim / 2 : kIdxDim;
   const uint8_t* kbase = k_idx + (size_t)b * (size_t)n_cap * kKeyBytes + half * (KF ? 16 : 64);
   const uint8_t* sbase = KF ? k_scales + (size_t)b * (size_t)n_cap * 4 : nullptr;
-  const int32_t* pl = MODE == 1 ? pool + (size_t)qi * kPoolBlocks : nullptr;
-  float* srow = scores ? scores + (size_t)qi * (size_t)n_items : nullptr;
-  float* brow = bmax ? bmax + (size_t)qi * (size_t)n_blk : nullptr;
+  const int32_t* pl = MODE == 1 ? pool + (size_t)qi[0] * kPoolBlocks : nullptr;
 
   constexpr int kTilesPerWave = tiles_per_wave<MODE, KF>();
   constexpr int kPrefetch = prefetch_tiles<KF>();
@@ -197,15 +212,16 @@ __global__ __launch_bounds__(256) void k_index_score_decode(
     const int64_t item = wave_base + (int64_t)it * kTilePos + col;
     blk[it] = (MODE == 1 && item < n_items) ? pl[item >> 3] : -1;
   }
+  // A tile is loaded where some query of the group sees the position.
   auto position_of = [&](int it, bool& ok) __attribute__((always_inline)) -> int64_t {
     const int64_t item = wave_base + (int64_t)it * kTilePos + col;
     if (MODE == 0) {
-      ok = item < nv;
+      ok = item < nv_max;
       return ok ? item : 0;
     }
     const int64_t b8 = blk[it];
     const int64_t pos = b8 * kBlock + (item & 7);
-    ok = b8 >= 0 && b8 < n_blk && pos < nv;
+    ok = b8 >= 0 && b8 < n_blk && pos < nv[0];
     return ok ? pos : 0;
   };
 
@@ -237,36 +253,42 @@ __global__ __launch_bounds__(256) void k_index_score_decode(
     }
     const Tile& cur = buf[it % kPrefetch];
     const bool cur_ok = okb[it % kPrefetch];
-    float s = -INFINITY;
-    // Skip the MFMA when no lane of the wave holds a visible position.
-    if (__any(cur_ok)) {
-      v16f acc = {};
-      if constexpr (KF == 1) {
-        // A: E4M3 (format 0) with scale 2^0 (E8M0 127); B: E2M1 (format 4)
-        // with the key's block scales (bytes 0 and 2 of the shifted word,
-        // each taken from byte 0 of the scale register)
-        acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a0, fp4_operand(cur.c[0]), acc, 0, 4,
-                                                              0, 127, 0, (int)cur.sc);
-        acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a1, fp4_operand(cur.c[1]), acc, 0, 4,
-                                                              0, 127, 0, (int)(cur.sc >> 16));
-      } else {
-        acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a0, as_v8i(cur.v[0], cur.v[1]), acc,
-                                                              0, 0, 0, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a1, as_v8i(cur.v[2], cur.v[3]), acc,
-                                                              0, 0, 0, 0, 0, 0);
-      }
-      const float part = weighted_relu_sum(acc, wr);
-      // lo-half + hi-half row sums, in every lane
-      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(part), __float_as_uint(part),
-                                                       false, false);
-      const float tot = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
-      if (cur_ok) s = tot;
-    }
     const int64_t item = tile0 + col;
-    if (srow && half == 0 && item < n_items) srow[item] = s;
-    if (brow) {
-      const float m = max_over_8_lanes(s);
-      if (half == 0 && (col & 7) == 0 && item < n_items) brow[item >> 3] = m;
+    const bool any_ok = __any(cur_ok);   // skip the MFMAs when no lane holds a visible key
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+      float s = -INFINITY;
+      if (any_ok) {
+        v16f acc = {};
+        if constexpr (KF == 1) {
+          // A: E4M3 (format 0) with scale 2^0 (E8M0 127); B: E2M1 (format 4)
+          // with the key's block scales (bytes 0 and 2 of the shifted word,
+          // each taken from byte 0 of the scale register)
+          acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a0[q], fp4_operand(cur.c[0]), acc, 0,
+                                                                4, 0, 127, 0, (int)cur.sc);
+          acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a1[q], fp4_operand(cur.c[1]), acc, 0,
+                                                                4, 0, 127, 0, (int)(cur.sc >> 16));
+        } else {
+          acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a0[q], as_v8i(cur.v[0], cur.v[1]),
+                                                                acc, 0, 0, 0, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a1[q], as_v8i(cur.v[2], cur.v[3]),
+                                                                acc, 0, 0, 0, 0, 0, 0);
+        }
+        const float part = weighted_relu_sum(acc, wr[q]);
+        // lo-half + hi-half row sums, in every lane
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(part),
+                                                         __float_as_uint(part), false, false);
+        const float tot = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+        const bool vis = MODE == 0 ? item < nv[q] : cur_ok;
+        if (cur_ok && vis) s = tot;
+      }
+      if (!real[q]) continue;
+      if (scores && half == 0 && item < n_items) scores[(size_t)qi[q] * (size_t)n_items + item] = s;
+      if (bmax) {
+        const float m = max_over_8_lanes(s);
+        if (half == 0 && (col & 7) == 0 && item < n_items)
+          bmax[(size_t)qi[q] * (size_t)n_blk + (item >> 3)] = m;
+      }
     }
   }
 }
@@ -511,23 +533,37 @@ __global__ __launch_bounds__(kPfThreads) void k_index_score_prefill(
 
 }  // namespace
 
+// Queries per wave of the Full scan: several query tokens of one sequence share
+// each key tile.
+constexpr int kDecodeGroup = 4;
+
+template <int KF>
+hipError_t launch_decode(int mode, const uint8_t* q_idx, const float* w, const uint8_t* keys,
+                         const uint8_t* scales, const int32_t* n_vis, const int32_t* pool, int B,
+                         int T, int64_t n_cap, float* scores, float* bmax, hipStream_t st) {
+  const int64_t n_items = mode == 0 ? n_cap : (int64_t)kPoolCand;
+  const int64_t per_wg = mode == 0 ? items_per_wg<0, KF>() : items_per_wg<1, KF>();
+  const unsigned gx = (unsigned)((n_items + per_wg - 1) / per_wg);
+  if (mode == 1) {
+    hipLaunchKernelGGL((k_index_score_decode<1, KF, 1>), dim3(gx, (unsigned)(B * T)), dim3(256), 0,
+                       st, q_idx, w, keys, scales, n_vis, pool, T, n_cap, n_items, scores, nullptr);
+  } else if (T == 1) {
+    hipLaunchKernelGGL((k_index_score_decode<0, KF, 1>), dim3(gx, (unsigned)B), dim3(256), 0, st,
+                       q_idx, w, keys, scales, n_vis, pool, T, n_cap, n_items, scores, bmax);
+  } else {
+    const unsigned gy = (unsigned)(B * ((T + kDecodeGroup - 1) / kDecodeGroup));
+    hipLaunchKernelGGL((k_index_score_decode<0, KF, kDecodeGroup>), dim3(gx, gy), dim3(256), 0, st,
+                       q_idx, w, keys, scales, n_vis, pool, T, n_cap, n_items, scores, bmax);
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_index_score_decode(int mode, const uint8_t* q_idx, const float* w,
                                      const uint8_t* k_idx, const int32_t* n_vis,
                                      const int32_t* pool, int B, int T, int64_t n_cap,
                                      float* scores, float* bmax, hipStream_t st) {
-  const int Q = B * T;
-  const int64_t n_items = mode == 0 ? n_cap : (int64_t)kPoolCand;
-  const int64_t per_wg = mode == 0 ? items_per_wg<0, 0>() : items_per_wg<1, 0>();
-  const int64_t gx = (n_items + per_wg - 1) / per_wg;
-  const dim3 grid((unsigned)gx, (unsigned)Q);
-  if (mode == 0) {
-    hipLaunchKernelGGL((k_index_score_decode<0, 0>), grid, dim3(256), 0, st, q_idx, w, k_idx,
-                       nullptr, n_vis, pool, T, n_cap, n_items, scores, bmax);
-  } else {
-    hipLaunchKernelGGL((k_index_score_decode<1, 0>), grid, dim3(256), 0, st, q_idx, w, k_idx,
-                       nullptr, n_vis, pool, T, n_cap, n_items, scores, nullptr);
-  }
-  return hipGetLastError();
+  return launch_decode<0>(mode, q_idx, w, k_idx, nullptr, n_vis, pool, B, T, n_cap, scores, bmax,
+                          st);
 }
 
 hipError_t launch_index_score_decode_fp4k(int mode, const uint8_t* q_idx, const float* w,
@@ -535,19 +571,8 @@ hipError_t launch_index_score_decode_fp4k(int mode, const uint8_t* q_idx, const 
                                           const int32_t* n_vis, const int32_t* pool, int B, int T,
                                           int64_t n_cap, float* scores, float* bmax,
                                           hipStream_t st) {
-  const int Q = B * T;
-  const int64_t n_items = mode == 0 ? n_cap : (int64_t)kPoolCand;
-  const int64_t per_wg = mode == 0 ? items_per_wg<0, 1>() : items_per_wg<1, 1>();
-  const int64_t gx = (n_items + per_wg - 1) / per_wg;
-  const dim3 grid((unsigned)gx, (unsigned)Q);
-  if (mode == 0) {
-    hipLaunchKernelGGL((k_index_score_decode<0, 1>), grid, dim3(256), 0, st, q_idx, w, k_codes,
-                       k_scales, n_vis, pool, T, n_cap, n_items, scores, bmax);
-  } else {
-    hipLaunchKernelGGL((k_index_score_decode<1, 1>), grid, dim3(256), 0, st, q_idx, w, k_codes,
-                       k_scales, n_vis, pool, T, n_cap, n_items, scores, nullptr);
-  }
-  return hipGetLastError();
+  return launch_decode<1>(mode, q_idx, w, k_codes, k_scales, n_vis, pool, B, T, n_cap, scores,
+                          bmax, st);
 }
 
 hipError_t launch_index_score_prefill(const uint8_t* q_idx, const float* w, const uint8_t* k_idx,

@@ -132,7 +132,10 @@ int csa2_quantize_kv(const void* kv_bf16, const float* cos_sin, const int64_t* d
  *   n_vis [B][T] int32 (device; values are clamped to [0, n_cap]),
  *   pool  [B][T][2048] int32 (device, REINDEX only; entries >= ceil(n_cap/8) are
  *         treated as -1).
- * Products are exact; sums are float32 (MFMA accumulation order).
+ * Products are exact; sums are float32 (MFMA accumulation order). Every query's
+ * score is the same bits whatever T is: in FULL mode the query tokens of a
+ * sequence (T >= 2, e.g. speculative decode) share each key read, four at a time
+ * below T = 64 and in tiles of 32 from T = 64 on.
  * Errors: CSA2_EINVAL for REUSE, NULL/misaligned pointers, REINDEX without a
  * pool, nothing to write, B < 1, T < 1, n_cap < 1 or n_cap >= 2^31. */
 int csa2_index_score(int mode, const uint8_t* q_idx, const float* w, const uint8_t* k_idx,
@@ -184,6 +187,8 @@ int csa2_quantize_e4m3(const void* rows_bf16, int64_t n, int width, const int64_
  * Each element is the E2M1 code nearest |v| / 2^(scale - 127) (ties to the even
  * code, saturating at 6); its sign bit is the sign bit of v.
  * Errors: CSA2_EINVAL for NULL/misaligned pointers, n < 0, rows < 1. */
+/* (`scales` needs only 4-byte alignment, so one sequence's slice of a [B][n_cap][4]
+ * buffer can be passed.) */
 int csa2_quantize_index_k(const void* k_bf16, const int64_t* dst_slot, int64_t n,
                           uint8_t* codes, uint8_t* scales, int64_t rows, void* stream);
 
@@ -193,7 +198,8 @@ int csa2_quantize_index_k(const void* k_bf16, const int64_t* dst_slot, int64_t n
  * multiplied exactly with the E4M3 query by the scaled FP8 x FP4 matrix
  * instruction. Modes, outputs, masking and errors are those of
  * csa2_index_score; every T runs the decode-shaped scan, and REINDEX
- * re-scores a position to the same bits as FULL. */
+ * re-scores a position to the same bits as FULL. `k_scales` needs only 4-byte
+ * alignment. */
 int csa2_index_score_fp4k(int mode, const uint8_t* q_idx, const float* w, const uint8_t* k_codes,
                           const uint8_t* k_scales, const int32_t* n_vis, const int32_t* pool,
                           int B, int T, int64_t n_cap, float* scores, float* bmax, void* stream);

@@ -148,7 +148,7 @@ def test_fp4_key_calls_reject_bad_arguments():
     assert q(F, None, 11, F, F, 10, None) == C.CSA2_EINVAL      # rows beyond the buffers
     assert q(F, None, 4, F, F, 0, None) == C.CSA2_EINVAL
     assert q(None, None, 4, F, F, 10, None) == C.CSA2_EINVAL
-    assert q(F, None, 4, F, M, 10, None) == C.CSA2_EINVAL
+    assert q(F, None, 4, F, _p(FAKE + 2), 10, None) == C.CSA2_EINVAL
     assert q(F, M, 4, F, F, 10, None) == C.CSA2_EINVAL
     assert q(F, None, 0, F, F, 10, None) == C.CSA2_OK            # nothing to do
     f = C.lib().csa2_index_score_fp4k
@@ -161,7 +161,7 @@ def test_fp4_key_calls_reject_bad_arguments():
 
     assert call(mode=2) == C.CSA2_EINVAL
     assert call(ks=0) == C.CSA2_EINVAL                          # scales are required
-    assert call(ks=FAKE_MIS) == C.CSA2_EINVAL
+    assert call(ks=FAKE + 2) == C.CSA2_EINVAL                  # scales: 4-byte aligned
     assert call(mode=1, pool=0) == C.CSA2_EINVAL
     assert call(mode=1, bm=FAKE) == C.CSA2_EINVAL
     assert call(s=0) == C.CSA2_EINVAL

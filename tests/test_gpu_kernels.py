@@ -437,3 +437,64 @@ def test_sparse_attn_scale_and_outliers():
         ref = OA.sparse_attention(qn[b, 0], OracleCache(main[b], 1), idx[b, 0], to_np(swa)[b],
                                   q_pos[b, 0], pos0[b], scale=0.5)
         assert_attn_close(o[b, 0], ref, "outliers b%d" % b)
+
+
+@pytest.mark.parametrize("T,kf", [(2, 0), (4, 0), (5, 0), (33, 0), (4, 1), (7, 1)])
+def test_multi_token_decode_shares_keys(T, kf):
+    """Several query tokens of one sequence (T < 64, Full mode) are scored in
+    groups that share each key tile; every query's scores and block maxima must
+    equal, bit for bit, those of a single-query call, and lie within the score
+    bound of the oracle. Visibility is causal per query (T and n_cap ragged)."""
+    from oracle import mxfp4 as OM
+    B, n_cap = 2, 20011
+    _stage("multi-token decode", T, kf)
+    q = synth.e4m3_rows(B * T * 32, 128, DEV, T, "mq").view(B, T, 32, 128)
+    w = synth.head_weights(B * T, DEV, T, "mw").view(B, T, 32)
+    if kf:
+        kb = synth.normal_rows(B * n_cap, 128, DEV, T, "mk4").to(torch.bfloat16)
+        codes = torch.empty((B, n_cap, 64), dtype=torch.uint8, device=DEV)
+        scl = torch.empty((B, n_cap, 4), dtype=torch.uint8, device=DEV)
+        C.csa2_quantize_index_k(kb, None, codes, scl)
+        oc, osc = OM.quantize_index_keys(kb.float().cpu().numpy())
+        oc, osc = oc.reshape(B, n_cap, 64), osc.reshape(B, n_cap, 4)
+
+        def score(mode, qq, ww, nv, s, bm):
+            C.csa2_index_score_fp4k(mode, qq, ww, codes, scl, nv, None, s, bm)
+    else:
+        k = synth.e4m3_rows(B * n_cap, 128, DEV, T, "mk").view(B, n_cap, 128)
+        oc, osc = to_np(k), None
+
+        def score(mode, qq, ww, nv, s, bm, kk=k):
+            C.csa2_index_score(mode, qq, ww, kk, nv, None, s, bm)
+    nv = (n_cap - T + 1 + np.arange(T))[None, :].repeat(B, 0).astype(np.int32)
+    nv[1, 0] = 0
+    nv[1, -1] = 5
+    n_vis = torch.from_numpy(nv).to(DEV)
+    nb = (n_cap + 7) // 8
+    scores = torch.empty((B, T, n_cap), dtype=torch.float32, device=DEV)
+    bmax = torch.empty((B, T, nb), dtype=torch.float32, device=DEV)
+    score(C.CSA2_FULL, q, w, n_vis, scores, bmax)
+    one_s = torch.empty((1, 1, n_cap), dtype=torch.float32, device=DEV)
+    one_b = torch.empty((1, 1, nb), dtype=torch.float32, device=DEV)
+    sn, bn, qn, wn = to_np(scores), to_np(bmax), to_np(q), to_np(w)
+    for b in range(B):
+        for t in range(T):
+            if kf:
+                C.csa2_index_score_fp4k(C.CSA2_FULL, q[b:b + 1, t:t + 1], w[b:b + 1, t:t + 1],
+                                        codes[b:b + 1], scl[b:b + 1], n_vis[b:b + 1, t:t + 1].clone(),
+                                        None, one_s, one_b)
+            else:
+                C.csa2_index_score(C.CSA2_FULL, q[b:b + 1, t:t + 1], w[b:b + 1, t:t + 1], k[b:b + 1],
+                                   n_vis[b:b + 1, t:t + 1].clone(), None, one_s, one_b)
+            assert np.array_equal(to_np(one_s)[0, 0].view(np.uint32), sn[b, t].view(np.uint32)), (b, t)
+            assert np.array_equal(to_np(one_b)[0, 0].view(np.uint32), bn[b, t].view(np.uint32)), (b, t)
+    for b, t in [(0, 0), (0, T - 1), (1, 0), (1, T - 1), (1, T // 2)]:
+        ref = OI.index_scores(qn[b, t], wn[b, t], oc[b], nv[b, t],
+                              k_scales=None if osc is None else osc[b])
+        if kf:
+            qa = np.abs(OF.e4m3_decode(qn[b, t].reshape(32, 128)))
+            ka = np.abs(OM.dequantize_index_keys(oc[b], osc[b]))
+            bound = 160.0 * 2.0 ** -24 * (ka @ qa.T) @ np.abs(wn[b, t].astype(np.float64))
+        else:
+            bound = score_bound(qn[b, t], wn[b, t], oc[b])
+        assert_scores_close(sn[b, t], ref, bound, "b%d t%d" % (b, t))
