@@ -533,9 +533,11 @@ __global__ __launch_bounds__(kPfThreads) void k_index_score_prefill(
 
 }  // namespace
 
-// Queries per wave of the Full scan: several query tokens of one sequence share
-// each key tile.
-constexpr int kDecodeGroup = 4;
+// Queries per wave of the Full scan when several query tokens of one sequence
+// share each key tile: 4 with FP8 keys, 2 with FP4 keys (fewer registers per
+// wave; measured fastest for each format at 4 tokens per sequence).
+template <int KF>
+constexpr int decode_group() { return KF ? 2 : 4; }
 
 template <int KF>
 hipError_t launch_decode(int mode, const uint8_t* q_idx, const float* w, const uint8_t* keys,
@@ -551,8 +553,9 @@ hipError_t launch_decode(int mode, const uint8_t* q_idx, const float* w, const u
     hipLaunchKernelGGL((k_index_score_decode<0, KF, 1>), dim3(gx, (unsigned)B), dim3(256), 0, st,
                        q_idx, w, keys, scales, n_vis, pool, T, n_cap, n_items, scores, bmax);
   } else {
-    const unsigned gy = (unsigned)(B * ((T + kDecodeGroup - 1) / kDecodeGroup));
-    hipLaunchKernelGGL((k_index_score_decode<0, KF, kDecodeGroup>), dim3(gx, gy), dim3(256), 0, st,
+    constexpr int G = decode_group<KF>();
+    const unsigned gy = (unsigned)(B * ((T + G - 1) / G));
+    hipLaunchKernelGGL((k_index_score_decode<0, KF, G>), dim3(gx, gy), dim3(256), 0, st,
                        q_idx, w, keys, scales, n_vis, pool, T, n_cap, n_items, scores, bmax);
   }
   return hipGetLastError();

@@ -135,7 +135,8 @@ int csa2_quantize_kv(const void* kv_bf16, const float* cos_sin, const int64_t* d
  * Products are exact; sums are float32 (MFMA accumulation order). Every query's
  * score is the same bits whatever T is: in FULL mode the query tokens of a
  * sequence (T >= 2, e.g. speculative decode) share each key read, four at a time
- * below T = 64 and in tiles of 32 from T = 64 on.
+ * below T = 64 and in tiles of 32 from T = 64 on (csa2_index_score_fp4k: two at
+ * a time, for every T).
  * Errors: CSA2_EINVAL for REUSE, NULL/misaligned pointers, REINDEX without a
  * pool, nothing to write, B < 1, T < 1, n_cap < 1 or n_cap >= 2^31. */
 int csa2_index_score(int mode, const uint8_t* q_idx, const float* w, const uint8_t* k_idx,
