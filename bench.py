@@ -65,6 +65,10 @@ def parse():
     p.add_argument("--spec-tokens", type=int, default=1,
                    help="query tokens per sequence of a decode workload (the last T "
                         "positions, e.g. speculative decode); 1 = the workload as defined")
+    p.add_argument("--fused-topk", default="auto", choices=["auto", "on", "off"],
+                   help="groups without a pool (c1, c3, c4) take the Full layer's Top-K from "
+                        "the fused scan + Top-K entry point (no score rows written): 'auto' "
+                        "where it is faster (decode shapes over >= 262,144 positions)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--graph", dest="graph", action="store_true", default=True,
                    help="replay each step segment as a HIP graph (default)")
@@ -210,6 +214,10 @@ def main():
     from synth.configs import WORKLOADS, make_inputs
 
     w = WORKLOADS[args.workload]
+    if args.fused_topk == "on" and not args.graph:
+        print("--fused-topk on times the scan in its own graph: use it without --eager",
+              file=sys.stderr)
+        sys.exit(2)
     if args.spec_tokens > 1:
         import dataclasses
         if w.T != 1 or args.spec_tokens >= 64:
@@ -293,7 +301,10 @@ def main():
     # keys visible to some query of each sequence: what a scan that shares the
     # key reads among a sequence's query tokens must move (decode shapes)
     n_keys = int(n_vis.max(dim=1).values.sum().item())
-    g = LayerGroup(w.kind, B, T, n_cap, device=dev)
+    fused = {"auto": "auto", "on": True, "off": False}[args.fused_topk]
+    if not args.graph:
+        fused = False          # eager timing brackets the scan inside the step
+    g = LayerGroup(w.kind, B, T, n_cap, device=dev, fused_topk=fused)
     stream = torch.cuda.current_stream()
 
     args_rest = (keys, cache, n_vis, inp["q_pos"], inp["swa_pos0"], inp["q_idx"],
@@ -315,6 +326,11 @@ def main():
 
     def seg_scan():
         g.scan(keys, n_vis, inp["q_idx"], inp["w"])
+
+    def seg_scan_timed():
+        # the Full scan alone, for its roofline (with --fused-topk the step runs
+        # it inside csa2_index_topk, writing block maxima only, as here)
+        g.scan_only(keys, n_vis, inp["q_idx"], inp["w"])
 
     def seg_rest():
         g.rest(*args_rest)
@@ -351,7 +367,7 @@ def main():
         scan_graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(scan_graph):
             for _ in range(R):
-                seg_scan()
+                seg_scan_timed()
         torch.cuda.synchronize()
         for _ in range(max(1, args.warmup)):
             step_graph.replay()
@@ -440,6 +456,7 @@ def main():
             "write_path": {"main": "one compressed main-KV row per sequence (RoPE + FP4)",
                            "full": "m tokens compressed on device, main row RoPE + FP4, indexer "
                                    "key appended, window row appended in every layer"}[args.write_path],
+            "fused_topk": bool(g.fused),
             "index_k": {"fp8": "FP8 E4M3 indexer keys (128 B)",
                         "fp4": "FP4 E2M1 indexer keys + E8M0 per 32 channels (68 B)"}[args.index_k],
             "timing": ("one HIP graph per step; scan timed over back-to-back launches"

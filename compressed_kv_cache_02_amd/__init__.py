@@ -18,11 +18,12 @@ __all__ = [
     "csa2_abi_version", "csa2_status_string", "csa2_workspace_bytes", "csa2_rope_table",
     "csa2_quantize_kv", "csa2_index_score", "csa2_build_pool", "csa2_topk",
     "csa2_sparse_attn", "csa2_quantize_index_k", "csa2_index_score_fp4k",
-    "csa2_compress_tokens", "csa2_quantize_e4m3",
+    "csa2_compress_tokens", "csa2_quantize_e4m3", "csa2_index_topk", "CSA2_OP_INDEX_TOPK",
 ]
 
 CSA2_FULL, CSA2_REINDEX, CSA2_REUSE = 0, 1, 2
 CSA2_OP_INDEX_SCORE, CSA2_OP_BUILD_POOL, CSA2_OP_TOPK, CSA2_OP_SPARSE_ATTN = 0, 1, 2, 3
+CSA2_OP_INDEX_TOPK = 4
 CSA2_OK, CSA2_EINVAL, CSA2_EUNSUPPORTED, CSA2_EWORKSPACE, CSA2_EHIP = 0, -1, -2, -3, -4
 
 IDX_HEADS, IDX_DIM, HEADS, DIM = 32, 128, 64, 512
@@ -45,6 +46,7 @@ _SIGS = {
     "csa2_rope_table": (_i32, [_vp, _i64, _vp]),
     "csa2_quantize_kv": (_i32, [_vp, _vp, _vp, _i64, _vp, _i64, _vp]),
     "csa2_index_score": (_i32, [_i32, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i64, _vp, _vp, _vp]),
+    "csa2_index_topk": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i64, _vp, _vp, _sz, _vp]),
     "csa2_compress_tokens": (_i32, [_vp, _i64, _i32, _i32, _vp, _vp]),
     "csa2_quantize_e4m3": (_i32, [_vp, _i64, _i32, _vp, _vp, _i64, _vp]),
     "csa2_quantize_index_k": (_i32, [_vp, _vp, _i64, _vp, _vp, _i64, _vp]),
@@ -175,6 +177,31 @@ def csa2_index_score(mode, q_idx, w, k_idx, n_vis, pool, scores, bmax=None, stre
     _check("csa2_index_score", lib().csa2_index_score(mode, _p(q_idx), _p(w), _p(k_idx),
                                                       _p(n_vis), _p(pool), B, T, n_cap,
                                                       _p(scores), _p(bmax), _stream(stream)))
+
+
+def csa2_index_topk(q_idx, w, keys, n_vis, idx, ws, stream=None):
+    """Fused Full scan + Top-512. keys: FP8 keys [B,n_cap,128] uint8, or a pair
+    (codes [B,n_cap,64], scales [B,n_cap,4]) of FP4 keys; idx [B,T,512] int32;
+    ws a uint8 device tensor of csa2_workspace_bytes(CSA2_OP_INDEX_TOPK, ...) bytes."""
+    import torch
+    B, T = q_idx.shape[0], q_idx.shape[1]
+    if isinstance(keys, tuple):
+        k, ks = keys
+        n_cap = k.shape[1]
+        _expect(k, "k_codes", torch.uint8, (B, n_cap, IDX_FP4_CODE_BYTES))
+        _expect(ks, "k_scales", torch.uint8, (B, n_cap, IDX_FP4_SCALES))
+    else:
+        k, ks = keys, None
+        n_cap = k.shape[1]
+        _expect(k, "k_idx", torch.uint8, (B, n_cap, IDX_DIM))
+    _expect(q_idx, "q_idx", torch.uint8, (B, T, IDX_HEADS, IDX_DIM))
+    _expect(w, "w", torch.float32, (B, T, IDX_HEADS))
+    _expect(n_vis, "n_vis", torch.int32, (B, T))
+    _expect(idx, "idx", torch.int32, (B, T, TOPK))
+    _expect(ws, "ws", torch.uint8)
+    _check("csa2_index_topk", lib().csa2_index_topk(_p(q_idx), _p(w), _p(k), _p(ks), _p(n_vis), B,
+                                                    T, n_cap, _p(idx), _p(ws), ws.numel(),
+                                                    _stream(stream)))
 
 
 def csa2_compress_tokens(tokens_bf16, m, out_bf16, stream=None):

@@ -30,6 +30,33 @@ inline bool sizes_ok(int B, int T, int64_t n_cap) {
 
 inline int status_of(hipError_t e) { return e == hipSuccess ? CSA2_OK : CSA2_EHIP; }
 
+// Workspace of csa2_index_topk: the whole score rows when one selection covers
+// them (n_cap <= 16,384); otherwise block maxima, the 512 best blocks, their
+// 4,096 re-scored positions and the best-blocks selection's own scratch.
+struct FusedWs {
+  size_t scores, bmax, sel_blk, vals, blocks_ws, total;
+};
+
+inline FusedWs fused_layout(int Q, int64_t n_cap) {
+  FusedWs l{};
+  if (n_cap <= CSA2_POOL_CAND) {
+    l.total = round_up((size_t)Q * (size_t)n_cap * sizeof(float));
+    return l;
+  }
+  const int64_t n_blk = (n_cap + CSA2_BLOCK - 1) / CSA2_BLOCK;
+  l.bmax = 0;
+  l.sel_blk = round_up((size_t)Q * (size_t)n_blk * sizeof(float));
+  l.vals = l.sel_blk + round_up((size_t)Q * CSA2_TOPK * sizeof(int32_t));
+  l.blocks_ws = l.vals + round_up((size_t)Q * CSA2_TOPK * CSA2_BLOCK * sizeof(float));
+  l.total = l.blocks_ws + round_up(csa2::best_blocks_workspace_bytes(Q, n_cap));
+  return l;
+}
+
+template <typename T>
+inline T* ws_at(void* ws, size_t off) {
+  return reinterpret_cast<T*>(static_cast<uint8_t*>(ws) + off);
+}
+
 inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 
 }  // namespace
@@ -59,6 +86,7 @@ size_t csa2_workspace_bytes(int op, int mode, int B, int T, int64_t n_cap) {
       if (mode == CSA2_FULL) return round_up(csa2::topk_workspace_bytes(Q, n_cap));
       return 0;
     case CSA2_OP_SPARSE_ATTN: return round_up(csa2::attn_workspace_bytes(Q));
+    case CSA2_OP_INDEX_TOPK: return fused_layout(Q, n_cap).total;
     default: return 0;
   }
 }
@@ -156,6 +184,44 @@ int csa2_index_score_fp4k(int mode, const uint8_t* q_idx, const float* w, const 
   return status_of(csa2::launch_index_score_decode_fp4k(mode, q_idx, w, k_codes, k_scales, n_vis,
                                                         pool, B, T, n_cap, scores, bmax,
                                                         as_stream(stream)));
+}
+
+int csa2_index_topk(const uint8_t* q_idx, const float* w, const uint8_t* k_idx,
+                    const uint8_t* k_scales, const int32_t* n_vis, int B, int T, int64_t n_cap,
+                    int32_t* idx, void* ws, size_t ws_bytes, void* stream) {
+  if (!sizes_ok(B, T, n_cap)) return CSA2_EINVAL;
+  if (!aligned16(q_idx) || !aligned16(w) || !aligned16(k_idx) || !aligned16(n_vis) ||
+      !aligned16(idx) || (k_scales && !aligned4(k_scales)))
+    return CSA2_EINVAL;
+  if (n_cap > CSA2_INDEX_TOPK_MAX_CAP) return CSA2_EUNSUPPORTED;
+  const FusedWs l = fused_layout(B * T, n_cap);
+  if (!aligned16(ws)) return ws ? CSA2_EINVAL : CSA2_EWORKSPACE;
+  if (ws_bytes < l.total) return CSA2_EWORKSPACE;
+  hipStream_t st = as_stream(stream);
+  const int Q = B * T;
+  // the Full scan: score rows (short contexts) or block maxima only
+  float* scores = n_cap <= CSA2_POOL_CAND ? ws_at<float>(ws, l.scores) : nullptr;
+  float* bmax = scores ? nullptr : ws_at<float>(ws, l.bmax);
+  hipError_t e;
+  if (k_scales)
+    e = csa2::launch_index_score_decode_fp4k(CSA2_FULL, q_idx, w, k_idx, k_scales, n_vis, nullptr,
+                                             B, T, n_cap, scores, bmax, st);
+  else if (T >= 64)
+    e = csa2::launch_index_score_prefill(q_idx, w, k_idx, n_vis, B, T, n_cap, scores, bmax, st);
+  else
+    e = csa2::launch_index_score_decode(CSA2_FULL, q_idx, w, k_idx, n_vis, nullptr, B, T, n_cap,
+                                        scores, bmax, st);
+  if (e != hipSuccess) return CSA2_EHIP;
+  if (scores) return status_of(csa2::launch_topk_direct(scores, n_vis, Q, n_cap, idx, st));
+  int32_t* sel_blk = ws_at<int32_t>(ws, l.sel_blk);
+  float* vals = ws_at<float>(ws, l.vals);
+  if ((e = csa2::launch_best_blocks(bmax, n_vis, Q, n_cap, sel_blk, ws_at<void>(ws, l.blocks_ws),
+                                    st)) != hipSuccess)
+    return CSA2_EHIP;
+  if ((e = csa2::launch_rescore_blocks(q_idx, w, k_idx, k_scales, n_vis, sel_blk, CSA2_TOPK, B, T,
+                                       n_cap, vals, st)) != hipSuccess)
+    return CSA2_EHIP;
+  return status_of(csa2::launch_topk_of_blocks(vals, sel_blk, n_vis, Q, n_cap, idx, st));
 }
 
 int csa2_build_pool(const float* src, int is_bmax, const int32_t* n_vis, int B, int T,

@@ -197,7 +197,9 @@ __global__ __launch_bounds__(256) void k_index_score_decode(
   constexpr int kKeyBytes = KF ? kIdxDim / 2 : kIdxDim;
   const uint8_t* kbase = k_idx + (size_t)b * (size_t)n_cap * kKeyBytes + half * (KF ? 16 : 64);
   const uint8_t* sbase = KF ? k_scales + (size_t)b * (size_t)n_cap * 4 : nullptr;
-  const int32_t* pl = MODE == 1 ? pool + (size_t)qi[0] * kPoolBlocks : nullptr;
+  // a Reindex query's block list: n_items / 8 entries (the pool's 2,048, or the
+  // 512 best blocks of a fused Top-K)
+  const int32_t* pl = MODE == 1 ? pool + (size_t)qi[0] * (size_t)(n_items >> 3) : nullptr;
 
   constexpr int kTilesPerWave = tiles_per_wave<MODE, KF>();
   constexpr int kPrefetch = prefetch_tiles<KF>();
@@ -557,6 +559,27 @@ hipError_t launch_decode(int mode, const uint8_t* q_idx, const float* w, const u
     const unsigned gy = (unsigned)(B * ((T + G - 1) / G));
     hipLaunchKernelGGL((k_index_score_decode<0, KF, G>), dim3(gx, gy), dim3(256), 0, st,
                        q_idx, w, keys, scales, n_vis, pool, T, n_cap, n_items, scores, bmax);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_rescore_blocks(const uint8_t* q_idx, const float* w, const uint8_t* keys,
+                                 const uint8_t* scales, const int32_t* n_vis, const int32_t* blocks,
+                                 int n_blocks, int B, int T, int64_t n_cap, float* vals,
+                                 hipStream_t st) {
+  const int64_t n_items = (int64_t)n_blocks * kBlock;
+  if (scales) {
+    const int64_t per_wg = items_per_wg<1, 1>();
+    hipLaunchKernelGGL((k_index_score_decode<1, 1, 1>),
+                       dim3((unsigned)((n_items + per_wg - 1) / per_wg), (unsigned)(B * T)),
+                       dim3(256), 0, st, q_idx, w, keys, scales, n_vis, blocks, T, n_cap, n_items,
+                       vals, nullptr);
+  } else {
+    const int64_t per_wg = items_per_wg<1, 0>();
+    hipLaunchKernelGGL((k_index_score_decode<1, 0, 1>),
+                       dim3((unsigned)((n_items + per_wg - 1) / per_wg), (unsigned)(B * T)),
+                       dim3(256), 0, st, q_idx, w, keys, nullptr, n_vis, blocks, T, n_cap, n_items,
+                       vals, nullptr);
   }
   return hipGetLastError();
 }

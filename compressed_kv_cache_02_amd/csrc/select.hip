@@ -934,6 +934,38 @@ hipError_t launch_topk_full(const float* scores, const float* bmax, const int32_
                    st);
 }
 
+size_t best_blocks_workspace_bytes(int Q, int64_t n_cap) {
+  const int64_t n_sb = n_blocks(n_blocks(n_cap));
+  return up((size_t)Q * n_sb * sizeof(float)) + up((size_t)Q * kTopK * sizeof(int32_t));
+}
+
+hipError_t launch_best_blocks(const float* bmax, const int32_t* n_vis, int Q, int64_t n_cap,
+                              int32_t* sel_blk, void* ws, hipStream_t st) {
+  const int64_t n_blk = n_blocks(n_cap);
+  const int64_t n_sb = n_blocks(n_blk);
+  if (n_sb > kOneWgMax) return hipErrorInvalidValue;
+  float* smax = at<float>(ws, 0);
+  int32_t* sel_sb = at<int32_t>(ws, up((size_t)Q * n_sb * sizeof(float)));
+  hipError_t e;
+  if ((e = launch_super_max(bmax, Q, n_blk, smax, st)) != hipSuccess) return e;
+  e = run_stage(direct(smax, n_sb, 64, n_vis, n_cap, n_sb), Q, kTopK, sel_sb, kTopK, st);
+  if (e != hipSuccess) return e;
+  return run_stage(child(bmax, n_blk, 8, sel_sb, kTopK, 0, n_vis, n_cap), Q, kTopK, sel_blk,
+                   kTopK, st);
+}
+
+hipError_t launch_topk_of_blocks(const float* vals, const int32_t* sel_blk, const int32_t* n_vis,
+                                 int Q, int64_t n_cap, int32_t* out, hipStream_t st) {
+  return run_stage(child(vals, (int64_t)kTopK * kBlock, 1, sel_blk, kTopK, 1, n_vis, n_cap), Q,
+                   kTopK, out, kTopK, st);
+}
+
+hipError_t launch_topk_direct(const float* scores, const int32_t* n_vis, int Q, int64_t n_cap,
+                              int32_t* out, hipStream_t st) {
+  if (n_cap > kOneWgMax) return hipErrorInvalidValue;
+  return run_stage(direct(scores, n_cap, 1, n_vis, n_cap, n_cap), Q, kTopK, out, kTopK, st);
+}
+
 hipError_t launch_topk_reindex(const float* scores_pool, const int32_t* pool, const int32_t* n_vis,
                                int Q, int64_t n_cap, int32_t* out, hipStream_t st) {
   return run_stage(child(scores_pool, kPoolCand, 1, pool, kPoolBlocks, 1, n_vis, n_cap), Q, kTopK,

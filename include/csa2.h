@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define CSA2_ABI_VERSION 4
+#define CSA2_ABI_VERSION 5
 
 #define CSA2_IDX_HEADS 32
 #define CSA2_IDX_DIM 128
@@ -56,6 +56,7 @@ extern "C" {
 #define CSA2_POOL_CAND 16384
 #define CSA2_WINDOW 128
 #define CSA2_ROPE_PAIRS 32      /* RoPE on channels 448..511, adjacent pairs */
+#define CSA2_INDEX_TOPK_MAX_CAP 1048576   /* longest context csa2_index_topk serves */
 #define CSA2_MAX_M 64                /* largest compression ratio csa2_compress_tokens accepts */
 #define CSA2_MAX_WIDTH 8192          /* widest row of the write-path helpers */
 #define CSA2_IDX_FP4_CODE_BYTES 64   /* FP4 indexer key: 128 E2M1 codes ... */
@@ -77,7 +78,13 @@ enum {
 };
 
 /* Operation ids for csa2_workspace_bytes(). */
-enum { CSA2_OP_INDEX_SCORE = 0, CSA2_OP_BUILD_POOL = 1, CSA2_OP_TOPK = 2, CSA2_OP_SPARSE_ATTN = 3 };
+enum {
+  CSA2_OP_INDEX_SCORE = 0,
+  CSA2_OP_BUILD_POOL = 1,
+  CSA2_OP_TOPK = 2,
+  CSA2_OP_SPARSE_ATTN = 3,
+  CSA2_OP_INDEX_TOPK = 4
+};
 
 /* Version of this ABI (CSA2_ABI_VERSION). */
 int csa2_abi_version(void);
@@ -204,6 +211,29 @@ int csa2_quantize_index_k(const void* k_bf16, const int64_t* dst_slot, int64_t n
 int csa2_index_score_fp4k(int mode, const uint8_t* q_idx, const float* w, const uint8_t* k_codes,
                           const uint8_t* k_scales, const int32_t* n_vis, const int32_t* pool,
                           int B, int T, int64_t n_cap, float* scores, float* bmax, void* stream);
+
+/* DEVICE. Fused Full-mode scan and Top-512: the result of csa2_index_score(FULL)
+ * followed by csa2_topk(FULL) ([P1] §二 layer layout, mode table and hierarchical
+ * sparse indexer), without writing any score row. Beyond 16,384 positions the
+ * scan keeps only block maxima; the 512 best blocks of 8 (by block maximum, ties
+ * to the lower block; found through the 512 best super-blocks of 8 blocks) are
+ * re-scored position by position to the scan's own bits, and the Top-512 is
+ * taken among those 4,096 positions. This is exact: each block ranked ahead of
+ * the block holding one of the 512 best positions holds, as its maximum, a
+ * distinct position ranked ahead of it, so the 512 best positions lie in the 512
+ * best blocks. Up to 16,384 positions the score rows go to the workspace and one
+ * selection takes the Top-512.
+ *   q_idx, w, n_vis: as csa2_index_score; k_idx [B][n_cap][128] E4M3 keys when
+ *   k_scales is NULL, else [B][n_cap][64] FP4 codes with k_scales [B][n_cap][4]
+ *   (csa2_quantize_index_k's layout; 4-byte aligned);
+ *   idx [B][T][512] int32 (device, written) as csa2_topk writes it: ascending,
+ *   -1 padded; ranking by (score descending, position ascending);
+ *   ws   csa2_workspace_bytes(CSA2_OP_INDEX_TOPK, 0, B, T, n_cap) bytes (device).
+ * Errors: CSA2_EINVAL (pointers, sizes), CSA2_EWORKSPACE, CSA2_EUNSUPPORTED for
+ * n_cap > CSA2_INDEX_TOPK_MAX_CAP. */
+int csa2_index_topk(const uint8_t* q_idx, const float* w, const uint8_t* k_idx,
+                    const uint8_t* k_scales, const int32_t* n_vis, int B, int T, int64_t n_cap,
+                    int32_t* idx, void* ws, size_t ws_bytes, void* stream);
 
 /* DEVICE. Hierarchical candidate pool ([P1] §二 hierarchical sparse indexer;
  * [P3] 第二刀, Fig. 5): per query, among blocks j < ceil(n_vis/8), the 2,048

@@ -33,11 +33,11 @@ def declared_functions():
 
 def test_header_functions_are_exported():
     names = declared_functions()
-    assert len(names) == 13, names
+    assert len(names) == 14, names
     L = C.lib()
     for n in names:
         assert hasattr(L, n), n
-    assert C.csa2_abi_version() == 4
+    assert C.csa2_abi_version() == 5
 
 
 def test_status_strings():
@@ -64,8 +64,9 @@ def test_workspace_sizes():
     assert ws(C.CSA2_OP_BUILD_POOL, 0, 8, 1, 1 << 20) > 0
     assert ws(C.CSA2_OP_TOPK, C.CSA2_FULL, 0, 1, 100) == 0         # invalid sizes
     assert ws(C.CSA2_OP_TOPK, C.CSA2_FULL, 1, 1, 1 << 31) == 0
-    for op in range(4):
+    for op in range(5):
         assert ws(op, 0, 3, 5, 1000) % 256 == 0
+    assert ws(C.CSA2_OP_INDEX_TOPK, 0, 8, 1, 1 << 20) > ws(C.CSA2_OP_INDEX_TOPK, 0, 8, 1, 16384) > 0
 
 
 def _p(x):
@@ -187,3 +188,17 @@ def test_write_path_helpers_reject_bad_arguments():
     assert q(None, 4, 512, None, F, 10, None) == C.CSA2_EINVAL
     assert q(F, 4, 512, None, F, 0, None) == C.CSA2_EINVAL
     assert q(F, 0, 512, None, F, 10, None) == C.CSA2_OK
+
+
+def test_index_topk_rejects_bad_arguments():
+    f = C.lib().csa2_index_topk
+    F, M = _p(FAKE), _p(FAKE_MIS)
+    need = C.csa2_workspace_bytes(C.CSA2_OP_INDEX_TOPK, 0, 1, 1, 100000)
+    assert f(F, F, F, None, F, 1, 1, 100000, F, None, 0, None) == C.CSA2_EWORKSPACE
+    assert f(F, F, F, None, F, 1, 1, 100000, F, F, need - 1, None) == C.CSA2_EWORKSPACE
+    assert f(F, F, F, None, F, 1, 1, (1 << 20) + 1, F, F, 1 << 40, None) == C.CSA2_EUNSUPPORTED
+    assert f(F, F, M, None, F, 1, 1, 100000, F, F, need, None) == C.CSA2_EINVAL
+    assert f(F, F, F, _p(FAKE + 2), F, 1, 1, 100000, F, F, need, None) == C.CSA2_EINVAL
+    assert f(F, F, F, None, F, 1, 1, 100000, M, F, need, None) == C.CSA2_EINVAL
+    assert f(F, F, F, None, F, 0, 1, 100000, F, F, need, None) == C.CSA2_EINVAL
+    assert f(F, F, F, None, F, 1, 1, 100000, F, M, need, None) == C.CSA2_EINVAL

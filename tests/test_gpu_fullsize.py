@@ -153,10 +153,24 @@ def check_pool_topk(idx, sp, pool, nv, n_cap, what):
     check_selection(sidx.to(torch.int32), sp, None, what)
 
 
-def check_properties(w, g, n_vis):
+def fused_scores(w, g, inp, n_vis):
+    """A group with the fused Full Top-K writes neither score rows nor block
+    maxima; recompute both with a plain FULL scan (the same bits) to check its
+    selection against."""
+    li = [i for i, (mode, _) in enumerate(g.sched) if mode == "F"][0]
+    scores = torch.empty((w.B, w.T, w.n_cap), dtype=torch.float32, device=DEV)
+    C.csa2_index_score(C.CSA2_FULL, inp["q_idx"][li], inp["w"][li], inp["k_idx"], n_vis, None,
+                       scores, g.bmax)
+    torch.cuda.synchronize()
+    return scores
+
+
+def check_properties(w, g, n_vis, inp=None):
     Q = w.B * w.T
     nv = n_vis.reshape(Q).long()
     n_blk = (w.n_cap + 7) // 8
+    if g.fused:
+        g.scores = fused_scores(w, g, inp, n_vis)
     bmax = g.bmax.reshape(Q, n_blk)
     nb = (nv + 7) // 8
     blk_vis = torch.arange(n_blk, device=DEV)[None, :] < nb[:, None]
@@ -210,7 +224,7 @@ def test_full_size_workload(name):
     _stage(name, "graph step")
     g, n_vis = run_graph_step(w, inp, cache, write)
     _stage(name, "properties of every query")
-    check_properties(w, g, n_vis)
+    check_properties(w, g, n_vis, inp)
     _stage(name, "oracle on sampled queries")
     checked, swaps = check_queries(w, inp, g, CASES[name], regen_cache(w, inp, seed),
                                    log=lambda s: _stage(name, s))

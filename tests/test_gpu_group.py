@@ -105,3 +105,22 @@ def test_encoder_group_write_path_outliers():
     got = to_np(cache)[:, n_cap - 1]
     for b in range(B):
         assert np.array_equal(got[b], oc[b][[n_cap - 1]][0])
+
+
+def test_encoder_group_fused_topk():
+    """[F, U x5] at m = 2 over 40,000 entries with the Full Top-K from the fused
+    scan + Top-K entry point (no score rows), checked against the oracle."""
+    w = scaled(WORKLOADS["c4"], 80000, 40000, "c4_80k_fused")
+    B = 2
+    _stage("encoder group fused", w)
+    inp = _inputs(w, B, seed=6)
+    cache = build_cache(inp, w, B)
+    n_vis = visible_entries(inp["q_pos"], w.m).to(torch.int32)
+    g = LayerGroup(w.kind, B, w.T, w.n_cap, fused_topk=True)
+    assert g.fused and g.scores is None
+    g.step(inp["k_idx"], cache, n_vis, inp["q_pos"], inp["swa_pos0"], inp["q_idx"], inp["w"],
+           inp["q"], inp["swa"])
+    torch.cuda.synchronize()
+    checked, swaps = check_group(w, inp, g, B)
+    print("attention checked:", checked, "near-tie swaps:", swaps)
+    assert checked >= 6 * B - 5 * swaps

@@ -498,3 +498,55 @@ def test_multi_token_decode_shares_keys(T, kf):
         else:
             bound = score_bound(qn[b, t], wn[b, t], oc[b])
         assert_scores_close(sn[b, t], ref, bound, "b%d t%d" % (b, t))
+
+
+@pytest.mark.parametrize("B,T,n_cap,kf", [(2, 1, 40003, 0), (2, 3, 200003, 0), (1, 70, 30011, 0),
+                                          (2, 1, 9000, 0), (2, 1, 100003, 1), (1, 5, 50001, 1)])
+def test_index_topk_fused_equals_scan_then_topk(B, T, n_cap, kf):
+    """csa2_index_topk writes no score row (block maxima, the 512 best blocks
+    re-scored) yet must give byte for byte the Top-512 of csa2_index_score(FULL)
+    followed by csa2_topk(FULL); two queries are also checked against the oracle."""
+    from oracle import mxfp4 as OM
+    from tests.helpers import assert_topk_near
+    _stage("index_topk fused", B, T, n_cap, kf)
+    q = synth.e4m3_rows(B * T * 32, 128, DEV, n_cap, "fq").view(B, T, 32, 128)
+    w = synth.head_weights(B * T, DEV, n_cap, "fw").view(B, T, 32)
+    if kf:
+        kb = synth.normal_rows(B * n_cap, 128, DEV, n_cap, "fk4").to(torch.bfloat16)
+        codes = torch.empty((B, n_cap, 64), dtype=torch.uint8, device=DEV)
+        scl = torch.empty((B, n_cap, 4), dtype=torch.uint8, device=DEV)
+        C.csa2_quantize_index_k(kb, None, codes, scl)
+        keys = (codes, scl)
+        oc, osc = OM.quantize_index_keys(kb.float().cpu().numpy())
+        oc, osc = oc.reshape(B, n_cap, 64), osc.reshape(B, n_cap, 4)
+    else:
+        keys = synth.e4m3_rows(B * n_cap, 128, DEV, n_cap, "fk").view(B, n_cap, 128)
+        oc, osc = to_np(keys), None
+    rng = np.random.default_rng(T)
+    nv = np.minimum(n_cap, (n_cap - T + 1 + np.arange(T))[None, :].repeat(B, 0)).astype(np.int32)
+    if B * T > 2:
+        nv.flat[1] = 0
+        nv.flat[2] = int(rng.integers(1, min(n_cap, 20000)))
+    n_vis = torch.from_numpy(nv).to(DEV)
+    ws = torch.empty(C.csa2_workspace_bytes(C.CSA2_OP_INDEX_TOPK, 0, B, T, n_cap), dtype=torch.uint8,
+                     device=DEV)
+    idx = torch.full((B, T, 512), -7, dtype=torch.int32, device=DEV)
+    C.csa2_index_topk(q, w, keys, n_vis, idx, ws)
+    scores = torch.empty((B, T, n_cap), dtype=torch.float32, device=DEV)
+    bmax = torch.empty((B, T, (n_cap + 7) // 8), dtype=torch.float32, device=DEV)
+    if kf:
+        C.csa2_index_score_fp4k(C.CSA2_FULL, q, w, codes, scl, n_vis, None, scores, bmax)
+    else:
+        C.csa2_index_score(C.CSA2_FULL, q, w, keys, n_vis, None, scores, bmax)
+    ref = torch.empty((B, T, 512), dtype=torch.int32, device=DEV)
+    ws2 = torch.empty(max(256, C.csa2_workspace_bytes(C.CSA2_OP_TOPK, C.CSA2_FULL, B, T, n_cap)),
+                      dtype=torch.uint8, device=DEV)
+    C.csa2_topk(C.CSA2_FULL, scores, n_vis, None, None, n_cap, ref, ws2, bmax=bmax)
+    torch.cuda.synchronize()
+    assert to_np(idx).tobytes() == to_np(ref).tobytes()
+    qn, wn, gi = to_np(q), to_np(w), to_np(idx)
+    for b, t in [(0, 0), (B - 1, T - 1)]:
+        s = OI.index_scores(qn[b, t], wn[b, t], oc[b], nv[b, t],
+                            k_scales=None if osc is None else osc[b])
+        o = OS.topk_positions(s[:nv[b, t]], np.arange(nv[b, t]))
+        assert_topk_near(gi[b, t], o, lambda p: s[p], what="b%d t%d" % (b, t))
