@@ -68,7 +68,7 @@ def parse():
     p.add_argument("--fused-topk", default="auto", choices=["auto", "on", "off"],
                    help="groups without a pool (c1, c3, c4) take the Full layer's Top-K from "
                         "the fused scan + Top-K entry point (no score rows written): 'auto' "
-                        "where it is faster (decode shapes over >= 262,144 positions)")
+                        "where it is faster (prefill chunks, decode over >= 262,144 positions)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--graph", dest="graph", action="store_true", default=True,
                    help="replay each step segment as a HIP graph (default)")

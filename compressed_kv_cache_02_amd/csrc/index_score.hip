@@ -27,11 +27,14 @@ namespace {
 
 constexpr int kTilePos = 32;       // positions per MFMA tile
 constexpr int kWaves = 4;          // waves per work-group of the decode scan
+// MODE 0: the Full scan; MODE 1: scores of listed blocks (Reindex inside the
+// pool, or the re-scoring of a fused Top-K); MODE 2: as MODE 1, shaped for
+// hundreds of queries or more.
 // Tiles per wave: 8 for the Full scan (long rows, many work-groups anyway);
-// 2 inside the pool, where each query has only 16,384 candidates and more,
-// shorter work-groups spread a Reindex scan over more of the chip.
+// 2 for a block list of a few queries, where more, shorter work-groups spread
+// the work over more of the chip; 8 again once the queries alone fill it.
 template <int MODE, int KF>
-constexpr int tiles_per_wave() { return MODE == 0 ? 8 : 2; }
+constexpr int tiles_per_wave() { return MODE == 1 ? 2 : 8; }
 template <int MODE, int KF>
 constexpr int items_per_wg() { return kTilePos * tiles_per_wave<MODE, KF>() * kWaves; }
 // Tiles in registers per wave (one scored, the rest in flight).
@@ -199,7 +202,7 @@ __global__ __launch_bounds__(256) void k_index_score_decode(
   const uint8_t* sbase = KF ? k_scales + (size_t)b * (size_t)n_cap * 4 : nullptr;
   // a Reindex query's block list: n_items / 8 entries (the pool's 2,048, or the
   // 512 best blocks of a fused Top-K)
-  const int32_t* pl = MODE == 1 ? pool + (size_t)qi[0] * (size_t)(n_items >> 3) : nullptr;
+  const int32_t* pl = MODE != 0 ? pool + (size_t)qi[0] * (size_t)(n_items >> 3) : nullptr;
 
   constexpr int kTilesPerWave = tiles_per_wave<MODE, KF>();
   constexpr int kPrefetch = prefetch_tiles<KF>();
@@ -212,7 +215,7 @@ __global__ __launch_bounds__(256) void k_index_score_decode(
 #pragma unroll
   for (int it = 0; it < kTilesPerWave; ++it) {
     const int64_t item = wave_base + (int64_t)it * kTilePos + col;
-    blk[it] = (MODE == 1 && item < n_items) ? pl[item >> 3] : -1;
+    blk[it] = (MODE != 0 && item < n_items) ? pl[item >> 3] : -1;
   }
   // A tile is loaded where some query of the group sees the position.
   auto position_of = [&](int it, bool& ok) __attribute__((always_inline)) -> int64_t {
@@ -563,23 +566,30 @@ hipError_t launch_decode(int mode, const uint8_t* q_idx, const float* w, const u
   return hipGetLastError();
 }
 
+// From this many queries on, a block-list re-scoring uses 8 tiles per wave.
+constexpr int kManyQueries = 512;
+
 hipError_t launch_rescore_blocks(const uint8_t* q_idx, const float* w, const uint8_t* keys,
                                  const uint8_t* scales, const int32_t* n_vis, const int32_t* blocks,
                                  int n_blocks, int B, int T, int64_t n_cap, float* vals,
                                  hipStream_t st) {
   const int64_t n_items = (int64_t)n_blocks * kBlock;
-  if (scales) {
-    const int64_t per_wg = items_per_wg<1, 1>();
-    hipLaunchKernelGGL((k_index_score_decode<1, 1, 1>),
-                       dim3((unsigned)((n_items + per_wg - 1) / per_wg), (unsigned)(B * T)),
-                       dim3(256), 0, st, q_idx, w, keys, scales, n_vis, blocks, T, n_cap, n_items,
-                       vals, nullptr);
+  const int Q = B * T;
+  auto go = [&](auto mode_c, auto kf_c) {
+    constexpr int M = decltype(mode_c)::value, K = decltype(kf_c)::value;
+    const int64_t per_wg = items_per_wg<M, K>();
+    hipLaunchKernelGGL((k_index_score_decode<M, K, 1>),
+                       dim3((unsigned)((n_items + per_wg - 1) / per_wg), (unsigned)Q), dim3(256),
+                       0, st, q_idx, w, keys, scales, n_vis, blocks, T, n_cap, n_items, vals,
+                       nullptr);
+  };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  if (Q >= kManyQueries) {
+    if (scales) go(I2{}, I1{}); else go(I2{}, I0{});
   } else {
-    const int64_t per_wg = items_per_wg<1, 0>();
-    hipLaunchKernelGGL((k_index_score_decode<1, 0, 1>),
-                       dim3((unsigned)((n_items + per_wg - 1) / per_wg), (unsigned)(B * T)),
-                       dim3(256), 0, st, q_idx, w, keys, nullptr, n_vis, blocks, T, n_cap, n_items,
-                       vals, nullptr);
+    if (scales) go(I1{}, I1{}); else go(I1{}, I0{});
   }
   return hipGetLastError();
 }

@@ -63,10 +63,11 @@ class LayerGroup:
     def __init__(self, kind, B, T, n_cap, device="cuda", keep_scores=False, fused_topk="auto"):
         """fused_topk: a group without a pool takes its Full layer's Top-K from
         the fused csa2_index_topk (no score rows written) instead of a scan
-        followed by csa2_topk. "auto" does so for decode-shaped steps (T < 64)
-        over at least 262,144 positions, where the score rows saved outweigh
-        re-scoring 4,096 positions per query (measured on MI355X: c4 +4%; c1
-        and the 4,096-query prefill chunk 3% slower fused)."""
+        followed by csa2_topk. "auto" does so for prefill chunks (T >= 64) and
+        for decode steps over at least 262,144 positions, where the score rows
+        saved outweigh re-scoring 4,096 positions per query (measured on
+        MI355X: the 4,096-query prefill chunk +4%, c4 +4%; c1, 65,536 entries,
+        3% slower fused)."""
         self.sched = schedule(kind)
         self.B, self.T, self.n_cap = B, T, n_cap
         dev = torch.device(device)
@@ -74,7 +75,7 @@ class LayerGroup:
         n_blk = (n_cap + BLOCK - 1) // BLOCK
         need_pool = any(m == REINDEX for m, _ in self.sched)
         if fused_topk == "auto":
-            fused_topk = T < 64 and n_cap >= (1 << 18)
+            fused_topk = T >= 64 or n_cap >= (1 << 18)
         self.fused = bool(fused_topk) and not need_pool and not keep_scores
         # Block maxima come with the scan and drive the hierarchical selections.
         # A group with a pool writes no full score rows: its Full layer

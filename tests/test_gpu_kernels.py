@@ -501,7 +501,8 @@ def test_multi_token_decode_shares_keys(T, kf):
 
 
 @pytest.mark.parametrize("B,T,n_cap,kf", [(2, 1, 40003, 0), (2, 3, 200003, 0), (1, 70, 30011, 0),
-                                          (2, 1, 9000, 0), (2, 1, 100003, 1), (1, 5, 50001, 1)])
+                                          (2, 1, 9000, 0), (2, 1, 100003, 1), (1, 5, 50001, 1),
+                                          (1, 520, 20011, 0), (2, 300, 17011, 1)])
 def test_index_topk_fused_equals_scan_then_topk(B, T, n_cap, kf):
     """csa2_index_topk writes no score row (block maxima, the 512 best blocks
     re-scored) yet must give byte for byte the Top-512 of csa2_index_score(FULL)
