@@ -29,6 +29,7 @@ CSA2_OK, CSA2_EINVAL, CSA2_EUNSUPPORTED, CSA2_EWORKSPACE, CSA2_EHIP = 0, -1, -2,
 IDX_HEADS, IDX_DIM, HEADS, DIM = 32, 128, 64, 512
 ROW_BYTES, TOPK, POOL_BLOCKS, BLOCK, POOL_CAND, WINDOW = 288, 512, 2048, 8, 16384, 128
 IDX_FP4_CODE_BYTES, IDX_FP4_SCALES = 64, 4
+INDEX_TOPK_MAX_CAP = 1 << 20        # longest context csa2_index_topk serves
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB = None

@@ -15,7 +15,7 @@ arithmetic runs in the library's kernels.
 
 import torch
 
-from . import (CSA2_FULL, CSA2_REINDEX, CSA2_REUSE, CSA2_OP_BUILD_POOL, CSA2_OP_INDEX_TOPK,
+from . import (INDEX_TOPK_MAX_CAP, CSA2_FULL, CSA2_REINDEX, CSA2_REUSE, CSA2_OP_BUILD_POOL, CSA2_OP_INDEX_TOPK,
                CSA2_OP_SPARSE_ATTN, CSA2_OP_TOPK, POOL_BLOCKS, POOL_CAND, TOPK, HEADS, DIM, BLOCK,
                csa2_build_pool, csa2_index_score, csa2_index_score_fp4k, csa2_index_topk,
                csa2_quantize_kv, csa2_sparse_attn, csa2_topk, csa2_workspace_bytes)
@@ -52,6 +52,13 @@ def index_score(mode, q_idx, w, keys, n_vis, pool, scores, bmax=None, stream=Non
         csa2_index_score(mode, q_idx, w, keys, n_vis, pool, scores, bmax, stream=stream)
 
 
+def fused_topk_auto(T, n_cap):
+    """Whether a group without a pool takes the fused scan + Top-K by default:
+    prefill chunks and decode over at least 262,144 positions, within the
+    context the fused entry point serves."""
+    return (T >= 64 or n_cap >= (1 << 18)) and n_cap <= INDEX_TOPK_MAX_CAP
+
+
 def visible_entries(t, m):
     """Complete compressed entries visible at token t: floor((t + 1) / m)."""
     return (t + 1) // m
@@ -75,7 +82,7 @@ class LayerGroup:
         n_blk = (n_cap + BLOCK - 1) // BLOCK
         need_pool = any(m == REINDEX for m, _ in self.sched)
         if fused_topk == "auto":
-            fused_topk = T >= 64 or n_cap >= (1 << 18)
+            fused_topk = fused_topk_auto(T, n_cap)
         self.fused = bool(fused_topk) and not need_pool and not keep_scores
         # Block maxima come with the scan and drive the hierarchical selections.
         # A group with a pool writes no full score rows: its Full layer
