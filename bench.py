@@ -105,8 +105,12 @@ def step_algorithmic_bytes(w, n_keys, index_k="fp8"):
 
 
 def source_sha(path):
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """Hash of a kernel source's code: `//` comments and blank lines are left
+    out, so a comment edit does not void counters taken on the same code."""
+    import re
+    with open(path, encoding="utf-8") as f:
+        lines = [re.sub(r"//.*$", "", ln).rstrip() for ln in f.read().splitlines()]
+    return hashlib.sha256("\n".join(ln for ln in lines if ln.strip()).encode()).hexdigest()[:16]
 
 
 def read_traffic(n_launch_bytes):

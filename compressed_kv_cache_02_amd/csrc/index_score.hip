@@ -17,6 +17,14 @@
 // position; the epilogue applies ReLU and the head weights and adds the other
 // half with one cross-half shuffle. The scan is HBM-bound (64 FLOP per byte);
 // the MFMA only keeps the 4096 MACs per key off the vector ALU.
+//
+// Variants of the same kernel (one instruction sequence per score, so every
+// variant produces the same bits for a position): FP4 indexer keys (E2M1 codes
+// with one E8M0 scale per 32 channels) through the scaled FP8 x FP4 MFMA; NQ
+// query tokens of one sequence per wave sharing each key tile; and scores of
+// per-query block lists (the Reindex pool, or the 512 best blocks that a fused
+// Top-K re-scores). The prefill shape further down shares key chunks among 32
+// queries through LDS.
 #include <type_traits>
 
 #include "device_common.hpp"
