@@ -12,16 +12,16 @@ idempotent).
     layers hold their source's indices; attention outputs are finite.
 
 Workloads: Full decode, 32 x 65,536 entries; the decoder group at 1,048,576
-positions, batch 8; a Full prefill chunk of 4,096 queries over 131,072-133,120
-entries; the encoder group with write path and outliers at 524,288 entries,
-batch 64."""
+positions, batch 8 (also with FP4 indexer keys); a Full prefill chunk of 4,096
+queries over 131,072-133,120 entries; the encoder group with write path and
+outliers at 524,288 entries, batch 64."""
 
 import numpy as np
 import pytest
 import torch
 
 import compressed_kv_cache_02_amd as C
-from compressed_kv_cache_02_amd.group import LayerGroup, visible_entries
+from compressed_kv_cache_02_amd.group import LayerGroup, index_score, visible_entries
 import synth
 from synth.configs import WORKLOADS, make_inputs
 from tests.group_check import check_queries
@@ -36,10 +36,18 @@ def _stage(*a):
     print("[gpu-fullsize]", *a, flush=True)
 
 
-def setup(w, seed=0, write_path=True):
+def setup(w, seed=0, write_path=True, index_k="fp8"):
     """Inputs, the packed cache built by the write-path kernel, and the
-    per-step write (one new row per sequence into the newest slot)."""
-    inp = make_inputs(w, DEV, seed=seed)
+    per-step write (one new row per sequence into the newest slot). With FP4
+    indexer keys, inp["keys"] is the device-quantised (codes, scales) pair."""
+    inp = make_inputs(w, DEV, seed=seed, index_k=index_k)
+    if index_k == "fp4":
+        codes = torch.empty((w.B, w.n_cap, 64), dtype=torch.uint8, device=DEV)
+        scales = torch.empty((w.B, w.n_cap, 4), dtype=torch.uint8, device=DEV)
+        C.csa2_quantize_index_k(inp["k_bf16"].reshape(w.B * w.n_cap, 128), None, codes, scales)
+        inp["keys"] = (codes, scales)
+    else:
+        inp["keys"] = inp["k_idx"]
     B, n_cap, m = w.B, w.n_cap, w.m
     cache = torch.empty((B, n_cap, 288), dtype=torch.uint8, device=DEV)
     cs_all = torch.from_numpy(C.csa2_rope_table(np.arange(n_cap, dtype=np.int64) * m)).to(DEV)
@@ -65,7 +73,7 @@ def run_graph_step(w, inp, cache, write, replays=2):
     g = LayerGroup(w.kind, w.B, w.T, w.n_cap, device=DEV)
 
     def step():
-        g.step(inp["k_idx"], cache, n_vis, inp["q_pos"], inp["swa_pos0"], inp["q_idx"], inp["w"],
+        g.step(inp["keys"], cache, n_vis, inp["q_pos"], inp["swa_pos0"], inp["q_idx"], inp["w"],
                inp["q"], inp["swa"], write=write)
 
     side = torch.cuda.Stream()
@@ -159,8 +167,8 @@ def fused_scores(w, g, inp, n_vis):
     selection against."""
     li = [i for i, (mode, _) in enumerate(g.sched) if mode == "F"][0]
     scores = torch.empty((w.B, w.T, w.n_cap), dtype=torch.float32, device=DEV)
-    C.csa2_index_score(C.CSA2_FULL, inp["q_idx"][li], inp["w"][li], inp["k_idx"], n_vis, None,
-                       scores, g.bmax)
+    index_score(C.CSA2_FULL, inp["q_idx"][li], inp["w"][li], inp["keys"], n_vis, None, scores,
+                g.bmax)
     torch.cuda.synchronize()
     return scores
 
@@ -215,12 +223,13 @@ CASES = {
 }
 
 
-@pytest.mark.parametrize("name", ["c1", "c2", "c3", "c4"])
-def test_full_size_workload(name):
+@pytest.mark.parametrize("name,index_k", [("c1", "fp8"), ("c2", "fp8"), ("c3", "fp8"),
+                                          ("c4", "fp8"), ("c2", "fp4")])
+def test_full_size_workload(name, index_k):
     w = WORKLOADS[name]
     seed = 0
-    _stage(name, "inputs")
-    inp, cache, write = setup(w, seed, write_path=(w.kind != "full" or w.T == 1))
+    _stage(name, index_k, "inputs")
+    inp, cache, write = setup(w, seed, write_path=(w.kind != "full" or w.T == 1), index_k=index_k)
     _stage(name, "graph step")
     g, n_vis = run_graph_step(w, inp, cache, write)
     _stage(name, "properties of every query")
