@@ -181,6 +181,9 @@ int csa2_index_score_fp4k(int mode, const uint8_t* q_idx, const float* w, const 
     return CSA2_EINVAL;
   if (!scores && (mode != CSA2_FULL || !bmax)) return CSA2_EINVAL;
   if (mode == CSA2_REINDEX && (!aligned16(pool) || bmax)) return CSA2_EINVAL;
+  if (mode == CSA2_FULL && T >= 64)
+    return status_of(csa2::launch_index_score_prefill_fp4k(q_idx, w, k_codes, k_scales, n_vis, B, T,
+                                                           n_cap, scores, bmax, as_stream(stream)));
   return status_of(csa2::launch_index_score_decode_fp4k(mode, q_idx, w, k_codes, k_scales, n_vis,
                                                         pool, B, T, n_cap, scores, bmax,
                                                         as_stream(stream)));
@@ -203,7 +206,10 @@ int csa2_index_topk(const uint8_t* q_idx, const float* w, const uint8_t* k_idx,
   float* scores = n_cap <= CSA2_POOL_CAND ? ws_at<float>(ws, l.scores) : nullptr;
   float* bmax = scores ? nullptr : ws_at<float>(ws, l.bmax);
   hipError_t e;
-  if (k_scales)
+  if (k_scales && T >= 64)
+    e = csa2::launch_index_score_prefill_fp4k(q_idx, w, k_idx, k_scales, n_vis, B, T, n_cap, scores,
+                                              bmax, st);
+  else if (k_scales)
     e = csa2::launch_index_score_decode_fp4k(CSA2_FULL, q_idx, w, k_idx, k_scales, n_vis, nullptr,
                                              B, T, n_cap, scores, bmax, st);
   else if (T >= 64)

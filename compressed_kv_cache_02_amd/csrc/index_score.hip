@@ -106,6 +106,14 @@ __device__ __forceinline__ void lds_dma16(const uint4* src, uint4* dst) {
                "global_load_lds_dwordx4 %1, off\n\ts_mov_b32 m0, %0"
                : "=&s"(saved) : "v"(src), "s"(lds_addr) : "memory");
 }
+// The same for one 4-byte word per lane (64 consecutive words at `dst`).
+__device__ __forceinline__ void lds_dma4(const uint32_t* src, uint32_t* dst) {
+  const uint32_t lds_addr = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint32_t*)dst;
+  uint32_t saved;
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\t"
+               "global_load_lds_dword %1, off\n\ts_mov_b32 m0, %0"
+               : "=&s"(saved) : "v"(src), "s"(lds_addr) : "memory");
+}
 __device__ __forceinline__ void wait_lds_dma() {
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
@@ -332,12 +340,24 @@ constexpr int kPfPieces = kPfChunk * (kIdxDim / 16);      // 2048 16-byte pieces
 constexpr int kPfLoads = kPfPieces / kPfThreads;            // 4 per thread
 static_assert(kPfPieces % kPfThreads == 0, "a chunk is a whole number of loads per thread");
 
-template <bool BMAX>
+// FP4 keys (KF = 1): a chunk holds 256 x 64 bytes of codes (4 pieces per key,
+// piece j of row r at slot 4r + (j ^ ((r/8) & 3))) and the keys' 4-byte scale
+// words; the B operand of MFMA j is code piece 2j + h with scale byte 2j + h,
+// as in the decode-shaped scan (reading of the scaled FP8 x FP4 operand order),
+// so both give the same bits. The scale word rides in the FP4 operand's four
+// unused registers.
+constexpr int kPfPieces4 = kPfChunk * (kIdxDim / 2 / 16);   // 1024 code pieces
+constexpr int kPfLoads4 = kPfPieces4 / kPfThreads;           // 2 per thread
+static_assert(kPfChunk % 64 == 0 && kPfChunk / 64 <= kPfWaves, "one scale word per lane");
+
+template <bool BMAX, int KF>
 __global__ __launch_bounds__(kPfThreads) void k_index_score_prefill(
     const uint8_t* __restrict__ q_idx, const float* __restrict__ w,
-    const uint8_t* __restrict__ k_idx, const int32_t* __restrict__ n_vis, int T, int64_t n_cap,
+    const uint8_t* __restrict__ k_idx, const uint8_t* __restrict__ k_scales,
+    const int32_t* __restrict__ n_vis, int T, int64_t n_cap,
     int n_kb, int n_qb, float* __restrict__ scores, float* __restrict__ bmax) {
-  __shared__ uint4 lds[2][kPfPieces];
+  __shared__ uint4 lds[2][KF ? kPfPieces4 : kPfPieces];
+  __shared__ uint32_t lsc[2][KF ? kPfChunk : 1];
   const int kb = blockIdx.x % n_kb;
   const int rest = blockIdx.x / n_kb;
   const int qb = rest % n_qb;
@@ -365,9 +385,9 @@ __global__ __launch_bounds__(kPfThreads) void k_index_score_prefill(
     nv[q] = tq[q] < T ? v : 0;
     nv_max = nv[q] > nv_max ? nv[q] : nv_max;
     const uint4* q4 = reinterpret_cast<const uint4*>(q_idx + qi * (kIdxHeads * kIdxDim) +
-                                                     col * kIdxDim + half * 64);
-    a0[q] = as_v8i(q4[0], q4[1]);
-    a1[q] = as_v8i(q4[2], q4[3]);
+                                                     col * kIdxDim);
+    a0[q] = KF ? as_v8i(q4[half], q4[2 + half]) : as_v8i(q4[4 * half], q4[4 * half + 1]);
+    a1[q] = KF ? as_v8i(q4[4 + half], q4[6 + half]) : as_v8i(q4[4 * half + 2], q4[4 * half + 3]);
 #pragma unroll
     for (int r = 0; r < 16; ++r) wr[q][r] = w[qi * kIdxHeads + acc32_row(lane, r)];
   }
@@ -376,23 +396,45 @@ __global__ __launch_bounds__(kPfThreads) void k_index_score_prefill(
   int64_t span = n_cap - key0;
   span = span < kPfKeysPerWG ? span : kPfKeysPerWG;
   const int n_chunks = (int)((span + kPfChunk - 1) / kPfChunk);
-  const uint8_t* kseq = k_idx + (size_t)b * (size_t)n_cap * kIdxDim;
+  constexpr int kKeyBytes = KF ? kIdxDim / 2 : kIdxDim;
+  const uint8_t* kseq = k_idx + (size_t)b * (size_t)n_cap * kKeyBytes;
+  const uint32_t* sseq = KF ? reinterpret_cast<const uint32_t*>(k_scales) + (size_t)b * (size_t)n_cap
+                            : nullptr;
 
   // K rows of chunk c go straight from global memory into LDS buffer `buf`
   // (no registers on the way): LDS slot s = row*8 + j holds piece
-  // j ^ ((row/8) & 7) of the chunk's row `row`. Each wave's load fills 64
-  // consecutive slots. Rows past n_cap repeat the last row; their scores are
-  // masked to -inf.
+  // j ^ ((row/8) & 7) of the chunk's row `row` (FP4: slot row*4 + j holds
+  // piece j ^ ((row/8) & 3), and waves 0..3 copy the scale words). Each wave's
+  // load fills 64 consecutive slots. Rows past n_cap repeat the last row; their
+  // scores are masked to -inf.
   auto load_chunk = [&](int c, int buf) __attribute__((always_inline)) {
+    if constexpr (KF == 1) {
 #pragma unroll
-    for (int i = 0; i < kPfLoads; ++i) {
-      const int slot = tid + i * kPfThreads;
-      const int row = slot >> 3;
-      int64_t krow = key0 + (int64_t)c * kPfChunk + row;
-      krow = krow < n_cap ? krow : n_cap - 1;
-      const int piece = (slot & 7) ^ ((row >> 3) & 7);
-      lds_dma16(reinterpret_cast<const uint4*>(kseq + krow * kIdxDim) + piece,
-                &lds[buf][i * kPfThreads + wave * 64]);
+      for (int i = 0; i < kPfLoads4; ++i) {
+        const int slot = tid + i * kPfThreads;
+        const int row = slot >> 2;
+        int64_t krow = key0 + (int64_t)c * kPfChunk + row;
+        krow = krow < n_cap ? krow : n_cap - 1;
+        const int piece = (slot & 3) ^ ((row >> 3) & 3);
+        lds_dma16(reinterpret_cast<const uint4*>(kseq + krow * kKeyBytes) + piece,
+                  &lds[buf][i * kPfThreads + wave * 64]);
+      }
+      if (wave < kPfChunk / 64) {
+        int64_t krow = key0 + (int64_t)c * kPfChunk + tid;
+        krow = krow < n_cap ? krow : n_cap - 1;
+        lds_dma4(sseq + krow, &lsc[buf][wave * 64]);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < kPfLoads; ++i) {
+        const int slot = tid + i * kPfThreads;
+        const int row = slot >> 3;
+        int64_t krow = key0 + (int64_t)c * kPfChunk + row;
+        krow = krow < n_cap ? krow : n_cap - 1;
+        const int piece = (slot & 7) ^ ((row >> 3) & 7);
+        lds_dma16(reinterpret_cast<const uint4*>(kseq + krow * kIdxDim) + piece,
+                  &lds[buf][i * kPfThreads + wave * 64]);
+      }
     }
   };
 
@@ -400,16 +442,32 @@ __global__ __launch_bounds__(kPfThreads) void k_index_score_prefill(
   // 8*col + tt of the chunk, so over the chunk's 8 tiles a lane sees one whole
   // block of 8 positions (its block maximum stays in a register). Pieces are
   // swizzled by row/8, which differs across 8 consecutive lanes.
+  int cur_buf = 0;     // the buffer load_b reads (FP4 scale words)
   auto load_b = [&](const uint4* L, int tt, v8i& b0, v8i& b1) __attribute__((always_inline)) {
     const int row = kBlock * col + tt;
-    const int sw = col & 7;
-    b0 = as_v8i(L[row * 8 + ((half * 4 + 0) ^ sw)], L[row * 8 + ((half * 4 + 1) ^ sw)]);
-    b1 = as_v8i(L[row * 8 + ((half * 4 + 2) ^ sw)], L[row * 8 + ((half * 4 + 3) ^ sw)]);
+    if constexpr (KF == 1) {
+      const int sw = col & 3;
+      const uint4 c0 = L[row * 4 + (half ^ sw)], c1 = L[row * 4 + ((2 + half) ^ sw)];
+      const uint32_t scw = lsc[cur_buf][row] >> (8 * half);
+      b0 = fp4_operand(c0);
+      b1 = fp4_operand(c1);
+      b0[4] = (int)scw;            // scale bytes 0 and 2: MFMA 0 and MFMA 1
+      b1[4] = (int)(scw >> 16);
+    } else {
+      const int sw = col & 7;
+      b0 = as_v8i(L[row * 8 + ((half * 4 + 0) ^ sw)], L[row * 8 + ((half * 4 + 1) ^ sw)]);
+      b1 = as_v8i(L[row * 8 + ((half * 4 + 2) ^ sw)], L[row * 8 + ((half * 4 + 3) ^ sw)]);
+    }
   };
   auto mfma2 = [&](int q, const v8i& b0, const v8i& b1) __attribute__((always_inline)) -> v16f {
     v16f acc = {};
-    acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a0[q], b0, acc, 0, 0, 0, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a1[q], b1, acc, 0, 0, 0, 0, 0, 0);
+    if constexpr (KF == 1) {
+      acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a0[q], b0, acc, 0, 4, 0, 127, 0, b0[4]);
+      acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a1[q], b1, acc, 0, 4, 0, 127, 0, b1[4]);
+    } else {
+      acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a0[q], b0, acc, 0, 0, 0, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a1[q], b1, acc, 0, 0, 0, 0, 0, 0);
+    }
     return acc;
   };
   constexpr int kPairs = kPfQPerWave / 2;
@@ -483,6 +541,7 @@ __global__ __launch_bounds__(kPfThreads) void k_index_score_prefill(
   for (int c = 0; c < n_chunks; ++c) {
     if (c + 1 < n_chunks) load_chunk(c + 1, (c + 1) & 1);
     const uint4* L = lds[c & 1];
+    cur_buf = c & 1;
     const int64_t chunk0 = key0 + (int64_t)c * kPfChunk;
     if (wave_full && chunk0 + kPfChunk <= n_cap && chunk0 < nv_max) {
       // Whole chunk in range: a flat software pipeline over the 32 (tile,
@@ -619,20 +678,34 @@ hipError_t launch_index_score_decode_fp4k(int mode, const uint8_t* q_idx, const 
                           bmax, st);
 }
 
-hipError_t launch_index_score_prefill(const uint8_t* q_idx, const float* w, const uint8_t* k_idx,
-                                      const int32_t* n_vis, int B, int T, int64_t n_cap,
-                                      float* scores, float* bmax, hipStream_t st) {
+template <int KF>
+hipError_t launch_prefill(const uint8_t* q_idx, const float* w, const uint8_t* keys,
+                          const uint8_t* scales, const int32_t* n_vis, int B, int T, int64_t n_cap,
+                          float* scores, float* bmax, hipStream_t st) {
   const int n_kb = (int)((n_cap + kPfKeysPerWG - 1) / kPfKeysPerWG);
   const int n_qb = (T + kPfQueries - 1) / kPfQueries;
   const int64_t grid = (int64_t)n_kb * n_qb * B;
   if (bmax) {
-    hipLaunchKernelGGL(k_index_score_prefill<true>, dim3((unsigned)grid), dim3(kPfThreads), 0, st,
-                       q_idx, w, k_idx, n_vis, T, n_cap, n_kb, n_qb, scores, bmax);
+    hipLaunchKernelGGL((k_index_score_prefill<true, KF>), dim3((unsigned)grid), dim3(kPfThreads), 0,
+                       st, q_idx, w, keys, scales, n_vis, T, n_cap, n_kb, n_qb, scores, bmax);
   } else {
-    hipLaunchKernelGGL(k_index_score_prefill<false>, dim3((unsigned)grid), dim3(kPfThreads), 0, st,
-                       q_idx, w, k_idx, n_vis, T, n_cap, n_kb, n_qb, scores, bmax);
+    hipLaunchKernelGGL((k_index_score_prefill<false, KF>), dim3((unsigned)grid), dim3(kPfThreads),
+                       0, st, q_idx, w, keys, scales, n_vis, T, n_cap, n_kb, n_qb, scores, bmax);
   }
   return hipGetLastError();
+}
+
+hipError_t launch_index_score_prefill(const uint8_t* q_idx, const float* w, const uint8_t* k_idx,
+                                      const int32_t* n_vis, int B, int T, int64_t n_cap,
+                                      float* scores, float* bmax, hipStream_t st) {
+  return launch_prefill<0>(q_idx, w, k_idx, nullptr, n_vis, B, T, n_cap, scores, bmax, st);
+}
+
+hipError_t launch_index_score_prefill_fp4k(const uint8_t* q_idx, const float* w,
+                                           const uint8_t* k_codes, const uint8_t* k_scales,
+                                           const int32_t* n_vis, int B, int T, int64_t n_cap,
+                                           float* scores, float* bmax, hipStream_t st) {
+  return launch_prefill<1>(q_idx, w, k_codes, k_scales, n_vis, B, T, n_cap, scores, bmax, st);
 }
 
 }  // namespace csa2

@@ -35,6 +35,12 @@ hipError_t launch_index_score_decode_fp4k(int mode, const uint8_t* q_idx, const 
                                           int64_t n_cap, float* scores, float* bmax,
                                           hipStream_t st);
 
+// Prefill-shaped scan over FP4 indexer keys (the scaled FP8 x FP4 contraction).
+hipError_t launch_index_score_prefill_fp4k(const uint8_t* q_idx, const float* w,
+                                           const uint8_t* k_codes, const uint8_t* k_scales,
+                                           const int32_t* n_vis, int B, int T, int64_t n_cap,
+                                           float* scores, float* bmax, hipStream_t st);
+
 // Prefill-shaped scan: a dense FP8 contraction over (queries x 32 heads) x positions.
 hipError_t launch_index_score_prefill(const uint8_t* q_idx, const float* w, const uint8_t* k_idx,
                                       const int32_t* n_vis, int B, int T, int64_t n_cap,

@@ -143,7 +143,7 @@ int csa2_quantize_kv(const void* kv_bf16, const float* cos_sin, const int64_t* d
  * score is the same bits whatever T is: in FULL mode the query tokens of a
  * sequence (T >= 2, e.g. speculative decode) share each key read, four at a time
  * below T = 64 and in tiles of 32 from T = 64 on (csa2_index_score_fp4k: two at
- * a time, for every T).
+ * a time below T = 64).
  * Errors: CSA2_EINVAL for REUSE, NULL/misaligned pointers, REINDEX without a
  * pool, nothing to write, B < 1, T < 1, n_cap < 1 or n_cap >= 2^31. */
 int csa2_index_score(int mode, const uint8_t* q_idx, const float* w, const uint8_t* k_idx,
@@ -205,8 +205,9 @@ int csa2_quantize_index_k(const void* k_bf16, const int64_t* dst_slot, int64_t n
  * place of k_idx; the key value of channel c is E2M1(code) * 2^(scale - 127),
  * multiplied exactly with the E4M3 query by the scaled FP8 x FP4 matrix
  * instruction. Modes, outputs, masking and errors are those of
- * csa2_index_score; every T runs the decode-shaped scan, and REINDEX
- * re-scores a position to the same bits as FULL. `k_scales` needs only 4-byte
+ * csa2_index_score (FULL from T = 64 on runs the prefill-shaped contraction,
+ * below it the decode shape with two query tokens per key read); every shape,
+ * and REINDEX, gives a position the same bits. `k_scales` needs only 4-byte
  * alignment. */
 int csa2_index_score_fp4k(int mode, const uint8_t* q_idx, const float* w, const uint8_t* k_codes,
                           const uint8_t* k_scales, const int32_t* n_vis, const int32_t* pool,

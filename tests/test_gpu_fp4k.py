@@ -225,3 +225,40 @@ def test_decoder_group_fp4_keys():
                                    log=lambda *a: None)
     print("attention checked:", checked, "near-tie swaps:", swaps)
     assert checked >= 7 * B - 2 * swaps
+
+
+@pytest.mark.parametrize("B,T,n_cap", [(2, 77, 10003), (1, 64, 4096), (1, 130, 300)])
+def test_index_score_fp4k_prefill_shape(B, T, n_cap):
+    """From 64 queries per sequence the FP4-key scan is the prefill-shaped
+    contraction (key chunks shared through LDS); its scores and block maxima
+    must equal, bit for bit, single-query (decode-shaped) calls, and lie within
+    the score bound of the oracle. T and n_cap are ragged."""
+    _stage("index_score_fp4k prefill", B, T, n_cap)
+    q, w, codes, scales, oc, os_ = _inputs(B, T, n_cap, 31 + n_cap)
+    rng = np.random.default_rng(T)
+    nv = np.minimum(n_cap, (np.arange(T) + n_cap - T + 1)[None, :].repeat(B, 0)).astype(np.int32)
+    nv[0, 0] = 0
+    nv[0, 1] = 1
+    nv[-1, 2] = 33
+    nv[-1, -1] = n_cap
+    nv[0, 3:8] = rng.integers(0, n_cap + 1, 5)
+    n_vis = torch.from_numpy(nv).to(DEV)
+    nb = (n_cap + 7) // 8
+    scores = torch.empty((B, T, n_cap), dtype=torch.float32, device=DEV)
+    bmax = torch.empty((B, T, nb), dtype=torch.float32, device=DEV)
+    C.csa2_index_score_fp4k(C.CSA2_FULL, q, w, codes, scales, n_vis, None, scores, bmax)
+    one_s = torch.empty((1, 1, n_cap), dtype=torch.float32, device=DEV)
+    one_b = torch.empty((1, 1, nb), dtype=torch.float32, device=DEV)
+    sn, bn, qn, wn = to_np(scores), to_np(bmax), to_np(q), to_np(w)
+    for b in range(B):
+        for t in range(T):
+            C.csa2_index_score_fp4k(C.CSA2_FULL, q[b:b + 1, t:t + 1], w[b:b + 1, t:t + 1],
+                                    codes[b:b + 1], scales[b:b + 1], n_vis[b:b + 1, t:t + 1].clone(),
+                                    None, one_s, one_b)
+            assert np.array_equal(to_np(one_s)[0, 0].view(np.uint32), sn[b, t].view(np.uint32)), (b, t)
+            assert np.array_equal(to_np(one_b)[0, 0].view(np.uint32), bn[b, t].view(np.uint32)), (b, t)
+    for b in range(B):
+        for t in sorted({0, 1, 2, T // 2, T - 1}):
+            ref = OI.index_scores(qn[b, t], wn[b, t], oc[b], nv[b, t], k_scales=os_[b])
+            assert_scores_close(sn[b, t], ref, _bound(qn[b, t], wn[b, t], oc[b], os_[b]),
+                                "b%d t%d" % (b, t))
