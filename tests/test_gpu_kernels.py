@@ -241,6 +241,11 @@ def _score_sets(n, seed):
     x[::7] = 0.0
     x[3::7] = -0.0
     yield "signed", x
+    # the best items all in the last threads (a floor taken from other threads is low)
+    yield "ascending", (np.arange(n) / n).astype(np.float32)
+    x = np.full(n, -3.0, dtype=np.float32)           # a few peaks over a constant
+    x[rng.choice(n, n // 40, replace=False)] = rng.standard_normal(n // 40).astype(np.float32)
+    yield "peaks", x
 
 
 @pytest.mark.parametrize("n_cap", [100, 512, 513, 5000, 16384, 16385, 70001, 1100000])
