@@ -411,22 +411,26 @@ def main():
     ms = el * 1e3 / args.steps
     qps = B * T * args.steps / el
     scan_bytes = scan_algorithmic_bytes(B, T, n_keys, args.index_k)
-    if prefill:
+    kf = 1 if args.index_k == "fp4" else 0
+    mfma_scan = T >= (C.PREFILL_MIN_T_FP4 if kf else C.PREFILL_MIN_T_FP8)
+    if mfma_scan:
         # a dense FP8 contraction: 32 heads x 128 channels x 2 FLOP per visible pair
         scan_flop = 8192 * n_vis_total
         achieved = scan_flop / (scan_ms * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": FP8_MFMA_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / FP8_MFMA_PEAK_TFLOPS, 4),
-                "traffic": None, "kernel": "k_index_score_prefill",
+                "traffic": None,
+                "kernel": "k_index_score_prefill<true, %d>" % kf,   # the group always keeps block maxima
                 "kernel_ms": round(scan_ms, 4), "algorithmic_flop_per_launch": scan_flop}
-        step_roof = None
     else:
         achieved = scan_bytes / (scan_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": read_traffic(scan_bytes),
-                "kernel": "%s<0, %d, 1>" % (SCAN_KERNEL, 1 if args.index_k == "fp4" else 0),
+                "kernel": "%s<0, %d, %d>" % (SCAN_KERNEL, kf, 1 if T == 1 else (2 if kf else 4)),
                 "kernel_ms": round(scan_ms, 4), "algorithmic_bytes_per_launch": scan_bytes}
+    step_roof = None
+    if not prefill:
         step_bytes = step_algorithmic_bytes(w, n_keys, args.index_k)
         step_roof = {"algorithmic_bytes": step_bytes,
                      "achieved_GBps": round(step_bytes / (ms * 1e-3) / 1e9, 1),

@@ -30,6 +30,8 @@ IDX_HEADS, IDX_DIM, HEADS, DIM = 32, 128, 64, 512
 ROW_BYTES, TOPK, POOL_BLOCKS, BLOCK, POOL_CAND, WINDOW = 288, 512, 2048, 8, 16384, 128
 IDX_FP4_CODE_BYTES, IDX_FP4_SCALES = 64, 4
 INDEX_TOPK_MAX_CAP = 1 << 20        # longest context csa2_index_topk serves
+# query tokens per sequence from which a Full scan is prefill-shaped (E4M3 / FP4 keys)
+PREFILL_MIN_T_FP8, PREFILL_MIN_T_FP4 = 5, 11
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB = None

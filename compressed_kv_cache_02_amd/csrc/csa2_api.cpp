@@ -130,7 +130,7 @@ int csa2_index_score(int mode, const uint8_t* q_idx, const float* w, const uint8
   if (!scores && (mode != CSA2_FULL || !bmax)) return CSA2_EINVAL;   // something to write
   if (mode == CSA2_REINDEX && (!aligned16(pool) || bmax)) return CSA2_EINVAL;
   hipError_t e;
-  if (mode == CSA2_FULL && T >= 64)
+  if (mode == CSA2_FULL && T >= CSA2_PREFILL_MIN_T_FP8)
     e = csa2::launch_index_score_prefill(q_idx, w, k_idx, n_vis, B, T, n_cap, scores, bmax,
                                          as_stream(stream));
   else
@@ -181,7 +181,7 @@ int csa2_index_score_fp4k(int mode, const uint8_t* q_idx, const float* w, const 
     return CSA2_EINVAL;
   if (!scores && (mode != CSA2_FULL || !bmax)) return CSA2_EINVAL;
   if (mode == CSA2_REINDEX && (!aligned16(pool) || bmax)) return CSA2_EINVAL;
-  if (mode == CSA2_FULL && T >= 64)
+  if (mode == CSA2_FULL && T >= CSA2_PREFILL_MIN_T_FP4)
     return status_of(csa2::launch_index_score_prefill_fp4k(q_idx, w, k_codes, k_scales, n_vis, B, T,
                                                            n_cap, scores, bmax, as_stream(stream)));
   return status_of(csa2::launch_index_score_decode_fp4k(mode, q_idx, w, k_codes, k_scales, n_vis,
@@ -206,13 +206,13 @@ int csa2_index_topk(const uint8_t* q_idx, const float* w, const uint8_t* k_idx,
   float* scores = n_cap <= CSA2_POOL_CAND ? ws_at<float>(ws, l.scores) : nullptr;
   float* bmax = scores ? nullptr : ws_at<float>(ws, l.bmax);
   hipError_t e;
-  if (k_scales && T >= 64)
+  if (k_scales && T >= CSA2_PREFILL_MIN_T_FP4)
     e = csa2::launch_index_score_prefill_fp4k(q_idx, w, k_idx, k_scales, n_vis, B, T, n_cap, scores,
                                               bmax, st);
   else if (k_scales)
     e = csa2::launch_index_score_decode_fp4k(CSA2_FULL, q_idx, w, k_idx, k_scales, n_vis, nullptr,
                                              B, T, n_cap, scores, bmax, st);
-  else if (T >= 64)
+  else if (T >= CSA2_PREFILL_MIN_T_FP8)
     e = csa2::launch_index_score_prefill(q_idx, w, k_idx, n_vis, B, T, n_cap, scores, bmax, st);
   else
     e = csa2::launch_index_score_decode(CSA2_FULL, q_idx, w, k_idx, n_vis, nullptr, B, T, n_cap,

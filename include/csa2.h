@@ -61,6 +61,14 @@ extern "C" {
 #define CSA2_MAX_WIDTH 8192          /* widest row of the write-path helpers */
 #define CSA2_IDX_FP4_CODE_BYTES 64   /* FP4 indexer key: 128 E2M1 codes ... */
 #define CSA2_IDX_FP4_SCALES 4        /* ... and one E8M0 scale per 32 channels */
+/* Query tokens per sequence from which a FULL scan (csa2_index_score,
+ * csa2_index_score_fp4k, csa2_index_topk) takes the prefill-shaped contraction:
+ * 32 queries x 4,096 keys per work-group, keys staged through LDS. Below it the
+ * decode shape scores the tokens in groups (4 per wave with E4M3 keys, 2 with
+ * FP4 keys) that each read the keys again. The switch points are where the two
+ * shapes cost the same (1M-position sequences). */
+#define CSA2_PREFILL_MIN_T_FP8 5
+#define CSA2_PREFILL_MIN_T_FP4 11
 
 /* Layer mode ([P1] §二 mode table; [P2] 黑科技之二; [P3] 第二刀, Fig. 4):
  *   FULL    -- own indexer keys, own scores over every visible position, own Top-K;
@@ -142,8 +150,8 @@ int csa2_quantize_kv(const void* kv_bf16, const float* cos_sin, const int64_t* d
  * Products are exact; sums are float32 (MFMA accumulation order). Every query's
  * score is the same bits whatever T is: in FULL mode the query tokens of a
  * sequence (T >= 2, e.g. speculative decode) share each key read, four at a time
- * below T = 64 and in tiles of 32 from T = 64 on (csa2_index_score_fp4k: two at
- * a time below T = 64).
+ * below T = CSA2_PREFILL_MIN_T_FP8 and in tiles of 32 from there on
+ * (csa2_index_score_fp4k: two at a time below T = CSA2_PREFILL_MIN_T_FP4).
  * Errors: CSA2_EINVAL for REUSE, NULL/misaligned pointers, REINDEX without a
  * pool, nothing to write, B < 1, T < 1, n_cap < 1 or n_cap >= 2^31. */
 int csa2_index_score(int mode, const uint8_t* q_idx, const float* w, const uint8_t* k_idx,
@@ -205,8 +213,9 @@ int csa2_quantize_index_k(const void* k_bf16, const int64_t* dst_slot, int64_t n
  * place of k_idx; the key value of channel c is E2M1(code) * 2^(scale - 127),
  * multiplied exactly with the E4M3 query by the scaled FP8 x FP4 matrix
  * instruction. Modes, outputs, masking and errors are those of
- * csa2_index_score (FULL from T = 64 on runs the prefill-shaped contraction,
- * below it the decode shape with two query tokens per key read); every shape,
+ * csa2_index_score (FULL from T = CSA2_PREFILL_MIN_T_FP4 on runs the
+ * prefill-shaped contraction, below it the decode shape with two query tokens
+ * per key read); every shape,
  * and REINDEX, gives a position the same bits. `k_scales` needs only 4-byte
  * alignment. */
 int csa2_index_score_fp4k(int mode, const uint8_t* q_idx, const float* w, const uint8_t* k_codes,

@@ -212,3 +212,20 @@ def test_group_fuses_only_within_the_fused_entry_limit():
     assert fused_topk_auto(4096, 133120) and fused_topk_auto(64, 1000)
     assert not fused_topk_auto(1, 65536) and not fused_topk_auto(63, 200000)
     assert not fused_topk_auto(1, (1 << 20) + 8) and not fused_topk_auto(4096, 1 << 21)
+
+
+def test_binding_constants_match_the_header():
+    """Every numeric #define of csa2.h that the binding mirrors has the same value."""
+    import re
+    text = open(os.path.join(ROOT, "include", "csa2.h")).read()
+    defs = {m.group(1): int(m.group(2)) for m in
+            re.finditer(r"^#define CSA2_([A-Z0-9_]+)\s+(-?\d+)\b", text, re.M)}
+    mirrored = {"IDX_FP4_CODE_BYTES": C.IDX_FP4_CODE_BYTES, "IDX_FP4_SCALES": C.IDX_FP4_SCALES,
+                "INDEX_TOPK_MAX_CAP": C.INDEX_TOPK_MAX_CAP,
+                "PREFILL_MIN_T_FP8": C.PREFILL_MIN_T_FP8, "PREFILL_MIN_T_FP4": C.PREFILL_MIN_T_FP4}
+    for k, v in mirrored.items():
+        assert defs[k] == v, k
+    for k in ("IDX_HEADS", "IDX_DIM", "HEADS", "DIM", "ROW_BYTES", "TOPK", "POOL_BLOCKS", "BLOCK",
+              "POOL_CAND", "WINDOW"):
+        if k in defs:
+            assert defs[k] == getattr(C, k), k
