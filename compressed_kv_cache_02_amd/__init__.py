@@ -31,7 +31,7 @@ ROW_BYTES, TOPK, POOL_BLOCKS, BLOCK, POOL_CAND, WINDOW = 288, 512, 2048, 8, 1638
 IDX_FP4_CODE_BYTES, IDX_FP4_SCALES = 64, 4
 INDEX_TOPK_MAX_CAP = 1 << 20        # longest context csa2_index_topk serves
 # query tokens per sequence from which a Full scan is prefill-shaped (E4M3 / FP4 keys)
-PREFILL_MIN_T_FP8, PREFILL_MIN_T_FP4 = 5, 11
+PREFILL_MIN_T_FP8, PREFILL_MIN_T_FP4 = 4, 5
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB = None

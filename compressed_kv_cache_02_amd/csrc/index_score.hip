@@ -333,6 +333,7 @@ constexpr int kPfQPerWave = 4;
 constexpr int kPfWaves = 8;
 constexpr int kPfThreads = kPfWaves * 64;
 constexpr int kPfQueries = kPfQPerWave * kPfWaves;   // 32
+constexpr int kPfSmallTile = 16;                     // 2 queries per wave up to this T
 constexpr int kPfChunk = 256;                        // keys per LDS chunk
 constexpr int kPfChunksPerWG = 16;
 constexpr int kPfKeysPerWG = kPfChunk * kPfChunksPerWG;   // 4096
@@ -350,7 +351,7 @@ constexpr int kPfPieces4 = kPfChunk * (kIdxDim / 2 / 16);   // 1024 code pieces
 constexpr int kPfLoads4 = kPfPieces4 / kPfThreads;           // 2 per thread
 static_assert(kPfChunk % 64 == 0 && kPfChunk / 64 <= kPfWaves, "one scale word per lane");
 
-template <bool BMAX, int KF>
+template <bool BMAX, int KF, int QPW>
 __global__ __launch_bounds__(kPfThreads) void k_index_score_prefill(
     const uint8_t* __restrict__ q_idx, const float* __restrict__ w,
     const uint8_t* __restrict__ k_idx, const uint8_t* __restrict__ k_scales,
@@ -370,14 +371,14 @@ __global__ __launch_bounds__(kPfThreads) void k_index_score_prefill(
   const int64_t n_blk = (n_cap + kBlock - 1) / kBlock;
 
   // this wave's queries (clamped for loads; stores check t < T)
-  int tq[kPfQPerWave];
-  int64_t nv[kPfQPerWave];
-  v8i a0[kPfQPerWave], a1[kPfQPerWave];
-  float wr[kPfQPerWave][16];
+  int tq[QPW];
+  int64_t nv[QPW];
+  v8i a0[QPW], a1[QPW];
+  float wr[QPW][16];
   int64_t nv_max = 0;
 #pragma unroll
-  for (int q = 0; q < kPfQPerWave; ++q) {
-    tq[q] = qb * kPfQueries + wave * kPfQPerWave + q;
+  for (int q = 0; q < QPW; ++q) {
+    tq[q] = qb * (QPW * kPfWaves) + wave * QPW + q;
     const int tc = tq[q] < T ? tq[q] : T - 1;
     const size_t qi = (size_t)b * T + tc;
     int64_t v = n_vis[qi];
@@ -470,7 +471,7 @@ __global__ __launch_bounds__(kPfThreads) void k_index_score_prefill(
     }
     return acc;
   };
-  constexpr int kPairs = kPfQPerWave / 2;
+  constexpr int kPairs = QPW / 2;
   // Lanes 0..31 take query 2qp, lanes 32..63 query 2qp+1 of each pair after
   // the swap; bm[qp] is the running maximum of this lane's block.
   float bm[kPairs];
@@ -532,7 +533,7 @@ __global__ __launch_bounds__(kPfThreads) void k_index_score_prefill(
       if (BMAX) bm[qp] = fmaxf(bm[qp], s);
     }
   };
-  const bool wave_full = tq[kPfQPerWave - 1] < T;
+  const bool wave_full = tq[QPW - 1] < T;
 
   constexpr int kTiles = kPfChunk / kTilePos;     // 8
   load_chunk(0, 0);
@@ -550,29 +551,29 @@ __global__ __launch_bounds__(kPfThreads) void k_index_score_prefill(
       // the current one has been issued.
       v8i bb0, bb1;
       v16f acc[2];
-      float p[kPfQPerWave];
+      float p[QPW];
       chunk_setup(chunk0);
       load_b(L, 0, bb0, bb1);
       acc[0] = mfma2(0, bb0, bb1);
 #pragma unroll
-      for (int j = 0; j < kTiles * kPfQPerWave; ++j) {
-        const int t = j / kPfQPerWave, q = j % kPfQPerWave;
-        if (j + 1 < kTiles * kPfQPerWave) {
-          const int t1 = (j + 1) / kPfQPerWave, q1 = (j + 1) % kPfQPerWave;
+      for (int j = 0; j < kTiles * QPW; ++j) {
+        const int t = j / QPW, q = j % QPW;
+        if (j + 1 < kTiles * QPW) {
+          const int t1 = (j + 1) / QPW, q1 = (j + 1) % QPW;
           // raised wave priority while issuing: the matrix core is kept fed
           // when the other wave on this SIMD is also ready to issue
           __builtin_amdgcn_s_setprio(1);
           acc[(j + 1) & 1] = mfma2(q1, bb0, bb1);
           __builtin_amdgcn_s_setprio(0);
           // the last MFMA on tile t1 is issued: fetch the next tile's operand
-          if (q1 == kPfQPerWave - 1 && t1 + 1 < kTiles) load_b(L, t1 + 1, bb0, bb1);
+          if (q1 == QPW - 1 && t1 + 1 < kTiles) load_b(L, t1 + 1, bb0, bb1);
         }
         // Keep this order: the epilogue below reads results issued one step
         // earlier, so it runs on the vector ALU while the matrix core works
         // on the MFMAs just issued.
         __builtin_amdgcn_sched_barrier(0);
         p[q] = weighted_relu_sum(acc[j & 1], wr[q]);
-        if (q == kPfQPerWave - 1) emit_fast(t, p);
+        if (q == QPW - 1) emit_fast(t, p);
         __builtin_amdgcn_sched_barrier(0);
       }
       emit_bmax(chunk0);
@@ -584,15 +585,15 @@ __global__ __launch_bounds__(kPfThreads) void k_index_score_prefill(
       const bool any_vis = chunk0 < nv_max;
 #pragma unroll 1
       for (int tt = 0; tt < kTiles; ++tt) {
-        float p[kPfQPerWave];
+        float p[QPW];
         if (any_vis) {
           v8i b0, b1;
           load_b(L, tt, b0, b1);
 #pragma unroll
-          for (int q = 0; q < kPfQPerWave; ++q) p[q] = weighted_relu_sum(mfma2(q, b0, b1), wr[q]);
+          for (int q = 0; q < QPW; ++q) p[q] = weighted_relu_sum(mfma2(q, b0, b1), wr[q]);
         } else {
 #pragma unroll
-          for (int q = 0; q < kPfQPerWave; ++q) p[q] = 0.0f;
+          for (int q = 0; q < QPW; ++q) p[q] = 0.0f;
         }
         emit(chunk0, tt, p);
       }
@@ -683,15 +684,26 @@ hipError_t launch_prefill(const uint8_t* q_idx, const float* w, const uint8_t* k
                           const uint8_t* scales, const int32_t* n_vis, int B, int T, int64_t n_cap,
                           float* scores, float* bmax, hipStream_t st) {
   const int n_kb = (int)((n_cap + kPfKeysPerWG - 1) / kPfKeysPerWG);
-  const int n_qb = (T + kPfQueries - 1) / kPfQueries;
-  const int64_t grid = (int64_t)n_kb * n_qb * B;
-  if (bmax) {
-    hipLaunchKernelGGL((k_index_score_prefill<true, KF>), dim3((unsigned)grid), dim3(kPfThreads), 0,
-                       st, q_idx, w, keys, scales, n_vis, T, n_cap, n_kb, n_qb, scores, bmax);
-  } else {
-    hipLaunchKernelGGL((k_index_score_prefill<false, KF>), dim3((unsigned)grid), dim3(kPfThreads),
-                       0, st, q_idx, w, keys, scales, n_vis, T, n_cap, n_kb, n_qb, scores, bmax);
-  }
+  auto go = [&](auto qpw_c) {
+    constexpr int QPW = decltype(qpw_c)::value;
+    constexpr int kQ = QPW * kPfWaves;
+    const int n_qb = (T + kQ - 1) / kQ;
+    const int64_t grid = (int64_t)n_kb * n_qb * B;
+    if (bmax)
+      hipLaunchKernelGGL((k_index_score_prefill<true, KF, QPW>), dim3((unsigned)grid),
+                         dim3(kPfThreads), 0, st, q_idx, w, keys, scales, n_vis, T, n_cap, n_kb,
+                         n_qb, scores, bmax);
+    else
+      hipLaunchKernelGGL((k_index_score_prefill<false, KF, QPW>), dim3((unsigned)grid),
+                         dim3(kPfThreads), 0, st, q_idx, w, keys, scales, n_vis, T, n_cap, n_kb,
+                         n_qb, scores, bmax);
+  };
+  // up to 16 query tokens per sequence: 16-query tiles (2 per wave) keep twice
+  // as many waves busy as half-empty 32-query tiles
+  if (T <= kPfSmallTile)
+    go(std::integral_constant<int, 2>{});
+  else
+    go(std::integral_constant<int, kPfQPerWave>{});
   return hipGetLastError();
 }
 

@@ -63,12 +63,13 @@ extern "C" {
 #define CSA2_IDX_FP4_SCALES 4        /* ... and one E8M0 scale per 32 channels */
 /* Query tokens per sequence from which a FULL scan (csa2_index_score,
  * csa2_index_score_fp4k, csa2_index_topk) takes the prefill-shaped contraction:
- * 32 queries x 4,096 keys per work-group, keys staged through LDS. Below it the
+ * 16 (up to 16 tokens) or 32 queries x 4,096 keys per work-group, keys staged
+ * through LDS. Below it the
  * decode shape scores the tokens in groups (4 per wave with E4M3 keys, 2 with
  * FP4 keys) that each read the keys again. The switch points are where the two
  * shapes cost the same (1M-position sequences). */
-#define CSA2_PREFILL_MIN_T_FP8 5
-#define CSA2_PREFILL_MIN_T_FP4 11
+#define CSA2_PREFILL_MIN_T_FP8 4
+#define CSA2_PREFILL_MIN_T_FP4 5
 
 /* Layer mode ([P1] §二 mode table; [P2] 黑科技之二; [P3] 第二刀, Fig. 4):
  *   FULL    -- own indexer keys, own scores over every visible position, own Top-K;
@@ -150,7 +151,7 @@ int csa2_quantize_kv(const void* kv_bf16, const float* cos_sin, const int64_t* d
  * Products are exact; sums are float32 (MFMA accumulation order). Every query's
  * score is the same bits whatever T is: in FULL mode the query tokens of a
  * sequence (T >= 2, e.g. speculative decode) share each key read, four at a time
- * below T = CSA2_PREFILL_MIN_T_FP8 and in tiles of 32 from there on
+ * below T = CSA2_PREFILL_MIN_T_FP8 and in tiles of 16 or 32 from there on
  * (csa2_index_score_fp4k: two at a time below T = CSA2_PREFILL_MIN_T_FP4).
  * Errors: CSA2_EINVAL for REUSE, NULL/misaligned pointers, REINDEX without a
  * pool, nothing to write, B < 1, T < 1, n_cap < 1 or n_cap >= 2^31. */

@@ -229,7 +229,7 @@ def test_decoder_group_fp4_keys():
 
 @pytest.mark.parametrize("B,T,n_cap", [(2, 77, 10003), (1, 64, 4096), (1, 130, 300)])
 def test_index_score_fp4k_prefill_shape(B, T, n_cap):
-    """From 11 queries per sequence the FP4-key scan is the prefill-shaped
+    """From 5 queries per sequence the FP4-key scan is the prefill-shaped
     contraction (key chunks shared through LDS); its scores and block maxima
     must equal, bit for bit, single-query (decode-shaped) calls, and lie within
     the score bound of the oracle. T and n_cap are ragged."""

@@ -444,13 +444,14 @@ def test_sparse_attn_scale_and_outliers():
         assert_attn_close(o[b, 0], ref, "outliers b%d" % b)
 
 
-@pytest.mark.parametrize("T,kf", [(2, 0), (4, 0), (5, 0), (8, 0), (33, 0), (4, 1), (7, 1), (10, 1),
-                                  (11, 1), (33, 1)])
+@pytest.mark.parametrize("T,kf", [(2, 0), (3, 0), (4, 0), (5, 0), (16, 0), (17, 0), (33, 0),
+                                  (2, 1), (3, 1), (4, 1), (5, 1), (7, 1), (16, 1), (17, 1), (33, 1)])
 def test_multi_token_decode_shares_keys(T, kf):
     """Several query tokens of one sequence (Full mode) are scored in groups
-    that share each key tile (4 or 2 per wave below the prefill threshold, 32
-    per work-group from it on: T = 4 | 5 with E4M3 keys, 10 | 11 with FP4 keys
-    straddle it); every query's scores and block maxima must equal, bit for
+    that share each key tile (4 or 2 per wave below the prefill threshold, 16
+    or 32 per work-group from it on: T = 3 | 4 with E4M3 keys and 4 | 5 with
+    FP4 keys straddle it, 16 | 17 the tile sizes); every query's scores and
+    block maxima must equal, bit for
     bit, those of a single-query call, and lie within the score bound of the
     oracle. Visibility is causal per query (T and n_cap ragged)."""
     from oracle import mxfp4 as OM
@@ -511,7 +512,8 @@ def test_multi_token_decode_shares_keys(T, kf):
 @pytest.mark.parametrize("B,T,n_cap,kf", [(2, 1, 40003, 0), (2, 3, 200003, 0), (1, 70, 30011, 0),
                                           (2, 1, 9000, 0), (2, 1, 100003, 1), (1, 5, 50001, 1),
                                           (1, 520, 20011, 0), (2, 300, 17011, 1),
-                                          (2, 6, 40009, 0), (2, 12, 40009, 1)])
+                                          (2, 6, 40009, 0), (2, 12, 40009, 1), (2, 3, 60013, 1),
+                                          (1, 17, 30011, 1)])
 def test_index_topk_fused_equals_scan_then_topk(B, T, n_cap, kf):
     """csa2_index_topk writes no score row (block maxima, the 512 best blocks
     re-scored) yet must give byte for byte the Top-512 of csa2_index_score(FULL)
