@@ -612,6 +612,11 @@ __global__ __launch_bounds__(kPfThreads) void k_index_score_prefill(
 template <int KF>
 constexpr int decode_group() { return KF ? 2 : 4; }
 
+// From this many queries on, the Reindex scan over the pool uses 8 tiles per
+// wave (2 below it, where more work-groups per query pay off): 1-2% faster
+// steps at 64-256 queries of 1M-entry contexts.
+constexpr int kPoolManyQueries = 64;
+
 template <int KF>
 hipError_t launch_decode(int mode, const uint8_t* q_idx, const float* w, const uint8_t* keys,
                          const uint8_t* scales, const int32_t* n_vis, const int32_t* pool, int B,
@@ -619,7 +624,12 @@ hipError_t launch_decode(int mode, const uint8_t* q_idx, const float* w, const u
   const int64_t n_items = mode == 0 ? n_cap : (int64_t)kPoolCand;
   const int64_t per_wg = mode == 0 ? items_per_wg<0, KF>() : items_per_wg<1, KF>();
   const unsigned gx = (unsigned)((n_items + per_wg - 1) / per_wg);
-  if (mode == 1) {
+  if (mode == 1 && B * T >= kPoolManyQueries) {
+    constexpr int64_t per2 = items_per_wg<2, KF>();
+    hipLaunchKernelGGL((k_index_score_decode<2, KF, 1>), dim3((unsigned)((n_items + per2 - 1) / per2),
+                       (unsigned)(B * T)), dim3(256), 0, st, q_idx, w, keys, scales, n_vis, pool, T,
+                       n_cap, n_items, scores, nullptr);
+  } else if (mode == 1) {
     hipLaunchKernelGGL((k_index_score_decode<1, KF, 1>), dim3(gx, (unsigned)(B * T)), dim3(256), 0,
                        st, q_idx, w, keys, scales, n_vis, pool, T, n_cap, n_items, scores, nullptr);
   } else if (T == 1) {

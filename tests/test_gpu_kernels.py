@@ -228,6 +228,67 @@ def test_index_score_reindex():
             assert_scores_close(sn[b, t], ref, bound, "reindex b%d t%d" % (b, t))
 
 
+@pytest.mark.parametrize("kf", [0, 1])
+def test_index_score_reindex_many_queries(kf):
+    """From 64 queries on the Reindex scan over the pool runs 8 tiles per wave
+    (2 below); every query's 16,384 scores must equal, bit for bit, those of a
+    single-query call, and one query is checked against the oracle."""
+    from oracle import mxfp4 as OM
+    B, T, n_cap = 2, 40, 20011
+    _stage("index_score reindex many queries", kf)
+    q, w, k = _idx_inputs(B, T, n_cap, 23)
+    if kf:
+        kb = synth.normal_rows(B * n_cap, 128, DEV, 23, "rk4").to(torch.bfloat16)
+        codes = torch.empty((B, n_cap, 64), dtype=torch.uint8, device=DEV)
+        scl = torch.empty((B, n_cap, 4), dtype=torch.uint8, device=DEV)
+        C.csa2_quantize_index_k(kb, None, codes, scl)
+
+        def score(qq, ww, kk, ss, nv, pl, out):
+            C.csa2_index_score_fp4k(C.CSA2_REINDEX, qq, ww, kk, ss, nv, pl, out, None)
+        keys, kscl = codes, scl
+    else:
+        def score(qq, ww, kk, ss, nv, pl, out):
+            C.csa2_index_score(C.CSA2_REINDEX, qq, ww, kk, nv, pl, out, None)
+        keys, kscl = k, None
+    rng = np.random.default_rng(23)
+    nb = (n_cap + 7) // 8
+    pool = np.full((B, T, 2048), -1, dtype=np.int32)
+    for b in range(B):
+        for t in range(T):
+            cnt = 2048 if t % 7 else int(rng.integers(1, 2048))
+            pool[b, t, :cnt] = np.sort(rng.choice(nb, cnt, replace=False))
+    nv = np.minimum(n_cap, n_cap - T + 1 + np.arange(T))[None, :].repeat(B, 0).astype(np.int32)
+    nv[1, 3] = 9
+    n_vis, pool_d = torch.from_numpy(nv).to(DEV), torch.from_numpy(pool).to(DEV)
+    scores = torch.empty((B, T, 16384), dtype=torch.float32, device=DEV)
+    score(q, w, keys, kscl, n_vis, pool_d, scores)
+    one = torch.empty((1, 1, 16384), dtype=torch.float32, device=DEV)
+    sn = to_np(scores)
+    for b in range(B):
+        for t in range(T):
+            score(q[b:b + 1, t:t + 1], w[b:b + 1, t:t + 1], keys[b:b + 1],
+                  None if kscl is None else kscl[b:b + 1], n_vis[b:b + 1, t:t + 1].clone(),
+                  pool_d[b:b + 1, t:t + 1].clone(), one)
+            assert np.array_equal(to_np(one)[0, 0].view(np.uint32), sn[b, t].view(np.uint32)), (b, t)
+    b, t = 1, 3
+    p = pool[b, t]
+    pos = (np.maximum(p, 0)[:, None] * 8 + np.arange(8)[None, :]).reshape(-1)
+    qn, wn = to_np(q), to_np(w)
+    if kf:
+        oc, osc = OM.quantize_index_keys(kb.float().cpu().numpy())
+        oc, osc = oc.reshape(B, n_cap, 64), osc.reshape(B, n_cap, 4)
+        ref = OI.index_scores(qn[b, t], wn[b, t], oc[b], nv[b, t], positions=pos, k_scales=osc[b])
+        qa = np.abs(OF.e4m3_decode(qn[b, t].reshape(32, 128)))
+        ka = np.abs(OM.dequantize_index_keys(oc[b][np.minimum(pos, n_cap - 1)],
+                                             osc[b][np.minimum(pos, n_cap - 1)]))
+        bound = 160.0 * 2.0 ** -24 * (ka @ qa.T) @ np.abs(wn[b, t].astype(np.float64))
+    else:
+        ref = OI.index_scores(qn[b, t], wn[b, t], to_np(k)[b], nv[b, t], positions=pos)
+        bound = score_bound(qn[b, t], wn[b, t], to_np(k)[b][np.minimum(pos, n_cap - 1)])
+    ref[np.repeat(p < 0, 8)] = -np.inf
+    assert_scores_close(sn[b, t], ref, bound, "reindex many b%d t%d" % (b, t))
+
+
 # -------------------------------------------------------------- selection -----
 
 def _score_sets(n, seed):
