@@ -69,6 +69,11 @@ def parse():
                    help="groups without a pool (c1, c3, c4) take the Full layer's Top-K from "
                         "the fused scan + Top-K entry point (no score rows written): 'auto' "
                         "where it is faster (prefill chunks, decode over >= 262,144 positions)")
+    p.add_argument("--rotate", type=int, default=None,
+                   help="copies of the indexer keys and the main cache that consecutive timed "
+                        "steps cycle through, so that a working set the 256 MB MALL could hold "
+                        "is read from HBM (default: 3 for decode workloads whose keys fit in "
+                        "1 GiB, else 1)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--graph", dest="graph", action="store_true", default=True,
                    help="replay each step segment as a HIP graph (default)")
@@ -308,10 +313,19 @@ def main():
     g = LayerGroup(w.kind, B, T, n_cap, device=dev, fused_topk=fused)
     stream = torch.cuda.current_stream()
 
-    args_rest = (keys, cache, n_vis, inp["q_pos"], inp["swa_pos0"], inp["q_idx"],
-                 inp["w"], inp["q"], inp["swa"])
+    # copies of the keys and the main cache that consecutive steps cycle through
+    key_total = B * n_cap * key_bytes(args.index_k)
+    rot = args.rotate if args.rotate is not None else (3 if not prefill and key_total < (1 << 30)
+                                                        else 1)
+    rot = max(1, rot)
+    sets = [(keys, cache)]
+    for _ in range(rot - 1):
+        kc = tuple(t.clone() for t in keys) if isinstance(keys, tuple) else keys.clone()
+        sets.append((kc, cache.clone()))
+    cur = [0]
 
     def seg_write():
+        keys, cache = sets[cur[0]]
         if full_write is not None:
             tok_main, tok_k, win, entry, kentry, wslot = full_write
             C.csa2_compress_tokens(tok_main, m, entry)
@@ -326,15 +340,17 @@ def main():
             g.write(cache, write)
 
     def seg_scan():
-        g.scan(keys, n_vis, inp["q_idx"], inp["w"])
+        g.scan(sets[cur[0]][0], n_vis, inp["q_idx"], inp["w"])
 
     def seg_scan_timed():
         # the Full scan alone, for its roofline (with --fused-topk the step runs
         # it inside csa2_index_topk, writing block maxima only, as here)
-        g.scan_only(keys, n_vis, inp["q_idx"], inp["w"])
+        g.scan_only(sets[cur[0]][0], n_vis, inp["q_idx"], inp["w"])
 
     def seg_rest():
-        g.rest(*args_rest)
+        keys, cache = sets[cur[0]]
+        g.rest(keys, cache, n_vis, inp["q_pos"], inp["swa_pos0"], inp["q_idx"], inp["w"], inp["q"],
+               inp["swa"])
 
     log("cache built; warmup %d steps" % args.warmup)
     for _ in range(max(1, args.warmup)):
@@ -362,20 +378,26 @@ def main():
             step()
         torch.cuda.current_stream().wait_stream(side)
         torch.cuda.synchronize()
-        step_graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(step_graph):
-            step()
+        step_graphs = []
+        for ci in range(rot):
+            cur[0] = ci
+            gr = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gr):
+                step()
+            step_graphs.append(gr)
         scan_graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(scan_graph):
-            for _ in range(R):
+            for r in range(R):
+                cur[0] = r % rot
                 seg_scan_timed()
+        cur[0] = 0
         torch.cuda.synchronize()
-        for _ in range(max(1, args.warmup)):
-            step_graph.replay()
+        for i in range(max(1, args.warmup)):
+            step_graphs[i % rot].replay()
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for i in range(args.steps):
-            step_graph.replay()
+            step_graphs[i % rot].replay()
         torch.cuda.synchronize()
         el = time.perf_counter() - t0
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -393,6 +415,7 @@ def main():
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for i in range(args.steps):
+            cur[0] = i % rot
             seg_write()
             ev[i][0].record(stream)
             seg_scan()
@@ -463,6 +486,7 @@ def main():
                            "full": "m tokens compressed on device, main row RoPE + FP4, indexer "
                                    "key appended, window row appended in every layer"}[args.write_path],
             "fused_topk": bool(g.fused),
+            "cache_copies": rot,
             "index_k": {"fp8": "FP8 E4M3 indexer keys (128 B)",
                         "fp4": "FP4 E2M1 indexer keys + E8M0 per 32 channels (68 B)"}[args.index_k],
             "timing": ("one HIP graph per step; scan timed over back-to-back launches"
