@@ -12,9 +12,13 @@ idempotent).
     layers hold their source's indices; attention outputs are finite.
 
 Workloads: Full decode, 32 x 65,536 entries; the decoder group at 1,048,576
-positions, batch 8 (also with FP4 indexer keys); a Full prefill chunk of 4,096
-queries over 131,072-133,120 entries; the encoder group with write path and
-outliers at 524,288 entries, batch 64."""
+positions, batch 8 (also with FP4 indexer keys, and with 16 or 5 query tokens
+per sequence: the prefill-shaped scan with 16-query tiles and, at 128 queries,
+the 8-tile Reindex scan); a Full prefill chunk of 4,096 queries over
+131,072-133,120 entries; the encoder group with write path and outliers at
+524,288 entries, batch 64."""
+
+import dataclasses
 
 import numpy as np
 import pytest
@@ -223,20 +227,26 @@ CASES = {
 }
 
 
-@pytest.mark.parametrize("name,index_k", [("c1", "fp8"), ("c2", "fp8"), ("c3", "fp8"),
-                                          ("c4", "fp8"), ("c2", "fp4")])
-def test_full_size_workload(name, index_k):
+@pytest.mark.parametrize("name,index_k,spec", [("c1", "fp8", 1), ("c2", "fp8", 1), ("c3", "fp8", 1),
+                                               ("c4", "fp8", 1), ("c2", "fp4", 1), ("c2", "fp8", 16),
+                                               ("c2", "fp4", 5)])
+def test_full_size_workload(name, index_k, spec):
     w = WORKLOADS[name]
+    cases = CASES[name]
+    if spec > 1:
+        # several query tokens per sequence (speculative decode), as bench.py --spec-tokens
+        w = dataclasses.replace(w, T=spec, first_q=w.first_q - (spec - 1))
+        cases = [(0, 0), (0, spec - 1), (w.B - 1, spec // 2)]
     seed = 0
-    _stage(name, index_k, "inputs")
+    _stage(name, index_k, "T=%d" % w.T, "inputs")
     inp, cache, write = setup(w, seed, write_path=(w.kind != "full" or w.T == 1), index_k=index_k)
     _stage(name, "graph step")
     g, n_vis = run_graph_step(w, inp, cache, write)
     _stage(name, "properties of every query")
     check_properties(w, g, n_vis, inp)
     _stage(name, "oracle on sampled queries")
-    checked, swaps = check_queries(w, inp, g, CASES[name], regen_cache(w, inp, seed),
+    checked, swaps = check_queries(w, inp, g, cases, regen_cache(w, inp, seed),
                                    log=lambda s: _stage(name, s))
     _stage(name, "attention checked %d, near-tie swaps %d" % (checked, swaps))
     # a differing index set spoils at most its own layer and the Reuse layers after it
-    assert checked >= len(CASES[name]) * w.n_layers - swaps * w.n_layers
+    assert checked >= len(cases) * w.n_layers - swaps * w.n_layers
