@@ -338,18 +338,27 @@ __device__ __forceinline__ uint32_t block_prefix(uint32_t v, uint32_t* sh, uint3
 constexpr int kSelBins = 4096;       // 12-bit digits: two levels cover 24 bits
 constexpr int kSelDigit = 12;
 
-// One work-group per query: exact selection of the K best items (NT threads x
-// IPT items). Writes ids ascending to out[q * out_stride + r], -1 padded to K.
+// LDS of one selection: the radix histogram, the per-wave exchange words
+// (regions: 0-2 count/range, 0/3 levels, 4 ties, 5 output) and the result of
+// each level's threshold search.
+template <int NT>
+struct SelLds {
+  __align__(16) uint32_t lh[kSelBins];
+  uint32_t sh[6][NT / 64];
+  uint32_t res[3];
+};
+
+// The selection of query q by one work-group of NT threads: writes the ids of
+// the K best items ascending to o[0..K), -1 padded (o may point to LDS).
 template <int KIND, int NT, int IPT>
-__global__ __launch_bounds__(NT) void k_select(Src src, int K, int32_t* __restrict__ out,
-                                               int out_stride) {
+__device__ __forceinline__ void select_wg(const Src& src, int q, int K, int32_t* o,
+                                          SelLds<NT>& L) {
   static_assert(IPT <= 32, "item masks are 32-bit");
   constexpr int NW = NT / 64;
   constexpr int PER = kSelBins / NT;                 // bins per thread in the threshold search
-  __shared__ __align__(16) uint32_t lh[kSelBins];
-  __shared__ uint32_t sh[6][NW];   // regions: 0-2 count/range, 0/3 levels, 4 ties, 5 output
-  __shared__ uint32_t res[3];
-  const int q = blockIdx.x;
+  uint32_t* const lh = L.lh;
+  uint32_t (*const sh)[NW] = L.sh;
+  uint32_t* const res = L.res;
   const int t = threadIdx.x;
   const int lane = t & 63, wave = t >> 6;
   const int64_t lim = src.limit(q);
@@ -468,11 +477,39 @@ __global__ __launch_bounds__(NT) void k_select(Src src, int K, int32_t* __restri
   }
   uint32_t sel_tot;
   uint32_t rank = block_prefix<NT>(__popc(sel), sh[5], sel_tot);
-  int32_t* o = out + (size_t)q * out_stride;
 #pragma unroll
   for (int j = 0; j < IPT; ++j)
     if ((sel >> j) & 1u) o[rank++] = (int32_t)id[j];
   for (int i = (int)kk + t; i < K; i += NT) o[i] = -1;
+}
+
+// One work-group per query: exact selection of the K best items (NT threads x
+// IPT items). Writes ids ascending to out[q * out_stride + r], -1 padded to K.
+template <int KIND, int NT, int IPT>
+__global__ __launch_bounds__(NT) void k_select(Src src, int K, int32_t* __restrict__ out,
+                                               int out_stride) {
+  __shared__ SelLds<NT> L;
+  const int q = blockIdx.x;
+  select_wg<KIND, NT, IPT>(src, q, K, out + (size_t)q * out_stride, L);
+}
+
+// Two chained selections in one work-group per query: the K1 best parents
+// (super-blocks) by their values, kept in LDS, then the K2 best of their
+// children (blocks, value indexed by the child id). The same result as two
+// k_select launches, without the second launch and its load of the parents.
+template <int NT, int IPT>
+__global__ __launch_bounds__(NT) void k_select_pair(Src parents, int K1, Src children, int K2,
+                                                    int32_t* __restrict__ out, int out_stride) {
+  __shared__ SelLds<NT> L;
+  __shared__ int32_t par[kPoolBlocks];
+  const int q = blockIdx.x;
+  select_wg<kDirect, NT, IPT>(parents, q, K1, par, L);
+  __syncthreads();                 // the parents are in LDS; the exchange words are free
+  Src c = children;
+  c.sel = par;                     // read through a generic pointer: LDS
+  c.sel_stride = 0;
+  c.n_items = (int64_t)K1 * kBlock;
+  select_wg<kChild, NT, IPT>(c, q, K2, out + (size_t)q * out_stride, L);
 }
 
 // ------------------------------------------------------------ large inputs --
@@ -805,6 +842,24 @@ hipError_t run_stage(const Stage& g, int Q, int K, int32_t* out, int out_stride,
   return run_stage_k<kChild>(g.src, Q, K, out, out_stride, st);
 }
 
+// Parents (a direct stage) and children (a child stage by id) chained in one
+// work-group per query; the children's parent list is the first selection's
+// result in LDS.
+hipError_t run_pair(const Stage& parents, int K1, const Stage& children, int K2, int Q,
+                    int32_t* out, int out_stride, hipStream_t st) {
+  if (parents.kind != kDirect || children.kind != kChild || K1 > kPoolBlocks)
+    return hipErrorInvalidValue;
+  const int64_t n = parents.src.n_items > (int64_t)K1 * kBlock ? parents.src.n_items
+                                                                : (int64_t)K1 * kBlock;
+  if (n <= 4096)
+    hipLaunchKernelGGL((k_select_pair<256, 16>), dim3(Q), dim3(256), 0, st, parents.src, K1,
+                       children.src, K2, out, out_stride);
+  else
+    hipLaunchKernelGGL((k_select_pair<1024, 16>), dim3(Q), dim3(1024), 0, st, parents.src, K1,
+                       children.src, K2, out, out_stride);
+  return hipGetLastError();
+}
+
 Stage direct(const float* vals, int64_t vstride, int unit, const int32_t* n_vis, int64_t n_cap,
              int64_t n_items) {
   Stage g;
@@ -924,11 +979,11 @@ hipError_t launch_topk_full(const float* scores, const float* bmax, const int32_
   int32_t* sel_sb = at<int32_t>(ws, l.sel_a);
   int32_t* sel_blk = at<int32_t>(ws, l.sel_b);
   // best 512 super-blocks, then the best 512 of their blocks, then of their positions
+  (void)sel_sb;
   if ((e = launch_super_max(bmax, Q, n_blk, smax, st)) != hipSuccess) return e;
-  e = run_stage(direct(smax, n_sb, 64, n_vis, n_cap, n_sb), Q, kTopK, sel_sb, kTopK, st);
-  if (e != hipSuccess) return e;
-  e = run_stage(child(bmax, n_blk, 8, sel_sb, kTopK, 0, n_vis, n_cap), Q, kTopK, sel_blk, kTopK,
-                st);
+  e = run_pair(direct(smax, n_sb, 64, n_vis, n_cap, n_sb), kTopK,
+               child(bmax, n_blk, 8, nullptr, kTopK, 0, n_vis, n_cap), kTopK, Q, sel_blk, kTopK,
+               st);
   if (e != hipSuccess) return e;
   return run_stage(child(scores, n_cap, 1, sel_blk, kTopK, 0, n_vis, n_cap), Q, kTopK, out, kTopK,
                    st);
@@ -945,13 +1000,11 @@ hipError_t launch_best_blocks(const float* bmax, const int32_t* n_vis, int Q, in
   const int64_t n_sb = n_blocks(n_blk);
   if (n_sb > kOneWgMax) return hipErrorInvalidValue;
   float* smax = at<float>(ws, 0);
-  int32_t* sel_sb = at<int32_t>(ws, up((size_t)Q * n_sb * sizeof(float)));
   hipError_t e;
   if ((e = launch_super_max(bmax, Q, n_blk, smax, st)) != hipSuccess) return e;
-  e = run_stage(direct(smax, n_sb, 64, n_vis, n_cap, n_sb), Q, kTopK, sel_sb, kTopK, st);
-  if (e != hipSuccess) return e;
-  return run_stage(child(bmax, n_blk, 8, sel_sb, kTopK, 0, n_vis, n_cap), Q, kTopK, sel_blk,
-                   kTopK, st);
+  return run_pair(direct(smax, n_sb, 64, n_vis, n_cap, n_sb), kTopK,
+                  child(bmax, n_blk, 8, nullptr, kTopK, 0, n_vis, n_cap), kTopK, Q, sel_blk, kTopK,
+                  st);
 }
 
 hipError_t launch_topk_of_blocks(const float* vals, const int32_t* sel_blk, const int32_t* n_vis,
@@ -992,13 +1045,10 @@ hipError_t launch_build_pool(const float* src, int is_bmax, const int32_t* n_vis
                      at<void>(ws, l.large), st);
   // best 2,048 super-blocks, then the best 2,048 of their 16,384 blocks
   float* smax = at<float>(ws, l.smax);
-  int32_t* sel_sb = at<int32_t>(ws, l.sel_a);
   if ((e = launch_super_max(bm, Q, n_blk, smax, st)) != hipSuccess) return e;
-  e = run_stage(direct(smax, n_sb, 64, n_vis, n_cap, n_sb), Q, kPoolBlocks, sel_sb, kPoolBlocks,
-                st);
-  if (e != hipSuccess) return e;
-  return run_stage(child(bm, n_blk, 8, sel_sb, kPoolBlocks, 0, n_vis, n_cap), Q, kPoolBlocks, pool,
-                   kPoolBlocks, st);
+  return run_pair(direct(smax, n_sb, 64, n_vis, n_cap, n_sb), kPoolBlocks,
+                  child(bm, n_blk, 8, nullptr, kPoolBlocks, 0, n_vis, n_cap), kPoolBlocks, Q, pool,
+                  kPoolBlocks, st);
 }
 
 hipError_t launch_block_max(const float* scores, const int32_t* n_vis, int Q, int64_t n_cap,
