@@ -62,7 +62,8 @@ hipError_t launch_block_max(const float* scores, const int32_t* n_vis, int Q, in
 hipError_t launch_copy_i32(const int32_t* src, int32_t* dst, int64_t n, hipStream_t st);
 
 // Fused Full Top-K pieces: the best 512 blocks from block maxima (super-block
-// maxima, then two selections; workspace best_blocks_workspace_bytes), the
+// maxima, then two chained selections in one kernel; workspace
+// best_blocks_workspace_bytes), the
 // re-scoring of a per-query block list ([Q][n_blocks] block ids, -1 padded;
 // values [Q][8 * n_blocks] by item), the Top-512 of the re-scored positions, and
 // the Top-512 of a short score row (n_cap <= 16,384).

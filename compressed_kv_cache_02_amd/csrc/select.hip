@@ -922,10 +922,10 @@ hipError_t run_large(const Items& it, int Q, int K, int32_t* out, void* ws, hipS
 }
 
 // Workspace layout shared by the Full Top-K and the pool:
-//   [block maxima, when computed here][super-block maxima][parent ids Q x 2048]
-//   [block ids Q x 512][large path]
+//   [block maxima, when computed here][super-block maxima][block ids Q x 512]
+//   [large path]
 struct WsLayout {
-  size_t bmax, smax, sel_a, sel_b, large, total;
+  size_t bmax, smax, sel_b, large, total;
 };
 
 WsLayout layout(int Q, int64_t n_cap, int K) {
@@ -933,8 +933,7 @@ WsLayout layout(int Q, int64_t n_cap, int K) {
   const int64_t n_blk = n_blocks(n_cap);
   l.bmax = 0;
   l.smax = up((size_t)Q * n_blk * sizeof(float));
-  l.sel_a = l.smax + up((size_t)Q * n_blocks(n_blk) * sizeof(float));
-  l.sel_b = l.sel_a + up((size_t)Q * kPoolBlocks * sizeof(int32_t));
+  l.sel_b = l.smax + up((size_t)Q * n_blocks(n_blk) * sizeof(float));
   l.large = l.sel_b + up((size_t)Q * kTopK * sizeof(int32_t));
   const bool need_large = n_blocks(n_blk) > kOneWgMax;
   l.total = l.large + (need_large ? up((size_t)Q * sel_stride(K)) : 0);
@@ -976,10 +975,8 @@ hipError_t launch_topk_full(const float* scores, const float* bmax, const int32_
     bmax = at<float>(ws, l.bmax);
   }
   float* smax = at<float>(ws, l.smax);
-  int32_t* sel_sb = at<int32_t>(ws, l.sel_a);
   int32_t* sel_blk = at<int32_t>(ws, l.sel_b);
   // best 512 super-blocks, then the best 512 of their blocks, then of their positions
-  (void)sel_sb;
   if ((e = launch_super_max(bmax, Q, n_blk, smax, st)) != hipSuccess) return e;
   e = run_pair(direct(smax, n_sb, 64, n_vis, n_cap, n_sb), kTopK,
                child(bmax, n_blk, 8, nullptr, kTopK, 0, n_vis, n_cap), kTopK, Q, sel_blk, kTopK,
@@ -991,7 +988,7 @@ hipError_t launch_topk_full(const float* scores, const float* bmax, const int32_
 
 size_t best_blocks_workspace_bytes(int Q, int64_t n_cap) {
   const int64_t n_sb = n_blocks(n_blocks(n_cap));
-  return up((size_t)Q * n_sb * sizeof(float)) + up((size_t)Q * kTopK * sizeof(int32_t));
+  return up((size_t)Q * n_sb * sizeof(float));        // super-block maxima
 }
 
 hipError_t launch_best_blocks(const float* bmax, const int32_t* n_vis, int Q, int64_t n_cap,
