@@ -23,8 +23,8 @@
 // with one E8M0 scale per 32 channels) through the scaled FP8 x FP4 MFMA; NQ
 // query tokens of one sequence per wave sharing each key tile; and scores of
 // per-query block lists (the Reindex pool, or the 512 best blocks that a fused
-// Top-K re-scores). The prefill shape further down shares key chunks among 32
-// queries through LDS.
+// Top-K re-scores). The prefill shape further down shares key chunks among 16
+// or 32 queries through LDS.
 #include <type_traits>
 
 #include "device_common.hpp"
@@ -37,7 +37,7 @@ constexpr int kTilePos = 32;       // positions per MFMA tile
 constexpr int kWaves = 4;          // waves per work-group of the decode scan
 // MODE 0: the Full scan; MODE 1: scores of listed blocks (Reindex inside the
 // pool, or the re-scoring of a fused Top-K); MODE 2: as MODE 1, shaped for
-// hundreds of queries or more.
+// many queries (8 tiles per wave instead of 2).
 // Tiles per wave: 8 for the Full scan (long rows, many work-groups anyway);
 // 2 for a block list of a few queries, where more, shorter work-groups spread
 // the work over more of the chip; 8 again once the queries alone fill it.
@@ -319,9 +319,11 @@ __global__ __launch_bounds__(256) void k_index_score_decode(
 // dense FP8 contraction of (queries x 32 heads) x 128 against positions x 128,
 // followed by the ReLU-weighted head sum. A work-group of 8 waves takes 32
 // consecutive queries of one sequence (4 per wave, their A operands and head
-// weights held in registers) and 4,096 positions, streamed through LDS in
-// double-buffered chunks of 256 keys (32 KiB each) so every key byte read from
-// L2 feeds 32 queries. The 16-byte pieces of a key row are stored at piece
+// weights held in registers; 16 queries, 2 per wave, when a sequence has at
+// most 16, so that more waves hold real queries) and 4,096 positions, streamed
+// through LDS in double-buffered chunks of 256 keys (32 KiB each) so every key
+// byte read from L2 feeds all of the tile's queries. Waves whose queries are
+// all padding skip their MFMAs. The 16-byte pieces of a key row are stored at piece
 // index (p ^ (row & 7)), which makes the B-operand reads (8 consecutive rows
 // per lane group) and the chunk writes conflict-free. Per 32-position tile and
 // query: two MFMAs, then 16 max + 16 fma per lane; the two half-sums of a
