@@ -150,6 +150,40 @@ def _block_max_ignores_visibility(scores, n_vis):
     return pad.reshape(n_blk, I.BLOCK).max(axis=1)
 
 
+def _bf16_truncating(x):
+    u = np.asarray(x, dtype=np.float32).view(np.uint32)
+    return (u >> 16).astype(np.uint16)                      # truncation, not nearest-even
+
+
+def _reindex_ignores_visibility(pool, n_vis):
+    pool = np.asarray(pool, dtype=np.int64)
+    b = pool[pool >= 0]
+    return (b[:, None] * S.BLOCK + np.arange(S.BLOCK)[None, :]).reshape(-1)
+
+
+def _e4m3_value_no_subnormals(code):
+    code = int(code)
+    sign = -1.0 if code & 0x80 else 1.0
+    e, m = (code >> 3) & 0xF, code & 0x7
+    if e == 15 and m == 7:
+        return float("nan")
+    return sign * (1.0 + m / 8.0) * 2.0 ** (e - 7)          # exponent 0 read as normal
+
+
+_E4M3_NO_SUB = np.array([_e4m3_value_no_subnormals(c) for c in range(256)])
+
+
+def _e4m3_decode_no_subnormals(codes):
+    return _E4M3_NO_SUB[np.asarray(codes, dtype=np.uint8)]
+
+
+def _dequantize_rows_per_32(rows):
+    codes, sc = F.unpack_codes(rows)
+    v = F.e2m1_decode(codes)
+    s = F.e4m3_decode(sc)[:, ::2]                             # one scale per 32 channels
+    return v * np.repeat(s, 2 * F.GROUP, axis=1)
+
+
 # --------------------------------------------------------------- the cases --
 
 CASES = [
@@ -187,6 +221,15 @@ CASES = [
      [TR.test_mean_matches_torch_and_closed_form]),
     ("block maxima: invisible positions counted", I, "block_max", _block_max_ignores_visibility,
      [TS.test_block_max]),
+    ("compressor: bf16 by truncation", Cm, "f32_to_bf16_bits", _bf16_truncating,
+     [TR.test_bf16_rounding_matches_torch]),
+    ("reindex: positions past n_vis kept", S, "reindex_candidates", _reindex_ignores_visibility,
+     [TS.test_reindex_candidates_respect_visibility]),
+    ("e4m3 decode: subnormals read as normals", F, "e4m3_decode", _e4m3_decode_no_subnormals,
+     [TF.test_e4m3_golden_points, TF.test_e4m3_decode_matches_torch]),
+    ("main KV: one scale per 32 channels", F, "dequantize_rows", _dequantize_rows_per_32,
+     [TF.test_grid_valued_group_round_trips,
+      lambda: TF.test_quantize_is_nearest_over_whole_rows(0)]),
 ]
 
 
