@@ -184,6 +184,18 @@ def _dequantize_rows_per_32(rows):
     return v * np.repeat(s, 2 * F.GROUP, axis=1)
 
 
+def _unpack_high_nibble_first(packed):
+    packed = np.asarray(packed, dtype=np.uint8)
+    codes = np.empty((packed.shape[0], 128), dtype=np.uint8)
+    codes[:, 0::2] = packed >> 4                              # nibble order swapped
+    codes[:, 1::2] = packed & 0xF
+    return codes
+
+
+def _mx_scale_values_bias_128(codes):
+    return np.ldexp(1.0, np.asarray(codes, dtype=np.int64) - 128)
+
+
 # --------------------------------------------------------------- the cases --
 
 CASES = [
@@ -227,6 +239,14 @@ CASES = [
      [TS.test_reindex_candidates_respect_visibility]),
     ("e4m3 decode: subnormals read as normals", F, "e4m3_decode", _e4m3_decode_no_subnormals,
      [TF.test_e4m3_golden_points, TF.test_e4m3_decode_matches_torch]),
+    ("fp4 keys: high nibble read as the even channel", M, "unpack_index_codes",
+     _unpack_high_nibble_first,
+     [TM.test_layout_low_nibble_even_channel_and_scale_bytes, TM.test_grid_valued_blocks_round_trip]),
+    ("fp4 keys: E8M0 bias 128", M, "mx_scale_values", _mx_scale_values_bias_128,
+     [TM.test_grid_valued_blocks_round_trip, TM.test_dequantised_values_are_code_times_power_of_two,
+      TM.test_worked_blocks]),
+    ("fp4 keys: E2M1 ties away from zero", M, "e2m1_codes", _e2m1_ties_away,
+     [lambda: TM.test_elements_vs_exact_rationals(0), TM.test_worked_blocks]),
     ("main KV: one scale per 32 channels", F, "dequantize_rows", _dequantize_rows_per_32,
      [TF.test_grid_valued_group_round_trips,
       lambda: TF.test_quantize_is_nearest_over_whole_rows(0)]),
