@@ -134,44 +134,38 @@ def read_traffic(n_launch_bytes):
     return None
 
 
-def cpu_baseline(w, inp, seed, new_rows, budget_s=10.0, index_k="fp8", oracle_rows=None):
-    """The oracle, single-threaded, on whole queries through the whole group
-    (write-path row included), one sequence after another until about
-    `budget_s` seconds of oracle time have accumulated (at least one query).
-    Only the oracle's own run is timed, not the staging of its inputs."""
+def cpu_baseline(workers, w, inp, seed, new_rows, budget_s=10.0, index_k="fp8",
+                 oracle_rows=None):
+    """The oracle on the host cores, on whole queries through the whole group
+    (write-path row included): a sample of the workload's queries (every query
+    of a decode workload up to two per worker; 64 evenly spaced queries of a
+    prefill chunk, the first and last included), each through the whole layer
+    group. The packed main-KV rows the oracle reads are staged before any
+    timing (found by an untimed oracle pass, packed by the oracle from the bf16
+    source rows); the timed region holds only oracle arithmetic on host arrays:
+    the step's new row (RoPE + FP4) and the group. One-core throughput: the
+    workers one after another, each alone on its core, until `budget_s` seconds
+    are spent; all-core throughput: every worker at once over its share."""
     import numpy as np
-    try:
-        from threadpoolctl import threadpool_limits
-    except ImportError:           # pragma: no cover
-        threadpool_limits = None
-    import contextlib
     import torch
-    from oracle import group as OG
-    from oracle import rope as OR, formats as OF
+    from oracle import cpu_timing as CT
     from oracle.compress import n_visible
+    from oracle import mxfp4 as OM
     import synth
 
-    from oracle import mxfp4 as OM
     n_cap, m = w.n_cap, w.m
-    sched = OG.layer_schedule(w.kind)
-    wall0 = time.perf_counter()
-    limit = threadpool_limits(limits=1) if threadpool_limits is not None else contextlib.nullcontext()
-    spent, done = 0.0, 0
-    with limit:
-        for b in range(w.B):
-            main_b = synth.pooled_main_rows(n_cap, m, "cuda", seed, w.name, "main", b,
-                                            outliers=w.outliers)
-            if new_rows is not None:
-                main_b[n_cap - 1] = new_rows[b]
+    n_q = w.B * w.T
+    if w.T >= 64:
+        picks = sorted(set(np.linspace(0, n_q - 1, 64).round().astype(int).tolist()))
+    else:
+        picks = list(range(min(n_q, 2 * len(workers))))
+    n_layers = w.n_layers
+    keys_of = {}
 
-            class Cache:
-                def __getitem__(self, sel, _rows=main_b):
-                    sel = np.asarray(sel, dtype=np.int64)
-                    x = _rows[torch.from_numpy(sel).to(_rows.device)].float().cpu().numpy()
-                    return OF.quantize_rows(OR.apply_rope(x, sel * m))
-
+    def keys(b):
+        if b not in keys_of:
+            keys_of.clear()
             if index_k == "fp4":
-                # the oracle quantises the bf16 keys itself (staging, not timed)
                 kn, ks = OM.quantize_index_keys(inp["k_bf16"][b].float().cpu().numpy())
             else:
                 kn, ks = inp["k_idx"][b].cpu().numpy().copy(), None
@@ -181,33 +175,57 @@ def cpu_baseline(w, inp, seed, new_rows, budget_s=10.0, index_k="fp8", oracle_ro
                     kn[n_cap - 1], ks[n_cap - 1] = oracle_rows["k"][0][b], oracle_rows["k"][1][b]
                 else:
                     kn[n_cap - 1] = oracle_rows["k"][b]
-            for t in range(w.T):
-                qi = {li: inp["q_idx"][li][b, t].cpu().numpy() for li in inp["q_idx"]}
-                wi = {li: inp["w"][li][b, t].cpu().numpy() for li in inp["w"]}
-                q = {li: inp["q"][li][b, t].float().cpu().numpy() for li in range(len(sched))}
-                swa = {li: inp["swa"][li][b].cpu().numpy() for li in range(len(sched))}
-                if oracle_rows is not None:
-                    for li in range(len(sched)):
-                        swa[li] = swa[li].copy()
-                        swa[li][-1] = oracle_rows["win"][li][b]
-                tq = w.q_positions[t]
-                nv = int(n_visible(tq, m))
-                t0 = time.perf_counter()
-                OG.run_group(sched, qi, wi, q, swa, kn, Cache(), nv, tq, w.swa_pos0, k_scales=ks)
-                spent += time.perf_counter() - t0
-                done += 1
-                if spent >= budget_s:
-                    break
-            del main_b
-            # staging (input copies, FP4 key quantisation) is not timed, but the
-            # whole sample stays within a few budgets of wall time
-            if spent >= budget_s or time.perf_counter() - wall0 >= 4 * budget_s:
-                break
-    return {"value": done / spent, "unit": "queries/s", "cores": 1, "kind": "oracle",
-            "sample": "%d of %d queries, each through all %d layers%s; "
-                      "%.1f s of single-threaded oracle time" % (
-                          done, w.B * w.T, len(sched),
-                          " incl. the write-path row" if new_rows is not None else "", spent)}
+            keys_of[b] = (kn, ks)
+        return keys_of[b]
+
+    tasks, seq_of = [], []
+    for qi in picks:
+        b, t = divmod(qi, w.T)
+        kn, ks = keys(b)
+        swa = {li: inp["swa"][li][b].cpu().numpy() for li in range(n_layers)}
+        if oracle_rows is not None:
+            for li in range(n_layers):
+                swa[li] = swa[li].copy()
+                swa[li][-1] = oracle_rows["win"][li][b]
+        tq = int(w.q_positions[t])
+        tasks.append({
+            "kind": w.kind, "n_cap": n_cap, "m": m, "t": tq, "n_vis": int(n_visible(tq, m)),
+            "swa_pos0": int(w.swa_pos0), "k": kn, "k_scales": ks,
+            "q_idx": {li: inp["q_idx"][li][b, t].cpu().numpy() for li in inp["q_idx"]},
+            "w": {li: inp["w"][li][b, t].cpu().numpy() for li in inp["w"]},
+            "q": {li: inp["q"][li][b, t].float().cpu().numpy() for li in range(n_layers)},
+            "swa": swa,
+            "new_row": (new_rows[b].float().cpu().numpy() if new_rows is not None else None),
+            "new_slot": n_cap - 1})
+        seq_of.append(b)
+    keys_of.clear()
+    src = {}
+
+    def source_rows(qi, pos):
+        b = seq_of[qi]
+        if b not in src:
+            src.clear()
+            src[b] = synth.pooled_main_rows(n_cap, m, "cuda", seed, w.name, "main", b,
+                                            outliers=w.outliers)
+        sel = torch.as_tensor(np.asarray(pos, dtype=np.int64), device=src[b].device)
+        return src[b][sel].float().cpu().numpy()
+
+    r = CT.measure(workers, tasks, source_rows, budget_1core_s=budget_s)
+    src.clear()
+    model, usable, total = CT.host_cpu()
+    sched_len = n_layers
+    return {"value": round(r["value_all_cores"], 4), "unit": "queries/s",
+            "cores": r["cores_all"], "kind": "oracle",
+            "value_1core": round(r["value_1core"], 4),
+            "value_all_cores": round(r["value_all_cores"], 4),
+            "cpu_model": model, "nproc": usable, "cpu_count": total,
+            "sample": "%d of %d queries, each through all %d layers%s, packed rows staged "
+                      "before timing; one core: %d queries in %.1f s (workers alone in turn); "
+                      "all cores: %d queries on %d single-threaded processes in %.1f s" % (
+                          len(picks), n_q, sched_len,
+                          " incl. the write-path row" if new_rows is not None else "",
+                          r["queries_1core"], r["seconds_1core"], r["queries_all_cores"],
+                          r["cores_all"], r["seconds_all_cores"])}
 
 
 def main():
@@ -216,6 +234,11 @@ def main():
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
+    workers = None
+    if not args.no_cpu_baseline:
+        # the oracle's worker processes start before anything touches the GPU
+        from oracle import cpu_timing as CT
+        workers = CT.Workers(max_workers=16)
     import numpy as np
     import torch
     import compressed_kv_cache_02_amd as C
@@ -496,8 +519,11 @@ def main():
     }
     log("timed %d steps: %.3f ms/step; running the oracle sample" % (args.steps, ms))
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(w, inp, seed, new_rows, index_k=args.index_k,
-                                           oracle_rows=oracle_rows)
+        try:
+            res["cpu_baseline"] = cpu_baseline(workers, w, inp, seed, new_rows,
+                                               index_k=args.index_k, oracle_rows=oracle_rows)
+        finally:
+            workers.close()
     else:
         res["cpu_baseline"] = None
     print(json.dumps(res), flush=True)

@@ -17,6 +17,17 @@ Readings taken:
   * logits z = scale * q_h . key with q taken exactly from bf16; the 1/sqrt(512)
     factor of the configs is folded into q, so scale = 1 there.
   * All arithmetic in float64; the output is rounded to float32.
+  * What a caller's buffers may not hold is skipped, not guessed: a selected
+    index outside [0, rows of the cache) contributes no key, and a window token
+    that the window buffer does not hold (outside [swa_pos0, swa_pos0 + S))
+    contributes no key.
+  * The window buffer is addressed in one of two ways. Linear: row s holds token
+    swa_pos0 + s. Ring: token tok sits in row tok mod S, so a decode loop appends
+    token t into row t mod S and advances swa_pos0 to max(0, t - S + 1); the
+    pages keep the window KV of the last n_win = 128 tokens per layer and replay
+    exactly that span ("DeepSeek V4.1 Flash vs V4 Pro", 黑科技之三;
+    "DeepSeek-V4.1-Flash：全局 KV 仅 890 B/token", 第三刀), which a ring of
+    S >= 128 rows holds.
 """
 
 import numpy as np
@@ -43,24 +54,38 @@ def softmax_attention(q, keys, scale):
     return p @ keys
 
 
-def gather_keys(cache_rows, idx, swa_codes, t, swa_pos0):
-    """Dequantised key rows for one query: selected main rows (idx >= 0) in idx
-    order, then the window rows in token order."""
-    idx = np.asarray(idx, dtype=np.int64)
-    sel = idx[idx >= 0]
-    main = dequantize_rows(np.asarray(cache_rows[sel]))
+def window_rows(t, swa_pos0, S, ring=False):
+    """(tokens, rows) of the window tokens of the query at token t that a
+    window buffer of S rows holds: tokens in [swa_pos0, swa_pos0 + S), each
+    at row tok - swa_pos0 (linear) or tok mod S (ring)."""
     toks = swa_tokens(t)
-    swa = e4m3_decode(np.asarray(swa_codes)[toks - int(swa_pos0)])
+    toks = toks[(toks >= int(swa_pos0)) & (toks < int(swa_pos0) + int(S))]
+    rows = toks % int(S) if ring else toks - int(swa_pos0)
+    return toks, rows
+
+
+def gather_keys(cache_rows, idx, swa_codes, t, swa_pos0, ring=False):
+    """Dequantised key rows for one query: selected main rows (0 <= idx < rows
+    of the cache) in idx order, then the window rows the buffer holds, in token
+    order."""
+    idx = np.asarray(idx, dtype=np.int64)
+    sel = idx[(idx >= 0) & (idx < len(cache_rows))]
+    main = dequantize_rows(np.asarray(cache_rows[sel]))
+    swa_codes = np.asarray(swa_codes)
+    _, rows = window_rows(t, swa_pos0, swa_codes.shape[0], ring)
+    swa = e4m3_decode(swa_codes[rows])
     return np.concatenate([main, swa], axis=0)
 
 
-def sparse_attention(q, cache_rows, idx, swa_codes, t, swa_pos0, scale=1.0):
+def sparse_attention(q, cache_rows, idx, swa_codes, t, swa_pos0, scale=1.0, ring=False):
     """One query's output [64, 512] float32.
 
     q: float array [64, 512] holding the bf16 query values exactly;
-    cache_rows: packed 288-byte main-KV rows indexed by position;
+    cache_rows: packed 288-byte main-KV rows indexed by position (an array, or
+    any object with len() and row indexing by an index array);
     idx: the selected positions (-1 padded); swa_codes: uint8 [S, 512] E4M3
-    window rows where row s holds token swa_pos0 + s; t: the query's token."""
-    keys = gather_keys(cache_rows, idx, swa_codes, t, swa_pos0)
+    window rows (linear: row s holds token swa_pos0 + s; ring: token tok sits
+    in row tok mod S); t: the query's token."""
+    keys = gather_keys(cache_rows, idx, swa_codes, t, swa_pos0, ring)
     q = np.asarray(q, dtype=np.float64).reshape(N_HEADS, D_MAIN)
     return softmax_attention(q, keys, float(scale)).astype(np.float32)

@@ -68,7 +68,7 @@ def layer_schedule(kind):
 
 
 def run_group(schedule, q_idx, w, q, swa, k_codes, cache_rows, n_vis, t,
-              swa_pos0, scale=1.0, with_pool=True, k_scales=None):
+              swa_pos0, scale=1.0, with_pool=True, k_scales=None, ring=False):
     """One query through a layer group.
 
     q_idx / w: dict layer -> indexer query [32,128] E4M3 codes / weights [32]
@@ -76,8 +76,9 @@ def run_group(schedule, q_idx, w, q, swa, k_codes, cache_rows, n_vis, t,
     [64,512] (bf16 values as floats) / window rows [S,512] E4M3 codes;
     k_codes [n_cap,128] and cache_rows [n_cap,288] are the group's shared
     indexer keys and packed main KV (with ``k_scales`` [n_cap,4], k_codes are
-    [n_cap,64] packed FP4 keys; see ``mxfp4``). Returns (idx per layer, out per layer,
-    pool, scores per index-producing layer)."""
+    [n_cap,64] packed FP4 keys; see ``mxfp4``). ``ring``: the window buffers
+    are rings (token tok in row tok mod S; see ``attention``). Returns (idx per
+    layer, out per layer, pool, scores per index-producing layer)."""
     idx_of, out_of, scores_of = {}, {}, {}
     pool = None
     for li, (mode, src) in enumerate(schedule):
@@ -99,5 +100,5 @@ def run_group(schedule, q_idx, w, q, swa, k_codes, cache_rows, n_vis, t,
         else:
             raise ValueError(mode)
         out_of[li] = sparse_attention(q[li], cache_rows, idx_of[li], swa[li], t,
-                                      swa_pos0, scale)
+                                      swa_pos0, scale, ring=ring)
     return idx_of, out_of, pool, scores_of

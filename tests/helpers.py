@@ -99,6 +99,9 @@ class OracleCache:
         self.m = m
         self.cache = {}
 
+    def __len__(self):
+        return int(self.src.shape[0])
+
     def __getitem__(self, sel):
         sel = np.asarray(sel, dtype=np.int64).reshape(-1)
         need = [int(j) for j in sel if int(j) not in self.cache]

@@ -134,12 +134,8 @@ def _group_inputs(rng, n_cap, n_layers, S):
 
 
 def test_reuse_is_byte_identical_and_sources_untouched():
-    rng = np.random.default_rng(5)
-    n_cap = 20000
-    k, cache, qi, w, q, swa = _group_inputs(rng, n_cap, 7, 128)
     sched = G.layer_schedule("decoder")
-    idx, out, pool, _ = G.run_group(sched, qi, w, q, swa, k, cache, n_vis=n_cap,
-                                    t=n_cap - 1, swa_pos0=n_cap - 128)
+    idx, out, pool, _ = _run(_decoder_case(5))
     snap = {l: idx[l].copy() for l in idx}
     for li, (m, src) in enumerate(sched):
         if m == "U":
@@ -182,3 +178,158 @@ def test_full_scores_block_max_consistent():
     for b in range(38):
         vis = s[8 * b:min(8 * b + 8, 250)]
         assert bm[b] == (vis.max() if vis.size else -np.inf)
+
+
+# ------------------------------------------------- per-layer routing pins -----
+# The pages fix that a Reindex layer scores with its own indexer query and that
+# every layer computes its own main query and window KV ("DeepSeek V4.1-Flash
+# 为什么这么强？", §二 mode table; "DeepSeek V4.1 Flash vs V4 Pro", 黑科技之二).
+
+def _decoder_case(seed, n_cap=20000):
+    # 20,000 positions = 2,500 blocks, so the 2,048-block pool is a strict subset
+    rng = np.random.default_rng(seed)
+    k = _rand_swa(rng, n_cap)[:, :128].copy()
+    # packed rows drawn directly: any E2M1 code byte, E4M3 scales 2^-3 .. 1.875
+    cache = np.concatenate([rng.integers(0, 256, (n_cap, 256)),
+                            rng.integers(0x20, 0x40, (n_cap, 32))], axis=1).astype(np.uint8)
+    qi = {l: _rand_swa(rng, 32)[:, :128].copy() for l in range(7)}
+    w = {l: (rng.uniform(0, 1, 32) / 32).astype(np.float32) for l in range(7)}
+    q = {l: rng.standard_normal((64, 512)) / np.sqrt(512) for l in range(7)}
+    swa = {l: _rand_swa(rng, 128) for l in range(7)}
+    t = n_cap - 1
+    return dict(k=k, cache=cache, qi=qi, w=w, q=q, swa=swa, n_vis=n_cap, t=t, pos0=t - 127)
+
+
+def _run(c, **over):
+    a = dict(c)
+    a.update(over)
+    return G.run_group(G.layer_schedule("decoder"), a["qi"], a["w"], a["q"], a["swa"], a["k"],
+                       a["cache"], n_vis=a["n_vis"], t=a["t"], swa_pos0=a["pos0"])
+
+
+def test_reindex_with_the_full_layers_query_reproduces_its_topk():
+    # the Full Top-512 lies inside the pool, so a Reindex layer given the Full
+    # layer's indexer query must pick exactly the Full layer's set
+    c = _decoder_case(20)
+    qi = {l: c["qi"][0] for l in c["qi"]}
+    w = {l: c["w"][0] for l in c["w"]}
+    idx, _, pool, _ = _run(c, qi=qi, w=w)
+    assert (pool >= 0).sum() == 2048 < -(-c["n_vis"] // 8)
+    for li in (1, 3, 5):
+        assert np.array_equal(idx[li], idx[0])
+
+
+def test_each_reindex_layer_scores_with_its_own_indexer_query():
+    c = _decoder_case(21)
+    idx = _run(c)[0]
+    sets = [frozenset(idx[li].tolist()) for li in (0, 1, 3, 5)]
+    assert len(set(sets)) == 4
+    # exchanging two Reindex layers' indexer queries exchanges their selections
+    # (and their Reuse layers'), leaving the others alone
+    qi, w = dict(c["qi"]), dict(c["w"])
+    qi[1], qi[3] = c["qi"][3], c["qi"][1]
+    w[1], w[3] = c["w"][3], c["w"][1]
+    sw = _run(c, qi=qi, w=w)[0]
+    for a, b in ((0, 0), (1, 3), (2, 4), (3, 1), (4, 2), (5, 5), (6, 6)):
+        assert np.array_equal(sw[a], idx[b]), (a, b)
+
+
+def test_each_layer_attends_with_its_own_query():
+    # a zero query gives the plain mean of the layer's own keys (closed form);
+    # only the one layer given a real query may differ from it
+    c = _decoder_case(22)
+    zero = np.zeros((64, 512))
+    for R in (0, 3, 6):
+        q = {l: zero for l in range(7)}
+        q[R] = c["q"][R]
+        idx, out, _, _ = _run(c, q=q)
+        for li in range(7):
+            mean = A.gather_keys(c["cache"], idx[li], c["swa"][li], c["t"], c["pos0"]).mean(axis=0)
+            close = np.allclose(out[li], mean[None, :], rtol=0, atol=1e-6)
+            assert close == (li != R), (R, li)
+
+
+def test_each_layer_attends_over_its_own_window():
+    # main rows all zero and a constant window row a_l per layer: every head's
+    # logits are 0 for the 512 selected rows and a_l * sum_c q_hc for the 128
+    # window rows, so out[h] = a_l * 128 e^{a_l s_h} / (512 + 128 e^{a_l s_h})
+    c = _decoder_case(23)
+    cache = np.zeros_like(c["cache"])
+    vals = [0.5, 1.0, 1.5, 2.0, 3.0, -1.0, -2.5]
+    codes = torch.tensor(vals).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    swa = {l: np.full((128, 512), codes[l], dtype=np.uint8) for l in range(7)}
+    _, out, _, _ = _run(c, cache=cache, swa=swa)
+    for li in range(7):
+        a = vals[li]
+        s = c["q"][li].sum(axis=1)
+        e = 128.0 * np.exp(a * s)
+        want = (a * e / (512.0 + e))[:, None] * np.ones((1, 512))
+        assert np.allclose(out[li], want, rtol=1e-6, atol=1e-7), li
+
+
+# --------------------------------- window buffer: skip rules and ring layout ---
+
+def test_out_of_range_indices_and_unheld_window_tokens_are_skipped():
+    # constant rows: selected main rows hold 3.0 (scale 0.5, code 6: exact),
+    # window rows 2.0; a zero query
+    # averages exactly the keys that count, so the output names their number.
+    # 7 indices lie in [0, 64); 5 do not. The query at t = 300 has window
+    # tokens 173..300, of which the 40-row buffer from token 250 holds 250..289.
+    one = Fm.quantize_rows(np.full((64, 512), 3.0, dtype=np.float32))
+    assert np.all(Fm.dequantize_rows(one) == 3.0)
+    idx = np.full(512, -1, dtype=np.int32)
+    idx[:12] = [0, 3, 5, 9, 20, 33, 63, 64, 100, -7, 2**31 - 1, -(2**31)]
+    two = np.full((40, 512), torch.tensor([2.0]).to(torch.float8_e4m3fn).view(torch.uint8)
+                  .item(), dtype=np.uint8)
+    out = A.sparse_attention(np.zeros((64, 512)), one, idx, two, t=300, swa_pos0=250)
+    assert np.allclose(out, (7 * 3.0 + 40 * 2.0) / 47, rtol=0, atol=1e-6)
+    # a window buffer that starts after the window: only the selected rows
+    out = A.sparse_attention(np.zeros((64, 512)), one, idx, two, t=300, swa_pos0=301)
+    assert np.allclose(out, 3.0, rtol=0, atol=0)
+
+
+def _token_rows(tokens):
+    # window row of token tok: the E4M3 value (tok mod 16) / 4 in every channel
+    v = torch.tensor([(int(x) % 16) / 4.0 for x in tokens]).to(torch.float8_e4m3fn)
+    return np.repeat(v.view(torch.uint8).numpy()[:, None], 512, axis=1)
+
+
+def test_ring_window_equals_linear_window():
+    # appending tokens 0..t one at a time into row tok mod S of a ring holds the
+    # same window as a linear buffer of the last S tokens
+    rng = np.random.default_rng(24)
+    cache = _rand_cache(rng, 900)
+    idx = np.sort(rng.choice(900, 512, replace=False)).astype(np.int32)
+    q = rng.standard_normal((64, 512)) / np.sqrt(512)
+    for S, t in ((128, 127), (128, 128), (128, 1000), (160, 1000), (200, 150), (130, 5)):
+        ring = np.zeros((S, 512), dtype=np.uint8)
+        for tok in range(t + 1):
+            ring[tok % S] = _token_rows([tok])[0]
+        pos0 = max(0, t - S + 1)
+        lin = _token_rows(range(pos0, pos0 + S))
+        a = A.sparse_attention(q, cache, idx, ring, t=t, swa_pos0=pos0, ring=True)
+        b = A.sparse_attention(q, cache, idx, lin, t=t, swa_pos0=pos0)
+        assert np.array_equal(a, b), (S, t)
+        toks, rows = A.window_rows(t, pos0, S, ring=True)
+        assert toks.tolist() == list(range(max(0, t - 127), t + 1))
+        assert rows.tolist() == [x % S for x in toks.tolist()]
+
+
+def test_ring_window_closed_form_names_the_tokens_used():
+    # with no selected rows and a zero query the output is the mean of the
+    # window rows' values (tok mod 16) / 4 over exactly the held window tokens
+    S = 128
+    ring = np.zeros((S, 512), dtype=np.uint8)
+    t = 1000
+    for tok in range(t + 1):
+        ring[tok % S] = _token_rows([tok])[0]
+    idx = np.full(512, -1, dtype=np.int32)
+    out = A.sparse_attention(np.zeros((64, 512)), _rand_cache(np.random.default_rng(0), 4), idx,
+                             ring, t=t, swa_pos0=t - S + 1, ring=True)
+    want = np.mean([(x % 16) / 4.0 for x in range(t - 127, t + 1)])
+    assert np.allclose(out, want, rtol=0, atol=1e-6)
+    # the oldest held token is t - 100: only tokens t-100..t count
+    out = A.sparse_attention(np.zeros((64, 512)), _rand_cache(np.random.default_rng(0), 4), idx,
+                             ring, t=t, swa_pos0=t - 100, ring=True)
+    want = np.mean([(x % 16) / 4.0 for x in range(t - 100, t + 1)])
+    assert np.allclose(out, want, rtol=0, atol=1e-6)

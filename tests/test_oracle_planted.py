@@ -11,6 +11,7 @@ import pytest
 from oracle import attention as A
 from oracle import compress as Cm
 from oracle import formats as F
+from oracle import group as G
 from oracle import indexer as I
 from oracle import mxfp4 as M
 from oracle import rope as R
@@ -198,6 +199,71 @@ def _mx_scale_values_bias_128(codes):
 
 # --------------------------------------------------------------- the cases --
 
+def _run_group_mutant(kind):
+    """run_group with one per-layer routing mistake: a Reindex layer scoring
+    with the first layer's indexer query, every attention reading the first
+    layer's query or window, or a Reuse layer copying the first layer's
+    indices."""
+    def run_group(schedule, q_idx, w, q, swa, k_codes, cache_rows, n_vis, t, swa_pos0,
+                  scale=1.0, with_pool=True, k_scales=None, ring=False):
+        idx_of, out_of, scores_of = {}, {}, {}
+        pool = None
+        for li, (mode, src) in enumerate(schedule):
+            if mode == "F":
+                s = I.index_scores(q_idx[li], w[li], k_codes, n_vis, k_scales=k_scales)
+                nv = min(int(n_vis), s.shape[0])
+                idx_of[li] = S.topk_positions(s[:nv], np.arange(nv))
+                if with_pool and pool is None:
+                    pool = S.build_pool(I.block_max(s, n_vis), n_vis)
+                scores_of[li] = s
+            elif mode == "X":
+                qs = 0 if kind == "reindex_q0" else li
+                cand = S.reindex_candidates(pool, n_vis)
+                s = I.index_scores(q_idx[qs], w[qs], k_codes, n_vis, positions=cand,
+                                   k_scales=k_scales)
+                idx_of[li] = S.topk_positions(s, cand)
+                scores_of[li] = (cand, s)
+            else:
+                idx_of[li] = idx_of[0 if kind == "reuse_0" else src].copy()
+            out_of[li] = A.sparse_attention(q[0 if kind == "q0" else li], cache_rows, idx_of[li],
+                                            swa[0 if kind == "swa0" else li], t, swa_pos0, scale,
+                                            ring=ring)
+        return idx_of, out_of, pool, scores_of
+    return run_group
+
+
+def _window_rows_mutant(kind):
+    """Window rows with a ring addressed from swa_pos0, or without the check
+    that the buffer holds a token."""
+    def window_rows(t, swa_pos0, S_, ring=False):
+        toks = A.swa_tokens(t)
+        if kind != "no_hold_check":
+            toks = toks[(toks >= int(swa_pos0)) & (toks < int(swa_pos0) + int(S_))]
+        if ring:
+            rows = (toks - int(swa_pos0)) % int(S_) if kind == "ring_from_pos0" else toks % int(S_)
+        else:
+            rows = (toks - int(swa_pos0)) % int(S_)
+        return toks, rows
+    return window_rows
+
+
+def _gather_keys_clamped(cache_rows, idx, swa_codes, t, swa_pos0, ring=False):
+    """Selected indices clamped into the cache instead of skipped."""
+    idx = np.asarray(idx, dtype=np.int64)
+    sel = np.clip(idx[idx >= 0], 0, len(cache_rows) - 1)
+    main = F.dequantize_rows(np.asarray(cache_rows[sel]))
+    swa_codes = np.asarray(swa_codes)
+    _, rows = A.window_rows(t, swa_pos0, swa_codes.shape[0], ring)
+    return np.concatenate([main, F.e4m3_decode(swa_codes[rows])], axis=0)
+
+
+_ROUTING_PINS = [TA.test_reindex_with_the_full_layers_query_reproduces_its_topk,
+                 TA.test_each_reindex_layer_scores_with_its_own_indexer_query,
+                 TA.test_each_layer_attends_with_its_own_query,
+                 TA.test_each_layer_attends_over_its_own_window,
+                 TA.test_reuse_is_byte_identical_and_sources_untouched]
+
+
 CASES = [
     ("score: ReLU dropped", I, "index_scores", _scores_mutant(relu=False),
      [TS.test_scores_vs_exact_brute_force, TS.test_closed_form_unit_vectors_and_relu]),
@@ -250,6 +316,23 @@ CASES = [
     ("main KV: one scale per 32 channels", F, "dequantize_rows", _dequantize_rows_per_32,
      [TF.test_grid_valued_group_round_trips,
       lambda: TF.test_quantize_is_nearest_over_whole_rows(0)]),
+    ("group: Reindex scores with the first layer's indexer query", G, "run_group",
+     _run_group_mutant("reindex_q0"), _ROUTING_PINS),
+    ("group: every attention reads the first layer's query", G, "run_group",
+     _run_group_mutant("q0"), _ROUTING_PINS),
+    ("group: every attention reads the first layer's window", G, "run_group",
+     _run_group_mutant("swa0"), _ROUTING_PINS),
+    ("group: Reuse copies the first layer's indices", G, "run_group",
+     _run_group_mutant("reuse_0"), _ROUTING_PINS),
+    ("window: ring rows counted from swa_pos0", A, "window_rows",
+     _window_rows_mutant("ring_from_pos0"),
+     [TA.test_ring_window_equals_linear_window, TA.test_ring_window_closed_form_names_the_tokens_used]),
+    ("window: tokens the buffer does not hold are read", A, "window_rows",
+     _window_rows_mutant("no_hold_check"),
+     [TA.test_out_of_range_indices_and_unheld_window_tokens_are_skipped,
+      TA.test_ring_window_closed_form_names_the_tokens_used]),
+    ("attention: out-of-range indices clamped into the cache", A, "gather_keys",
+     _gather_keys_clamped, [TA.test_out_of_range_indices_and_unheld_window_tokens_are_skipped]),
 ]
 
 
