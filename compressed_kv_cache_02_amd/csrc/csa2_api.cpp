@@ -30,24 +30,42 @@ inline bool sizes_ok(int B, int T, int64_t n_cap) {
 
 inline int status_of(hipError_t e) { return e == hipSuccess ? CSA2_OK : CSA2_EHIP; }
 
-// Workspace of csa2_index_topk: the whole score rows when one selection covers
-// them (n_cap <= 16,384); otherwise block maxima, the 512 best blocks, their
-// 4,096 re-scored positions and the best-blocks selection's own scratch.
+// Workspace of csa2_index_topk. Decode-shaped scans (FP32-accurate scores):
+// the whole score rows when one selection covers them (n_cap <= 16,384);
+// otherwise block maxima, the 512 best blocks, their 4,096 re-scored
+// positions and the best-blocks selection's own scratch. Prefill-shaped scans
+// (the FP8 contraction, whose scores only narrow the candidates): block
+// maxima, the 1,024 best blocks and their 8,192 positions re-scored.
 struct FusedWs {
   size_t scores, bmax, sel_blk, vals, blocks_ws, total;
+  int n_best;     // 0: one selection over the score rows
 };
 
-inline FusedWs fused_layout(int Q, int64_t n_cap) {
+// Best blocks kept for re-scoring: 512 when the block maxima come from
+// FP32-accurate scores (the 512 best positions lie in the 512 best blocks),
+// 1,024 when they come from the FP8 contraction. There a block holding one of
+// the 512 best positions could only fall out of the list if more than 512
+// other blocks' maxima came within twice the contraction's error (below
+// 2.5e-4 of the score on the workloads) of its own.
+constexpr int kBestExact = CSA2_TOPK;
+constexpr int kBestNarrowed = 2 * CSA2_TOPK;
+
+inline bool prefill_shaped(int T, bool fp4) {
+  return T >= (fp4 ? CSA2_PREFILL_MIN_T_FP4 : CSA2_PREFILL_MIN_T_FP8);
+}
+
+inline FusedWs fused_layout(int Q, int64_t n_cap, bool narrowed) {
   FusedWs l{};
-  if (n_cap <= CSA2_POOL_CAND) {
+  if (!narrowed && n_cap <= CSA2_POOL_CAND) {
     l.total = round_up((size_t)Q * (size_t)n_cap * sizeof(float));
     return l;
   }
+  l.n_best = narrowed ? kBestNarrowed : kBestExact;
   const int64_t n_blk = (n_cap + CSA2_BLOCK - 1) / CSA2_BLOCK;
   l.bmax = 0;
   l.sel_blk = round_up((size_t)Q * (size_t)n_blk * sizeof(float));
-  l.vals = l.sel_blk + round_up((size_t)Q * CSA2_TOPK * sizeof(int32_t));
-  l.blocks_ws = l.vals + round_up((size_t)Q * CSA2_TOPK * CSA2_BLOCK * sizeof(float));
+  l.vals = l.sel_blk + round_up((size_t)Q * l.n_best * sizeof(int32_t));
+  l.blocks_ws = l.vals + round_up((size_t)Q * l.n_best * CSA2_BLOCK * sizeof(float));
   l.total = l.blocks_ws + round_up(csa2::best_blocks_workspace_bytes(Q, n_cap));
   return l;
 }
@@ -86,7 +104,12 @@ size_t csa2_workspace_bytes(int op, int mode, int B, int T, int64_t n_cap) {
       if (mode == CSA2_FULL) return round_up(csa2::topk_workspace_bytes(Q, n_cap));
       return 0;
     case CSA2_OP_SPARSE_ATTN: return round_up(csa2::attn_workspace_bytes(Q));
-    case CSA2_OP_INDEX_TOPK: return fused_layout(Q, n_cap).total;
+    case CSA2_OP_INDEX_TOPK: {
+      // enough for either key format at this T
+      const FusedWs a = fused_layout(Q, n_cap, prefill_shaped(T, false));
+      const FusedWs b = fused_layout(Q, n_cap, prefill_shaped(T, true));
+      return a.total > b.total ? a.total : b.total;
+    }
     default: return 0;
   }
 }
@@ -197,37 +220,42 @@ int csa2_index_topk(const uint8_t* q_idx, const float* w, const uint8_t* k_idx,
       !aligned16(idx) || (k_scales && !aligned4(k_scales)))
     return CSA2_EINVAL;
   if (n_cap > CSA2_INDEX_TOPK_MAX_CAP) return CSA2_EUNSUPPORTED;
-  const FusedWs l = fused_layout(B * T, n_cap);
+  const bool fp4 = k_scales != nullptr;
+  const bool narrowed = prefill_shaped(T, fp4);
+  const FusedWs l = fused_layout(B * T, n_cap, narrowed);
   if (!aligned16(ws)) return ws ? CSA2_EINVAL : CSA2_EWORKSPACE;
   if (ws_bytes < l.total) return CSA2_EWORKSPACE;
   hipStream_t st = as_stream(stream);
   const int Q = B * T;
-  // the Full scan: score rows (short contexts) or block maxima only
-  float* scores = n_cap <= CSA2_POOL_CAND ? ws_at<float>(ws, l.scores) : nullptr;
+  // the Full scan: score rows (short contexts, decode shape) or block maxima only
+  float* scores = l.n_best == 0 ? ws_at<float>(ws, l.scores) : nullptr;
   float* bmax = scores ? nullptr : ws_at<float>(ws, l.bmax);
   hipError_t e;
-  if (k_scales && T >= CSA2_PREFILL_MIN_T_FP4)
+  if (fp4 && narrowed)
     e = csa2::launch_index_score_prefill_fp4k(q_idx, w, k_idx, k_scales, n_vis, B, T, n_cap, scores,
                                               bmax, st);
-  else if (k_scales)
+  else if (fp4)
     e = csa2::launch_index_score_decode_fp4k(CSA2_FULL, q_idx, w, k_idx, k_scales, n_vis, nullptr,
                                              B, T, n_cap, scores, bmax, st);
-  else if (T >= CSA2_PREFILL_MIN_T_FP8)
+  else if (narrowed)
     e = csa2::launch_index_score_prefill(q_idx, w, k_idx, n_vis, B, T, n_cap, scores, bmax, st);
   else
     e = csa2::launch_index_score_decode(CSA2_FULL, q_idx, w, k_idx, n_vis, nullptr, B, T, n_cap,
                                         scores, bmax, st);
   if (e != hipSuccess) return CSA2_EHIP;
   if (scores) return status_of(csa2::launch_topk_direct(scores, n_vis, Q, n_cap, idx, st));
+  // the best blocks by block maximum, their positions re-scored by the
+  // FP32-accurate decode-shaped kernel, the Top-512 of those
   int32_t* sel_blk = ws_at<int32_t>(ws, l.sel_blk);
   float* vals = ws_at<float>(ws, l.vals);
-  if ((e = csa2::launch_best_blocks(bmax, n_vis, Q, n_cap, sel_blk, ws_at<void>(ws, l.blocks_ws),
-                                    st)) != hipSuccess)
+  if ((e = csa2::launch_best_blocks(bmax, n_vis, Q, n_cap, l.n_best, sel_blk,
+                                    ws_at<void>(ws, l.blocks_ws), st)) != hipSuccess)
     return CSA2_EHIP;
-  if ((e = csa2::launch_rescore_blocks(q_idx, w, k_idx, k_scales, n_vis, sel_blk, CSA2_TOPK, B, T,
+  if ((e = csa2::launch_rescore_blocks(q_idx, w, k_idx, k_scales, n_vis, sel_blk, l.n_best, B, T,
                                        n_cap, vals, st)) != hipSuccess)
     return CSA2_EHIP;
-  return status_of(csa2::launch_topk_of_blocks(vals, sel_blk, n_vis, Q, n_cap, idx, st));
+  return status_of(
+      csa2::launch_topk_of_blocks(vals, sel_blk, l.n_best, n_vis, Q, n_cap, idx, st));
 }
 
 int csa2_build_pool(const float* src, int is_bmax, const int32_t* n_vis, int B, int T,

@@ -7,24 +7,40 @@
 // 仅 890 B/token", 第二刀 and Fig. 5). The weighted ReLU sum is the reading
 // stated in the header csa2.h.
 //
-// Mapping: per query the 32 x 128 indexer query is the A operand of
-// v_mfma_f32_32x32x64_f8f6f4 (rows = heads) and 32 keys are the B operand
-// (columns = positions), two MFMAs per 32 positions (K = 128). Lane l holds
-// head/position l%32 and bytes (l/32)*64 .. +63 of the 128-byte row, so a wave
-// streams 32 whole rows (4 KiB) per tile with 16-byte loads. The channel order
-// inside a lane is irrelevant to the dot product as long as A and B agree.
-// The accumulator holds, per lane, 16 of the 32 head dot products of one
-// position; the epilogue applies ReLU and the head weights and adds the other
-// half with one cross-half shuffle. The scan is HBM-bound (64 FLOP per byte);
-// the MFMA only keeps the 4096 MACs per key off the vector ALU.
+// Mapping (decode shape): per query the 32 x 128 indexer query is the A
+// operand of v_mfma_f32_32x32x16_f16 (rows = heads) and 32 keys are the B
+// operand (columns = positions), eight MFMAs per 32 positions (K = 128). Lane
+// l holds head/position l%32 and bytes (l/32)*64 .. +63 of the 128-byte row,
+// so a wave streams 32 whole rows (4 KiB) per tile with 16-byte loads; the
+// E4M3 bytes are converted to fp16 in registers (exact) just before their
+// MFMA. The channel order inside a lane is irrelevant to the dot product as
+// long as A and B agree. The accumulator holds, per lane, 16 of the 32 head
+// dot products of one position; the epilogue applies ReLU and the head
+// weights and adds the other half with one cross-half shuffle. The scan is
+// HBM-bound (64 FLOP per byte); the MFMA keeps the 4096 MACs per key off the
+// vector ALU.
+//
+// Why fp16 and not the FP8 MFMA here: on gfx950 v_mfma_f32_32x32x64_f8f6f4
+// truncates each product to 13 fractional bits below the largest product of
+// the instruction (measured with in-bounds probes: beside a product 2^8 a
+// product below 2^-5 is dropped, 3 * 2^-6 becomes 2^-5), so its scores carry
+// errors of 2e-5 .. 2e-4 of the 512-th score on the workloads' values, more
+// than the 1e-5 near-tie band of the Top-K. The fp16 MFMA keeps products to
+// 24 bits with round-to-nearest-even (beside 2^16 a product 2^-7 survives,
+// 3 * 2^-8 rounds to 2^-6), i.e. FP32 accumulation; E4M3 and E2M1 values are
+// exact in fp16. Every Top-K and pool decision is therefore taken on scores
+// of this kernel.
 //
 // Variants of the same kernel (one instruction sequence per score, so every
 // variant produces the same bits for a position): FP4 indexer keys (E2M1 codes
-// with one E8M0 scale per 32 channels) through the scaled FP8 x FP4 MFMA; NQ
-// query tokens of one sequence per wave sharing each key tile; and scores of
-// per-query block lists (the Reindex pool, or the 512 best blocks that a fused
-// Top-K re-scores). The prefill shape further down shares key chunks among 16
-// or 32 queries through LDS.
+// with one E8M0 scale per 32 channels: codes converted to fp16 with the block
+// scale relative to the key's largest block scale, that largest scale applied
+// to the finished score as an exact power of two); NQ query tokens of one
+// sequence per wave sharing each key tile; and scores of per-query block lists
+// (the Reindex pool, or the blocks that a fused Top-K re-scores). The prefill
+// shape further down shares key chunks among 16 or 32 queries through LDS and
+// keeps the FP8 contraction (its roofline): its scores only narrow the
+// candidates of a fused Top-K, which re-scores them here.
 #include <type_traits>
 
 #include "device_common.hpp"
@@ -137,7 +153,7 @@ __device__ __forceinline__ float weighted_relu_sum(const v16f& acc, const float*
 // 16-byte pieces 4j+h and 4j+2+h.
 struct KTile4 {
   uint4 c[2];      // code bytes 16h..16h+15 and 32+16h..32+16h+15 of the key
-  uint32_t sc;     // the key's four scale bytes shifted right by 8h
+  uint32_t sc;     // the key's four scale bytes (byte b: channels 32b..32b+31)
 };
 
 __device__ __forceinline__ void load_tile4(KTile4& t, const uint8_t* codes, const uint8_t* scales,
@@ -145,7 +161,7 @@ __device__ __forceinline__ void load_tile4(KTile4& t, const uint8_t* codes, cons
   if (ok) {
     t.c[0] = *reinterpret_cast<const uint4*>(codes);
     t.c[1] = *reinterpret_cast<const uint4*>(codes + 32);
-    t.sc = *reinterpret_cast<const uint32_t*>(scales) >> (8 * half);
+    t.sc = *reinterpret_cast<const uint32_t*>(scales);
   } else {
     t.c[0] = t.c[1] = make_uint4(0, 0, 0, 0);
     t.sc = 0;
@@ -157,6 +173,83 @@ __device__ __forceinline__ v8i fp4_operand(const uint4& a) {
   r[0] = (int)a.x; r[1] = (int)a.y; r[2] = (int)a.z; r[3] = (int)a.w;
   r[4] = r[5] = r[6] = r[7] = 0;   // an FP4 operand uses the first four registers
   return r;
+}
+
+// 8 E4M3 bytes (two words) -> 8 fp16 values, exact.
+__device__ __forceinline__ v8h e4m3x8_to_f16(uint32_t d0, uint32_t d1) {
+  const auto p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d0, 1.0f, false);
+  const auto p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d0, 1.0f, true);
+  const auto p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d1, 1.0f, false);
+  const auto p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d1, 1.0f, true);
+  v8h r;
+  r[0] = p0[0]; r[1] = p0[1]; r[2] = p1[0]; r[3] = p1[1];
+  r[4] = p2[0]; r[5] = p2[1]; r[6] = p3[0]; r[7] = p3[1];
+  return r;
+}
+// 8 E2M1 codes (one word, channel 2k in the low nibble of byte k) times the
+// power of two `scale` -> 8 fp16 values (exact while the product stays in the
+// fp16 range).
+__device__ __forceinline__ v8h e2m1x8_to_f16(uint32_t d, float scale) {
+  const auto p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d, scale, 0);
+  const auto p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d, scale, 1);
+  const auto p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d, scale, 2);
+  const auto p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d, scale, 3);
+  v8h r;
+  r[0] = p0[0]; r[1] = p0[1]; r[2] = p1[0]; r[3] = p1[1];
+  r[4] = p2[0]; r[5] = p2[1]; r[6] = p3[0]; r[7] = p3[1];
+  return r;
+}
+
+// The query operands of the eight fp16 MFMAs of a tile (lane: head l%32,
+// half h = l/32). FP8 keys: MFMA j takes channels 64h + 8j .. +7. FP4 keys:
+// MFMA j < 4 takes channels 32h + 8j .. +7 (scale block h), j >= 4 channels
+// 64 + 32h + 8(j-4) .. +7 (block 2 + h), the order of the key lane's codes.
+template <int KF>
+__device__ __forceinline__ void query_f16(const uint4* q4, int half, v8h (&a)[8]) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int byte = KF ? (j < 4 ? 32 * half + 8 * j : 64 + 32 * half + 8 * (j - 4))
+                        : 64 * half + 8 * j;
+    const uint4 u = q4[byte >> 4];
+    const bool hi = (byte & 8) != 0;
+    a[j] = e4m3x8_to_f16(hi ? u.z : u.x, hi ? u.w : u.y);
+  }
+}
+
+// 2^e as a float for any integer e >= -149 (exact).
+__device__ __forceinline__ float pow2f(int e) { return ldexpf(1.0f, e); }
+
+// The 32x32 head-by-position dot products of one tile, FP32-accurate; for FP4
+// keys also the power of two that the finished score must be multiplied by.
+__device__ __forceinline__ v16f dots_tile(const v8h (&a)[8], const KTile& t, float& post) {
+  v16f acc = {};
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const uint4& u = t.v[j >> 1];
+    const v8h b = e4m3x8_to_f16((j & 1) ? u.z : u.x, (j & 1) ? u.w : u.y);
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[j], b, acc, 0, 0, 0);
+  }
+  post = 1.0f;
+  return acc;
+}
+__device__ __forceinline__ v16f dots_tile(const v8h (&a)[8], const KTile4& t, float& post,
+                                          int half) {
+  // block scales relative to the key's largest, so every code fits fp16
+  const uint32_t s0 = (t.sc >> (8 * half)) & 0xFFu, s1 = (t.sc >> (16 + 8 * half)) & 0xFFu;
+  const uint32_t m01 = max(t.sc & 0xFFu, (t.sc >> 8) & 0xFFu);
+  const uint32_t m23 = max((t.sc >> 16) & 0xFFu, t.sc >> 24);
+  const int smax = (int)max(m01, m23);
+  const float f0 = pow2f(max((int)s0 - smax, -126)), f1 = pow2f(max((int)s1 - smax, -126));
+  v16f acc = {};
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const uint4& u = t.c[j >> 2];
+    const uint32_t d = (j & 3) == 0 ? u.x : (j & 3) == 1 ? u.y : (j & 3) == 2 ? u.z : u.w;
+    const v8h b = e2m1x8_to_f16(d, j < 4 ? f0 : f1);
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[j], b, acc, 0, 0, 0);
+  }
+  post = pow2f(smax - 127);
+  return acc;
 }
 
 // NQ > 1 (Full mode, several query tokens of one sequence, e.g. speculative
@@ -181,13 +274,12 @@ __global__ __launch_bounds__(256) void k_index_score_decode(
   const int col = lane & 31;
   const int64_t n_blk = (n_cap + kBlock - 1) / kBlock;
 
-  // per query of the group: index, visibility (0 past T), A operands, weights.
-  // FP8 keys pair a query lane's channels with the key lane's in the same
-  // order (64h..64h+63); FP4 keys need the FP8 x FP4 order above.
+  // per query of the group: index, visibility (0 past T), A operands (fp16,
+  // in the channel order of the key lane's bytes; see query_f16), weights.
   int qi[NQ];
   bool real[NQ];
   int64_t nv[NQ];
-  v8i a0[NQ], a1[NQ];
+  v8h a16[NQ][8];
   float wr[NQ][16];     // weights of the lane's 16 accumulator rows: 4 runs of 4 heads
   int64_t nv_max = 0;
 #pragma unroll
@@ -200,8 +292,7 @@ __global__ __launch_bounds__(256) void k_index_score_decode(
     nv_max = nv[q] > nv_max ? nv[q] : nv_max;
     const uint4* q4 = reinterpret_cast<const uint4*>(q_idx + (size_t)qi[q] * (kIdxHeads * kIdxDim) +
                                                      col * kIdxDim);
-    a0[q] = KF ? as_v8i(q4[half], q4[2 + half]) : as_v8i(q4[4 * half], q4[4 * half + 1]);
-    a1[q] = KF ? as_v8i(q4[4 + half], q4[6 + half]) : as_v8i(q4[4 * half + 2], q4[4 * half + 3]);
+    query_f16<KF>(q4, half, a16[q]);
     const float4* w4 = reinterpret_cast<const float4*>(w + (size_t)qi[q] * kIdxHeads);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -280,26 +371,17 @@ __global__ __launch_bounds__(256) void k_index_score_decode(
     for (int q = 0; q < NQ; ++q) {
       float s = -INFINITY;
       if (any_ok) {
-        v16f acc = {};
-        if constexpr (KF == 1) {
-          // A: E4M3 (format 0) with scale 2^0 (E8M0 127); B: E2M1 (format 4)
-          // with the key's block scales (bytes 0 and 2 of the shifted word,
-          // each taken from byte 0 of the scale register)
-          acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a0[q], fp4_operand(cur.c[0]), acc, 0,
-                                                                4, 0, 127, 0, (int)cur.sc);
-          acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a1[q], fp4_operand(cur.c[1]), acc, 0,
-                                                                4, 0, 127, 0, (int)(cur.sc >> 16));
-        } else {
-          acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a0[q], as_v8i(cur.v[0], cur.v[1]),
-                                                                acc, 0, 0, 0, 0, 0, 0);
-          acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a1[q], as_v8i(cur.v[2], cur.v[3]),
-                                                                acc, 0, 0, 0, 0, 0, 0);
-        }
+        float post;
+        v16f acc;
+        if constexpr (KF == 1)
+          acc = dots_tile(a16[q], cur, post, half);
+        else
+          acc = dots_tile(a16[q], cur, post);
         const float part = weighted_relu_sum(acc, wr[q]);
         // lo-half + hi-half row sums, in every lane
         const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(part),
                                                          __float_as_uint(part), false, false);
-        const float tot = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+        const float tot = (__uint_as_float(sw[0]) + __uint_as_float(sw[1])) * post;
         const bool vis = MODE == 0 ? item < nv[q] : cur_ok;
         if (cur_ok && vis) s = tot;
       }
@@ -609,10 +691,9 @@ __global__ __launch_bounds__(kPfThreads) void k_index_score_prefill(
 }  // namespace
 
 // Queries per wave of the Full scan when several query tokens of one sequence
-// share each key tile: 4 with FP8 keys, 2 with FP4 keys (fewer registers per
-// wave; measured fastest for each format at 4 tokens per sequence).
+// share each key tile: 2 (each query's fp16 operands take 32 registers).
 template <int KF>
-constexpr int decode_group() { return KF ? 2 : 4; }
+constexpr int decode_group() { return 2; }
 
 // From this many queries on, the Reindex scan over the pool uses 8 tiles per
 // wave (2 below it, where more work-groups per query pay off): 1-2% faster

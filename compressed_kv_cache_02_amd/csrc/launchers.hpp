@@ -61,21 +61,22 @@ hipError_t launch_block_max(const float* scores, const int32_t* n_vis, int Q, in
                             float* bmax, hipStream_t st);
 hipError_t launch_copy_i32(const int32_t* src, int32_t* dst, int64_t n, hipStream_t st);
 
-// Fused Full Top-K pieces: the best 512 blocks from block maxima (super-block
-// maxima, then two chained selections in one kernel; workspace
-// best_blocks_workspace_bytes), the
-// re-scoring of a per-query block list ([Q][n_blocks] block ids, -1 padded;
-// values [Q][8 * n_blocks] by item), the Top-512 of the re-scored positions, and
-// the Top-512 of a short score row (n_cap <= 16,384).
+// Fused Full Top-K pieces: the n_best (<= 2,048) best blocks from block maxima
+// (super-block maxima, then two chained selections in one kernel; workspace
+// best_blocks_workspace_bytes), the re-scoring of a per-query block list
+// ([Q][n_blocks] block ids, -1 padded; values [Q][8 * n_blocks] by item), the
+// Top-512 of the re-scored positions, and the Top-512 of a short score row
+// (n_cap <= 16,384).
 size_t best_blocks_workspace_bytes(int Q, int64_t n_cap);
 hipError_t launch_best_blocks(const float* bmax, const int32_t* n_vis, int Q, int64_t n_cap,
-                              int32_t* sel_blk, void* ws, hipStream_t st);
+                              int n_best, int32_t* sel_blk, void* ws, hipStream_t st);
 hipError_t launch_rescore_blocks(const uint8_t* q_idx, const float* w, const uint8_t* keys,
                                  const uint8_t* scales, const int32_t* n_vis, const int32_t* blocks,
                                  int n_blocks, int B, int T, int64_t n_cap, float* vals,
                                  hipStream_t st);
-hipError_t launch_topk_of_blocks(const float* vals, const int32_t* sel_blk, const int32_t* n_vis,
-                                 int Q, int64_t n_cap, int32_t* out, hipStream_t st);
+hipError_t launch_topk_of_blocks(const float* vals, const int32_t* sel_blk, int n_best,
+                                 const int32_t* n_vis, int Q, int64_t n_cap, int32_t* out,
+                                 hipStream_t st);
 hipError_t launch_topk_direct(const float* scores, const int32_t* n_vis, int Q, int64_t n_cap,
                               int32_t* out, hipStream_t st);
 

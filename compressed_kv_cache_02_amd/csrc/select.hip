@@ -992,21 +992,22 @@ size_t best_blocks_workspace_bytes(int Q, int64_t n_cap) {
 }
 
 hipError_t launch_best_blocks(const float* bmax, const int32_t* n_vis, int Q, int64_t n_cap,
-                              int32_t* sel_blk, void* ws, hipStream_t st) {
+                              int n_best, int32_t* sel_blk, void* ws, hipStream_t st) {
   const int64_t n_blk = n_blocks(n_cap);
   const int64_t n_sb = n_blocks(n_blk);
-  if (n_sb > kOneWgMax) return hipErrorInvalidValue;
+  if (n_sb > kOneWgMax || n_best < 1 || n_best > kPoolBlocks) return hipErrorInvalidValue;
   float* smax = at<float>(ws, 0);
   hipError_t e;
   if ((e = launch_super_max(bmax, Q, n_blk, smax, st)) != hipSuccess) return e;
-  return run_pair(direct(smax, n_sb, 64, n_vis, n_cap, n_sb), kTopK,
-                  child(bmax, n_blk, 8, nullptr, kTopK, 0, n_vis, n_cap), kTopK, Q, sel_blk, kTopK,
-                  st);
+  return run_pair(direct(smax, n_sb, 64, n_vis, n_cap, n_sb), n_best,
+                  child(bmax, n_blk, 8, nullptr, n_best, 0, n_vis, n_cap), n_best, Q, sel_blk,
+                  n_best, st);
 }
 
-hipError_t launch_topk_of_blocks(const float* vals, const int32_t* sel_blk, const int32_t* n_vis,
-                                 int Q, int64_t n_cap, int32_t* out, hipStream_t st) {
-  return run_stage(child(vals, (int64_t)kTopK * kBlock, 1, sel_blk, kTopK, 1, n_vis, n_cap), Q,
+hipError_t launch_topk_of_blocks(const float* vals, const int32_t* sel_blk, int n_best,
+                                 const int32_t* n_vis, int Q, int64_t n_cap, int32_t* out,
+                                 hipStream_t st) {
+  return run_stage(child(vals, (int64_t)n_best * kBlock, 1, sel_blk, n_best, 1, n_vis, n_cap), Q,
                    kTopK, out, kTopK, st);
 }
 

@@ -15,7 +15,8 @@ arithmetic runs in the library's kernels.
 
 import torch
 
-from . import (INDEX_TOPK_MAX_CAP, CSA2_FULL, CSA2_REINDEX, CSA2_REUSE, CSA2_OP_BUILD_POOL, CSA2_OP_INDEX_TOPK,
+from . import (INDEX_TOPK_MAX_CAP, PREFILL_MIN_T_FP8, PREFILL_MIN_T_FP4, CSA2_FULL,
+               CSA2_REINDEX, CSA2_REUSE, CSA2_OP_BUILD_POOL, CSA2_OP_INDEX_TOPK,
                CSA2_OP_SPARSE_ATTN, CSA2_OP_TOPK, POOL_BLOCKS, POOL_CAND, TOPK, HEADS, DIM, BLOCK,
                csa2_build_pool, csa2_index_score, csa2_index_score_fp4k, csa2_index_topk,
                csa2_quantize_kv, csa2_sparse_attn, csa2_topk, csa2_workspace_bytes)
@@ -54,9 +55,13 @@ def index_score(mode, q_idx, w, keys, n_vis, pool, scores, bmax=None, stream=Non
 
 def fused_topk_auto(T, n_cap):
     """Whether a group without a pool takes the fused scan + Top-K by default:
-    prefill chunks and decode over at least 262,144 positions, within the
-    context the fused entry point serves."""
-    return (T >= 64 or n_cap >= (1 << 18)) and n_cap <= INDEX_TOPK_MAX_CAP
+    whenever the scan is prefill-shaped (from PREFILL_MIN_T_FP8 query tokens
+    per sequence: its FP8 contraction's scores only narrow the candidates,
+    which the fused call re-scores FP32-accurately before selecting), and for
+    decode over at least 262,144 positions, within the context the fused entry
+    point serves."""
+    return ((T >= min(PREFILL_MIN_T_FP8, PREFILL_MIN_T_FP4) or n_cap >= (1 << 18))
+            and n_cap <= INDEX_TOPK_MAX_CAP)
 
 
 def visible_entries(t, m):
@@ -70,11 +75,12 @@ class LayerGroup:
     def __init__(self, kind, B, T, n_cap, device="cuda", keep_scores=False, fused_topk="auto"):
         """fused_topk: a group without a pool takes its Full layer's Top-K from
         the fused csa2_index_topk (no score rows written) instead of a scan
-        followed by csa2_topk. "auto" does so for prefill chunks (T >= 64) and
-        for decode steps over at least 262,144 positions, where the score rows
-        saved outweigh re-scoring 4,096 positions per query (measured on
-        MI355X: the 4,096-query prefill chunk +4%, c4 +4%; c1, 65,536 entries,
-        3% slower fused)."""
+        followed by csa2_topk. "auto" does so whenever the scan is
+        prefill-shaped (its FP8 scores only narrow the candidates; the fused
+        call re-scores them FP32-accurately) and for decode steps over at least
+        262,144 positions, where the score rows saved outweigh re-scoring 4,096
+        positions per query (measured on MI355X: c4 +4%; c1, 65,536 entries, 3%
+        slower fused)."""
         self.sched = schedule(kind)
         self.B, self.T, self.n_cap = B, T, n_cap
         dev = torch.device(device)
@@ -86,9 +92,9 @@ class LayerGroup:
         self.fused = bool(fused_topk) and not need_pool and not keep_scores
         # Block maxima come with the scan and drive the hierarchical selections.
         # A group with a pool writes no full score rows: its Full layer
-        # re-scores the pool's 16,384 positions (bit-identical to the scan) and
-        # takes its Top-K there, exact because the 512 best positions always
-        # lie inside the 2,048 best blocks.
+        # re-scores the pool's 16,384 positions (bit-identical to a
+        # decode-shaped scan) and takes its Top-K there, exact because the 512
+        # best positions always lie inside the 2,048 best blocks.
         self.bmax = torch.empty((B, T, n_blk), dtype=torch.float32, device=dev)
         self.scores = None if (need_pool or self.fused) else torch.empty(
             (B, T, n_cap), dtype=torch.float32, device=dev)

@@ -205,12 +205,15 @@ def test_index_topk_rejects_bad_arguments():
 
 
 def test_group_fuses_only_within_the_fused_entry_limit():
-    """The automatic choice of the fused scan + Top-K (host logic only)."""
+    """The automatic choice of the fused scan + Top-K (host logic only): long
+    decode contexts, and every step whose scan is prefill-shaped (its FP8
+    scores are re-scored FP32-accurately only inside the fused call)."""
     from compressed_kv_cache_02_amd.group import fused_topk_auto
     assert C.INDEX_TOPK_MAX_CAP == 1 << 20
     assert fused_topk_auto(1, 1 << 20) and fused_topk_auto(1, 524288)
     assert fused_topk_auto(4096, 133120) and fused_topk_auto(64, 1000)
-    assert not fused_topk_auto(1, 65536) and not fused_topk_auto(63, 200000)
+    assert fused_topk_auto(63, 200000) and fused_topk_auto(4, 8192)
+    assert not fused_topk_auto(1, 65536) and not fused_topk_auto(3, 200000)
     assert not fused_topk_auto(1, (1 << 20) + 8) and not fused_topk_auto(4096, 1 << 21)
 
 

@@ -34,7 +34,9 @@ def build_cache(inp, w, B):
 def run_gpu(w, inp, B, write=None):
     cache = build_cache(inp, w, B)
     n_vis = visible_entries(inp["q_pos"], w.m).to(torch.int32)
-    g = LayerGroup(w.kind, B, w.T, w.n_cap, keep_scores=True)
+    # score buffers are kept for the comparison with the oracle where the scan is
+    # decode-shaped; a prefill-shaped step (c0's 4 tokens) takes the fused Top-K
+    g = LayerGroup(w.kind, B, w.T, w.n_cap, keep_scores=w.T < C.PREFILL_MIN_T_FP8)
     g.step(inp["k_idx"], cache, n_vis, inp["q_pos"], inp["swa_pos0"], inp["q_idx"], inp["w"],
            inp["q"], inp["swa"], write=write)
     torch.cuda.synchronize()
@@ -60,9 +62,9 @@ def test_c0_full_decode_end_to_end():
     _stage("c0 group", w)
     inp = _inputs(w, w.B)
     g, _ = run_gpu(w, inp, w.B)
-    checked, swaps = check_group(w, inp, g, w.B)
-    print("attention checked:", checked, "near-tie swaps:", swaps)
-    assert checked >= w.B * w.T - swaps
+    st = check_group(w, inp, g, w.B)
+    print(st.line())
+    assert st.attn == st.queries * len(g.sched) and st.queries == w.B * w.T
 
 
 def test_decoder_group_small_context():
@@ -72,9 +74,9 @@ def test_decoder_group_small_context():
     _stage("decoder group", w)
     inp = _inputs(w, B, seed=3)
     g, _ = run_gpu(w, inp, B)
-    checked, swaps = check_group(w, inp, g, B)
-    print("attention checked:", checked, "near-tie swaps:", swaps)
-    assert checked >= 7 * B - 2 * swaps
+    st = check_group(w, inp, g, B)
+    print(st.line())
+    assert st.attn == st.queries * len(g.sched) and st.queries == B * w.T
     # Reuse layers alias their source buffers; source indices never change
     snap = [to_np(x).copy() for x in g.idx]
     for li, (m, src) in enumerate(g.sched):
@@ -97,9 +99,9 @@ def test_encoder_group_write_path_outliers():
     for b in range(B):
         inp["main"][b] = inp["main"][b].clone()
         inp["main"][b][n_cap - 1] = inp["write_bf16"][b]
-    checked, swaps = check_group(w, inp, g, B)
-    print("attention checked:", checked, "near-tie swaps:", swaps)
-    assert checked >= 6 * B - 5 * swaps
+    st = check_group(w, inp, g, B)
+    print(st.line())
+    assert st.attn == st.queries * len(g.sched) and st.queries == B * w.T
     # the written rows are bit-exact
     oc = [OracleCache(inp["main"][b], w.m) for b in range(B)]
     got = to_np(cache)[:, n_cap - 1]
@@ -121,6 +123,6 @@ def test_encoder_group_fused_topk():
     g.step(inp["k_idx"], cache, n_vis, inp["q_pos"], inp["swa_pos0"], inp["q_idx"], inp["w"],
            inp["q"], inp["swa"])
     torch.cuda.synchronize()
-    checked, swaps = check_group(w, inp, g, B)
-    print("attention checked:", checked, "near-tie swaps:", swaps)
-    assert checked >= 6 * B - 5 * swaps
+    st = check_group(w, inp, g, B)
+    print(st.line())
+    assert st.attn == st.queries * len(g.sched) and st.queries == B * w.T

@@ -128,9 +128,13 @@ def test_index_score_full(B, T, n_cap):
 @pytest.mark.parametrize("B,T,n_cap", [(2, 77, 10003), (1, 64, 4096), (1, 130, 300)])
 def test_index_score_prefill_shape(B, T, n_cap):
     """Many queries per sequence take the prefill kernel (a shared FP8
-    contraction); its scores and block maxima must equal, bit for bit, those of
-    the per-query decode kernel, and lie within the float32 bound of the oracle.
-    T and n_cap are ragged (not multiples of the 32-query / 4,096-key tiles)."""
+    contraction). Its scores lie within the FP8 contraction bound of the
+    oracle (the instruction truncates products below 2^-13 of its largest),
+    its block maxima are the maxima of its own scores, bit for bit, and the
+    same queries scored one at a time by the decode-shaped kernel lie within
+    the float32 bound. T and n_cap are ragged (not multiples of the 32-query /
+    4,096-key tiles)."""
+    from tests.helpers import fp8_contraction_bound
     _stage("index_score prefill", B, T, n_cap)
     q, w, k = _idx_inputs(B, T, n_cap, 7 + n_cap)
     rng = np.random.default_rng(T)
@@ -146,28 +150,36 @@ def test_index_score_prefill_shape(B, T, n_cap):
     scores = torch.empty((B, T, n_cap), dtype=torch.float32, device=DEV)
     bmax = torch.empty((B, T, nb), dtype=torch.float32, device=DEV)
     C.csa2_index_score(C.CSA2_FULL, q, w, k, n_vis, None, scores, bmax)
+    torch.cuda.synchronize()
     one_s = torch.empty((1, 1, n_cap), dtype=torch.float32, device=DEV)
     one_b = torch.empty((1, 1, nb), dtype=torch.float32, device=DEV)
     sn, bn = to_np(scores), to_np(bmax)
     qn, wn, kn = to_np(q), to_np(w), to_np(k)
     for b in range(B):
         for t in range(T):
-            C.csa2_index_score(C.CSA2_FULL, q[b:b + 1, t:t + 1], w[b:b + 1, t:t + 1], k[b:b + 1],
-                               n_vis[b:b + 1, t:t + 1].clone(), None, one_s, one_b)
-            assert np.array_equal(to_np(one_s)[0, 0].view(np.uint32), sn[b, t].view(np.uint32)), (b, t)
-            assert np.array_equal(to_np(one_b)[0, 0].view(np.uint32), bn[b, t].view(np.uint32)), (b, t)
+            assert np.array_equal(bn[b, t], OI.block_max(sn[b, t], nv[b, t])), (b, t)
     for b in range(B):
+        kv = OF.e4m3_decode(kn[b])
         for t in sorted({0, 1, 2, T // 2, T - 1}):
             ref = OI.index_scores(qn[b, t], wn[b, t], kn[b], nv[b, t])
-            assert_scores_close(sn[b, t], ref, score_bound(qn[b, t], wn[b, t], kn[b]),
-                                "b%d t%d" % (b, t))
+            qv = OF.e4m3_decode(qn[b, t].reshape(32, 128))
+            assert_scores_close(sn[b, t], ref, fp8_contraction_bound(qv, wn[b, t], kv),
+                                "prefill-shaped b%d t%d" % (b, t))
+            C.csa2_index_score(C.CSA2_FULL, q[b:b + 1, t:t + 1], w[b:b + 1, t:t + 1], k[b:b + 1],
+                               n_vis[b:b + 1, t:t + 1].clone(), None, one_s, one_b)
+            torch.cuda.synchronize()
+            assert_scores_close(to_np(one_s)[0, 0], ref, score_bound(qn[b, t], wn[b, t], kn[b]),
+                                "decode-shaped b%d t%d" % (b, t))
 
 
 @pytest.mark.parametrize("T", [1, 70])
 def test_full_scan_block_maxima_only_and_rescoring(T):
     """A FULL scan that writes only block maxima gives the same maxima bit for
-    bit, and REINDEX over a pool reproduces the FULL scores of its positions bit
-    for bit (so a Top-K over re-scored pool positions is the Full Top-K)."""
+    bit. REINDEX over a pool reproduces the decode-shaped FULL scores of its
+    positions bit for bit (so a Top-K over re-scored pool positions is the Full
+    Top-K); against the prefill-shaped scan (T = 70) it agrees within the FP8
+    contraction bound and with the oracle within the float32 bound."""
+    from tests.helpers import fp8_contraction_bound
     B, n_cap = 2, 40003
     _stage("scan bmax-only + rescoring", B, T, n_cap)
     q, w, k = _idx_inputs(B, T, n_cap, 11)
@@ -190,6 +202,8 @@ def test_full_scan_block_maxima_only_and_rescoring(T):
     torch.cuda.synchronize()
     assert np.array_equal(to_np(bmax).view(np.uint32), to_np(bmax2).view(np.uint32))
     sn, spn, pn = to_np(scores), to_np(sp), to_np(pool)
+    qn, wn, kn = to_np(q), to_np(w), to_np(k)
+    prefill = T >= C.PREFILL_MIN_T_FP8
     for b in range(B):
         for t in range(T):
             cand = OS.reindex_candidates(pn[b, t], nv[b, t])
@@ -197,8 +211,19 @@ def test_full_scan_block_maxima_only_and_rescoring(T):
             pos_all = (np.maximum(p, 0)[:, None] * 8 + np.arange(8)[None, :]).reshape(-1)
             valid = np.repeat(p >= 0, 8) & (pos_all < nv[b, t])
             assert np.array_equal(pos_all[valid], cand)
-            assert np.array_equal(spn[b, t][valid].view(np.uint32), sn[b, t][cand].view(np.uint32))
             assert np.all(np.isneginf(spn[b, t][~valid]))
+            if not prefill:
+                assert np.array_equal(spn[b, t][valid].view(np.uint32),
+                                      sn[b, t][cand].view(np.uint32))
+            elif t in (0, T // 2, T - 1):
+                kv = OF.e4m3_decode(kn[b][cand])
+                qv = OF.e4m3_decode(qn[b, t].reshape(32, 128))
+                lim = fp8_contraction_bound(qv, wn[b, t], kv) + score_bound(qn[b, t], wn[b, t],
+                                                                             kn[b][cand])
+                assert np.all(np.abs(spn[b, t][valid].astype(np.float64) - sn[b, t][cand]) <= lim)
+                ref = OI.index_scores(qn[b, t], wn[b, t], kn[b], nv[b, t], positions=cand)
+                assert_scores_close(spn[b, t][valid], ref,
+                                    score_bound(qn[b, t], wn[b, t], kn[b][cand]), "reindex")
 
 
 def test_index_score_reindex():
@@ -509,12 +534,14 @@ def test_sparse_attn_scale_and_outliers():
                                   (2, 1), (3, 1), (4, 1), (5, 1), (7, 1), (16, 1), (17, 1), (33, 1)])
 def test_multi_token_decode_shares_keys(T, kf):
     """Several query tokens of one sequence (Full mode) are scored in groups
-    that share each key tile (4 or 2 per wave below the prefill threshold, 16
-    or 32 per work-group from it on: T = 3 | 4 with E4M3 keys and 4 | 5 with
-    FP4 keys straddle it, 16 | 17 the tile sizes); every query's scores and
-    block maxima must equal, bit for
-    bit, those of a single-query call, and lie within the score bound of the
-    oracle. Visibility is causal per query (T and n_cap ragged)."""
+    that share each key tile (2 per wave below the prefill threshold, 16 or 32
+    per work-group from it on: T = 3 | 4 with E4M3 keys and 4 | 5 with FP4 keys
+    straddle it, 16 | 17 the tile sizes). Below the threshold every query's
+    scores and block maxima must equal, bit for bit, those of a single-query
+    call and lie within the float32 bound of the oracle; from it on (the FP8
+    contraction) within the FP8 contraction bound, with block maxima equal to
+    the maxima of the kernel's own scores. Visibility is causal per query (T
+    and n_cap ragged)."""
     from oracle import mxfp4 as OM
     B, n_cap = 2, 20011
     _stage("multi-token decode", T, kf)
@@ -547,8 +574,12 @@ def test_multi_token_decode_shares_keys(T, kf):
     one_s = torch.empty((1, 1, n_cap), dtype=torch.float32, device=DEV)
     one_b = torch.empty((1, 1, nb), dtype=torch.float32, device=DEV)
     sn, bn, qn, wn = to_np(scores), to_np(bmax), to_np(q), to_np(w)
+    prefill = T >= (C.PREFILL_MIN_T_FP4 if kf else C.PREFILL_MIN_T_FP8)
     for b in range(B):
         for t in range(T):
+            if prefill:
+                assert np.array_equal(bn[b, t], OI.block_max(sn[b, t], nv[b, t])), (b, t)
+                continue
             if kf:
                 C.csa2_index_score_fp4k(C.CSA2_FULL, q[b:b + 1, t:t + 1], w[b:b + 1, t:t + 1],
                                         codes[b:b + 1], scl[b:b + 1], n_vis[b:b + 1, t:t + 1].clone(),
@@ -561,12 +592,12 @@ def test_multi_token_decode_shares_keys(T, kf):
     for b, t in [(0, 0), (0, T - 1), (1, 0), (1, T - 1), (1, T // 2)]:
         ref = OI.index_scores(qn[b, t], wn[b, t], oc[b], nv[b, t],
                               k_scales=None if osc is None else osc[b])
-        if kf:
-            qa = np.abs(OF.e4m3_decode(qn[b, t].reshape(32, 128)))
-            ka = np.abs(OM.dequantize_index_keys(oc[b], osc[b]))
-            bound = 160.0 * 2.0 ** -24 * (ka @ qa.T) @ np.abs(wn[b, t].astype(np.float64))
-        else:
-            bound = score_bound(qn[b, t], wn[b, t], oc[b])
+        qv = OF.e4m3_decode(qn[b, t].reshape(32, 128))
+        kv = OM.dequantize_index_keys(oc[b], osc[b]) if kf else OF.e4m3_decode(oc[b])
+        bound = 160.0 * 2.0 ** -24 * (np.abs(kv) @ np.abs(qv).T) @ np.abs(wn[b, t].astype(np.float64))
+        if prefill:
+            from tests.helpers import fp8_contraction_bound
+            bound = fp8_contraction_bound(qv, wn[b, t], kv)
         assert_scores_close(sn[b, t], ref, bound, "b%d t%d" % (b, t))
 
 
@@ -576,9 +607,13 @@ def test_multi_token_decode_shares_keys(T, kf):
                                           (2, 6, 40009, 0), (2, 12, 40009, 1), (2, 3, 60013, 1),
                                           (1, 17, 30011, 1)])
 def test_index_topk_fused_equals_scan_then_topk(B, T, n_cap, kf):
-    """csa2_index_topk writes no score row (block maxima, the 512 best blocks
-    re-scored) yet must give byte for byte the Top-512 of csa2_index_score(FULL)
-    followed by csa2_topk(FULL); two queries are also checked against the oracle."""
+    """csa2_index_topk writes no score row (block maxima, the best blocks
+    re-scored) yet must give byte for byte the exact Top-512 of the
+    FP32-accurate decode-shaped scores: those of csa2_index_score(FULL)
+    followed by csa2_topk(FULL) below the prefill threshold, and from it on
+    (where the fused call narrows with the FP8 contraction's block maxima to
+    1,024 blocks) those of the same queries scored one at a time; two queries
+    are also checked against the oracle."""
     from oracle import mxfp4 as OM
     from tests.helpers import assert_topk_near
     _stage("index_topk fused", B, T, n_cap, kf)
@@ -607,10 +642,23 @@ def test_index_topk_fused_equals_scan_then_topk(B, T, n_cap, kf):
     C.csa2_index_topk(q, w, keys, n_vis, idx, ws)
     scores = torch.empty((B, T, n_cap), dtype=torch.float32, device=DEV)
     bmax = torch.empty((B, T, (n_cap + 7) // 8), dtype=torch.float32, device=DEV)
-    if kf:
-        C.csa2_index_score_fp4k(C.CSA2_FULL, q, w, codes, scl, n_vis, None, scores, bmax)
+
+    def full_scan(qq, ww, nv, s, bm):
+        if kf:
+            C.csa2_index_score_fp4k(C.CSA2_FULL, qq, ww, codes, scl, nv, None, s, bm)
+        else:
+            C.csa2_index_score(C.CSA2_FULL, qq, ww, keys, nv, None, s, bm)
+    if T < (C.PREFILL_MIN_T_FP4 if kf else C.PREFILL_MIN_T_FP8):
+        full_scan(q, w, n_vis, scores, bmax)
     else:
-        C.csa2_index_score(C.CSA2_FULL, q, w, keys, n_vis, None, scores, bmax)
+        # the decode-shaped (FP32-accurate) scores, one query token at a time
+        for t in range(T):
+            one_s = torch.empty((B, 1, n_cap), dtype=torch.float32, device=DEV)
+            one_b = torch.empty((B, 1, (n_cap + 7) // 8), dtype=torch.float32, device=DEV)
+            full_scan(q[:, t:t + 1].contiguous(), w[:, t:t + 1].contiguous(),
+                      n_vis[:, t:t + 1].clone(), one_s, one_b)
+            scores[:, t] = one_s[:, 0]
+            bmax[:, t] = one_b[:, 0]
     ref = torch.empty((B, T, 512), dtype=torch.int32, device=DEV)
     ws2 = torch.empty(max(256, C.csa2_workspace_bytes(C.CSA2_OP_TOPK, C.CSA2_FULL, B, T, n_cap)),
                       dtype=torch.uint8, device=DEV)
