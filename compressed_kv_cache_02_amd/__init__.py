@@ -19,6 +19,7 @@ __all__ = [
     "csa2_quantize_kv", "csa2_index_score", "csa2_build_pool", "csa2_topk",
     "csa2_sparse_attn", "csa2_quantize_index_k", "csa2_index_score_fp4k",
     "csa2_compress_tokens", "csa2_quantize_e4m3", "csa2_index_topk", "CSA2_OP_INDEX_TOPK",
+    "csa2_sparse_attn_ring",
 ]
 
 CSA2_FULL, CSA2_REINDEX, CSA2_REUSE = 0, 1, 2
@@ -59,6 +60,8 @@ _SIGS = {
     "csa2_topk": (_i32, [_i32, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i64, _vp, _vp, _sz, _vp]),
     "csa2_sparse_attn": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i64, _i32, _f32,
                                 _vp, _vp, _sz, _vp]),
+    "csa2_sparse_attn_ring": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i64, _i32, _f32,
+                                     _vp, _vp, _sz, _vp]),
 }
 
 
@@ -314,10 +317,7 @@ def csa2_topk(mode, scores, n_vis, pool, src_idx, n_cap, idx, ws, stream=None, b
                                         0 if ws is None else ws.numel(), _stream(stream)))
 
 
-def csa2_sparse_attn(q, cache, idx, swa, q_pos, swa_pos0, scale, out, ws, stream=None):
-    """q [B,T,64,512] bf16, cache [B,n_cap,288] uint8, idx [B,T,512] int32,
-    swa [B,S,512] uint8, q_pos [B,T] int64, swa_pos0 [B] int64,
-    out [B,T,64,512] f32."""
+def _attn_args(q, cache, idx, swa, q_pos, swa_pos0, out):
     import torch
     B, T = q.shape[0], q.shape[1]
     n_cap = cache.shape[1]
@@ -329,8 +329,26 @@ def csa2_sparse_attn(q, cache, idx, swa, q_pos, swa_pos0, scale, out, ws, stream
     _expect(q_pos, "q_pos", torch.int64, (B, T))
     _expect(swa_pos0, "swa_pos0", torch.int64, (B,))
     _expect(out, "out", torch.float32, (B, T, HEADS, DIM))
+    return B, T, n_cap, S
+
+
+def csa2_sparse_attn(q, cache, idx, swa, q_pos, swa_pos0, scale, out, ws=None, stream=None):
+    """q [B,T,64,512] bf16, cache [B,n_cap,288] uint8, idx [B,T,512] int32,
+    swa [B,S,512] uint8 (row s = token swa_pos0 + s), q_pos [B,T] int64,
+    swa_pos0 [B] int64, out [B,T,64,512] f32; ws: uint8 device workspace of
+    csa2_workspace_bytes(CSA2_OP_SPARSE_ATTN, ...) bytes (None when that is 0)."""
+    B, T, n_cap, S = _attn_args(q, cache, idx, swa, q_pos, swa_pos0, out)
     _check("csa2_sparse_attn", lib().csa2_sparse_attn(_p(q), _p(cache), _p(idx), _p(swa),
                                                       _p(q_pos), _p(swa_pos0), B, T, n_cap, S,
                                                       float(scale), _p(out), _p(ws),
                                                       0 if ws is None else ws.numel(),
                                                       _stream(stream)))
+
+
+def csa2_sparse_attn_ring(q, cache, idx, swa, q_pos, swa_pos0, scale, out, ws=None, stream=None):
+    """csa2_sparse_attn over a ring-buffer window: token t of sequence b in row
+    t mod S of swa [B,S,512]; rows hold tokens [swa_pos0, swa_pos0 + S)."""
+    B, T, n_cap, S = _attn_args(q, cache, idx, swa, q_pos, swa_pos0, out)
+    _check("csa2_sparse_attn_ring", lib().csa2_sparse_attn_ring(
+        _p(q), _p(cache), _p(idx), _p(swa), _p(q_pos), _p(swa_pos0), B, T, n_cap, S,
+        float(scale), _p(out), _p(ws), 0 if ws is None else ws.numel(), _stream(stream)))

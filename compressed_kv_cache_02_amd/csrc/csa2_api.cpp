@@ -298,10 +298,12 @@ int csa2_topk(int mode, const float* scores, const float* bmax, const int32_t* n
   return status_of(csa2::launch_topk_full(scores, bmax, pool, n_vis, Q, n_cap, idx, ws, st));
 }
 
-int csa2_sparse_attn(const void* q_bf16, const uint8_t* cache, const int32_t* idx,
-                     const uint8_t* swa, const int64_t* q_pos, const int64_t* swa_pos0, int B,
-                     int T, int64_t n_cap, int S, float softmax_scale, float* out, void* ws,
-                     size_t ws_bytes, void* stream) {
+namespace {
+
+int sparse_attn(const void* q_bf16, const uint8_t* cache, const int32_t* idx, const uint8_t* swa,
+                const int64_t* q_pos, const int64_t* swa_pos0, int B, int T, int64_t n_cap, int S,
+                int ring, float softmax_scale, float* out, void* ws, size_t ws_bytes,
+                void* stream) {
   if (!sizes_ok(B, T, n_cap) || S < 1) return CSA2_EINVAL;
   if (!std::isfinite(softmax_scale)) return CSA2_EINVAL;
   if (!aligned16(q_bf16) || !aligned16(cache) || !aligned16(idx) || !aligned16(swa) ||
@@ -313,8 +315,26 @@ int csa2_sparse_attn(const void* q_bf16, const uint8_t* cache, const int32_t* id
     if (ws_bytes < need) return CSA2_EWORKSPACE;
   }
   return status_of(csa2::launch_sparse_attn(static_cast<const uint16_t*>(q_bf16), cache, idx, swa,
-                                            q_pos, swa_pos0, B, T, n_cap, S, softmax_scale, out,
-                                            ws, as_stream(stream)));
+                                            q_pos, swa_pos0, B, T, n_cap, S, ring, softmax_scale,
+                                            out, need > 0 ? ws : nullptr, as_stream(stream)));
+}
+
+}  // namespace
+
+int csa2_sparse_attn(const void* q_bf16, const uint8_t* cache, const int32_t* idx,
+                     const uint8_t* swa, const int64_t* q_pos, const int64_t* swa_pos0, int B,
+                     int T, int64_t n_cap, int S, float softmax_scale, float* out, void* ws,
+                     size_t ws_bytes, void* stream) {
+  return sparse_attn(q_bf16, cache, idx, swa, q_pos, swa_pos0, B, T, n_cap, S, 0, softmax_scale,
+                     out, ws, ws_bytes, stream);
+}
+
+int csa2_sparse_attn_ring(const void* q_bf16, const uint8_t* cache, const int32_t* idx,
+                          const uint8_t* swa, const int64_t* q_pos, const int64_t* swa_pos0, int B,
+                          int T, int64_t n_cap, int S, float softmax_scale, float* out, void* ws,
+                          size_t ws_bytes, void* stream) {
+  return sparse_attn(q_bf16, cache, idx, swa, q_pos, swa_pos0, B, T, n_cap, S, 1, softmax_scale,
+                     out, ws, ws_bytes, stream);
 }
 
 }  // extern "C"

@@ -80,11 +80,14 @@ hipError_t launch_topk_of_blocks(const float* vals, const int32_t* sel_blk, int 
 hipError_t launch_topk_direct(const float* scores, const int32_t* n_vis, int Q, int64_t n_cap,
                               int32_t* out, hipStream_t st);
 
-// Sparse attention.
+// Sparse attention; the workspace holds the key slices' partial results when
+// a call has fewer than 64 queries (attn_workspace_bytes). ring != 0: the
+// window buffer is a ring, token t in row t mod S; else row s holds token
+// swa_pos0 + s.
 size_t attn_workspace_bytes(int Q);
 hipError_t launch_sparse_attn(const uint16_t* q, const uint8_t* cache, const int32_t* idx,
                               const uint8_t* swa, const int64_t* q_pos, const int64_t* swa_pos0,
-                              int B, int T, int64_t n_cap, int S, float scale, float* out,
+                              int B, int T, int64_t n_cap, int S, int ring, float scale, float* out,
                               void* ws, hipStream_t st);
 
 }  // namespace csa2

@@ -7,32 +7,51 @@
 // window KV stays FP8 ("DeepSeek-V4.1-Flash：全局 KV 仅 890 B/token", 第三刀);
 // every layer has its own query and window ("DeepSeek V4.1 Flash vs V4 Pro",
 // 黑科技之二). Key = value = the dequantised 512-wide row (reading in csa2.h).
+// The window buffer is linear (row s = token swa_pos0 + s) or a ring (token t
+// in row t mod S), the latter for a decode loop that keeps the last n_win
+// tokens of window KV per layer ("DeepSeek V4.1 Flash vs V4 Pro", 黑科技之三).
 //
-// Common to both work shapes: rows are dequantised to fp16 exactly with the
+// Common to all work shapes: rows are dequantised to fp16 exactly with the
 // gfx950 converts (v_cvt_scalef32_pk_f16_fp4 with the power-of-two part of the
 // E4M3 scale, then one v_pk_mul_f16 by its mantissa part; window rows with
-// v_cvt_scalef32_pk_f16_fp8). Q.K: v_mfma_f32_16x16x32_f16 with 16 keys as A
-// and 16 query heads as B (each head scaled by a power of two into fp16 range;
-// the logits are scaled back). P.V: v_mfma_f32_16x16x32_f16 with V^T as A,
-// read from a row-major fp16 LDS copy by the transposing LDS read
-// ds_read_b64_tr_b16, and P as B. P is split as P = hi + lo with both parts in
-// fp16 (two MFMAs per tile), which keeps the product accurate to about 2^-22
-// of P even when rows carry large outlier channels.
+// v_cvt_scalef32_pk_f16_fp8). Q.K: v_mfma_f32_16x16x32_f16 with 16 keys as A and
+// 16 query heads as B (each head scaled by a power of two into fp16 range; the
+// logits are scaled back). P.V: v_mfma_f32_16x16x32_f16 with V^T as A, read
+// from a row-major fp16 LDS copy by the transposing LDS read
+// ds_read_b64_tr_b16, and P as B; P = hi + lo in fp16 (two MFMAs per tile),
+// which keeps the product accurate to about 2^-22 of P even for rows with large
+// outlier channels. Work-groups that gather the same rows get ids equal mod 8,
+// so the dispatcher's round-robin over the 8 XCDs puts them on one XCD (one L2).
 //
-// Two work shapes:
-//   prefill (512 queries or more): one work-group of 8 waves per query over
-//          its 640 key slots in chunks of 64 with an online softmax; wave w
-//          serves 16 heads (w % 4), and the 4 head groups share each
-//          dequantised chunk through LDS.
-//   decode (fewer than 512 queries): one work-group of 8 waves per (query, 16-head
-//          group, slice of 128 key slots). Each lane dequantises 128 channels
-//          of one key straight into its Q.K operand registers (both operands
-//          use the same permuted channel order) and into the row-major LDS
-//          copy; wave w forms the logits of its 16 keys, the work-group agrees
-//          on the slice maximum, and wave w accumulates P.V for output channels
-//          64w..64w+63. The query is converted once per work-group (two heads
-//          per wave) and shared through LDS. Slices are merged by log-sum-exp
-//          in a second kernel.
+// Three work shapes, by the number of queries Q in the call:
+//   Q < 64 (decode): one 8-wave work-group per (query, 16 heads, slice of 128
+//          key slots); each lane dequantises 128 channels of one key straight
+//          into its Q.K operand registers and the slice's LDS copy; the waves
+//          agree on the slice maximum through LDS; slices are merged by
+//          log-sum-exp in a second kernel (k_attn_merge). Spreads a few
+//          queries over 20 work-groups each.
+//   64 <= Q < 512: one 4-wave work-group per (query, 16 heads), no workspace.
+//          The query's 640 key slots form 20 steps of 32; wave w takes steps
+//          w, w+4, w+8, w+12 (selected rows) and 16+w (window), so every wave
+//          has the same mix, known at compile time, and runs its own online
+//          softmax over its 160 keys with no barrier:
+//          * lane (g, c) loads key c of a 16-key tile, channels 128g..128g+127,
+//            and dequantises them straight into its Q.K operand registers (both
+//            operands in the same permuted channel order) and into the wave's
+//            own 32-row fp16 LDS tile;
+//          * the logit of key 4g + r of each tile for head c lands in lane
+//            (g, c), the lane and order P.V's B operand needs, so P never
+//            leaves the registers;
+//          * the running maximum is raised only when a step's maximum exceeds
+//            it by more than 8 (p stays below e^8, inside fp16), so the
+//            accumulators are rescaled about once per wave.
+//          At the end the four waves' (max, sum, output) are merged by
+//          log-sum-exp through LDS and the work-group writes its 16 heads'
+//          output directly.
+//   Q >= 512 (prefill): one 8-wave work-group per query over its 640 key slots
+//          in chunks of 64 with an online softmax; wave w serves 16 heads
+//          (w % 4), and the 4 head groups share each dequantised chunk through
+//          LDS (each row is dequantised once for all 64 heads).
 #include "device_common.hpp"
 #include "launchers.hpp"
 
@@ -40,10 +59,27 @@ namespace csa2 {
 namespace {
 
 constexpr int kSlots = kTopK + kWindow;           // 640 key slots per query
-constexpr int kKrowStride = kDim + 8;             // fp16 elements per LDS key row
-constexpr int kHG = 16;                           // heads per head group
-constexpr int kHeadGroups = kHeads / kHG;
-constexpr int kPrefillMinQueries = 512;
+constexpr int kHG = 16;                           // heads per work-group
+constexpr int kHeadGroups = kHeads / kHG;         // 4
+constexpr int kWaves = 4;
+constexpr int kThreads = kWaves * 64;
+constexpr int kSlotsPerWave = kSlots / kWaves;    // 160
+constexpr int kStepKeys = 32;                     // keys per softmax step (one P.V MFMA)
+constexpr int kSteps = kSlotsPerWave / kStepKeys; // 5 per wave
+constexpr int kMainSteps = kTopK / kStepKeys / kWaves;   // 4 per wave, then 1 window step
+constexpr int kPvGroup = 4;                       // channel tiles per P.V issue group
+constexpr int kVRow = kDim + 8;                   // fp16 per LDS key row
+constexpr int kDecodeMaxQueries = 64;             // below: the split decode shape
+constexpr int kPrefillMinQueries = 512;           // from here: one work-group per query
+constexpr int kOutRow = kDim + 4;                 // floats per LDS row of the final merge
+constexpr float kLazyMax = 8.0f;                  // headroom before the running max moves
+constexpr int kXcds = 8;
+static_assert(kSlotsPerWave % kStepKeys == 0, "whole steps per wave");
+static_assert(kTopK % (kStepKeys * kWaves) == 0 && kWindow == kStepKeys * kWaves,
+              "each wave: whole steps of selected rows, then one window step");
+static_assert(kWaves * kHG * kOutRow * 4 <= kWaves * kStepKeys * kVRow * 2,
+              "the final merge fits in the key tiles");
+static_assert(kThreads == 256, "one thread per E4M3 scale code fills the table");
 
 typedef _Float16 v2h __attribute__((ext_vector_type(2)));
 
@@ -55,13 +91,14 @@ struct AttnArgs {
   const int64_t* q_pos;
   const int64_t* swa_pos0;
   int T;
+  int Q;
   int64_t n_cap;
   int S;
+  int ring;
   float scale;
   float* out;
-  float* part;     // [Q][splits][64][512] unnormalised outputs
-  float* part_ml;  // [Q][splits][64][2] running max and sum
-  int splits;
+  float* part;     // decode shape: [Q][slices][64][512] unnormalised outputs
+  float* part_ml;  // decode shape: [Q][slices][64][2] running max and sum
 };
 
 // Exponent shift that brings a per-head maximum |q| into [2^14, 2^15): q * 2^s
@@ -94,28 +131,6 @@ __device__ __forceinline__ float bf16x8_absmax(const uint4& raw) {
   }
   return m;
 }
-
-// ------------------------------------------------------- decode kernel --
-
-// Decode shape: 5 slices of 128 key slots (slices 0-3 hold the selected rows,
-// slice 4 the window), one work-group of 8 waves per (query, 16-head group,
-// slice). Three phases separated by two barriers:
-//   1. every thread dequantises 4 keys x 32 channels into a row-major fp16
-//      buffer of all 128 keys;
-//   2. wave w forms the logits of keys 16w..16w+15 for the 16 heads over all
-//      512 channels and publishes its per-head maximum; with the slice maximum
-//      it writes p = exp(z - max) of its keys (fp16 hi + lo) and their sum;
-//   3. wave w accumulates P.V for output channels 64w..64w+63 over the 128 keys,
-//      reading V through the transposing LDS read (ds_read_b64_tr_b16).
-// The slices are merged by log-sum-exp in a second kernel.
-constexpr int kDecSplits = 5;
-constexpr int kDecKeys = kSlots / kDecSplits;     // 128 key slots per work-group
-constexpr int kDecWaves = 8;
-constexpr int kDecThreads = kDecWaves * 64;
-constexpr int kPRow = kDecKeys + 8;               // fp16 elements per LDS row of P
-static_assert(kDecKeys == 16 * kDecWaves, "one 16-key tile per wave");
-static_assert(kTopK % kDecKeys == 0, "a slice holds only selected rows or only window rows");
-static_assert(kDecThreads / 16 * 4 == kDecKeys, "4 keys x 32 channels per thread");
 
 typedef _Float16 v4h __attribute__((ext_vector_type(4)));
 typedef short v4s __attribute__((ext_vector_type(4)));
@@ -163,6 +178,31 @@ __device__ __forceinline__ void fp4x16_to_f16(uint32_t w0, uint32_t w1, uint32_t
   pr[6] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w1, hw, 2) * m2);
   pr[7] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w1, hw, 3) * m2);
 }
+// The two factors of an E4M3 scale code c for the FP4 dequantisation above,
+// as one table entry: .x = the float power of two 2^(E-7) (2^-6 for a
+// subnormal scale, E = 0), .y = its mantissa part twice as an fp16 pair
+// (1 + M/8, or M/8 for E = 0). Filled once per work-group into LDS.
+__device__ __forceinline__ uint2 scale_entry(uint32_t c) {
+  const uint32_t E = (c >> 3) & 15u, M = c & 7u;
+  const uint32_t hw = E ? (E + 120u) << 23 : 118u << 23;
+  const _Float16 mf = E ? __builtin_bit_cast(_Float16, (uint16_t)(0x3C00u | (M << 7)))
+                        : (_Float16)(float)M;
+  const uint32_t mb = __builtin_bit_cast(uint16_t, mf);
+  return make_uint2(hw, mb | (mb << 16));
+}
+// 16 FP4 codes with their scale's table entry -> 8 fp16 pairs (exact).
+__device__ __forceinline__ void fp4x16_to_f16_t(uint32_t w0, uint32_t w1, uint2 e, uint32_t* pr) {
+  const float hw = __uint_as_float(e.x);
+  const v2h m2 = __builtin_bit_cast(v2h, e.y);
+  pr[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w0, hw, 0) * m2);
+  pr[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w0, hw, 1) * m2);
+  pr[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w0, hw, 2) * m2);
+  pr[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w0, hw, 3) * m2);
+  pr[4] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w1, hw, 0) * m2);
+  pr[5] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w1, hw, 1) * m2);
+  pr[6] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w1, hw, 2) * m2);
+  pr[7] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w1, hw, 3) * m2);
+}
 // 4 E4M3 bytes -> 2 fp16 pairs (exact).
 __device__ __forceinline__ void fp8x4_to_f16(uint32_t w, uint32_t* pr) {
   pr[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false));
@@ -180,11 +220,49 @@ __device__ __forceinline__ float half_max(float m) {
   return fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
 }
 
+
+// Maximum over each row of 16 lanes (DPP: swap neighbours, swap pairs, mirror
+// within half-rows, mirror the row).
+__device__ __forceinline__ float row16_max(float m) {
+  m = fmaxf(m, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(m), 0xB1, 0xF, 0xF, false)));
+  m = fmaxf(m, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(m), 0x4E, 0xF, 0xF, false)));
+  m = fmaxf(m, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(m), 0x141, 0xF, 0xF, false)));
+  m = fmaxf(m, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(m), 0x140, 0xF, 0xF, false)));
+  return m;
+}
+
+// Orders this wave's LDS accesses: waits for its LDS operations and keeps the
+// compiler from moving memory accesses across (lanes of one wave exchange
+// values through their private rows).
+__device__ __forceinline__ void wave_lds_sync() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+}
+
+// ------------------------------------------------------- decode kernel --
+
+// Decode shape: 5 slices of 128 key slots (slices 0-3 hold the selected rows,
+// slice 4 the window), one work-group of 8 waves per (query, 16-head group,
+// slice). Lane (grp, col) of wave w dequantises channels 128grp..128grp+127 of
+// key 16w + col into its Q.K operand registers and the slice's row-major LDS
+// copy; wave w forms the logits of its 16 keys for the 16 heads and publishes
+// its per-head maximum; with the slice maximum (after a barrier) it writes
+// p = exp(z - max) of its keys (fp16 hi + lo) and their sum; after a second
+// barrier wave w accumulates P.V for output channels 64w..64w+63 over the 128
+// keys, reading V through the transposing LDS read (ds_read_b64_tr_b16). The
+// slices are merged by log-sum-exp in a second kernel.
+constexpr int kDecSplits = 5;
+constexpr int kDecKeys = kSlots / kDecSplits;     // 128 key slots per work-group
+constexpr int kDecWaves = 8;
+constexpr int kDecThreads = kDecWaves * 64;
+constexpr int kPRow = kDecKeys + 8;               // fp16 elements per LDS row of P
+static_assert(kDecKeys == 16 * kDecWaves, "one 16-key tile per wave");
+static_assert(kTopK % kDecKeys == 0, "a slice holds only selected rows or only window rows");
+
 __global__ __launch_bounds__(kDecThreads) void k_sparse_attn_decode(AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t krow[kDecKeys * kKrowStride];
-  // fp16 query [16 heads][kKrowStride] until the logits are formed, then P
+  __shared__ __attribute__((aligned(16))) uint16_t krow[kDecKeys * kVRow];
+  // fp16 query [16 heads][kVRow] until the logits are formed, then P
   // (hi, lo) [16 heads][kPRow] each
-  constexpr int kQP = kHG * kKrowStride > 2 * kHG * kPRow ? kHG * kKrowStride : 2 * kHG * kPRow;
+  constexpr int kQP = kHG * kVRow > 2 * kHG * kPRow ? kHG * kVRow : 2 * kHG * kPRow;
   __shared__ __attribute__((aligned(16))) uint16_t qp_buf[kQP];
   __shared__ float wmax[kDecWaves][kHG];
   __shared__ float wsum[kDecWaves][kHG];
@@ -192,9 +270,14 @@ __global__ __launch_bounds__(kDecThreads) void k_sparse_attn_decode(AttnArgs a) 
   uint16_t* const qf = qp_buf;
   uint16_t* const pbuf = qp_buf;   // P hi at [0, kHG*kPRow), lo after it
 
-  const int qi = blockIdx.y;
-  const int hg = blockIdx.x % kHeadGroups;
-  const int split = blockIdx.x / kHeadGroups;
+  // ids 32j + 8g + x: unit 8j + x = (query, slice), head group g (the four
+  // head-group work-groups of a unit gather the same rows: one XCD, one L2)
+  const int id = blockIdx.x;
+  const int unit = (id / (kXcds * kHeadGroups)) * kXcds + id % kXcds;
+  const int hg = (id % (kXcds * kHeadGroups)) / kXcds;
+  if (unit >= a.Q * kDecSplits) return;            // the whole work-group, before any barrier
+  const int qi = unit / kDecSplits;
+  const int split = unit % kDecSplits;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
   const int col = lane & 15, grp = lane >> 4;
@@ -229,10 +312,10 @@ __global__ __launch_bounds__(kDecThreads) void k_sparse_attn_decode(AttnArgs a) 
   } else {
     const int64_t tq = a.q_pos[qi], pos0 = a.swa_pos0[b];
     const int64_t tok = tq - (kWindow - 1) + (slot0 + kk - kTopK);
-    const int64_t rr = tok - pos0;
-    ok = tok >= 0 && rr >= 0 && rr < a.S;
+    ok = tok >= 0 && tok >= pos0 && tok < pos0 + a.S;
+    const int64_t rr = !ok ? 0 : (a.ring ? tok % a.S : tok - pos0);
     const uint4* r4 = reinterpret_cast<const uint4*>(
-        a.swa + ((size_t)b * (size_t)a.S + (size_t)(ok ? rr : 0)) * kDim + 128 * grp);
+        a.swa + ((size_t)b * (size_t)a.S + (size_t)rr) * kDim + 128 * grp);
 #pragma unroll
     for (int i = 0; i < 8; ++i) raw[i] = r4[i];
   }
@@ -242,15 +325,15 @@ __global__ __launch_bounds__(kDecThreads) void k_sparse_attn_decode(AttnArgs a) 
     const float amax = half_max(fmaxf(bf16x8_absmax(qr0), bf16x8_absmax(qr1)));
     const int sh = q_shift(amax);
     const v8h h0 = q_to_f16(qr0, sh), h1 = q_to_f16(qr1, sh);
-    *reinterpret_cast<v8h*>(&qf[qh * kKrowStride + qc]) = h0;
-    *reinterpret_cast<v8h*>(&qf[qh * kKrowStride + qc + 8]) = h1;
+    *reinterpret_cast<v8h*>(&qf[qh * kVRow + qc]) = h0;
+    *reinterpret_cast<v8h*>(&qf[qh * kVRow + qc + 8]) = h1;
     if ((lane & 31) == 0) qsh[qh] = sh;
   }
   lds_barrier();
   v8h qreg[16];
 #pragma unroll
   for (int kb = 0; kb < 16; ++kb)
-    qreg[kb] = *reinterpret_cast<const v8h*>(&qf[col * kKrowStride + 128 * grp + 8 * kb]);
+    qreg[kb] = *reinterpret_cast<const v8h*>(&qf[col * kVRow + 128 * grp + 8 * kb]);
   const float zscale = ldexpf(a.scale, -qsh[col]);
 
   // ---- dequantise this lane's 128 channels: the Q.K operand in registers and
@@ -273,7 +356,7 @@ __global__ __launch_bounds__(kDecThreads) void k_sparse_attn_decode(AttnArgs a) 
       const uint4 hi = ok ? make_uint4(pr[4], pr[5], pr[6], pr[7]) : make_uint4(0u, 0u, 0u, 0u);
       kreg[2 * m] = __builtin_bit_cast(v8h, lo);
       kreg[2 * m + 1] = __builtin_bit_cast(v8h, hi);
-      uint4* dst = reinterpret_cast<uint4*>(&krow[kk * kKrowStride + 128 * grp + 16 * m]);
+      uint4* dst = reinterpret_cast<uint4*>(&krow[kk * kVRow + 128 * grp + 16 * m]);
       dst[0] = lo;
       dst[1] = hi;
     }
@@ -340,13 +423,13 @@ __global__ __launch_bounds__(kDecThreads) void k_sparse_attn_decode(AttnArgs a) 
     ph[ks] = *reinterpret_cast<const v8h*>(&pbuf[col * kPRow + ks * 32 + 8 * grp]);
     pl[ks] = *reinterpret_cast<const v8h*>(&pbuf[kHG * kPRow + col * kPRow + ks * 32 + 8 * grp]);
     const uint16_t* vsrc =
-        &krow[(ks * 32 + 8 * grp + (col >> 2)) * kKrowStride + wave * 64 + 4 * (col & 3)];
+        &krow[(ks * 32 + 8 * grp + (col >> 2)) * kVRow + wave * 64 + 4 * (col & 3)];
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) {
       const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
           (__attribute__((address_space(3))) v4s*)(vsrc + dt * 16));
       const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (__attribute__((address_space(3))) v4s*)(vsrc + 4 * kKrowStride + dt * 16));
+          (__attribute__((address_space(3))) v4s*)(vsrc + 4 * kVRow + dt * 16));
       vv[ks][dt] = __builtin_bit_cast(v8h, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
     }
   };
@@ -380,6 +463,246 @@ __global__ __launch_bounds__(kDecThreads) void k_sparse_attn_decode(AttnArgs a) 
   }
 }
 
+// Raw bytes of one lane's share of a 16-key tile: FP4 rows v[0..3] codes and
+// v[4].xy the 8 scale bytes; window rows v[0..7].
+struct Raw {
+  uint4 v[8];
+};
+
+__global__ __launch_bounds__(kThreads) void k_sparse_attn_hg(AttnArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t vbuf[kWaves * kStepKeys * kVRow];
+  __shared__ __attribute__((aligned(16))) uint16_t qf[kHG * kVRow];
+  __shared__ int qsh[kHG];
+  __shared__ float mbuf[kWaves][kHG];
+  __shared__ float lbuf[kWaves][kHG];
+  __shared__ uint2 stab[256];                      // E4M3 scale code -> dequantisation factors
+
+  // ids 32j + 8g + x: query 8j + x, head group g (a query's four work-groups
+  // are equal mod 8: one XCD)
+  const int id = blockIdx.x;
+  const int qi = (id / (kXcds * kHeadGroups)) * kXcds + id % kXcds;
+  const int hg = (id % (kXcds * kHeadGroups)) / kXcds;
+  if (qi >= a.Q) return;                           // the whole work-group, before any barrier
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+  const int col = lane & 15, grp = lane >> 4;
+  const int b = qi / a.T;
+  const int64_t tq = a.q_pos[qi], pos0 = a.swa_pos0[b];
+
+  // first slot of this wave's step s (tile t2 adds 16 t2; lane: key col)
+  auto step_slot = [&](int s) __attribute__((always_inline)) -> int {
+    return s < kMainSteps ? kStepKeys * (wave + kWaves * s) : kTopK + kStepKeys * wave;
+  };
+  // selected positions of this wave's tiles
+  int32_t pj[2 * kMainSteps];
+#pragma unroll
+  for (int s = 0; s < kMainSteps; ++s)
+#pragma unroll
+    for (int t2 = 0; t2 < 2; ++t2)
+      pj[2 * s + t2] = a.idx[(size_t)qi * kTopK + step_slot(s) + 16 * t2 + col];
+  const uint8_t* cache_b = a.cache + (size_t)b * (size_t)a.n_cap * kRowBytes;
+  const uint8_t* swa_b = a.swa + (size_t)b * (size_t)a.S * kDim;
+  // this lane's share of tile t2 of step s: key col, channels 128grp .. 128grp+127
+  auto load = [&](int s, int t2, Raw& r) __attribute__((always_inline)) -> bool {
+    bool ok;
+    if (s < kMainSteps) {
+      const int32_t p = pj[2 * s + t2];
+      ok = p >= 0 && (int64_t)p < a.n_cap;
+      const uint8_t* row = cache_b + (size_t)(ok ? p : 0) * kRowBytes;
+      const uint4* c4 = reinterpret_cast<const uint4*>(row + 64 * grp);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) r.v[i] = c4[i];
+      const uint2 sc = *reinterpret_cast<const uint2*>(row + kCodeBytes + 8 * grp);
+      r.v[4] = make_uint4(sc.x, sc.y, 0u, 0u);
+    } else {
+      const int64_t tok = tq - (kWindow - 1) + (step_slot(s) + 16 * t2 + col - kTopK);
+      ok = tok >= 0 && tok >= pos0 && tok < pos0 + a.S;
+      const int64_t rr = !ok ? 0 : (a.ring ? tok % a.S : tok - pos0);
+      const uint4* r4 = reinterpret_cast<const uint4*>(swa_b + (size_t)rr * kDim + 128 * grp);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) r.v[i] = r4[i];
+    }
+    return ok;
+  };
+
+  // the first step's rows are requested before the query is set up
+  Raw raw[2];
+  bool okr[2];
+  okr[0] = load(0, 0, raw[0]);
+  okr[1] = load(0, 1, raw[1]);
+
+  stab[threadIdx.x] = scale_entry(threadIdx.x);   // (kThreads == 256 codes)
+
+  // ---- the query in fp16: wave w converts heads 4w .. 4w+3 (lane: head
+  // 4w + grp, channels 32col .. 32col+31), each head shifted by a power of two
+  {
+    const int qh = 4 * wave + grp;
+    const uint4* qsrc = reinterpret_cast<const uint4*>(
+        a.q + ((size_t)qi * kHeads + hg * kHG + qh) * kDim + 32 * col);
+    uint4 qr[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) qr[i] = qsrc[i];
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) amax = fmaxf(amax, bf16x8_absmax(qr[i]));
+    const int sh = q_shift(row16_max(amax));
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      *reinterpret_cast<v8h*>(&qf[qh * kVRow + 32 * col + 8 * i]) = q_to_f16(qr[i], sh);
+    if (col == 0) qsh[qh] = sh;
+  }
+  lds_barrier();
+  v8h qreg[16];
+#pragma unroll
+  for (int kb = 0; kb < 16; ++kb)
+    qreg[kb] = *reinterpret_cast<const v8h*>(&qf[col * kVRow + 128 * grp + 8 * kb]);
+  const float zscale = ldexpf(a.scale, -qsh[col]);
+
+  uint16_t* const vw = vbuf + wave * kStepKeys * kVRow;   // this wave's 32 key rows
+  v4f acc[32];
+#pragma unroll
+  for (int ct = 0; ct < 32; ++ct) acc[ct] = v4f{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.0f;
+
+#pragma unroll
+  for (int s = 0; s < kSteps; ++s) {
+    const bool main_rows = s < kMainSteps;         // a compile-time constant per step
+    float z[2][4];
+#pragma unroll
+    for (int t2 = 0; t2 < 2; ++t2) {
+      // dequantise: the Q.K operand in registers and row 16t2 + col of the tile
+      const uint32_t* w = reinterpret_cast<const uint32_t*>(raw[t2].v);
+      const bool ok = okr[t2];
+      v4f sc[4];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) sc[c] = v4f{0.f, 0.f, 0.f, 0.f};
+      // a skipped key dequantises to zeros: an FP4 row through a zero scale
+      // (any code times 0), a window row through zeroed bytes (its bytes could
+      // hold NaN codes)
+      const uint32_t sc0 = ok ? w[16] : 0u, sc1 = ok ? w[17] : 0u;
+#pragma unroll
+      for (int m = 0; m < 8; ++m) {
+        uint32_t pr[8];
+        if (main_rows) {
+          const uint32_t c = ((m < 4 ? sc0 : sc1) >> (8 * (m % 4))) & 0xFFu;
+          fp4x16_to_f16_t(w[2 * m], w[2 * m + 1], stab[c], pr);
+        } else {
+          fp8x4_to_f16(ok ? w[4 * m + 0] : 0u, pr + 0);
+          fp8x4_to_f16(ok ? w[4 * m + 1] : 0u, pr + 2);
+          fp8x4_to_f16(ok ? w[4 * m + 2] : 0u, pr + 4);
+          fp8x4_to_f16(ok ? w[4 * m + 3] : 0u, pr + 6);
+        }
+        const uint4 lo = make_uint4(pr[0], pr[1], pr[2], pr[3]);
+        const uint4 hi = make_uint4(pr[4], pr[5], pr[6], pr[7]);
+        sc[(2 * m) & 3] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(v8h, lo),
+                                                                 qreg[2 * m], sc[(2 * m) & 3], 0, 0, 0);
+        sc[(2 * m + 1) & 3] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+            __builtin_bit_cast(v8h, hi), qreg[2 * m + 1], sc[(2 * m + 1) & 3], 0, 0, 0);
+        uint4* dst = reinterpret_cast<uint4*>(&vw[(16 * t2 + col) * kVRow + 128 * grp + 16 * m]);
+        dst[0] = lo;
+        dst[1] = hi;
+      }
+      // presence of the tile's 16 keys (lanes 0..15 hold them), wave-uniform
+      const uint32_t kmask = (uint32_t)__ballot(ok) & 0xFFFFu;
+      // the next step's rows for this tile are requested now
+      if (s + 1 < kSteps) okr[t2] = load(s + 1, t2, raw[t2]);
+      const v4f sv = (sc[0] + sc[1]) + (sc[2] + sc[3]);
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        z[t2][r] = ((kmask >> (4 * grp + r)) & 1u) ? sv[r] * zscale : -INFINITY;
+    }
+
+    // ---- online softmax for head col over this step's 32 keys
+    float zmax = fmaxf(fmaxf(fmaxf(z[0][0], z[0][1]), fmaxf(z[0][2], z[0][3])),
+                       fmaxf(fmaxf(z[1][0], z[1][1]), fmaxf(z[1][2], z[1][3])));
+    zmax = rows_max(zmax);
+    const bool raise = zmax > m_run + kLazyMax || (m_run == -INFINITY && zmax > -INFINITY);
+    const float m_new = raise ? zmax : m_run;
+    const float alpha = (raise && m_run != -INFINITY) ? __expf(m_run - m_new) : 1.0f;
+    if (__any(alpha != 1.0f)) {
+#pragma unroll
+      for (int ct = 0; ct < 32; ++ct) acc[ct] *= alpha;
+    }
+    float psum = 0.0f;
+    v8h ph, pl;
+#pragma unroll
+    for (int t2 = 0; t2 < 2; ++t2)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float p = m_new == -INFINITY ? 0.0f : __expf(z[t2][r] - m_new);
+        psum += p;
+        const _Float16 h = (_Float16)p;
+        ph[4 * t2 + r] = h;
+        pl[4 * t2 + r] = (_Float16)(p - (float)h);
+      }
+    l_run = l_run * alpha + rows_sum(psum);
+    m_run = m_new;
+
+    // ---- P.V: lane (grp, i) reads channel 16ct + i of keys 4grp..+3 of each
+    // tile (lane (grp, m) points at key 4grp + m/4, channels 16ct + 4(m%4)..+3);
+    // four channel tiles at a time, their hi MFMAs before their lo MFMAs so
+    // that no MFMA waits on the one just issued
+    wave_lds_sync();                                 // this wave's rows are in its tile
+    const uint16_t* vsrc = &vw[(4 * grp + (col >> 2)) * kVRow + 4 * (col & 3)];
+#pragma unroll
+    for (int cg = 0; cg < 32; cg += kPvGroup) {
+      v8h v[kPvGroup];
+#pragma unroll
+      for (int j = 0; j < kPvGroup; ++j) {
+        const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) v4s*)(vsrc + 16 * (cg + j)));
+        const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) v4s*)(vsrc + 16 * kVRow + 16 * (cg + j)));
+        v[j] = __builtin_bit_cast(v8h, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      }
+#pragma unroll
+      for (int j = 0; j < kPvGroup; ++j)
+        acc[cg + j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(v[j], ph, acc[cg + j], 0, 0, 0);
+#pragma unroll
+      for (int j = 0; j < kPvGroup; ++j)
+        acc[cg + j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(v[j], pl, acc[cg + j], 0, 0, 0);
+    }
+    wave_lds_sync();                                 // reads done before the next step writes
+  }
+
+  // ---- merge the four waves by log-sum-exp and write the 16 heads' output
+  if (grp == 0) {
+    mbuf[wave][col] = m_run;
+    lbuf[wave][col] = l_run;
+  }
+  __syncthreads();                                   // every wave is done with its key tile
+  float M = mbuf[0][col];
+#pragma unroll
+  for (int w = 1; w < kWaves; ++w) M = fmaxf(M, mbuf[w][col]);
+  float L = 0.0f;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w)
+    L += mbuf[w][col] == -INFINITY ? 0.0f : __expf(mbuf[w][col] - M) * lbuf[w][col];
+  const float f = (m_run == -INFINITY || !(L > 0.0f)) ? 0.0f : __expf(m_run - M) / L;
+  float* stage = reinterpret_cast<float*>(vbuf);
+#pragma unroll
+  for (int ct = 0; ct < 32; ++ct)
+    *reinterpret_cast<float4*>(&stage[(wave * kHG + col) * kOutRow + 16 * ct + 4 * grp]) =
+        make_float4(acc[ct][0] * f, acc[ct][1] * f, acc[ct][2] * f, acc[ct][3] * f);
+  __syncthreads();
+  float* out = a.out + ((size_t)qi * kHeads + hg * kHG) * kDim;
+#pragma unroll
+  for (int i = 0; i < kHG * kDim / 4 / kThreads; ++i) {
+    const int e = (int)threadIdx.x + kThreads * i;   // float4 index over 16 heads x 128
+    const int h = e / (kDim / 4), c4 = e % (kDim / 4);
+    float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const float4 x = *reinterpret_cast<const float4*>(&stage[(w * kHG + h) * kOutRow + 4 * c4]);
+      o.x += x.x;
+      o.y += x.y;
+      o.z += x.z;
+      o.w += x.w;
+    }
+    *reinterpret_cast<float4*>(&out[(size_t)h * kDim + 4 * c4]) = o;
+  }
+}
+
 // ------------------------------------------------------ prefill kernel --
 
 // 512 queries or more: one 8-wave work-group per query over its 640 key slots
@@ -402,7 +725,7 @@ static_assert(kTopK % kPfKeys == 0, "a chunk holds only selected rows or only wi
 static_assert(kPfThreadsA == kPfKeys * 8, "8 threads per key in the dequantisation");
 
 __global__ __launch_bounds__(kPfThreadsA) void k_sparse_attn_prefill(AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t krow[2][kPfKeys * kKrowStride];
+  __shared__ __attribute__((aligned(16))) uint16_t krow[2][kPfKeys * kVRow];
   __shared__ __attribute__((aligned(16))) uint16_t pbuf[2][kHeads * kPRowPf];   // hi, lo
   __shared__ float cmax[kPfWavesA][kHG];
   __shared__ float csum[kPfWavesA][kHG];
@@ -439,9 +762,9 @@ __global__ __launch_bounds__(kPfThreadsA) void k_sparse_attn_prefill(AttnArgs a)
       r[2].x = *reinterpret_cast<const uint32_t*>(row + kCodeBytes + 4 * dc);
     } else {
       const int64_t tok = tq - (kWindow - 1) + (c * kPfKeys + dk - kTopK);
-      const int64_t rr = tok - pos0;
-      v = tok >= 0 && rr >= 0 && rr < a.S;
-      const uint4* r4 = reinterpret_cast<const uint4*>(swa_b + (size_t)(v ? rr : 0) * kDim + 64 * dc);
+      v = tok >= 0 && tok >= pos0 && tok < pos0 + a.S;
+      const int64_t rr = !v ? 0 : (a.ring ? tok % a.S : tok - pos0);
+      const uint4* r4 = reinterpret_cast<const uint4*>(swa_b + (size_t)rr * kDim + 64 * dc);
 #pragma unroll
       for (int i = 0; i < 4; ++i) r[i] = r4[i];
     }
@@ -458,7 +781,7 @@ __global__ __launch_bounds__(kPfThreadsA) void k_sparse_attn_prefill(AttnArgs a)
 #pragma unroll
       for (int m = 0; m < 16; ++m) fp8x4_to_f16(w[m], pr + 2 * m);
     }
-    uint4* dst = reinterpret_cast<uint4*>(&krow[c & 1][dk * kKrowStride + 64 * dc]);
+    uint4* dst = reinterpret_cast<uint4*>(&krow[c & 1][dk * kVRow + 64 * dc]);
 #pragma unroll
     for (int m = 0; m < 8; ++m)
       dst[m] = v ? make_uint4(pr[4 * m], pr[4 * m + 1], pr[4 * m + 2], pr[4 * m + 3])
@@ -502,7 +825,7 @@ __global__ __launch_bounds__(kPfThreadsA) void k_sparse_attn_prefill(AttnArgs a)
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
       v4f sc[2] = {v4f{0.f, 0.f, 0.f, 0.f}, v4f{0.f, 0.f, 0.f, 0.f}};
-      const uint16_t* kr = &krow[buf][(32 * half + 16 * kt + col) * kKrowStride + grp * 8];
+      const uint16_t* kr = &krow[buf][(32 * half + 16 * kt + col) * kVRow + grp * 8];
 #pragma unroll
       for (int kb = 0; kb < 16; ++kb) {
         const v8h kv = *reinterpret_cast<const v8h*>(kr + kb * 32);
@@ -560,13 +883,13 @@ __global__ __launch_bounds__(kPfThreadsA) void k_sparse_attn_prefill(AttnArgs a)
       const v8h ph = *reinterpret_cast<const v8h*>(&pbuf[0][poff]);
       const v8h pl = *reinterpret_cast<const v8h*>(&pbuf[1][poff]);
       const uint16_t* vsrc =
-          &krow[buf][(ks * 32 + 8 * grp + (col >> 2)) * kKrowStride + 256 * half + 4 * (col & 3)];
+          &krow[buf][(ks * 32 + 8 * grp + (col >> 2)) * kVRow + 256 * half + 4 * (col & 3)];
 #pragma unroll
       for (int dt = 0; dt < 16; ++dt) {
         const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
             (__attribute__((address_space(3))) v4s*)(vsrc + dt * 16));
         const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) v4s*)(vsrc + 4 * kKrowStride + dt * 16));
+            (__attribute__((address_space(3))) v4s*)(vsrc + 4 * kVRow + dt * 16));
         const v8h v = __builtin_bit_cast(v8h, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
         acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(v, ph, acc[dt], 0, 0, 0);
         acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(v, pl, acc[dt], 0, 0, 0);
@@ -625,42 +948,17 @@ __global__ __launch_bounds__(128) void k_attn_merge(const float* __restrict__ pa
       make_float4(o.x * inv, o.y * inv, o.z * inv, o.w * inv);
 }
 
-// Work shape per query count: (kernel, slices). Slices divide the 20 chunks.
-struct Shape {
-  bool wide;
-  int splits;
-};
-
-Shape attn_shape(int Q) {
-  // Measured on MI355X (graph-replayed, 256K-entry caches, random selections):
-  // below 512 queries the 16-head work-groups over 5 slices are fastest
-  // (32 queries: 28 us vs 46 us for the 64-head work-groups over 4 slices;
-  // 128 queries: 84 us vs 91 us); from 512 queries on, one 64-head work-group
-  // per query, which writes its output directly.
-  Shape sh;
-  if (Q < kPrefillMinQueries) {
-    sh.wide = false;
-    sh.splits = kDecSplits;
-  } else {
-    sh.wide = true;
-    sh.splits = 1;
-  }
-  return sh;
-}
-
 }  // namespace
 
 size_t attn_workspace_bytes(int Q) {
-  const Shape sh = attn_shape(Q);
-  if (sh.splits == 1) return 0;
-  return (size_t)Q * sh.splits * kHeads * (kDim + 2) * sizeof(float);
+  if (Q >= kDecodeMaxQueries) return 0;
+  return (size_t)Q * kDecSplits * kHeads * (kDim + 2) * sizeof(float);
 }
 
 hipError_t launch_sparse_attn(const uint16_t* q, const uint8_t* cache, const int32_t* idx,
                               const uint8_t* swa, const int64_t* q_pos, const int64_t* swa_pos0,
-                              int B, int T, int64_t n_cap, int S, float scale, float* out,
+                              int B, int T, int64_t n_cap, int S, int ring, float scale, float* out,
                               void* ws, hipStream_t st) {
-  const int Q = B * T;
   AttnArgs a;
   a.q = q;
   a.cache = cache;
@@ -669,28 +967,31 @@ hipError_t launch_sparse_attn(const uint16_t* q, const uint8_t* cache, const int
   a.q_pos = q_pos;
   a.swa_pos0 = swa_pos0;
   a.T = T;
+  a.Q = B * T;
   a.n_cap = n_cap;
   a.S = S;
+  a.ring = ring;
   a.scale = scale;
   a.out = out;
   a.part = nullptr;
   a.part_ml = nullptr;
-  const Shape sh = attn_shape(Q);
-  if (sh.wide ? sh.splits != 1 : sh.splits != kDecSplits) return hipErrorInvalidValue;
-  a.splits = sh.splits;
-  if (a.splits > 1) {
-    a.part = reinterpret_cast<float*>(ws);
-    a.part_ml = a.part + (size_t)Q * a.splits * kHeads * kDim;
-  }
-  if (sh.wide) {
-    hipLaunchKernelGGL(k_sparse_attn_prefill, dim3(Q), dim3(kPfThreadsA), 0, st, a);
+  if (a.Q >= kPrefillMinQueries) {
+    hipLaunchKernelGGL(k_sparse_attn_prefill, dim3((unsigned)a.Q), dim3(kPfThreadsA), 0, st, a);
+  } else if (a.Q >= kDecodeMaxQueries) {
+    const int groups = (a.Q + kXcds - 1) / kXcds;
+    hipLaunchKernelGGL(k_sparse_attn_hg, dim3((unsigned)(groups * kXcds * kHeadGroups)),
+                       dim3(kThreads), 0, st, a);
   } else {
-    const dim3 grid(kDecSplits * kHeadGroups, Q);
-    hipLaunchKernelGGL(k_sparse_attn_decode, grid, dim3(kDecThreads), 0, st, a);
+    if (!ws) return hipErrorInvalidValue;
+    a.part = reinterpret_cast<float*>(ws);
+    a.part_ml = a.part + (size_t)a.Q * kDecSplits * kHeads * kDim;
+    const int units = a.Q * kDecSplits;
+    const int groups = (units + kXcds - 1) / kXcds;
+    hipLaunchKernelGGL(k_sparse_attn_decode, dim3((unsigned)(groups * kXcds * kHeadGroups)),
+                       dim3(kDecThreads), 0, st, a);
+    hipLaunchKernelGGL(k_attn_merge, dim3(kHeads, a.Q), dim3(128), 0, st, a.part, a.part_ml,
+                       kDecSplits, out);
   }
-  if (a.splits > 1)
-    hipLaunchKernelGGL(k_attn_merge, dim3(kHeads, Q), dim3(128), 0, st, a.part, a.part_ml,
-                       a.splits, out);
   return hipGetLastError();
 }
 

@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define CSA2_ABI_VERSION 5
+#define CSA2_ABI_VERSION 6
 
 #define CSA2_IDX_HEADS 32
 #define CSA2_IDX_DIM 128
@@ -64,10 +64,17 @@ extern "C" {
 /* Query tokens per sequence from which a FULL scan (csa2_index_score,
  * csa2_index_score_fp4k, csa2_index_topk) takes the prefill-shaped contraction:
  * 16 (up to 16 tokens) or 32 queries x 4,096 keys per work-group, keys staged
- * through LDS. Below it the
- * decode shape scores the tokens in groups (4 per wave with E4M3 keys, 2 with
- * FP4 keys) that each read the keys again. The switch points are where the two
- * shapes cost the same (1M-position sequences). */
+ * through LDS, on the FP8 MFMA. Below it the decode shape scores the tokens in
+ * pairs per wave that each read the keys again, on the fp16 MFMA.
+ *
+ * Precision. The decode shape (and every REINDEX scan and re-scoring) converts
+ * E4M3 and E2M1 values exactly to fp16 and accumulates with the fp16 MFMA,
+ * which keeps products to 24 bits and rounds to nearest: float32 accuracy. The
+ * prefill shape's FP8 MFMA truncates each product to 13 fractional bits below
+ * the largest product of its 64-term instruction, so a prefill-shaped score may
+ * be off by up to 2 * 63 * 2^-13 * sum_h w_h max_c |q_hc k_c| (about 2e-5 of
+ * the score on N(0,1) values). csa2_index_topk therefore narrows with those
+ * scores and decides on re-scored float32-accurate ones. */
 #define CSA2_PREFILL_MIN_T_FP8 4
 #define CSA2_PREFILL_MIN_T_FP4 5
 
@@ -138,9 +145,9 @@ int csa2_quantize_kv(const void* kv_bf16, const float* cos_sin, const int64_t* d
  *                 If `bmax` is not NULL, bmax[b][t][j] = max of scores over
  *                 positions 8j..8j+7 (visible ones; -inf if none), j < ceil(n_cap/8).
  *                 `scores` may be NULL when `bmax` is not: only the block maxima
- *                 are written (scores of chosen positions can be recomputed
- *                 bit for bit with REINDEX, which evaluates each position the
- *                 same way).
+ *                 are written (below CSA2_PREFILL_MIN_T_FP8 the scores of chosen
+ *                 positions can be recomputed bit for bit with REINDEX, which
+ *                 evaluates each position the same way).
  *   mode REINDEX: scores[b][t][i] for i < 16384 at position 8*pool[b][t][i/8] + i%8;
  *                 -inf where the pool entry is -1 or the position is >= n_vis.
  *                 `bmax` must be NULL.
@@ -148,11 +155,11 @@ int csa2_quantize_kv(const void* kv_bf16, const float* cos_sin, const int64_t* d
  *   n_vis [B][T] int32 (device; values are clamped to [0, n_cap]),
  *   pool  [B][T][2048] int32 (device, REINDEX only; entries >= ceil(n_cap/8) are
  *         treated as -1).
- * Products are exact; sums are float32 (MFMA accumulation order). Every query's
- * score is the same bits whatever T is: in FULL mode the query tokens of a
- * sequence (T >= 2, e.g. speculative decode) share each key read, four at a time
- * below T = CSA2_PREFILL_MIN_T_FP8 and in tiles of 16 or 32 from there on
- * (csa2_index_score_fp4k: two at a time below T = CSA2_PREFILL_MIN_T_FP4).
+ * Below T = CSA2_PREFILL_MIN_T_FP8 products are exact and sums float32 (MFMA
+ * accumulation order), and a query's score is the same bits whatever T is; in
+ * FULL mode the query tokens of a sequence (T >= 2, e.g. speculative decode)
+ * share each key read, two at a time, and from CSA2_PREFILL_MIN_T_FP8 on in
+ * tiles of 16 or 32 through the FP8 contraction (precision: see above).
  * Errors: CSA2_EINVAL for REUSE, NULL/misaligned pointers, REINDEX without a
  * pool, nothing to write, B < 1, T < 1, n_cap < 1 or n_cap >= 2^31. */
 int csa2_index_score(int mode, const uint8_t* q_idx, const float* w, const uint8_t* k_idx,
@@ -223,17 +230,23 @@ int csa2_index_score_fp4k(int mode, const uint8_t* q_idx, const float* w, const 
                           const uint8_t* k_scales, const int32_t* n_vis, const int32_t* pool,
                           int B, int T, int64_t n_cap, float* scores, float* bmax, void* stream);
 
-/* DEVICE. Fused Full-mode scan and Top-512: the result of csa2_index_score(FULL)
- * followed by csa2_topk(FULL) ([P1] §二 layer layout, mode table and hierarchical
- * sparse indexer), without writing any score row. Beyond 16,384 positions the
- * scan keeps only block maxima; the 512 best blocks of 8 (by block maximum, ties
- * to the lower block; found through the 512 best super-blocks of 8 blocks) are
- * re-scored position by position to the scan's own bits, and the Top-512 is
- * taken among those 4,096 positions. This is exact: each block ranked ahead of
- * the block holding one of the 512 best positions holds, as its maximum, a
- * distinct position ranked ahead of it, so the 512 best positions lie in the 512
- * best blocks. Up to 16,384 positions the score rows go to the workspace and one
- * selection takes the Top-512.
+/* DEVICE. Fused Full-mode scan and Top-512 ([P1] §二 layer layout, mode table
+ * and hierarchical sparse indexer): the exact Top-512 of the float32-accurate
+ * (decode-shaped) scores, without writing any score row.
+ * Below CSA2_PREFILL_MIN_T_FP8 (E4M3 keys) / _FP4 (FP4 keys) query tokens: up to
+ * 16,384 positions the score rows go to the workspace and one selection takes
+ * the Top-512; beyond, the scan keeps only block maxima, the 512 best blocks of
+ * 8 (by block maximum, ties to the lower block; found through the 512 best
+ * super-blocks of 8 blocks) are re-scored position by position to the scan's
+ * own bits, and the Top-512 is taken among those 4,096 positions. This is
+ * exact: each block ranked ahead of the block holding one of the 512 best
+ * positions holds, as its maximum, a distinct position ranked ahead of it, so
+ * the 512 best positions lie in the 512 best blocks.
+ * From that T on the scan is the prefill-shaped FP8 contraction: its block
+ * maxima narrow the candidates to the 1,024 best blocks, whose 8,192 positions
+ * are re-scored float32-accurately before the selection. A block holding one
+ * of the 512 best positions could drop out of that list only if more than 512
+ * other blocks came within twice the contraction's error of its maximum.
  *   q_idx, w, n_vis: as csa2_index_score; k_idx [B][n_cap][128] E4M3 keys when
  *   k_scales is NULL, else [B][n_cap][64] FP4 codes with k_scales [B][n_cap][4]
  *   (csa2_quantize_index_k's layout; 4-byte aligned);
@@ -298,12 +311,29 @@ int csa2_topk(int mode, const float* scores, const float* bmax, const int32_t* n
  * Keys = the selected rows and the window tokens max(0, t-127) .. t (tokens
  * outside [swa_pos0, swa_pos0 + S) are skipped); one softmax over all of them of
  * scale * q_h . key; out[b][t][h] = sum_j p_hj key_j, float32 [B][T][64][512].
- * Needs csa2_workspace_bytes(CSA2_OP_SPARSE_ATTN, 0, B, T, n_cap) bytes of workspace.
- * Errors: CSA2_EINVAL (pointers, sizes, S < 1), CSA2_EWORKSPACE. */
+ * Needs csa2_workspace_bytes(CSA2_OP_SPARSE_ATTN, 0, B, T, n_cap) bytes of
+ * workspace: the partial results of 5 key slices per query when B*T < 64 (a
+ * few queries spread over more work-groups), none from 64 queries on (then `ws`
+ * may be NULL).
+ * Errors: CSA2_EINVAL (pointers, sizes, S < 1, a non-finite scale), CSA2_EWORKSPACE. */
 int csa2_sparse_attn(const void* q_bf16, const uint8_t* cache, const int32_t* idx,
                      const uint8_t* swa, const int64_t* q_pos, const int64_t* swa_pos0, int B,
                      int T, int64_t n_cap, int S, float softmax_scale, float* out, void* ws,
                      size_t ws_bytes, void* stream);
+
+/* DEVICE. csa2_sparse_attn over a window kept as a ring buffer: the window KV
+ * of the last n_win = 128 tokens per layer, replayed as a bounded span ([P2]
+ * 黑科技之三, SWA Bounded Replay; [P3] 第三刀). Token tok of sequence b sits in
+ * row tok mod S of swa [B][S][512]; the rows hold tokens
+ * [swa_pos0[b], swa_pos0[b] + S), and window tokens outside that range are
+ * skipped. A decode loop appends token t into row t mod S (csa2_quantize_e4m3
+ * with dst_slot = b * S + t mod S) and sets swa_pos0 = max(0, t - S + 1); with
+ * S >= 127 + T every query of a T-token step sees its whole window. Arguments,
+ * workspace, result and errors otherwise as csa2_sparse_attn. */
+int csa2_sparse_attn_ring(const void* q_bf16, const uint8_t* cache, const int32_t* idx,
+                          const uint8_t* swa, const int64_t* q_pos, const int64_t* swa_pos0, int B,
+                          int T, int64_t n_cap, int S, float softmax_scale, float* out, void* ws,
+                          size_t ws_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -33,11 +33,11 @@ def declared_functions():
 
 def test_header_functions_are_exported():
     names = declared_functions()
-    assert len(names) == 14, names
+    assert len(names) == 15, names
     L = C.lib()
     for n in names:
         assert hasattr(L, n), n
-    assert C.csa2_abi_version() == 5
+    assert C.csa2_abi_version() == 6
 
 
 def test_status_strings():
@@ -129,11 +129,21 @@ def test_attn_and_quantize_reject_bad_arguments():
     bad = list(args)
     bad[2] = None
     assert f(*bad, 1, 1, 100, 128, ctypes.c_float(1.0), _p(FAKE), _p(FAKE), 1 << 30, None) == C.CSA2_EINVAL
-    # a single decode query is split over key slices, so it needs a workspace;
-    # without one the call must be rejected before any launch
+    # fewer than 64 queries split their keys over slices whose partial results
+    # need a workspace; without one the call is rejected before any launch
     assert C.csa2_workspace_bytes(C.CSA2_OP_SPARSE_ATTN, 0, 1, 1, 100) > 0
+    assert C.csa2_workspace_bytes(C.CSA2_OP_SPARSE_ATTN, 0, 1, 64, 100) == 0
+    assert C.csa2_workspace_bytes(C.CSA2_OP_SPARSE_ATTN, 0, 8, 512, 100) == 0
     assert f(*args, 1, 1, 100, 128, ctypes.c_float(1.0), _p(FAKE), None, 0, None) == C.CSA2_EWORKSPACE
     assert f(*args, 1, 1, 100, 128, ctypes.c_float(1.0), _p(FAKE), _p(FAKE), 64, None) == C.CSA2_EWORKSPACE
+    r = C.lib().csa2_sparse_attn_ring
+    assert r(*args, 1, 1, 100, 0, ctypes.c_float(1.0), _p(FAKE), _p(FAKE), 1 << 30, None) == C.CSA2_EINVAL
+    assert r(*args, 1, 1, 100, 128, ctypes.c_float(float("inf")), _p(FAKE), _p(FAKE), 1 << 30,
+             None) == C.CSA2_EINVAL
+    assert r(*bad, 1, 1, 100, 128, ctypes.c_float(1.0), _p(FAKE), _p(FAKE), 1 << 30, None) == C.CSA2_EINVAL
+    assert r(*args, 1, 1, 100, 128, ctypes.c_float(1.0), _p(FAKE_MIS), _p(FAKE), 1 << 30,
+             None) == C.CSA2_EINVAL
+    assert r(*args, 1, 1, 100, 128, ctypes.c_float(1.0), _p(FAKE), None, 0, None) == C.CSA2_EWORKSPACE
     q = C.lib().csa2_quantize_kv
     assert q(_p(FAKE), _p(FAKE), None, -1, _p(FAKE), 10, None) == C.CSA2_EINVAL
     assert q(_p(FAKE), _p(FAKE), None, 11, _p(FAKE), 10, None) == C.CSA2_EINVAL   # rows beyond the cache

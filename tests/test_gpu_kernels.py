@@ -486,8 +486,9 @@ def _attn_case(B, T, n_cap, S, t0, n_sel, seed, outliers=False):
 @pytest.mark.parametrize("B,T,n_cap,t0,n_sel", [
     (2, 2, 3000, 5000, [512, 300]),     # full window, short selections
     (1, 3, 700, 40, [0, 512, 17]),      # window clipped at token 0, empty selection
-    (8, 1, 20000, 20000, [512]),        # decode shape (many key splits)
-    (70, 1, 5000, 9000, [512]),         # more queries, decode shape
+    (8, 1, 20000, 20000, [512]),        # the decoder group's 8 queries
+    (70, 1, 5000, 9000, [512]),         # query count not a multiple of 8
+    (13, 5, 4000, 300, [512, 1, 0, 511]),  # ragged selections, 65 queries
     (1, 520, 3000, 3000, [512, 200]),   # 512 queries or more: one work-group per query
 ])
 def test_sparse_attn_vs_oracle(B, T, n_cap, t0, n_sel):
@@ -528,6 +529,72 @@ def test_sparse_attn_scale_and_outliers():
         ref = OA.sparse_attention(qn[b, 0], OracleCache(main[b], 1), idx[b, 0], to_np(swa)[b],
                                   q_pos[b, 0], pos0[b], scale=0.5)
         assert_attn_close(o[b, 0], ref, "outliers b%d" % b)
+
+
+def test_sparse_attn_partial_window_and_out_of_range_indices():
+    """Window tokens the buffer does not hold (it starts after t - 127) and
+    selected indices outside [0, n_cap) are skipped, as the oracle skips them."""
+    _stage("sparse_attn partial window")
+    B, T, n_cap, t0 = 2, 3, 3000, 4000
+    S = 60
+    main, cache, q, swa, idx, q_pos, pos0 = _attn_case(B, T, n_cap, S, t0, [512], 5)
+    pos0 = np.array([t0 - 40, t0 + 1], dtype=np.int64)     # holds t0-40 .. ; starts past t0
+    idx[0, 0, :5] = [-5, n_cap, n_cap + 77, 2 ** 31 - 1, -(2 ** 31)]
+    idx[1, 2, 100:110] = n_cap + np.arange(10)
+    out = torch.empty((B, T, 64, 512), dtype=torch.float32, device=DEV)
+    ws = torch.empty(max(256, C.csa2_workspace_bytes(C.CSA2_OP_SPARSE_ATTN, 0, B, T, n_cap)),
+                     dtype=torch.uint8, device=DEV)
+    C.csa2_sparse_attn(q, cache, torch.from_numpy(idx).to(DEV), swa, torch.from_numpy(q_pos).to(DEV),
+                       torch.from_numpy(pos0).to(DEV), 1.0, out, ws)
+    torch.cuda.synchronize()
+    o, qn, swn = to_np(out), q.float().cpu().numpy(), to_np(swa)
+    for b in range(B):
+        oc = OracleCache(main[b], 1)
+        for t in range(T):
+            ref = OA.sparse_attention(qn[b, t], oc, idx[b, t], swn[b], q_pos[b, t], pos0[b])
+            assert_attn_close(o[b, t], ref, "b%d t%d" % (b, t))
+
+
+@pytest.mark.parametrize("B", [2, 64, 520])
+def test_sparse_attn_ring_window_decode_loop(B):
+    """A decode loop appends 300 tokens one at a time into a 128-row ring per
+    sequence (row t mod 128, csa2_quantize_e4m3) and attends with
+    csa2_sparse_attn_ring at several steps; the ring's bytes equal the oracle's
+    E4M3 encoding appended the same way, and the outputs match the oracle's
+    attention over its own ring (the window of the last 128 tokens). B covers
+    the three work shapes (fewer than 64 queries, 64..511, 512 or more)."""
+    _stage("sparse_attn ring decode loop", B)
+    n_cap, S, n_tok = 2000, 128, 300
+    main, cache, _, _, idx, _, _ = _attn_case(B, 1, n_cap, 1, 0, [512], 17)
+    tok_rows = synth.normal_rows(B * n_tok, 512, DEV, 17, "ring_tokens").to(torch.bfloat16)
+    tok_rows = tok_rows.view(n_tok, B, 512)
+    ring = torch.zeros((B, S, 512), dtype=torch.uint8, device=DEV)
+    oring = np.zeros((B, S, 512), dtype=np.uint8)
+    idx_d = torch.from_numpy(idx).to(DEV)
+    out = torch.empty((B, 1, 64, 512), dtype=torch.float32, device=DEV)
+    check_at = {0, 1, 126, 127, 128, 129, 200, 255, 256, 299} if B < 64 else {0, 127, 128, 299}
+    seqs = list(range(B)) if B < 64 else [0, B // 2, B - 1]
+    oc = {b: OracleCache(main[b], 1) for b in seqs}
+    ws = torch.empty(max(256, C.csa2_workspace_bytes(C.CSA2_OP_SPARSE_ATTN, 0, B, 1, n_cap)),
+                     dtype=torch.uint8, device=DEV)
+    for t in range(n_tok):
+        slot = torch.tensor([b * S + t % S for b in range(B)], dtype=torch.int64, device=DEV)
+        C.csa2_quantize_e4m3(tok_rows[t].contiguous(), slot, ring.view(B * S, 512))
+        rows = tok_rows[t].float().cpu().numpy()
+        oring[:, t % S] = OF.e4m3_encode(rows)
+        if t not in check_at:
+            continue
+        pos0 = max(0, t - S + 1)
+        q_pos = torch.full((B, 1), t, dtype=torch.int64, device=DEV)
+        p0 = torch.full((B,), pos0, dtype=torch.int64, device=DEV)
+        q_t = synth.main_queries(B, DEV, 17, "ring_q", t).view(B, 1, 64, 512)
+        C.csa2_sparse_attn_ring(q_t, cache, idx_d, ring, q_pos, p0, 1.0, out, ws)
+        torch.cuda.synchronize()
+        assert np.array_equal(to_np(ring), oring), "ring bytes at t=%d" % t
+        qn, o = q_t.float().cpu().numpy(), to_np(out)
+        for b in seqs:
+            ref = OA.sparse_attention(qn[b, 0], oc[b], idx[b, 0], oring[b], t, pos0, ring=True)
+            assert_attn_close(o[b, 0], ref, "ring t%d b%d" % (t, b))
 
 
 @pytest.mark.parametrize("T,kf", [(2, 0), (3, 0), (4, 0), (5, 0), (16, 0), (17, 0), (33, 0),
