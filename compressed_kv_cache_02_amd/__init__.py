@@ -19,7 +19,7 @@ __all__ = [
     "csa2_quantize_kv", "csa2_index_score", "csa2_build_pool", "csa2_topk",
     "csa2_sparse_attn", "csa2_quantize_index_k", "csa2_index_score_fp4k",
     "csa2_compress_tokens", "csa2_quantize_e4m3", "csa2_index_topk", "CSA2_OP_INDEX_TOPK",
-    "csa2_sparse_attn_ring",
+    "csa2_sparse_attn_ring", "csa2_index_topk_noalloc", "NOALLOC_SCRATCH_BYTES",
 ]
 
 CSA2_FULL, CSA2_REINDEX, CSA2_REUSE = 0, 1, 2
@@ -31,6 +31,7 @@ IDX_HEADS, IDX_DIM, HEADS, DIM = 32, 128, 64, 512
 ROW_BYTES, TOPK, POOL_BLOCKS, BLOCK, POOL_CAND, WINDOW = 288, 512, 2048, 8, 16384, 128
 IDX_FP4_CODE_BYTES, IDX_FP4_SCALES = 64, 4
 INDEX_TOPK_MAX_CAP = 1 << 20        # longest context csa2_index_topk serves
+NOALLOC_SCRATCH_BYTES = 32 << 20    # library-owned scratch of csa2_index_topk_noalloc
 # query tokens per sequence from which a Full scan is prefill-shaped (E4M3 / FP4 keys)
 PREFILL_MIN_T_FP8, PREFILL_MIN_T_FP4 = 4, 5
 
@@ -51,6 +52,7 @@ _SIGS = {
     "csa2_quantize_kv": (_i32, [_vp, _vp, _vp, _i64, _vp, _i64, _vp]),
     "csa2_index_score": (_i32, [_i32, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i64, _vp, _vp, _vp]),
     "csa2_index_topk": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i64, _vp, _vp, _sz, _vp]),
+    "csa2_index_topk_noalloc": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i64, _vp, _vp]),
     "csa2_compress_tokens": (_i32, [_vp, _i64, _i32, _i32, _vp, _vp]),
     "csa2_quantize_e4m3": (_i32, [_vp, _i64, _i32, _vp, _vp, _i64, _vp]),
     "csa2_quantize_index_k": (_i32, [_vp, _vp, _i64, _vp, _vp, _i64, _vp]),
@@ -208,6 +210,28 @@ def csa2_index_topk(q_idx, w, keys, n_vis, idx, ws, stream=None):
     _check("csa2_index_topk", lib().csa2_index_topk(_p(q_idx), _p(w), _p(k), _p(ks), _p(n_vis), B,
                                                     T, n_cap, _p(idx), _p(ws), ws.numel(),
                                                     _stream(stream)))
+
+
+def csa2_index_topk_noalloc(q_idx, w, keys, n_vis, idx, stream=None):
+    """csa2_index_topk with the library's own scratch (no workspace argument;
+    allocates nothing). Calls that overlap on one GPU race."""
+    import torch
+    B, T = q_idx.shape[0], q_idx.shape[1]
+    if isinstance(keys, tuple):
+        k, ks = keys
+        n_cap = k.shape[1]
+        _expect(k, "k_codes", torch.uint8, (B, n_cap, IDX_FP4_CODE_BYTES))
+        _expect(ks, "k_scales", torch.uint8, (B, n_cap, IDX_FP4_SCALES))
+    else:
+        k, ks = keys, None
+        n_cap = k.shape[1]
+        _expect(k, "k_idx", torch.uint8, (B, n_cap, IDX_DIM))
+    _expect(q_idx, "q_idx", torch.uint8, (B, T, IDX_HEADS, IDX_DIM))
+    _expect(w, "w", torch.float32, (B, T, IDX_HEADS))
+    _expect(n_vis, "n_vis", torch.int32, (B, T))
+    _expect(idx, "idx", torch.int32, (B, T, TOPK))
+    _check("csa2_index_topk_noalloc", lib().csa2_index_topk_noalloc(
+        _p(q_idx), _p(w), _p(k), _p(ks), _p(n_vis), B, T, n_cap, _p(idx), _stream(stream)))
 
 
 def csa2_compress_tokens(tokens_bf16, m, out_bf16, stream=None):

@@ -7,6 +7,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 #include "launchers.hpp"
 
@@ -68,6 +69,33 @@ inline FusedWs fused_layout(int Q, int64_t n_cap, bool narrowed) {
   l.blocks_ws = l.vals + round_up((size_t)Q * l.n_best * CSA2_BLOCK * sizeof(float));
   l.total = l.blocks_ws + round_up(csa2::best_blocks_workspace_bytes(Q, n_cap));
   return l;
+}
+
+// Scratch of csa2_index_topk_noalloc: a file-scope device array, so the call
+// needs no allocation. Every GPU the library runs on holds its own copy until
+// the process ends. Its address is resolved once per device, with that device
+// current, and kept; host code never passes the array's name itself.
+constexpr size_t kScratchBytes = CSA2_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 256;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+hipError_t scratch_address(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
 }
 
 template <typename T>
@@ -256,6 +284,19 @@ int csa2_index_topk(const uint8_t* q_idx, const float* w, const uint8_t* k_idx,
     return CSA2_EHIP;
   return status_of(
       csa2::launch_topk_of_blocks(vals, sel_blk, l.n_best, n_vis, Q, n_cap, idx, st));
+}
+
+int csa2_index_topk_noalloc(const uint8_t* q_idx, const float* w, const uint8_t* k_idx,
+                            const uint8_t* k_scales, const int32_t* n_vis, int B, int T,
+                            int64_t n_cap, int32_t* idx, void* stream) {
+  if (!sizes_ok(B, T, n_cap)) return CSA2_EINVAL;
+  if (n_cap > CSA2_INDEX_TOPK_MAX_CAP) return CSA2_EUNSUPPORTED;
+  const FusedWs l = fused_layout(B * T, n_cap, prefill_shaped(T, k_scales != nullptr));
+  if (l.total > kScratchBytes) return CSA2_EWORKSPACE;
+  void* ws = nullptr;
+  if (scratch_address(&ws) != hipSuccess) return CSA2_EHIP;
+  return csa2_index_topk(q_idx, w, k_idx, k_scales, n_vis, B, T, n_cap, idx, ws, kScratchBytes,
+                         stream);
 }
 
 int csa2_build_pool(const float* src, int is_bmax, const int32_t* n_vis, int B, int T,

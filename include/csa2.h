@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define CSA2_ABI_VERSION 6
+#define CSA2_ABI_VERSION 7
 
 #define CSA2_IDX_HEADS 32
 #define CSA2_IDX_DIM 128
@@ -61,6 +61,7 @@ extern "C" {
 #define CSA2_MAX_WIDTH 8192          /* widest row of the write-path helpers */
 #define CSA2_IDX_FP4_CODE_BYTES 64   /* FP4 indexer key: 128 E2M1 codes ... */
 #define CSA2_IDX_FP4_SCALES 4        /* ... and one E8M0 scale per 32 channels */
+#define CSA2_NOALLOC_SCRATCH_BYTES 33554432   /* 32 MiB: scratch of csa2_index_topk_noalloc */
 /* Query tokens per sequence from which a FULL scan (csa2_index_score,
  * csa2_index_score_fp4k, csa2_index_topk) takes the prefill-shaped contraction:
  * 16 (up to 16 tokens) or 32 queries x 4,096 keys per work-group, keys staged
@@ -258,6 +259,26 @@ int csa2_index_score_fp4k(int mode, const uint8_t* q_idx, const float* w, const 
 int csa2_index_topk(const uint8_t* q_idx, const float* w, const uint8_t* k_idx,
                     const uint8_t* k_scales, const int32_t* n_vis, int B, int T, int64_t n_cap,
                     int32_t* idx, void* ws, size_t ws_bytes, void* stream);
+
+/* DEVICE. csa2_index_topk for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same computation, kernels and result, with the workspace
+ * taken from a library-owned device array of CSA2_NOALLOC_SCRATCH_BYTES (32 MiB)
+ * instead of a caller buffer. The call allocates nothing; each GPU holds its
+ * own copy of the array from the first call on that device until the process
+ * ends. Every call on a GPU shares that GPU's array, so calls that overlap in
+ * time on one GPU (on different streams, or from several threads) race and
+ * must be ordered by the caller; no part of the array needs to start at zero
+ * (each call writes every byte it later reads). Arguments as csa2_index_topk,
+ * without `ws` and `ws_bytes`.
+ * Errors: as csa2_index_topk; CSA2_EWORKSPACE when the request needs more than
+ * CSA2_NOALLOC_SCRATCH_BYTES (csa2_workspace_bytes(CSA2_OP_INDEX_TOPK, ...)
+ * bytes: e.g. 64 sequences x 524,288 positions need about 18 MB, a
+ * 4,096-query prefill chunk over 133,120 positions far more); CSA2_EHIP if the
+ * array's device address cannot be resolved. */
+int csa2_index_topk_noalloc(const uint8_t* q_idx, const float* w, const uint8_t* k_idx,
+                            const uint8_t* k_scales, const int32_t* n_vis, int B, int T,
+                            int64_t n_cap, int32_t* idx, void* stream);
 
 /* DEVICE. Hierarchical candidate pool ([P1] §二 hierarchical sparse indexer;
  * [P3] 第二刀, Fig. 5): per query, among blocks j < ceil(n_vis/8), the 2,048

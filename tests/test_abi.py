@@ -33,11 +33,11 @@ def declared_functions():
 
 def test_header_functions_are_exported():
     names = declared_functions()
-    assert len(names) == 15, names
+    assert len(names) == 16, names
     L = C.lib()
     for n in names:
         assert hasattr(L, n), n
-    assert C.csa2_abi_version() == 6
+    assert C.csa2_abi_version() == 7
 
 
 def test_status_strings():
@@ -235,6 +235,7 @@ def test_binding_constants_match_the_header():
             re.finditer(r"^#define CSA2_([A-Z0-9_]+)\s+(-?\d+)\b", text, re.M)}
     mirrored = {"IDX_FP4_CODE_BYTES": C.IDX_FP4_CODE_BYTES, "IDX_FP4_SCALES": C.IDX_FP4_SCALES,
                 "INDEX_TOPK_MAX_CAP": C.INDEX_TOPK_MAX_CAP,
+                "NOALLOC_SCRATCH_BYTES": C.NOALLOC_SCRATCH_BYTES,
                 "PREFILL_MIN_T_FP8": C.PREFILL_MIN_T_FP8, "PREFILL_MIN_T_FP4": C.PREFILL_MIN_T_FP4}
     for k, v in mirrored.items():
         assert defs[k] == v, k
