@@ -226,13 +226,16 @@ __device__ __forceinline__ uint32_t load_items(const Src& src, int q, int t, int
                                                uint32_t* key, uint32_t* id) {
   static_assert(IPT % kBlock == 0, "whole groups of 8 per thread");
   const float* row = src.vals + (size_t)q * (size_t)src.vstride;
-  const int64_t i0 = (int64_t)t * IPT;
+  // ids, item counts and limits stay below 2^31 + 8 (n_cap < 2^31): 32-bit math
+  const uint32_t n_items = (uint32_t)src.n_items;
+  const uint32_t lim32 = (uint32_t)lim;
+  const uint32_t i0 = (uint32_t)t * IPT;
   float v[IPT];
-  int64_t c[IPT];
+  uint32_t c[IPT];
   bool ok[IPT];
   // 8 consecutive values starting at `base` (clamped element-wise at the row end)
-  auto load8 = [&](int64_t base, float* dst) __attribute__((always_inline)) {
-    if (src.vec && base + kBlock <= src.vstride) {
+  auto load8 = [&](uint32_t base, float* dst) __attribute__((always_inline)) {
+    if (src.vec && (int64_t)base + kBlock <= src.vstride) {
       const float4* r4 = reinterpret_cast<const float4*>(row + base);
       const float4 a = r4[0], b = r4[1];
       dst[0] = a.x; dst[1] = a.y; dst[2] = a.z; dst[3] = a.w;
@@ -240,7 +243,7 @@ __device__ __forceinline__ uint32_t load_items(const Src& src, int q, int t, int
     } else {
 #pragma unroll
       for (int r = 0; r < kBlock; ++r) {
-        const int64_t k = base + r;
+        const int64_t k = (int64_t)base + r;
         dst[r] = row[k < src.vstride ? k : src.vstride - 1];
       }
     }
@@ -251,14 +254,14 @@ __device__ __forceinline__ uint32_t load_items(const Src& src, int q, int t, int
 #pragma unroll
     for (int j = 0; j < IPT; ++j) {
       c[j] = i0 + j;
-      ok[j] = c[j] < src.n_items && c[j] < lim;
+      ok[j] = c[j] < n_items && c[j] < lim32;
     }
   } else {
     int32_t par[IPT / kBlock];
 #pragma unroll
     for (int p = 0; p < IPT / kBlock; ++p) {
-      const int64_t i = i0 + p * kBlock;
-      par[p] = i < src.n_items ? src.sel[(size_t)q * src.sel_stride + (i >> 3)] : -1;
+      const uint32_t i = i0 + p * kBlock;
+      par[p] = i < n_items ? src.sel[(size_t)q * src.sel_stride + (i >> 3)] : -1;
     }
     if (KIND == kChildItem) {
 #pragma unroll
@@ -266,14 +269,13 @@ __device__ __forceinline__ uint32_t load_items(const Src& src, int q, int t, int
     }
 #pragma unroll
     for (int p = 0; p < IPT / kBlock; ++p) {
-      const int64_t pa = par[p];
-      const int64_t cb = pa * kBlock;
-      const bool in = pa >= 0 && cb < lim;
-      if (KIND == kChild) load8(in ? cb : 0, v + p * kBlock);
+      const bool has = par[p] >= 0;
+      const uint32_t cb = has ? (uint32_t)par[p] * kBlock : 0u;
+      if (KIND == kChild) load8(has && cb < lim32 ? cb : 0u, v + p * kBlock);
 #pragma unroll
       for (int r = 0; r < kBlock; ++r) {
         c[p * kBlock + r] = cb + r;
-        ok[p * kBlock + r] = pa >= 0 && cb + r < lim;
+        ok[p * kBlock + r] = has && cb + r < lim32;
       }
     }
   }
@@ -281,7 +283,7 @@ __device__ __forceinline__ uint32_t load_items(const Src& src, int q, int t, int
 #pragma unroll
   for (int j = 0; j < IPT; ++j) {
     key[j] = float_key(v[j]);
-    id[j] = (uint32_t)c[j];
+    id[j] = c[j];
     valid |= (ok[j] ? 1u : 0u) << j;
   }
   return valid;
@@ -338,15 +340,82 @@ __device__ __forceinline__ uint32_t block_prefix(uint32_t v, uint32_t* sh, uint3
 constexpr int kSelBins = 4096;       // 12-bit digits: two levels cover 24 bits
 constexpr int kSelDigit = 12;
 
+// Largest K-th bin ranked item against item instead of by further radix
+// levels: NT/8 candidates, so that each thread compares at most 16 pairs.
+template <int NT>
+constexpr int sel_cand_max() { return NT / 8; }
+
 // LDS of one selection: the radix histogram, the per-wave exchange words
-// (regions: 0-2 count/range, 0/3 levels, 4 ties, 5 output) and the result of
-// each level's threshold search.
+// (regions: 0-2 count/range, 0/3 levels, 4 ties, 5 output), the result of
+// each level's threshold search, and the candidates of the K-th bin with their
+// ranks and the per-thread masks of the items taken from them.
 template <int NT>
 struct SelLds {
   __align__(16) uint32_t lh[kSelBins];
   uint32_t sh[6][NT / 64];
   uint32_t res[3];
+  uint32_t n_cand;
+  uint2 cand[sel_cand_max<NT>()];    // (key, item) of each item in the K-th bin
+  uint32_t ahead[sel_cand_max<NT>()];
+  uint32_t take[NT];
 };
+
+// The items of the K-th bin -- those whose offset d = key - kmin has the top
+// bits d >> nb == prefix, n_c of them -- ranked by (key descending, item
+// ascending); the first `need` are selected. Returns this thread's selection:
+// its items above that bin and its selected candidates. The candidates are
+// appended to LDS one wave-aggregated atomic at a time (their order there is
+// arbitrary: the rank compares keys and item numbers, not slots).
+template <int NT, int IPT>
+__device__ uint32_t select_candidates(const uint32_t* key, uint32_t valid, uint32_t kmin, int nb,
+                                      uint32_t prefix, uint32_t need, uint32_t n_c,
+                                      SelLds<NT>& L) {
+  const int t = threadIdx.x, lane = t & 63;
+  uint32_t sel = 0;
+#pragma unroll
+  for (int j = 0; j < IPT; ++j) {
+    const bool v = (valid >> j) & 1u;
+    const uint32_t top = (key[j] - kmin) >> nb;      // 0 < nb < 32
+    if (v && top > prefix) sel |= 1u << j;
+    const bool c = v && top == prefix;
+    const uint64_t m = __ballot(c);
+    if (m) {
+      const int leader = __ffsll((unsigned long long)m) - 1;
+      uint32_t base = 0;
+      if (lane == leader) base = atomicAdd(&L.n_cand, (uint32_t)__popcll(m));
+      base = __shfl(base, leader, 64);
+      if (c)
+        L.cand[base + (uint32_t)__popcll(m & ((1ull << lane) - 1ull))] =
+            make_uint2(key[j], (uint32_t)(t * IPT + j));
+    }
+  }
+  __syncthreads();
+  // thread t ranks candidate t % P against slice t / P of the candidates
+  // (P a power of two >= n_c, at least a wave, so a wave reads one slice in
+  // step: LDS broadcasts)
+  int P = 64;
+  while (P < (int)n_c) P <<= 1;
+  const int S = NT / P;
+  const int c = t & (P - 1), s = t / P;
+  if (c < (int)n_c) {
+    const uint2 me = L.cand[c];
+    const int per = ((int)n_c + S - 1) / S;
+    const int i0 = s * per, i1 = min((int)n_c, i0 + per);
+    uint32_t ahead = 0;
+    for (int i = i0; i < i1; ++i) {
+      const uint2 o = L.cand[i];
+      ahead += (o.x > me.x || (o.x == me.x && o.y < me.y)) ? 1u : 0u;
+    }
+    if (ahead) atomicAdd(&L.ahead[c], ahead);
+  }
+  __syncthreads();
+  if (t < (int)n_c && L.ahead[t] < need) {
+    const uint32_t item = L.cand[t].y;
+    atomicOr(&L.take[item / IPT], 1u << (item % IPT));
+  }
+  __syncthreads();
+  return sel | L.take[t];
+}
 
 // The selection of query q by one work-group of NT threads: writes the ids of
 // the K best items ascending to o[0..K), -1 padded (o may point to LDS).
@@ -354,6 +423,7 @@ template <int KIND, int NT, int IPT>
 __device__ __forceinline__ void select_wg(const Src& src, int q, int K, int32_t* o,
                                           SelLds<NT>& L) {
   static_assert(IPT <= 32, "item masks are 32-bit");
+  static_assert(sel_cand_max<NT>() <= NT, "one thread per candidate");
   constexpr int NW = NT / 64;
   constexpr int PER = kSelBins / NT;                 // bins per thread in the threshold search
   uint32_t* const lh = L.lh;
@@ -364,6 +434,15 @@ __device__ __forceinline__ void select_wg(const Src& src, int q, int K, int32_t*
   const int64_t lim = src.limit(q);
   uint32_t key[IPT], id[IPT];
   const uint32_t valid = load_items<KIND, IPT>(src, q, t, lim, key, id);
+  // the first level's histogram and the candidate records are cleared while
+  // the loads are in flight (the exchange barrier below orders both)
+  {
+    uint4* l4 = reinterpret_cast<uint4*>(lh);
+    for (int i = t; i < kSelBins / 4; i += NT) l4[i] = make_uint4(0, 0, 0, 0);
+    if (t < sel_cand_max<NT>()) L.ahead[t] = 0;
+    L.take[t] = 0;
+    if (t == 0) L.n_cand = 0;
+  }
   // one exchange for the count of valid items and their key range
   uint32_t mx = 0, cmn = 0;
 #pragma unroll
@@ -395,20 +474,25 @@ __device__ __forceinline__ void select_wg(const Src& src, int q, int K, int32_t*
   const bool all = total <= (uint32_t)K;
   uint32_t kth = 0, ties_needed = 0;   // select key > kth, plus the first ties_needed == kth
   uint32_t eq_count = total;           // items equal to kth (all of them if the range is 0)
+  uint32_t sel = 0;
+  bool ranked = false;                 // selection made by ranking the K-th bin's items
   if (!all) {
-    // radix select on d = key - kmin, digits of up to 12 bits from the top
+    // radix select on d = key - kmin, digits of up to 12 bits from the top,
+    // until the K-th bin is small enough to rank its items directly
     const uint32_t range = kmax - kmin;
     int nb = range ? 32 - __clz(range) : 0;
     uint32_t prefix = 0, above = 0;
     int reg = 3;
-    while (nb > 0) {                       // uniform across the block
+    bool clear = false;                // the first level's histogram is clear already
+    while (nb > 0) {                   // uniform across the block
       const int lo = nb > kSelDigit ? nb - kSelDigit : 0;
       const uint32_t mask = (1u << (nb - lo)) - 1u;
-      {
+      if (clear) {
         uint4* l4 = reinterpret_cast<uint4*>(lh);
         for (int i = t; i < kSelBins / 4; i += NT) l4[i] = make_uint4(0, 0, 0, 0);
+        __syncthreads();
       }
-      __syncthreads();
+      clear = true;
 #pragma unroll
       for (int j = 0; j < IPT; ++j) {
         const uint32_t d = key[j] - kmin;
@@ -447,12 +531,19 @@ __device__ __forceinline__ void select_wg(const Src& src, int q, int K, int32_t*
       eq_count = res[2];   // after the last level: the items equal to the K-th key
       prefix = (prefix << (nb - lo)) | bin;
       nb = lo;
+      if (nb > 0 && eq_count <= (uint32_t)sel_cand_max<NT>()) {
+        sel = select_candidates<NT, IPT>(key, valid, kmin, nb, prefix, (uint32_t)K - above,
+                                         eq_count, L);
+        ranked = true;
+        break;
+      }
     }
     kth = kmin + prefix;
     ties_needed = (uint32_t)K - above;
   }
-  uint32_t sel = 0;
-  if (!all && ties_needed < eq_count) {
+  if (ranked) {
+    // selected above
+  } else if (!all && ties_needed < eq_count) {
     // ties: the first `ties_needed` items equal to kth, in item order
     uint32_t nt = 0;
 #pragma unroll

@@ -30,22 +30,20 @@
 //          agree on the slice maximum through LDS; slices are merged by
 //          log-sum-exp in a second kernel (k_attn_merge). Spreads a few
 //          queries over 20 work-groups each.
-//   64 <= Q < 512: one 4-wave work-group per (query, 16 heads), no workspace.
-//          The query's 640 key slots form 20 steps of 32; wave w takes steps
-//          w, w+4, w+8, w+12 (selected rows) and 16+w (window), so every wave
-//          has the same mix, known at compile time, and runs its own online
-//          softmax over its 160 keys with no barrier:
-//          * lane (g, c) loads key c of a 16-key tile, channels 128g..128g+127,
-//            and dequantises them straight into its Q.K operand registers (both
-//            operands in the same permuted channel order) and into the wave's
-//            own 32-row fp16 LDS tile;
-//          * the logit of key 4g + r of each tile for head c lands in lane
-//            (g, c), the lane and order P.V's B operand needs, so P never
-//            leaves the registers;
-//          * the running maximum is raised only when a step's maximum exceeds
-//            it by more than 8 (p stays below e^8, inside fp16), so the
-//            accumulators are rescaled about once per wave.
-//          At the end the four waves' (max, sum, output) are merged by
+//   64 <= Q < 512: one 8-wave work-group per (query, 16 heads), no workspace.
+//          The query's 640 key slots form 20 steps of 32; wave pair p takes
+//          steps p, p+4, p+8, p+12 (selected rows) and 16+p (window):
+//          * wave p + 4h dequantises keys 16h..16h+15 of the step (lane (g, c):
+//            key c, channels 128g..128g+127) straight into its Q.K operand
+//            registers and into the pair's 32-row fp16 LDS tile, and forms
+//            their logits for the 16 heads;
+//          * the pair swaps logits through LDS; the logit of key 16t + 4g + r
+//            for head c sits in lane (g, c), the lane and order P.V's B operand
+//            needs; both waves run the same online softmax over the 32 keys,
+//            raising the running maximum only when a step's maximum exceeds it
+//            by more than 8 (p stays below e^8, inside fp16);
+//          * wave p + 4h accumulates P.V for output channels 256h..256h+255.
+//          At the end the four pairs' (max, sum, output) are merged by
 //          log-sum-exp through LDS and the work-group writes its 16 heads'
 //          output directly.
 //   Q >= 512 (prefill): one 8-wave work-group per query over its 640 key slots
@@ -61,25 +59,27 @@ namespace {
 constexpr int kSlots = kTopK + kWindow;           // 640 key slots per query
 constexpr int kHG = 16;                           // heads per work-group
 constexpr int kHeadGroups = kHeads / kHG;         // 4
-constexpr int kWaves = 4;
+constexpr int kPairs = 4;                         // wave pairs of the head-group shape
+constexpr int kWaves = 2 * kPairs;                // 8: two waves per SIMD
 constexpr int kThreads = kWaves * 64;
-constexpr int kSlotsPerWave = kSlots / kWaves;    // 160
 constexpr int kStepKeys = 32;                     // keys per softmax step (one P.V MFMA)
-constexpr int kSteps = kSlotsPerWave / kStepKeys; // 5 per wave
-constexpr int kMainSteps = kTopK / kStepKeys / kWaves;   // 4 per wave, then 1 window step
+constexpr int kSteps = kSlots / kStepKeys / kPairs;      // 5 per pair
+constexpr int kMainSteps = kTopK / kStepKeys / kPairs;   // 4 per pair, then 1 window step
+constexpr int kHalfTiles = kDim / 16 / 2;         // P.V channel tiles per wave (16)
 constexpr int kPvGroup = 4;                       // channel tiles per P.V issue group
 constexpr int kVRow = kDim + 8;                   // fp16 per LDS key row
 constexpr int kDecodeMaxQueries = 64;             // below: the split decode shape
 constexpr int kPrefillMinQueries = 512;           // from here: one work-group per query
-constexpr int kOutRow = kDim + 4;                 // floats per LDS row of the final merge
+constexpr int kOutRow = kDim / 2 + 4;             // floats per LDS row of the final merge
 constexpr float kLazyMax = 8.0f;                  // headroom before the running max moves
 constexpr int kXcds = 8;
-static_assert(kSlotsPerWave % kStepKeys == 0, "whole steps per wave");
-static_assert(kTopK % (kStepKeys * kWaves) == 0 && kWindow == kStepKeys * kWaves,
-              "each wave: whole steps of selected rows, then one window step");
-static_assert(kWaves * kHG * kOutRow * 4 <= kWaves * kStepKeys * kVRow * 2,
+static_assert(kSlots == kSteps * kStepKeys * kPairs, "whole steps per pair");
+static_assert(kTopK % (kStepKeys * kPairs) == 0 && kWindow == kStepKeys * kPairs,
+              "each pair: whole steps of selected rows, then one window step");
+static_assert(kWaves * kHG * kOutRow * 4 <= kPairs * kStepKeys * kVRow * 2,
               "the final merge fits in the key tiles");
-static_assert(kThreads == 256, "one thread per E4M3 scale code fills the table");
+static_assert(kHG * kVRow <= kPairs * kStepKeys * kVRow, "the query staging fits in the key tiles");
+static_assert(kThreads >= 256, "one thread per E4M3 scale code fills the table");
 
 typedef _Float16 v2h __attribute__((ext_vector_type(2)));
 
@@ -469,12 +469,17 @@ struct Raw {
   uint4 v[8];
 };
 
+// 64 <= Q < 512: one 8-wave work-group per (query, 16 heads). Wave pair p
+// (waves p and p + 4) takes the 32-key steps p, p+4, p+8, p+12 (selected
+// rows) and 16+p (window); in each step wave p + 4h dequantises the step's 16
+// keys 16h..16h+15 and forms their logits for the 16 heads, the pair swaps
+// logits through LDS, both waves run the same online softmax over the 32 keys
+// and wave p + 4h accumulates P.V for output channels 256h..256h+255.
 __global__ __launch_bounds__(kThreads) void k_sparse_attn_hg(AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t vbuf[kWaves * kStepKeys * kVRow];
-  __shared__ __attribute__((aligned(16))) uint16_t qf[kHG * kVRow];
+  __shared__ __attribute__((aligned(16))) uint16_t vbuf[kPairs * kStepKeys * kVRow];
+  __shared__ __attribute__((aligned(16))) float4 zx[kPairs][2][64];   // logits swapped in a pair
   __shared__ int qsh[kHG];
-  __shared__ float mbuf[kWaves][kHG];
-  __shared__ float lbuf[kWaves][kHG];
+  __shared__ float2 mlbuf[kPairs][kHG];
   __shared__ uint2 stab[256];                      // E4M3 scale code -> dequantisation factors
 
   // ids 32j + 8g + x: query 8j + x, head group g (a query's four work-groups
@@ -485,28 +490,25 @@ __global__ __launch_bounds__(kThreads) void k_sparse_attn_hg(AttnArgs a) {
   if (qi >= a.Q) return;                           // the whole work-group, before any barrier
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+  const int pair = wave % kPairs, half = wave / kPairs;
   const int col = lane & 15, grp = lane >> 4;
   const int b = qi / a.T;
   const int64_t tq = a.q_pos[qi], pos0 = a.swa_pos0[b];
 
-  // first slot of this wave's step s (tile t2 adds 16 t2; lane: key col)
-  auto step_slot = [&](int s) __attribute__((always_inline)) -> int {
-    return s < kMainSteps ? kStepKeys * (wave + kWaves * s) : kTopK + kStepKeys * wave;
+  // first slot of this wave's 16 keys in step s (lane: key col)
+  auto tile_slot = [&](int s) __attribute__((always_inline)) -> int {
+    return (s < kMainSteps ? kStepKeys * (pair + kPairs * s) : kTopK + kStepKeys * pair) + 16 * half;
   };
-  // selected positions of this wave's tiles
-  int32_t pj[2 * kMainSteps];
+  int32_t pj[kMainSteps];
 #pragma unroll
-  for (int s = 0; s < kMainSteps; ++s)
-#pragma unroll
-    for (int t2 = 0; t2 < 2; ++t2)
-      pj[2 * s + t2] = a.idx[(size_t)qi * kTopK + step_slot(s) + 16 * t2 + col];
+  for (int s = 0; s < kMainSteps; ++s) pj[s] = a.idx[(size_t)qi * kTopK + tile_slot(s) + col];
   const uint8_t* cache_b = a.cache + (size_t)b * (size_t)a.n_cap * kRowBytes;
   const uint8_t* swa_b = a.swa + (size_t)b * (size_t)a.S * kDim;
-  // this lane's share of tile t2 of step s: key col, channels 128grp .. 128grp+127
-  auto load = [&](int s, int t2, Raw& r) __attribute__((always_inline)) -> bool {
+  // this lane's share of its tile of step s: key col, channels 128grp .. 128grp+127
+  auto load = [&](int s, Raw& r) __attribute__((always_inline)) -> bool {
     bool ok;
     if (s < kMainSteps) {
-      const int32_t p = pj[2 * s + t2];
+      const int32_t p = pj[s];
       ok = p >= 0 && (int64_t)p < a.n_cap;
       const uint8_t* row = cache_b + (size_t)(ok ? p : 0) * kRowBytes;
       const uint4* c4 = reinterpret_cast<const uint4*>(row + 64 * grp);
@@ -515,7 +517,7 @@ __global__ __launch_bounds__(kThreads) void k_sparse_attn_hg(AttnArgs a) {
       const uint2 sc = *reinterpret_cast<const uint2*>(row + kCodeBytes + 8 * grp);
       r.v[4] = make_uint4(sc.x, sc.y, 0u, 0u);
     } else {
-      const int64_t tok = tq - (kWindow - 1) + (step_slot(s) + 16 * t2 + col - kTopK);
+      const int64_t tok = tq - (kWindow - 1) + (tile_slot(s) + col - kTopK);
       ok = tok >= 0 && tok >= pos0 && tok < pos0 + a.S;
       const int64_t rr = !ok ? 0 : (a.ring ? tok % a.S : tok - pos0);
       const uint4* r4 = reinterpret_cast<const uint4*>(swa_b + (size_t)rr * kDim + 128 * grp);
@@ -526,30 +528,24 @@ __global__ __launch_bounds__(kThreads) void k_sparse_attn_hg(AttnArgs a) {
   };
 
   // the first step's rows are requested before the query is set up
-  Raw raw[2];
-  bool okr[2];
-  okr[0] = load(0, 0, raw[0]);
-  okr[1] = load(0, 1, raw[1]);
+  Raw raw;
+  bool okr = load(0, raw);
 
-  stab[threadIdx.x] = scale_entry(threadIdx.x);   // (kThreads == 256 codes)
+  if (threadIdx.x < 256) stab[threadIdx.x] = scale_entry(threadIdx.x);
 
-  // ---- the query in fp16: wave w converts heads 4w .. 4w+3 (lane: head
-  // 4w + grp, channels 32col .. 32col+31), each head shifted by a power of two
+  // ---- the query in fp16, staged in the key tiles: wave w converts heads 2w,
+  // 2w+1 (lane: head 2w + lane/32, channels 16(lane%32) .. +15), each head
+  // shifted by a power of two
+  uint16_t* const qf = vbuf;
   {
-    const int qh = 4 * wave + grp;
+    const int qh = 2 * wave + (lane >> 5), qc = 16 * (lane & 31);
     const uint4* qsrc = reinterpret_cast<const uint4*>(
-        a.q + ((size_t)qi * kHeads + hg * kHG + qh) * kDim + 32 * col);
-    uint4 qr[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) qr[i] = qsrc[i];
-    float amax = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) amax = fmaxf(amax, bf16x8_absmax(qr[i]));
-    const int sh = q_shift(row16_max(amax));
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      *reinterpret_cast<v8h*>(&qf[qh * kVRow + 32 * col + 8 * i]) = q_to_f16(qr[i], sh);
-    if (col == 0) qsh[qh] = sh;
+        a.q + ((size_t)qi * kHeads + hg * kHG + qh) * kDim + qc);
+    const uint4 q0 = qsrc[0], q1 = qsrc[1];
+    const int sh = q_shift(half_max(fmaxf(bf16x8_absmax(q0), bf16x8_absmax(q1))));
+    *reinterpret_cast<v8h*>(&qf[qh * kVRow + qc]) = q_to_f16(q0, sh);
+    *reinterpret_cast<v8h*>(&qf[qh * kVRow + qc + 8]) = q_to_f16(q1, sh);
+    if ((lane & 31) == 0) qsh[qh] = sh;
   }
   lds_barrier();
   v8h qreg[16];
@@ -557,22 +553,23 @@ __global__ __launch_bounds__(kThreads) void k_sparse_attn_hg(AttnArgs a) {
   for (int kb = 0; kb < 16; ++kb)
     qreg[kb] = *reinterpret_cast<const v8h*>(&qf[col * kVRow + 128 * grp + 8 * kb]);
   const float zscale = ldexpf(a.scale, -qsh[col]);
+  lds_barrier();                                   // every wave holds the query: the tiles are free
 
-  uint16_t* const vw = vbuf + wave * kStepKeys * kVRow;   // this wave's 32 key rows
-  v4f acc[32];
+  uint16_t* const vw = vbuf + pair * kStepKeys * kVRow;   // this pair's 32 key rows
+  v4f acc[kHalfTiles];
 #pragma unroll
-  for (int ct = 0; ct < 32; ++ct) acc[ct] = v4f{0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < kHalfTiles; ++j) acc[j] = v4f{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.0f;
 
 #pragma unroll
   for (int s = 0; s < kSteps; ++s) {
     const bool main_rows = s < kMainSteps;         // a compile-time constant per step
-    float z[2][4];
-#pragma unroll
-    for (int t2 = 0; t2 < 2; ++t2) {
-      // dequantise: the Q.K operand in registers and row 16t2 + col of the tile
-      const uint32_t* w = reinterpret_cast<const uint32_t*>(raw[t2].v);
-      const bool ok = okr[t2];
+    // ---- dequantise this wave's 16 keys: the Q.K operand in registers and
+    // rows 16half + col of the pair's tile
+    float4 z;
+    {
+      const uint32_t* w = reinterpret_cast<const uint32_t*>(raw.v);
+      const bool ok = okr;
       v4f sc[4];
 #pragma unroll
       for (int c = 0; c < 4; ++c) sc[c] = v4f{0.f, 0.f, 0.f, 0.f};
@@ -598,54 +595,61 @@ __global__ __launch_bounds__(kThreads) void k_sparse_attn_hg(AttnArgs a) {
                                                                  qreg[2 * m], sc[(2 * m) & 3], 0, 0, 0);
         sc[(2 * m + 1) & 3] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
             __builtin_bit_cast(v8h, hi), qreg[2 * m + 1], sc[(2 * m + 1) & 3], 0, 0, 0);
-        uint4* dst = reinterpret_cast<uint4*>(&vw[(16 * t2 + col) * kVRow + 128 * grp + 16 * m]);
+        uint4* dst = reinterpret_cast<uint4*>(&vw[(16 * half + col) * kVRow + 128 * grp + 16 * m]);
         dst[0] = lo;
         dst[1] = hi;
       }
-      // presence of the tile's 16 keys (lanes 0..15 hold them), wave-uniform
+      // presence of the 16 keys (lanes 0..15 hold them), wave-uniform
       const uint32_t kmask = (uint32_t)__ballot(ok) & 0xFFFFu;
-      // the next step's rows for this tile are requested now
-      if (s + 1 < kSteps) okr[t2] = load(s + 1, t2, raw[t2]);
+      // the next step's rows are requested now
+      if (s + 1 < kSteps) okr = load(s + 1, raw);
       const v4f sv = (sc[0] + sc[1]) + (sc[2] + sc[3]);
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        z[t2][r] = ((kmask >> (4 * grp + r)) & 1u) ? sv[r] * zscale : -INFINITY;
+      // lane (grp, col): logits of keys 4grp + r for head col
+      z.x = ((kmask >> (4 * grp + 0)) & 1u) ? sv[0] * zscale : -INFINITY;
+      z.y = ((kmask >> (4 * grp + 1)) & 1u) ? sv[1] * zscale : -INFINITY;
+      z.z = ((kmask >> (4 * grp + 2)) & 1u) ? sv[2] * zscale : -INFINITY;
+      z.w = ((kmask >> (4 * grp + 3)) & 1u) ? sv[3] * zscale : -INFINITY;
     }
+    zx[pair][half][lane] = z;
+    lds_barrier();                                   // both halves' rows and logits are in LDS
+    const float4 zo = zx[pair][half ^ 1][lane];
+    // P's k index 8grp + 4t + r is key 16t + 4grp + r of the step (t: the half)
+    const float4 zt0 = half == 0 ? z : zo, zt1 = half == 0 ? zo : z;
+    const float zz[8] = {zt0.x, zt0.y, zt0.z, zt0.w, zt1.x, zt1.y, zt1.z, zt1.w};
 
-    // ---- online softmax for head col over this step's 32 keys
-    float zmax = fmaxf(fmaxf(fmaxf(z[0][0], z[0][1]), fmaxf(z[0][2], z[0][3])),
-                       fmaxf(fmaxf(z[1][0], z[1][1]), fmaxf(z[1][2], z[1][3])));
+    // ---- online softmax for head col over this step's 32 keys (the same in
+    // both waves of the pair)
+    float zmax = zz[0];
+#pragma unroll
+    for (int i = 1; i < 8; ++i) zmax = fmaxf(zmax, zz[i]);
     zmax = rows_max(zmax);
     const bool raise = zmax > m_run + kLazyMax || (m_run == -INFINITY && zmax > -INFINITY);
     const float m_new = raise ? zmax : m_run;
     const float alpha = (raise && m_run != -INFINITY) ? __expf(m_run - m_new) : 1.0f;
     if (__any(alpha != 1.0f)) {
 #pragma unroll
-      for (int ct = 0; ct < 32; ++ct) acc[ct] *= alpha;
+      for (int j = 0; j < kHalfTiles; ++j) acc[j] *= alpha;
     }
     float psum = 0.0f;
     v8h ph, pl;
 #pragma unroll
-    for (int t2 = 0; t2 < 2; ++t2)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float p = m_new == -INFINITY ? 0.0f : __expf(z[t2][r] - m_new);
-        psum += p;
-        const _Float16 h = (_Float16)p;
-        ph[4 * t2 + r] = h;
-        pl[4 * t2 + r] = (_Float16)(p - (float)h);
-      }
+    for (int i = 0; i < 8; ++i) {
+      const float pv = m_new == -INFINITY ? 0.0f : __expf(zz[i] - m_new);
+      psum += pv;
+      const _Float16 h = (_Float16)pv;
+      ph[i] = h;
+      pl[i] = (_Float16)(pv - (float)h);
+    }
     l_run = l_run * alpha + rows_sum(psum);
     m_run = m_new;
 
-    // ---- P.V: lane (grp, i) reads channel 16ct + i of keys 4grp..+3 of each
-    // tile (lane (grp, m) points at key 4grp + m/4, channels 16ct + 4(m%4)..+3);
-    // four channel tiles at a time, their hi MFMAs before their lo MFMAs so
-    // that no MFMA waits on the one just issued
-    wave_lds_sync();                                 // this wave's rows are in its tile
-    const uint16_t* vsrc = &vw[(4 * grp + (col >> 2)) * kVRow + 4 * (col & 3)];
+    // ---- P.V over output channels 256half..: lane (grp, i) reads channel
+    // 16ct + i of keys 4grp..+3 of each half (lane (grp, m) points at key
+    // 4grp + m/4, channels 16ct + 4(m%4)..+3); four channel tiles at a time,
+    // their hi MFMAs before their lo MFMAs
+    const uint16_t* vsrc = &vw[(4 * grp + (col >> 2)) * kVRow + 4 * (col & 3) + 256 * half];
 #pragma unroll
-    for (int cg = 0; cg < 32; cg += kPvGroup) {
+    for (int cg = 0; cg < kHalfTiles; cg += kPvGroup) {
       v8h v[kPvGroup];
 #pragma unroll
       for (int j = 0; j < kPvGroup; ++j) {
@@ -662,38 +666,38 @@ __global__ __launch_bounds__(kThreads) void k_sparse_attn_hg(AttnArgs a) {
       for (int j = 0; j < kPvGroup; ++j)
         acc[cg + j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(v[j], pl, acc[cg + j], 0, 0, 0);
     }
-    wave_lds_sync();                                 // reads done before the next step writes
+    lds_barrier();                                   // tile reads done before the next step writes
   }
 
-  // ---- merge the four waves by log-sum-exp and write the 16 heads' output
-  if (grp == 0) {
-    mbuf[wave][col] = m_run;
-    lbuf[wave][col] = l_run;
-  }
-  __syncthreads();                                   // every wave is done with its key tile
-  float M = mbuf[0][col];
+  // ---- merge the four pairs by log-sum-exp and write the 16 heads' output
+  if (half == 0 && grp == 0) mlbuf[pair][col] = make_float2(m_run, l_run);
+  __syncthreads();
+  float M = mlbuf[0][col].x;
 #pragma unroll
-  for (int w = 1; w < kWaves; ++w) M = fmaxf(M, mbuf[w][col]);
+  for (int w = 1; w < kPairs; ++w) M = fmaxf(M, mlbuf[w][col].x);
   float L = 0.0f;
 #pragma unroll
-  for (int w = 0; w < kWaves; ++w)
-    L += mbuf[w][col] == -INFINITY ? 0.0f : __expf(mbuf[w][col] - M) * lbuf[w][col];
+  for (int w = 0; w < kPairs; ++w)
+    L += mlbuf[w][col].x == -INFINITY ? 0.0f : __expf(mlbuf[w][col].x - M) * mlbuf[w][col].y;
   const float f = (m_run == -INFINITY || !(L > 0.0f)) ? 0.0f : __expf(m_run - M) / L;
+  // lane (grp, col) holds channels 256half + 16j + 4grp .. +3 of head col
   float* stage = reinterpret_cast<float*>(vbuf);
 #pragma unroll
-  for (int ct = 0; ct < 32; ++ct)
-    *reinterpret_cast<float4*>(&stage[(wave * kHG + col) * kOutRow + 16 * ct + 4 * grp]) =
-        make_float4(acc[ct][0] * f, acc[ct][1] * f, acc[ct][2] * f, acc[ct][3] * f);
+  for (int j = 0; j < kHalfTiles; ++j)
+    *reinterpret_cast<float4*>(&stage[(wave * kHG + col) * kOutRow + 16 * j + 4 * grp]) =
+        make_float4(acc[j][0] * f, acc[j][1] * f, acc[j][2] * f, acc[j][3] * f);
   __syncthreads();
   float* out = a.out + ((size_t)qi * kHeads + hg * kHG) * kDim;
 #pragma unroll
   for (int i = 0; i < kHG * kDim / 4 / kThreads; ++i) {
     const int e = (int)threadIdx.x + kThreads * i;   // float4 index over 16 heads x 128
     const int h = e / (kDim / 4), c4 = e % (kDim / 4);
+    const int hw = c4 / (kDim / 8), cl = 4 * (c4 % (kDim / 8));   // channel half, channel in it
     float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      const float4 x = *reinterpret_cast<const float4*>(&stage[(w * kHG + h) * kOutRow + 4 * c4]);
+    for (int w = 0; w < kPairs; ++w) {
+      const float4 x = *reinterpret_cast<const float4*>(
+          &stage[((w + kPairs * hw) * kHG + h) * kOutRow + cl]);
       o.x += x.x;
       o.y += x.y;
       o.z += x.z;
