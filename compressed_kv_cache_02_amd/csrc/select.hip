@@ -914,7 +914,7 @@ inline int64_t n_blocks(int64_t n) { return (n + kBlock - 1) / kBlock; }
 template <int KIND>
 hipError_t run_stage_k(const Src& s, int Q, int K, int32_t* out, int out_stride, hipStream_t st) {
   if (s.n_items <= 4096)
-    hipLaunchKernelGGL((k_select<KIND, 256, 16>), dim3(Q), dim3(256), 0, st, s, K, out,
+    hipLaunchKernelGGL((k_select<KIND, 512, 8>), dim3(Q), dim3(512), 0, st, s, K, out,
                        out_stride);
   else if (s.n_items <= 8192)
     hipLaunchKernelGGL((k_select<KIND, 512, 16>), dim3(Q), dim3(512), 0, st, s, K, out,
@@ -946,7 +946,7 @@ hipError_t run_pair(const Stage& parents, int K1, const Stage& children, int K2,
   const int64_t n = parents.src.n_items > (int64_t)K1 * kBlock ? parents.src.n_items
                                                                 : (int64_t)K1 * kBlock;
   if (n <= 4096)
-    hipLaunchKernelGGL((k_select_pair<256, 16>), dim3(Q), dim3(256), 0, st, parents.src, K1,
+    hipLaunchKernelGGL((k_select_pair<512, 8>), dim3(Q), dim3(512), 0, st, parents.src, K1,
                        children.src, K2, out, out_stride);
   else if (n <= 8192)
     hipLaunchKernelGGL((k_select_pair<512, 16>), dim3(Q), dim3(512), 0, st, parents.src, K1,
