@@ -22,13 +22,16 @@
 //   pool         = the best 2,048 blocks inside the best 2,048 super-blocks.
 // It is the pages' hierarchical indexer applied once more, one level up.
 //
-// One selection = one work-group per query that holds up to 16 items per
-// thread in registers, in item order (= id order). It finds the exact K-th key
-// by radix select on order-preserving 32-bit keys; the digits are taken from
-// the offset to the smallest valid key, so the first level spreads values of
-// any range over its 2,048 bins and few LDS atomics collide. Ties are taken
-// lowest id first with a block prefix sum, and the selected ids are written
-// ascending with a second prefix sum (no sort).
+// One selection = one work-group per query that holds its items in registers,
+// in item order (= id order): 512 threads x 8 items up to 4,096 items, 512 x 16
+// up to 8,192, 1,024 x 16 up to 16,384. It finds the exact K-th key by radix
+// select on order-preserving 32-bit keys; the digits (12 bits, 4,096 bins) are
+// taken from the offset to the smallest valid key, so the first level spreads
+// values of any range over its bins. Once the bin holding the K-th key has at
+// most NT/8 items, those are gathered into LDS and ranked against each other
+// by (key descending, item ascending) instead of further levels. Otherwise ties
+// are taken lowest id first with a block prefix sum. The selected ids are
+// written ascending with a second prefix sum (no sort).
 //
 // Inputs beyond 2^20 positions per query use a multi-pass radix path over the
 // raw values instead (a grid over chunks x queries):
