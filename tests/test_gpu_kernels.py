@@ -334,10 +334,12 @@ def _score_sets(n, seed):
     yield "peaks", x
 
 
-@pytest.mark.parametrize("n_cap", [100, 512, 513, 5000, 16384, 16385, 70001, 1100000])
+@pytest.mark.parametrize("n_cap", [100, 512, 513, 4096, 4097, 5000, 8192, 8193, 16384, 16385,
+                                   70001, 1100000])
 def test_topk_full_bitexact(n_cap):
-    """Direct selection up to 16,384 positions, the block / super-block
-    hierarchy above, the multi-pass path beyond 2^20 positions."""
+    """Direct selection up to 16,384 positions (work-group shapes change past
+    4,096 and 8,192 items), the block / super-block hierarchy above, the
+    multi-pass path beyond 2^20 positions."""
     for name, vals in _score_sets(2 * n_cap, n_cap):
         _stage("topk full", n_cap, name)
         B, T = 2, 1
@@ -364,10 +366,12 @@ def _masked_block_max(s, nv):
     return OI.block_max(m, nv)
 
 
-@pytest.mark.parametrize("n_cap", [70001, 300007])
+@pytest.mark.parametrize("n_cap", [70001, 300007, 600001])
 def test_topk_full_with_block_max_and_pool(n_cap):
     """FULL with the optional helpers: caller-supplied block maxima, the pool
-    built from the same scores, or both, must give the same exact Top-512."""
+    built from the same scores, or both, must give the same exact Top-512.
+    The super-block counts (1,094 / 4,688 / 9,376) take the three work-group
+    shapes of the chained super-block and block selection."""
     B, T = 2, 2
     nv = np.array([[n_cap, n_cap - 5], [4000, 777]], dtype=np.int32)
     for name, vals in _score_sets(B * T * n_cap, n_cap + 3):
