@@ -118,6 +118,17 @@ def source_sha(path):
     return hashlib.sha256("\n".join(ln for ln in lines if ln.strip()).encode()).hexdigest()[:16]
 
 
+def scan_kernel_name(kf, B, T, n_cap):
+    """The decode-shaped Full scan's instantiation: <mode 0, key format,
+    queries per wave, tiles per wave>. Single-token scans whose grid at 8
+    tiles per wave (1,024 positions per work-group) has fewer than 16,384
+    work-groups run 4 tiles per wave; query groups share each tile 2 at a time."""
+    if T == 1:
+        tiles = 4 if B * ((n_cap + 1023) // 1024) < 16384 else 8
+        return "%s<0, %d, 1, %d>" % (SCAN_KERNEL, kf, tiles)
+    return "%s<0, %d, 2, 8>" % (SCAN_KERNEL, kf)
+
+
 def read_traffic(n_launch_bytes):
     """HBM traffic per scan launch from the committed rocprofv3 counter summary
     (one entry per key format), or None if no entry was taken on this version of
@@ -474,7 +485,7 @@ def main():
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": read_traffic(scan_bytes),
-                "kernel": "%s<0, %d, %d>" % (SCAN_KERNEL, kf, 1 if T == 1 else (2 if kf else 4)),
+                "kernel": scan_kernel_name(kf, B, T, n_cap),
                 "kernel_ms": round(scan_ms, 4), "algorithmic_bytes_per_launch": scan_bytes}
     step_roof = None
     if not prefill:

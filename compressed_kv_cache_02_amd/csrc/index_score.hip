@@ -54,16 +54,22 @@ constexpr int kWaves = 4;          // waves per work-group of the decode scan
 // MODE 0: the Full scan; MODE 1: scores of listed blocks (Reindex inside the
 // pool, or the re-scoring of a fused Top-K); MODE 2: as MODE 1, shaped for
 // many queries (8 tiles per wave instead of 2).
-// Tiles per wave: 8 for the Full scan (long rows, many work-groups anyway);
-// 2 for a block list of a few queries, where more, shorter work-groups spread
-// the work over more of the chip; 8 again once the queries alone fill it.
-template <int MODE, int KF>
+// Tiles per wave (default): 8 for the Full scan (long rows, many work-groups
+// anyway); 2 for a block list of a few queries, where more, shorter
+// work-groups spread the work over more of the chip; 8 again once the queries
+// alone fill it. A Full scan over few sequences takes 4 (kSmallFullGrid).
+template <int MODE>
 constexpr int tiles_per_wave() { return MODE == 1 ? 2 : 8; }
-template <int MODE, int KF>
-constexpr int items_per_wg() { return kTilePos * tiles_per_wave<MODE, KF>() * kWaves; }
-// Tiles in registers per wave (one scored, the rest in flight).
+template <int MODE>
+constexpr int items_per_wg(int tiles = tiles_per_wave<MODE>()) {
+  return kTilePos * tiles * kWaves;
+}
+// Tiles in registers per wave (one scored, the rest in flight), as deep as
+// three waves per SIMD allow (at most 168 registers with the 16 accumulators):
+// 4 for FP8 keys (16 registers a tile; 1% faster than 3), 5 for FP4 keys (9
+// registers a tile; 3% faster decoder steps than 3, 6 is slower).
 template <int KF>
-constexpr int prefetch_tiles() { return 3; }
+constexpr int prefetch_tiles() { return KF ? 5 : 4; }
 
 // Row (head) of accumulator register r in lane `lane` of a 32x32 MFMA result.
 __device__ __forceinline__ int acc32_row(int lane, int r) {
@@ -257,7 +263,7 @@ __device__ __forceinline__ v16f dots_tile(const v8h (&a)[8], const KTile4& t, fl
 // tile it loads, so a sequence's keys are read once per NQ queries. Every query
 // runs the same instruction sequence as with NQ = 1 (same bits); each keeps its
 // own visibility limit.
-template <int MODE, int KF, int NQ>
+template <int MODE, int KF, int NQ, int TPW = tiles_per_wave<MODE>()>
 __global__ __launch_bounds__(256) void k_index_score_decode(
     const uint8_t* __restrict__ q_idx, const float* __restrict__ w,
     const uint8_t* __restrict__ k_idx, const uint8_t* __restrict__ k_scales,
@@ -311,9 +317,9 @@ __global__ __launch_bounds__(256) void k_index_score_decode(
   // 512 best blocks of a fused Top-K)
   const int32_t* pl = MODE != 0 ? pool + (size_t)qi[0] * (size_t)(n_items >> 3) : nullptr;
 
-  constexpr int kTilesPerWave = tiles_per_wave<MODE, KF>();
+  constexpr int kTilesPerWave = TPW;
   constexpr int kPrefetch = prefetch_tiles<KF>();
-  const int64_t wave_base = (int64_t)blockIdx.x * items_per_wg<MODE, KF>() +
+  const int64_t wave_base = (int64_t)blockIdx.x * items_per_wg<MODE>(TPW) +
                             (int64_t)wave * kTilePos * kTilesPerWave;
 
   // Reindex: the pool entries of all of this wave's tiles are fetched first, so
@@ -700,21 +706,32 @@ constexpr int decode_group() { return 2; }
 // steps at 64-256 queries of 1M-entry contexts.
 constexpr int kPoolManyQueries = 64;
 
+// A single-token Full scan whose default grid has fewer work-groups than this
+// (a few sequences, e.g. 8 x 1M positions: 8,192) runs 4 tiles per wave: the
+// shorter work-groups leave a shorter tail before the dependent selection
+// (2% faster decoder steps at 8 x 1M); 64 x 512K (32,768) keeps 8.
+constexpr int64_t kSmallFullGrid = 16384;
+
 template <int KF>
 hipError_t launch_decode(int mode, const uint8_t* q_idx, const float* w, const uint8_t* keys,
                          const uint8_t* scales, const int32_t* n_vis, const int32_t* pool, int B,
                          int T, int64_t n_cap, float* scores, float* bmax, hipStream_t st) {
   const int64_t n_items = mode == 0 ? n_cap : (int64_t)kPoolCand;
-  const int64_t per_wg = mode == 0 ? items_per_wg<0, KF>() : items_per_wg<1, KF>();
+  const int64_t per_wg = mode == 0 ? items_per_wg<0>() : items_per_wg<1>();
   const unsigned gx = (unsigned)((n_items + per_wg - 1) / per_wg);
   if (mode == 1 && B * T >= kPoolManyQueries) {
-    constexpr int64_t per2 = items_per_wg<2, KF>();
+    constexpr int64_t per2 = items_per_wg<2>();
     hipLaunchKernelGGL((k_index_score_decode<2, KF, 1>), dim3((unsigned)((n_items + per2 - 1) / per2),
                        (unsigned)(B * T)), dim3(256), 0, st, q_idx, w, keys, scales, n_vis, pool, T,
                        n_cap, n_items, scores, nullptr);
   } else if (mode == 1) {
     hipLaunchKernelGGL((k_index_score_decode<1, KF, 1>), dim3(gx, (unsigned)(B * T)), dim3(256), 0,
                        st, q_idx, w, keys, scales, n_vis, pool, T, n_cap, n_items, scores, nullptr);
+  } else if (T == 1 && (int64_t)gx * B < kSmallFullGrid) {
+    constexpr int64_t per4 = items_per_wg<0>(4);
+    hipLaunchKernelGGL((k_index_score_decode<0, KF, 1, 4>),
+                       dim3((unsigned)((n_items + per4 - 1) / per4), (unsigned)B), dim3(256), 0,
+                       st, q_idx, w, keys, scales, n_vis, pool, T, n_cap, n_items, scores, bmax);
   } else if (T == 1) {
     hipLaunchKernelGGL((k_index_score_decode<0, KF, 1>), dim3(gx, (unsigned)B), dim3(256), 0, st,
                        q_idx, w, keys, scales, n_vis, pool, T, n_cap, n_items, scores, bmax);
@@ -738,7 +755,7 @@ hipError_t launch_rescore_blocks(const uint8_t* q_idx, const float* w, const uin
   const int Q = B * T;
   auto go = [&](auto mode_c, auto kf_c) {
     constexpr int M = decltype(mode_c)::value, K = decltype(kf_c)::value;
-    const int64_t per_wg = items_per_wg<M, K>();
+    const int64_t per_wg = items_per_wg<M>();
     hipLaunchKernelGGL((k_index_score_decode<M, K, 1>),
                        dim3((unsigned)((n_items + per_wg - 1) / per_wg), (unsigned)Q), dim3(256),
                        0, st, q_idx, w, keys, scales, n_vis, blocks, T, n_cap, n_items, vals,
