@@ -125,6 +125,50 @@ def test_index_score_full(B, T, n_cap):
             assert np.array_equal(bn[b, t], OI.block_max(sn[b, t], nv[b, t]))
 
 
+@pytest.mark.parametrize("kf", [0, 1])
+def test_full_scan_launch_shapes_bit_identical(kf):
+    """A single-token Full scan over many sequences (16 x 1,048,613 keys: at
+    least 16,384 work-groups of 8 key tiles per wave) and the same sequences
+    scanned one call each (4 tiles per wave) run different launch shapes of
+    one kernel: scores and block maxima must agree bit for bit, including the
+    -inf of invisible positions and the ragged last tile."""
+    B, n_cap = 16, (1 << 20) + 37
+    _stage("full scan launch shapes", kf, B, n_cap)
+    g = torch.Generator(device=DEV)
+    g.manual_seed(4242 + kf)
+    q = synth.e4m3_rows(B * 32, 128, DEV, 4242, "lq").view(B, 1, 32, 128)
+    w = synth.head_weights(B, DEV, 4242, "lw").view(B, 1, 32)
+    if kf:
+        codes = torch.randint(0, 256, (B, n_cap, 64), dtype=torch.uint8, device=DEV, generator=g)
+        scl = torch.randint(120, 135, (B, n_cap, 4), dtype=torch.uint8, device=DEV, generator=g)
+
+        def score(qq, ww, nv, s, bm, b0, b1):
+            C.csa2_index_score_fp4k(C.CSA2_FULL, qq, ww, codes[b0:b1], scl[b0:b1], nv, None, s, bm)
+    else:
+        k = synth.e4m3_rows(B * n_cap, 128, DEV, 4242, "lk").view(B, n_cap, 128)
+
+        def score(qq, ww, nv, s, bm, b0, b1):
+            C.csa2_index_score(C.CSA2_FULL, qq, ww, k[b0:b1], nv, None, s, bm)
+    rng = np.random.default_rng(4242)
+    nv = rng.integers(0, n_cap + 1, (B, 1)).astype(np.int32)
+    nv[0, 0], nv[1, 0], nv[2, 0], nv[3, 0], nv[4, 0] = n_cap, 0, 33, n_cap - 1, 1024 * 8 + 5
+    n_vis = torch.from_numpy(nv).to(DEV)
+    nb = (n_cap + 7) // 8
+    s_all = torch.empty((B, 1, n_cap), dtype=torch.float32, device=DEV)
+    b_all = torch.empty((B, 1, nb), dtype=torch.float32, device=DEV)
+    score(q, w, n_vis, s_all, b_all, 0, B)
+    s_one = torch.empty((1, 1, n_cap), dtype=torch.float32, device=DEV)
+    b_one = torch.empty((1, 1, nb), dtype=torch.float32, device=DEV)
+    for b in range(B):
+        score(q[b:b + 1], w[b:b + 1], n_vis[b:b + 1].clone(), s_one, b_one, b, b + 1)
+        torch.cuda.synchronize()
+        assert torch.equal(s_one[0], s_all[b]), ("scores", b)
+        assert torch.equal(b_one[0], b_all[b]), ("block maxima", b)
+        v = int(nv[b, 0])
+        assert bool(torch.isneginf(s_all[b, 0, v:]).all()), ("invisible", b)
+        assert not bool(torch.isneginf(s_all[b, 0, :v]).any()), ("visible", b)
+
+
 @pytest.mark.parametrize("B,T,n_cap", [(2, 77, 10003), (1, 64, 4096), (1, 130, 300)])
 def test_index_score_prefill_shape(B, T, n_cap):
     """Many queries per sequence take the prefill kernel (a shared FP8
