@@ -65,9 +65,11 @@ constexpr int items_per_wg(int tiles = tiles_per_wave<MODE>()) {
   return kTilePos * tiles * kWaves;
 }
 // Tiles in registers per wave (one scored, the rest in flight), as deep as
-// three waves per SIMD allow (at most 168 registers with the 16 accumulators):
-// 4 for FP8 keys (16 registers a tile; 1% faster than 3), 5 for FP4 keys (9
-// registers a tile; 3% faster decoder steps than 3, 6 is slower).
+// three waves per SIMD allow the Full scan (at most 168 registers with the 16
+// accumulators): 4 for FP8 keys (16 registers a tile; 1% faster than 3), 5 for
+// FP4 keys (9 registers a tile; 3% faster decoder steps than 3, 6 is slower).
+// The many-query block-list shape (MODE 2, FP8) then runs two waves per SIMD,
+// as fast as with 3 tiles and three.
 template <int KF>
 constexpr int prefetch_tiles() { return KF ? 5 : 4; }
 
