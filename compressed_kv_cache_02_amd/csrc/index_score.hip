@@ -451,8 +451,13 @@ __global__ __launch_bounds__(kPfThreads) void k_index_score_prefill(
     int n_kb, int n_qb, float* __restrict__ scores, float* __restrict__ bmax) {
   __shared__ uint4 lds[2][KF ? kPfPieces4 : kPfPieces];
   __shared__ uint32_t lsc[2][KF ? kPfChunk : 1];
-  const int kb = blockIdx.x % n_kb;
-  const int rest = blockIdx.x / n_kb;
+  // Key blocks vary slowest over the grid: the work-groups that run together
+  // share a key block through L2, and the last (ragged, shorter) key block's
+  // work-groups come last, where they fill the tail instead of leaving whole
+  // work-groups to start late (c3: 2.05 -> 1.97 ms).
+  const int per_kb = (int)(gridDim.x / (unsigned)n_kb);   // work-groups per key block
+  const int kb = (int)blockIdx.x / per_kb;
+  const int rest = (int)blockIdx.x % per_kb;
   const int qb = rest % n_qb;
   const int b = rest / n_qb;
   const int tid = threadIdx.x;
