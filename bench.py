@@ -242,7 +242,7 @@ def cpu_baseline(workers, w, inp, seed, new_rows, budget_s=10.0, index_k="fp8",
 def main():
     args = parse()
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
     workers = None

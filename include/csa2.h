@@ -89,7 +89,7 @@ typedef enum { CSA2_FULL = 0, CSA2_REINDEX = 1, CSA2_REUSE = 2 } csa2_mode;
 enum {
   CSA2_OK = 0,
   CSA2_EINVAL = -1,        /* null/misaligned pointer, bad size, bad mode combination */
-  CSA2_EUNSUPPORTED = -2,  /* valid request this build does not implement */
+  CSA2_EUNSUPPORTED = -2,  /* valid request the library does not implement */
   CSA2_EWORKSPACE = -3,    /* workspace smaller than csa2_workspace_bytes() */
   CSA2_EHIP = -4           /* a HIP launch failed */
 };
