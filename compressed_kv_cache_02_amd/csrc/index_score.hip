@@ -165,7 +165,7 @@ struct KTile4 {
 };
 
 __device__ __forceinline__ void load_tile4(KTile4& t, const uint8_t* codes, const uint8_t* scales,
-                                           int half, bool ok) {
+                                           bool ok) {
   if (ok) {
     t.c[0] = *reinterpret_cast<const uint4*>(codes);
     t.c[1] = *reinterpret_cast<const uint4*>(codes + 32);
@@ -351,7 +351,7 @@ __global__ __launch_bounds__(256) void k_index_score_decode(
   bool okb[kPrefetch];
   auto load = [&](Tile& t, int64_t pos, bool ok) __attribute__((always_inline)) {
     if constexpr (KF == 1)
-      load_tile4(t, kbase + pos * kKeyBytes, sbase + pos * 4, half, ok);
+      load_tile4(t, kbase + pos * kKeyBytes, sbase + pos * 4, ok);
     else
       load_tile(t, kbase + pos * kKeyBytes, ok);
   };
@@ -424,7 +424,6 @@ __global__ __launch_bounds__(256) void k_index_score_decode(
 constexpr int kPfQPerWave = 4;
 constexpr int kPfWaves = 8;
 constexpr int kPfThreads = kPfWaves * 64;
-constexpr int kPfQueries = kPfQPerWave * kPfWaves;   // 32
 constexpr int kPfSmallTile = 16;                     // 2 queries per wave up to this T
 constexpr int kPfChunk = 256;                        // keys per LDS chunk
 constexpr int kPfChunksPerWG = 16;

@@ -221,23 +221,6 @@ __device__ __forceinline__ float half_max(float m) {
 }
 
 
-// Maximum over each row of 16 lanes (DPP: swap neighbours, swap pairs, mirror
-// within half-rows, mirror the row).
-__device__ __forceinline__ float row16_max(float m) {
-  m = fmaxf(m, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(m), 0xB1, 0xF, 0xF, false)));
-  m = fmaxf(m, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(m), 0x4E, 0xF, 0xF, false)));
-  m = fmaxf(m, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(m), 0x141, 0xF, 0xF, false)));
-  m = fmaxf(m, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(m), 0x140, 0xF, 0xF, false)));
-  return m;
-}
-
-// Orders this wave's LDS accesses: waits for its LDS operations and keeps the
-// compiler from moving memory accesses across (lanes of one wave exchange
-// values through their private rows).
-__device__ __forceinline__ void wave_lds_sync() {
-  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-}
-
 // ------------------------------------------------------- decode kernel --
 
 // Decode shape: 5 slices of 128 key slots (slices 0-3 hold the selected rows,
