@@ -100,7 +100,8 @@ def _idx_inputs(B, T, n_cap, seed, outliers=False):
     return q, w, k
 
 
-@pytest.mark.parametrize("B,T,n_cap", [(2, 3, 5003), (1, 1, 31), (3, 2, 40000)])
+@pytest.mark.parametrize("B,T,n_cap", [(2, 3, 5003), (1, 1, 31), (3, 2, 40000), (2, 1, 1), (3, 1, 8),
+                                         (1, 3, 9)])
 def test_index_score_full(B, T, n_cap):
     _stage("index_score full", B, T, n_cap)
     q, w, k = _idx_inputs(B, T, n_cap, n_cap, outliers=(n_cap == 40000))
@@ -378,8 +379,8 @@ def _score_sets(n, seed):
     yield "peaks", x
 
 
-@pytest.mark.parametrize("n_cap", [100, 512, 513, 4096, 4097, 5000, 8192, 8193, 16384, 16385,
-                                   70001, 1100000])
+@pytest.mark.parametrize("n_cap", [1, 7, 100, 512, 513, 4096, 4097, 5000, 8192, 8193, 16384,
+                                   16385, 70001, 1100000])
 def test_topk_full_bitexact(n_cap):
     """Direct selection up to 16,384 positions (work-group shapes change past
     4,096 and 8,192 items), the block / super-block hierarchy above, the
