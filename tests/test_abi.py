@@ -243,3 +243,17 @@ def test_binding_constants_match_the_header():
               "POOL_CAND", "WINDOW"):
         if k in defs:
             assert defs[k] == getattr(C, k), k
+
+
+def test_zero_rows_are_a_no_op():
+    """Appending no rows is valid and launches nothing (no pointer is read), while
+    negative counts and empty destinations stay errors."""
+    L = C.lib()
+    assert L.csa2_quantize_kv(None, None, None, 0, None, 1, None) == C.CSA2_OK
+    assert L.csa2_quantize_kv(None, None, None, -1, None, 1, None) == C.CSA2_EINVAL
+    assert L.csa2_quantize_kv(None, None, None, 0, None, 0, None) == C.CSA2_EINVAL
+    assert L.csa2_quantize_e4m3(None, 0, 512, None, None, 1, None) == C.CSA2_OK
+    assert L.csa2_quantize_e4m3(None, 0, 500, None, None, 1, None) == C.CSA2_EINVAL
+    assert L.csa2_quantize_index_k(None, None, 0, None, None, 1, None) == C.CSA2_OK
+    assert L.csa2_quantize_index_k(None, None, -2, None, None, 1, None) == C.CSA2_EINVAL
+    assert L.csa2_compress_tokens(None, 0, 512, 2, None, None) == C.CSA2_OK
