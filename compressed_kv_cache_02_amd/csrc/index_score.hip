@@ -419,8 +419,11 @@ __global__ __launch_bounds__(256) void k_index_score_decode(
 // query: two MFMAs, then 16 max + 16 fma per lane; the two half-sums of a
 // query pair are combined with one v_permlane32_swap (lanes 0..31 end up with
 // the first query's 32 scores, lanes 32..63 with the second's), so each store
-// writes 2 x 128 contiguous bytes. The arithmetic per score is the same
-// sequence as in the decode kernel, so both produce identical bits.
+// writes 2 x 128 contiguous bytes. The head sum runs in the same order as in
+// the decode kernel, but the dot products come from the FP8 MFMA (which drops
+// product bits below 2^-13 of each instruction's largest product) instead of
+// the fp16 MFMA on exactly converted keys (float32-accurate), so the scores
+// agree with the decode kernel's within that truncation bound, not bit for bit.
 constexpr int kPfQPerWave = 4;
 constexpr int kPfWaves = 8;
 constexpr int kPfThreads = kPfWaves * 64;
@@ -669,6 +672,11 @@ __global__ __launch_bounds__(kPfThreads) void k_index_score_prefill(
         // on the MFMAs just issued.
         __builtin_amdgcn_sched_barrier(0);
         p[q] = weighted_relu_sum(acc[j & 1], wr[q]);
+        // The empty asm makes p[q] exist here: otherwise the compiler sinks
+        // each epilogue to its use in emit_fast and runs the four queries'
+        // epilogues back to back after their MFMAs, the last one waiting for
+        // results just issued (and 15 more registers live).
+        asm volatile("" : "+v"(p[q]));
         if (q == QPW - 1) emit_fast(t, p);
         __builtin_amdgcn_sched_barrier(0);
       }
