@@ -158,7 +158,10 @@ __device__ __forceinline__ float weighted_relu_sum(const v16f& acc, const float*
 // and 32+16h..32+16h+15 (bytes 16..31) (measured with in-bounds impulse
 // probes on gfx950). So MFMA j (channels 64j..64j+63) takes from a key lane
 // code bytes 32j+16h..+15 with scale byte 2j+h, and from a query lane the
-// 16-byte pieces 4j+h and 4j+2+h.
+// 16-byte pieces 4j+h and 4j+2+h. The prefill shape feeds these bytes to that
+// instruction; the decode shape loads the same bytes per lane (KTile4) and
+// converts them to fp16 for the fp16 MFMA, its query operands staged in the
+// matching channel order.
 struct KTile4 {
   uint4 c[2];      // code bytes 16h..16h+15 and 32+16h..32+16h+15 of the key
   uint32_t sc;     // the key's four scale bytes (byte b: channels 32b..32b+31)
@@ -437,10 +440,9 @@ static_assert(kPfPieces % kPfThreads == 0, "a chunk is a whole number of loads p
 
 // FP4 keys (KF = 1): a chunk holds 256 x 64 bytes of codes (4 pieces per key,
 // piece j of row r at slot 4r + (j ^ ((r/8) & 3))) and the keys' 4-byte scale
-// words; the B operand of MFMA j is code piece 2j + h with scale byte 2j + h,
-// as in the decode-shaped scan (reading of the scaled FP8 x FP4 operand order),
-// so both give the same bits. The scale word rides in the FP4 operand's four
-// unused registers.
+// words; the B operand of MFMA j is code piece 2j + h with scale byte 2j + h
+// (the operand order measured for the scaled FP8 x FP4 instruction, see
+// above). The scale word rides in the FP4 operand's four unused registers.
 constexpr int kPfPieces4 = kPfChunk * (kIdxDim / 2 / 16);   // 1024 code pieces
 constexpr int kPfLoads4 = kPfPieces4 / kPfThreads;           // 2 per thread
 static_assert(kPfChunk % 64 == 0 && kPfChunk / 64 <= kPfWaves, "one scale word per lane");

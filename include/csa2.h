@@ -224,9 +224,9 @@ int csa2_quantize_index_k(const void* k_bf16, const int64_t* dst_slot, int64_t n
  * instruction. Modes, outputs, masking and errors are those of
  * csa2_index_score (FULL from T = CSA2_PREFILL_MIN_T_FP4 on runs the
  * prefill-shaped contraction, below it the decode shape with two query tokens
- * per key read); every shape,
- * and REINDEX, gives a position the same bits. `k_scales` needs only 4-byte
- * alignment. */
+ * per key read); every decode shape, and REINDEX, gives a position the same
+ * bits, and the prefill-shaped scores lie within the FP8 contraction's
+ * truncation bound of them. `k_scales` needs only 4-byte alignment. */
 int csa2_index_score_fp4k(int mode, const uint8_t* q_idx, const float* w, const uint8_t* k_codes,
                           const uint8_t* k_scales, const int32_t* n_vis, const int32_t* pool,
                           int B, int T, int64_t n_cap, float* scores, float* bmax, void* stream);
