@@ -17,8 +17,8 @@ from oracle import rope as OR
 from oracle import select as OS
 from oracle import attention as OA
 import synth
-from tests.helpers import (OracleCache, assert_attn_close, assert_scores_close, score_bound,
-                           to_np)
+from tests.helpers import (SCORE_GAMMA, OracleCache, assert_attn_close, assert_scores_close,
+                           score_bound, to_np)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -787,3 +787,96 @@ def test_index_topk_fused_equals_scan_then_topk(B, T, n_cap, kf):
                             k_scales=None if osc is None else osc[b])
         o = OS.topk_positions(s[:nv[b, t]], np.arange(nv[b, t]))
         assert_topk_near(gi[b, t], o, lambda p: s[p], what="b%d t%d" % (b, t))
+
+
+@pytest.mark.parametrize("B,T,n_cap,kf", [(2, 1, 70001, 0), (2, 2, 40009, 1), (1, 6, 30011, 0),
+                                          (1, 7, 20011, 1)])
+def test_signed_head_weights(B, T, n_cap, kf):
+    """The score formula allows head weights of either sign (the workloads draw
+    w_h >= 0): with w_h ~ U(-1/32, 1/32) visible scores take both signs, so
+    the block maxima, the pool and the Top-K must order negative values too.
+    Decode-shaped scores (one query token at a time) lie within the float32
+    bound of the oracle, taken in |w_h|, and their block maxima are those of
+    the scores; the pool built from those block maxima equals the oracle's pool
+    over the same maxima; the fused Top-K equals csa2_topk over the same scores
+    byte for byte, and the oracle's Top-512 under the near-tie rule; from the
+    prefill threshold on, the prefill-shaped scores of the whole call lie within
+    the FP8 contraction bound."""
+    from oracle import mxfp4 as OM
+    from tests.helpers import assert_topk_near, fp8_contraction_bound
+    _stage("signed head weights", B, T, n_cap, kf)
+    q = synth.e4m3_rows(B * T * 32, 128, DEV, n_cap, "sq").view(B, T, 32, 128)
+    w = (synth.head_weights(B * T, DEV, n_cap, "sw") * 2.0 - 1.0 / 32.0).view(B, T, 32)
+    if kf:
+        kb = synth.normal_rows(B * n_cap, 128, DEV, n_cap, "sk4").to(torch.bfloat16)
+        codes = torch.empty((B, n_cap, 64), dtype=torch.uint8, device=DEV)
+        scl = torch.empty((B, n_cap, 4), dtype=torch.uint8, device=DEV)
+        C.csa2_quantize_index_k(kb, None, codes, scl)
+        keys = (codes, scl)
+        oc, osc = OM.quantize_index_keys(kb.float().cpu().numpy())
+        oc, osc = oc.reshape(B, n_cap, 64), osc.reshape(B, n_cap, 4)
+        kvals = [OM.dequantize_index_keys(oc[b], osc[b]) for b in range(B)]
+    else:
+        keys = synth.e4m3_rows(B * n_cap, 128, DEV, n_cap, "sk").view(B, n_cap, 128)
+        oc, osc = to_np(keys), None
+        kvals = [OF.e4m3_decode(oc[b]) for b in range(B)]
+
+    def full_scan(qq, ww, nv, s, bm):
+        if kf:
+            C.csa2_index_score_fp4k(C.CSA2_FULL, qq, ww, codes, scl, nv, None, s, bm)
+        else:
+            C.csa2_index_score(C.CSA2_FULL, qq, ww, keys, nv, None, s, bm)
+
+    nv = np.minimum(n_cap, (n_cap - T + 1 + np.arange(T))[None, :].repeat(B, 0)).astype(np.int32)
+    n_vis = torch.from_numpy(nv).to(DEV)
+    nb = (n_cap + 7) // 8
+    scores = torch.empty((B, T, n_cap), dtype=torch.float32, device=DEV)
+    bmax = torch.empty((B, T, nb), dtype=torch.float32, device=DEV)
+    for t in range(T):
+        one_s = torch.empty((B, 1, n_cap), dtype=torch.float32, device=DEV)
+        one_b = torch.empty((B, 1, nb), dtype=torch.float32, device=DEV)
+        full_scan(q[:, t:t + 1].contiguous(), w[:, t:t + 1].contiguous(), n_vis[:, t:t + 1].clone(),
+                  one_s, one_b)
+        scores[:, t] = one_s[:, 0]
+        bmax[:, t] = one_b[:, 0]
+    ws = torch.empty(C.csa2_workspace_bytes(C.CSA2_OP_INDEX_TOPK, 0, B, T, n_cap), dtype=torch.uint8,
+                     device=DEV)
+    idx = torch.full((B, T, 512), -7, dtype=torch.int32, device=DEV)
+    C.csa2_index_topk(q, w, keys, n_vis, idx, ws)
+    ref = torch.empty((B, T, 512), dtype=torch.int32, device=DEV)
+    ws2 = torch.empty(max(256, C.csa2_workspace_bytes(C.CSA2_OP_TOPK, C.CSA2_FULL, B, T, n_cap)),
+                      dtype=torch.uint8, device=DEV)
+    C.csa2_topk(C.CSA2_FULL, scores, n_vis, None, None, n_cap, ref, ws2, bmax=bmax)
+    pool = torch.empty((B, T, 2048), dtype=torch.int32, device=DEV)
+    wsp = torch.empty(C.csa2_workspace_bytes(C.CSA2_OP_BUILD_POOL, 0, B, T, n_cap), dtype=torch.uint8,
+                      device=DEV)
+    C.csa2_build_pool(bmax, True, n_vis, n_cap, pool, wsp)
+    torch.cuda.synchronize()
+    assert to_np(idx).tobytes() == to_np(ref).tobytes()
+    qn, wn, sn, bn, gi, gp = (to_np(q), to_np(w), to_np(scores), to_np(bmax), to_np(idx),
+                              to_np(pool))
+    for b in range(B):
+        for t in range(T):
+            v = int(nv[b, t])
+            s = OI.index_scores(qn[b, t], wn[b, t], oc[b], v, k_scales=None if osc is None else osc[b])
+            assert (s[:v] < 0).any() and (s[:v] > 0).any(), "both signs present"
+            qa = np.abs(OF.e4m3_decode(qn[b, t].reshape(32, 128)))
+            bound = SCORE_GAMMA * (np.abs(kvals[b]) @ qa.T) @ np.abs(wn[b, t].astype(np.float64))
+            assert_scores_close(sn[b, t], s, bound, "signed b%d t%d" % (b, t))
+            assert np.array_equal(bn[b, t], OI.block_max(sn[b, t], v)), (b, t)
+            assert np.array_equal(gp[b, t], OS.build_pool(bn[b, t], v)), (b, t)
+            o = OS.topk_positions(s[:v], np.arange(v))
+            assert_topk_near(gi[b, t], o, lambda p: s[p], what="signed b%d t%d" % (b, t))
+    if T >= (C.PREFILL_MIN_T_FP4 if kf else C.PREFILL_MIN_T_FP8):
+        pf = torch.empty((B, T, n_cap), dtype=torch.float32, device=DEV)
+        full_scan(q, w, n_vis, pf, None)
+        torch.cuda.synchronize()
+        pn = to_np(pf)
+        for b in range(B):
+            for t in (0, T - 1):
+                v = int(nv[b, t])
+                s = OI.index_scores(qn[b, t], wn[b, t], oc[b], v,
+                                    k_scales=None if osc is None else osc[b])
+                qv = OF.e4m3_decode(qn[b, t].reshape(32, 128))
+                assert_scores_close(pn[b, t], s, fp8_contraction_bound(qv, wn[b, t], kvals[b]),
+                                    "signed prefill-shaped b%d t%d" % (b, t))
