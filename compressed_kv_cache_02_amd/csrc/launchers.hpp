@@ -81,7 +81,7 @@ hipError_t launch_topk_direct(const float* scores, const int32_t* n_vis, int Q, 
                               int32_t* out, hipStream_t st);
 
 // Sparse attention; the workspace holds the key slices' partial results when
-// a call has fewer than 64 queries (attn_workspace_bytes). ring != 0: the
+// a call has at most 12 queries (attn_workspace_bytes). ring != 0: the
 // window buffer is a ring, token t in row t mod S; else row s holds token
 // swa_pos0 + s.
 size_t attn_workspace_bytes(int Q);

@@ -24,13 +24,16 @@
 // so the dispatcher's round-robin over the 8 XCDs puts them on one XCD (one L2).
 //
 // Three work shapes, by the number of queries Q in the call:
-//   Q < 64 (decode): one 8-wave work-group per (query, 16 heads, slice of 128
+//   Q <= 12 (decode): one 8-wave work-group per (query, 16 heads, slice of 128
 //          key slots); each lane dequantises 128 channels of one key straight
 //          into its Q.K operand registers and the slice's LDS copy; the waves
 //          agree on the slice maximum through LDS; slices are merged by
 //          log-sum-exp in a second kernel (k_attn_merge). Spreads a few
-//          queries over 20 work-groups each.
-//   64 <= Q < 512: one 8-wave work-group per (query, 16 heads), no workspace.
+//          queries over 20 work-groups each; with 151 KB of LDS each takes a
+//          whole CU, so up to 12 queries (240 work-groups) run in one round
+//          over the 256 CUs, and from 13 on the head-group shape below (one
+//          round up to 64 queries, no merge) is faster.
+//   13 <= Q < 512: one 8-wave work-group per (query, 16 heads), no workspace.
 //          The query's 640 key slots form 20 steps of 32; wave pair p takes
 //          steps p, p+4, p+8, p+12 (selected rows) and 16+p (window):
 //          * wave p + 4h dequantises keys 16h..16h+15 of the step (lane (g, c):
@@ -68,7 +71,7 @@ constexpr int kMainSteps = kTopK / kStepKeys / kPairs;   // 4 per pair, then 1 w
 constexpr int kHalfTiles = kDim / 16 / 2;         // P.V channel tiles per wave (16)
 constexpr int kPvGroup = 4;                       // channel tiles per P.V issue group
 constexpr int kVRow = kDim + 8;                   // fp16 per LDS key row
-constexpr int kDecodeMaxQueries = 64;             // below: the split decode shape
+constexpr int kDecodeMaxQueries = 13;             // below: the split decode shape
 constexpr int kPrefillMinQueries = 512;           // from here: one work-group per query
 constexpr int kOutRow = kDim / 2 + 4;             // floats per LDS row of the final merge
 constexpr float kLazyMax = 8.0f;                  // headroom before the running max moves
@@ -452,7 +455,7 @@ struct Raw {
   uint4 v[8];
 };
 
-// 64 <= Q < 512: one 8-wave work-group per (query, 16 heads). Wave pair p
+// 13 <= Q < 512: one 8-wave work-group per (query, 16 heads). Wave pair p
 // (waves p and p + 4) takes the 32-key steps p, p+4, p+8, p+12 (selected
 // rows) and 16+p (window); in each step wave p + 4h dequantises the step's 16
 // keys 16h..16h+15 and forms their logits for the 16 heads, the pair swaps

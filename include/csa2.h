@@ -333,8 +333,8 @@ int csa2_topk(int mode, const float* scores, const float* bmax, const int32_t* n
  * outside [swa_pos0, swa_pos0 + S) are skipped); one softmax over all of them of
  * scale * q_h . key; out[b][t][h] = sum_j p_hj key_j, float32 [B][T][64][512].
  * Needs csa2_workspace_bytes(CSA2_OP_SPARSE_ATTN, 0, B, T, n_cap) bytes of
- * workspace: the partial results of 5 key slices per query when B*T < 64 (a
- * few queries spread over more work-groups), none from 64 queries on (then `ws`
+ * workspace: the partial results of 5 key slices per query when B*T <= 12 (a
+ * few queries spread over more work-groups), none from 13 queries on (then `ws`
  * may be NULL).
  * Errors: CSA2_EINVAL (pointers, sizes, S < 1, a non-finite scale), CSA2_EWORKSPACE. */
 int csa2_sparse_attn(const void* q_bf16, const uint8_t* cache, const int32_t* idx,

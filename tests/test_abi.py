@@ -129,9 +129,11 @@ def test_attn_and_quantize_reject_bad_arguments():
     bad = list(args)
     bad[2] = None
     assert f(*bad, 1, 1, 100, 128, ctypes.c_float(1.0), _p(FAKE), _p(FAKE), 1 << 30, None) == C.CSA2_EINVAL
-    # fewer than 64 queries split their keys over slices whose partial results
-    # need a workspace; without one the call is rejected before any launch
+    # up to 12 queries split their keys over slices whose partial results need
+    # a workspace; without one the call is rejected before any launch
     assert C.csa2_workspace_bytes(C.CSA2_OP_SPARSE_ATTN, 0, 1, 1, 100) > 0
+    assert C.csa2_workspace_bytes(C.CSA2_OP_SPARSE_ATTN, 0, 3, 4, 100) > 0
+    assert C.csa2_workspace_bytes(C.CSA2_OP_SPARSE_ATTN, 0, 1, 13, 100) == 0
     assert C.csa2_workspace_bytes(C.CSA2_OP_SPARSE_ATTN, 0, 1, 64, 100) == 0
     assert C.csa2_workspace_bytes(C.CSA2_OP_SPARSE_ATTN, 0, 8, 512, 100) == 0
     assert f(*args, 1, 1, 100, 128, ctypes.c_float(1.0), _p(FAKE), None, 0, None) == C.CSA2_EWORKSPACE

@@ -536,6 +536,8 @@ def _attn_case(B, T, n_cap, S, t0, n_sel, seed, outliers=False):
     (2, 2, 3000, 5000, [512, 300]),     # full window, short selections
     (1, 3, 700, 40, [0, 512, 17]),      # window clipped at token 0, empty selection
     (8, 1, 20000, 20000, [512]),        # the decoder group's 8 queries
+    (12, 1, 6000, 6000, [512, 300]),    # 12 queries: the split shape at its largest
+    (1, 13, 6000, 6000, [512]),         # 13 queries: the head-group shape at its smallest
     (70, 1, 5000, 9000, [512]),         # query count not a multiple of 8
     (13, 5, 4000, 300, [512, 1, 0, 511]),  # ragged selections, 65 queries
     (1, 520, 3000, 3000, [512, 200]),   # 512 queries or more: one work-group per query
@@ -611,7 +613,7 @@ def test_sparse_attn_ring_window_decode_loop(B):
     csa2_sparse_attn_ring at several steps; the ring's bytes equal the oracle's
     E4M3 encoding appended the same way, and the outputs match the oracle's
     attention over its own ring (the window of the last 128 tokens). B covers
-    the three work shapes (fewer than 64 queries, 64..511, 512 or more)."""
+    the three work shapes (at most 12 queries, 13..511, 512 or more)."""
     _stage("sparse_attn ring decode loop", B)
     n_cap, S, n_tok = 2000, 128, 300
     main, cache, _, _, idx, _, _ = _attn_case(B, 1, n_cap, 1, 0, [512], 17)
