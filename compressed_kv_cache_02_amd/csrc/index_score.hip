@@ -138,6 +138,22 @@ __device__ __forceinline__ void lds_dma4(const uint32_t* src, uint32_t* dst) {
                "global_load_lds_dword %1, off\n\ts_mov_b32 m0, %0"
                : "=&s"(saved) : "v"(src), "s"(lds_addr) : "memory");
 }
+// The same copies with the address split into a wave-uniform base (SGPRs)
+// and a 32-bit per-lane byte offset: no per-lane 64-bit address arithmetic.
+__device__ __forceinline__ void lds_dma16_sv(uint32_t voff, const void* sbase, uint4* dst) {
+  const uint32_t lds_addr = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint4*)dst;
+  uint32_t saved;
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\ts_nop 0\n\t"
+               "global_load_lds_dwordx4 %1, %2\n\ts_mov_b32 m0, %0"
+               : "=&s"(saved) : "v"(voff), "s"(sbase), "s"(lds_addr) : "memory");
+}
+__device__ __forceinline__ void lds_dma4_sv(uint32_t voff, const void* sbase, uint32_t* dst) {
+  const uint32_t lds_addr = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint32_t*)dst;
+  uint32_t saved;
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\ts_nop 0\n\t"
+               "global_load_lds_dword %1, %2\n\ts_mov_b32 m0, %0"
+               : "=&s"(saved) : "v"(voff), "s"(sbase), "s"(lds_addr) : "memory");
+}
 __device__ __forceinline__ void wait_lds_dma() {
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
@@ -476,7 +492,7 @@ __global__ __launch_bounds__(kPfThreads) void k_index_score_prefill(
   int64_t nv[QPW];
   v8i a0[QPW], a1[QPW];
   float wr[QPW][16];
-  int64_t nv_max = 0;
+  int64_t nv_max = 0, nv_min = n_cap;
 #pragma unroll
   for (int q = 0; q < QPW; ++q) {
     tq[q] = qb * (QPW * kPfWaves) + wave * QPW + q;
@@ -486,6 +502,7 @@ __global__ __launch_bounds__(kPfThreads) void k_index_score_prefill(
     v = v < 0 ? 0 : (v > n_cap ? n_cap : v);
     nv[q] = tq[q] < T ? v : 0;
     nv_max = nv[q] > nv_max ? nv[q] : nv_max;
+    nv_min = nv[q] < nv_min ? nv[q] : nv_min;
     const uint4* q4 = reinterpret_cast<const uint4*>(q_idx + qi * (kIdxHeads * kIdxDim) +
                                                      col * kIdxDim);
     a0[q] = KF ? as_v8i(q4[half], q4[2 + half]) : as_v8i(q4[4 * half], q4[4 * half + 1]);
@@ -509,7 +526,29 @@ __global__ __launch_bounds__(kPfThreads) void k_index_score_prefill(
   // piece j ^ ((row/8) & 3), and waves 0..3 copy the scale words). Each wave's
   // load fills 64 consecutive slots. Rows past n_cap repeat the last row; their
   // scores are masked to -inf.
+  // Byte offsets of this thread's pieces inside a whole chunk (the same for
+  // every chunk): with them a chunk that lies below n_cap is copied from a
+  // wave-uniform base.
+  constexpr int kLoads = KF ? kPfLoads4 : kPfLoads;
+  uint32_t poff[kLoads];
+#pragma unroll
+  for (int i = 0; i < kLoads; ++i) {
+    const int slot = tid + i * kPfThreads;
+    const int row = KF ? slot >> 2 : slot >> 3;
+    const int piece = KF ? (slot & 3) ^ ((row >> 3) & 3) : (slot & 7) ^ ((row >> 3) & 7);
+    poff[i] = (uint32_t)(row * kKeyBytes + piece * 16);
+  }
   auto load_chunk = [&](int c, int buf) __attribute__((always_inline)) {
+    const int64_t first = key0 + (int64_t)c * kPfChunk;
+    if (first + kPfChunk <= n_cap) {
+      const uint8_t* base = kseq + first * kKeyBytes;
+#pragma unroll
+      for (int i = 0; i < kLoads; ++i) lds_dma16_sv(poff[i], base, &lds[buf][i * kPfThreads + wave * 64]);
+      if constexpr (KF == 1) {
+        if (wave < kPfChunk / 64) lds_dma4_sv((uint32_t)tid * 4u, sseq + first, &lsc[buf][wave * 64]);
+      }
+      return;
+    }
     if constexpr (KF == 1) {
 #pragma unroll
       for (int i = 0; i < kPfLoads4; ++i) {
@@ -623,13 +662,13 @@ __global__ __launch_bounds__(kPfThreads) void k_index_score_prefill(
       bm[qp] = -INFINITY;
     }
   };
-  auto emit_fast = [&](int t, const float* p) __attribute__((always_inline)) {
+  auto emit_fast = [&](int t, const float* p, auto masked) __attribute__((always_inline)) {
 #pragma unroll
     for (int qp = 0; qp < kPairs; ++qp) {
       const auto sw2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(p[2 * qp]),
                                                         __float_as_uint(p[2 * qp + 1]), false, false);
       float s = __uint_as_float(sw2[0]) + __uint_as_float(sw2[1]);
-      s = t < lim[qp] ? s : -INFINITY;
+      if constexpr (decltype(masked)::value) s = t < lim[qp] ? s : -INFINITY;
       if (scores) sp[qp][t] = s;
       if (BMAX) bm[qp] = fmaxf(bm[qp], s);
     }
@@ -649,40 +688,47 @@ __global__ __launch_bounds__(kPfThreads) void k_index_score_prefill(
       // Whole chunk in range: a flat software pipeline over the 32 (tile,
       // query) steps; step j+1's MFMAs are issued before step j's epilogue, and
       // the next tile's B operand is read from LDS as soon as the last MFMA on
-      // the current one has been issued.
-      v8i bb0, bb1;
-      v16f acc[2];
-      float p[QPW];
-      chunk_setup(chunk0);
-      load_b(L, 0, bb0, bb1);
-      acc[0] = mfma2(0, bb0, bb1);
+      // the current one has been issued. Chunks that every query of the wave
+      // sees whole skip the per-key visibility test (masked = false).
+      auto run_fast = [&](auto masked) __attribute__((always_inline)) {
+        v8i bb0, bb1;
+        v16f acc[2];
+        float p[QPW];
+        chunk_setup(chunk0);
+        load_b(L, 0, bb0, bb1);
+        acc[0] = mfma2(0, bb0, bb1);
 #pragma unroll
-      for (int j = 0; j < kTiles * QPW; ++j) {
-        const int t = j / QPW, q = j % QPW;
-        if (j + 1 < kTiles * QPW) {
-          const int t1 = (j + 1) / QPW, q1 = (j + 1) % QPW;
-          // raised wave priority while issuing: the matrix core is kept fed
-          // when the other wave on this SIMD is also ready to issue
-          __builtin_amdgcn_s_setprio(1);
-          acc[(j + 1) & 1] = mfma2(q1, bb0, bb1);
-          __builtin_amdgcn_s_setprio(0);
-          // the last MFMA on tile t1 is issued: fetch the next tile's operand
-          if (q1 == QPW - 1 && t1 + 1 < kTiles) load_b(L, t1 + 1, bb0, bb1);
+        for (int j = 0; j < kTiles * QPW; ++j) {
+          const int t = j / QPW, q = j % QPW;
+          if (j + 1 < kTiles * QPW) {
+            const int t1 = (j + 1) / QPW, q1 = (j + 1) % QPW;
+            // raised wave priority while issuing: the matrix core is kept fed
+            // when the other wave on this SIMD is also ready to issue
+            __builtin_amdgcn_s_setprio(1);
+            acc[(j + 1) & 1] = mfma2(q1, bb0, bb1);
+            __builtin_amdgcn_s_setprio(0);
+            // the last MFMA on tile t1 is issued: fetch the next tile's operand
+            if (q1 == QPW - 1 && t1 + 1 < kTiles) load_b(L, t1 + 1, bb0, bb1);
+          }
+          // Keep this order: the epilogue below reads results issued one step
+          // earlier, so it runs on the vector ALU while the matrix core works
+          // on the MFMAs just issued.
+          __builtin_amdgcn_sched_barrier(0);
+          p[q] = weighted_relu_sum(acc[j & 1], wr[q]);
+          // The empty asm makes p[q] exist here: otherwise the compiler sinks
+          // each epilogue to its use in emit_fast and runs the four queries'
+          // epilogues back to back after their MFMAs, the last one waiting for
+          // results just issued (and 15 more registers live).
+          asm volatile("" : "+v"(p[q]));
+          if (q == QPW - 1) emit_fast(t, p, masked);
+          __builtin_amdgcn_sched_barrier(0);
         }
-        // Keep this order: the epilogue below reads results issued one step
-        // earlier, so it runs on the vector ALU while the matrix core works
-        // on the MFMAs just issued.
-        __builtin_amdgcn_sched_barrier(0);
-        p[q] = weighted_relu_sum(acc[j & 1], wr[q]);
-        // The empty asm makes p[q] exist here: otherwise the compiler sinks
-        // each epilogue to its use in emit_fast and runs the four queries'
-        // epilogues back to back after their MFMAs, the last one waiting for
-        // results just issued (and 15 more registers live).
-        asm volatile("" : "+v"(p[q]));
-        if (q == QPW - 1) emit_fast(t, p);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      emit_bmax(chunk0);
+        emit_bmax(chunk0);
+      };
+      if (chunk0 + kPfChunk <= nv_min)
+        run_fast(std::false_type{});
+      else
+        run_fast(std::true_type{});
     } else {
       // Ragged last chunk, a partial wave, or nothing visible to this wave's
       // queries (rows past n_cap repeat the last row; keys checked one by one).
