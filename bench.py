@@ -477,8 +477,10 @@ def main():
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": FP8_MFMA_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / FP8_MFMA_PEAK_TFLOPS, 4),
                 "traffic": None,
-                # the group always keeps block maxima; 16-query tiles up to 16 tokens
-                "kernel": "k_index_score_prefill<true, %d, %d>" % (kf, 2 if T <= 16 else 4),
+                # the group always keeps block maxima (scores only without a pool or
+                # a fused Top-K); 16-query tiles up to 16 tokens
+                "kernel": "k_index_score_prefill<true, %d, %d, %s>" % (
+                    kf, 2 if T <= 16 else 4, "false" if g.scores is None else "true"),
                 "kernel_ms": round(scan_ms, 4), "algorithmic_flop_per_launch": scan_flop}
     else:
         achieved = scan_bytes / (scan_ms * 1e-3) / 1e9

@@ -463,7 +463,7 @@ constexpr int kPfPieces4 = kPfChunk * (kIdxDim / 2 / 16);   // 1024 code pieces
 constexpr int kPfLoads4 = kPfPieces4 / kPfThreads;           // 2 per thread
 static_assert(kPfChunk % 64 == 0 && kPfChunk / 64 <= kPfWaves, "one scale word per lane");
 
-template <bool BMAX, int KF, int QPW>
+template <bool BMAX, int KF, int QPW, bool SC>
 __global__ __launch_bounds__(kPfThreads) void k_index_score_prefill(
     const uint8_t* __restrict__ q_idx, const float* __restrict__ w,
     const uint8_t* __restrict__ k_idx, const uint8_t* __restrict__ k_scales,
@@ -628,7 +628,7 @@ __global__ __launch_bounds__(kPfThreads) void k_index_score_prefill(
       if (key >= nvq) s = -INFINITY;
       const bool store = tqq < T && key < n_cap;
       const size_t qi = (size_t)b * T + (size_t)tqq;
-      if (store && scores) scores[qi * (size_t)n_cap + key] = s;
+      if (SC && store) scores[qi * (size_t)n_cap + key] = s;
       bm[qp] = fmaxf(bm[qp], s);
     }
   };
@@ -656,7 +656,7 @@ __global__ __launch_bounds__(kPfThreads) void k_index_score_prefill(
       const int64_t nvq = half ? nv[2 * qp + 1] : nv[2 * qp];
       const int tqq = half ? tq[2 * qp + 1] : tq[2 * qp];
       const size_t qi = (size_t)b * T + (size_t)tqq;
-      sp[qp] = scores ? scores + qi * (size_t)n_cap + chunk0 + kBlock * col : nullptr;
+      if constexpr (SC) sp[qp] = scores + qi * (size_t)n_cap + chunk0 + kBlock * col;
       int64_t l = nvq - chunk0 - kBlock * col;
       lim[qp] = (int)(l < -1 ? -1 : (l > kBlock ? kBlock : l));
       bm[qp] = -INFINITY;
@@ -669,7 +669,7 @@ __global__ __launch_bounds__(kPfThreads) void k_index_score_prefill(
                                                         __float_as_uint(p[2 * qp + 1]), false, false);
       float s = __uint_as_float(sw2[0]) + __uint_as_float(sw2[1]);
       if constexpr (decltype(masked)::value) s = t < lim[qp] ? s : -INFINITY;
-      if (scores) sp[qp][t] = s;
+      if constexpr (SC) sp[qp][t] = s;
       if (BMAX) bm[qp] = fmaxf(bm[qp], s);
     }
   };
@@ -861,12 +861,16 @@ hipError_t launch_prefill(const uint8_t* q_idx, const float* w, const uint8_t* k
     constexpr int kQ = QPW * kPfWaves;
     const int n_qb = (T + kQ - 1) / kQ;
     const int64_t grid = (int64_t)n_kb * n_qb * B;
-    if (bmax)
-      hipLaunchKernelGGL((k_index_score_prefill<true, KF, QPW>), dim3((unsigned)grid),
+    if (bmax && scores)
+      hipLaunchKernelGGL((k_index_score_prefill<true, KF, QPW, true>), dim3((unsigned)grid),
+                         dim3(kPfThreads), 0, st, q_idx, w, keys, scales, n_vis, T, n_cap, n_kb,
+                         n_qb, scores, bmax);
+    else if (bmax)
+      hipLaunchKernelGGL((k_index_score_prefill<true, KF, QPW, false>), dim3((unsigned)grid),
                          dim3(kPfThreads), 0, st, q_idx, w, keys, scales, n_vis, T, n_cap, n_kb,
                          n_qb, scores, bmax);
     else
-      hipLaunchKernelGGL((k_index_score_prefill<false, KF, QPW>), dim3((unsigned)grid),
+      hipLaunchKernelGGL((k_index_score_prefill<false, KF, QPW, true>), dim3((unsigned)grid),
                          dim3(kPfThreads), 0, st, q_idx, w, keys, scales, n_vis, T, n_cap, n_kb,
                          n_qb, scores, bmax);
   };
