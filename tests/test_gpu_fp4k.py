@@ -227,14 +227,15 @@ def test_decoder_group_fp4_keys():
     assert checked.attn == checked.queries * 7 and checked.queries == len(samples)
 
 
-@pytest.mark.parametrize("B,T,n_cap", [(2, 77, 10003), (1, 64, 4096), (1, 130, 300)])
+@pytest.mark.parametrize("B,T,n_cap", [(2, 77, 10003), (1, 64, 4096), (1, 130, 300), (1, 32, 8448),
+                                         (2, 20, 12800)])
 def test_index_score_fp4k_prefill_shape(B, T, n_cap):
     """From 5 queries per sequence the FP4-key scan is the prefill-shaped
     contraction (key chunks shared through LDS, the scaled FP8 x FP4 MFMA): its
     scores lie within the FP8 contraction bound of the oracle and its block
     maxima are the maxima of its own scores; the same queries scored one at a
     time by the decode-shaped kernel lie within the float32 bound. T and n_cap
-    are ragged."""
+    are ragged, or whole 256-key chunks."""
     from oracle import formats as OF
     from oracle import mxfp4 as OM
     from tests.helpers import fp8_contraction_bound

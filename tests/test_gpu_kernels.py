@@ -170,7 +170,8 @@ def test_full_scan_launch_shapes_bit_identical(kf):
         assert not bool(torch.isneginf(s_all[b, 0, :v]).any()), ("visible", b)
 
 
-@pytest.mark.parametrize("B,T,n_cap", [(2, 77, 10003), (1, 64, 4096), (1, 130, 300)])
+@pytest.mark.parametrize("B,T,n_cap", [(2, 77, 10003), (1, 64, 4096), (1, 130, 300), (1, 32, 8448),
+                                         (2, 20, 12800)])
 def test_index_score_prefill_shape(B, T, n_cap):
     """Many queries per sequence take the prefill kernel (a shared FP8
     contraction). Its scores lie within the FP8 contraction bound of the
@@ -178,7 +179,10 @@ def test_index_score_prefill_shape(B, T, n_cap):
     its block maxima are the maxima of its own scores, bit for bit, and the
     same queries scored one at a time by the decode-shaped kernel lie within
     the float32 bound. T and n_cap are ragged (not multiples of the 32-query /
-    4,096-key tiles)."""
+    4,096-key tiles) or whole 256-key chunks (8,448 and 12,800 positions: the
+    last key block one or two chunks long), so both the clamped and the
+    uniform-base chunk copies run, and chunks seen whole by every query of a
+    wave next to chunks that are not."""
     from tests.helpers import fp8_contraction_bound
     _stage("index_score prefill", B, T, n_cap)
     q, w, k = _idx_inputs(B, T, n_cap, 7 + n_cap)
