@@ -15,10 +15,11 @@
 // block holds, as its maximum, a distinct position ranked ahead of it. The same
 // holds one level up for blocks inside super-blocks of 8 blocks. Hence
 //   Full Top-512 = the best 512 positions inside the best 512 blocks, found
-//                  inside the best 512 super-blocks (after the first, each
-//                  selection sees at most 4,096 candidates); or, when the group
-//                  has built the pool from the same scores, the best 512 of the
-//                  pool's 16,384 positions;
+//                  directly among at most 16,384 blocks and otherwise inside
+//                  the best 512 super-blocks (after the first, each selection
+//                  sees at most 4,096 candidates); or, when the group has built
+//                  the pool from the same scores, the best 512 of the pool's
+//                  16,384 positions;
 //   pool         = the best 2,048 blocks inside the best 2,048 super-blocks.
 // It is the pages' hierarchical indexer applied once more, one level up.
 //
@@ -1076,12 +1077,18 @@ hipError_t launch_topk_full(const float* scores, const float* bmax, const int32_
   }
   float* smax = at<float>(ws, l.smax);
   int32_t* sel_blk = at<int32_t>(ws, l.sel_b);
-  // best 512 super-blocks, then the best 512 of their blocks, then of their positions
-  if ((e = launch_super_max(bmax, Q, n_blk, smax, st)) != hipSuccess) return e;
-  e = run_pair(direct(smax, n_sb, 64, n_vis, n_cap, n_sb), kTopK,
-               child(bmax, n_blk, 8, nullptr, kTopK, 0, n_vis, n_cap), kTopK, Q, sel_blk, kTopK,
-               st);
+  if (n_blk <= kOneWgMax) {
+    // few enough blocks for one selection: the best 512 directly
+    e = run_stage(direct(bmax, n_blk, 8, n_vis, n_cap, n_blk), Q, kTopK, sel_blk, kTopK, st);
+  } else {
+    // best 512 super-blocks, then the best 512 of their blocks
+    if ((e = launch_super_max(bmax, Q, n_blk, smax, st)) != hipSuccess) return e;
+    e = run_pair(direct(smax, n_sb, 64, n_vis, n_cap, n_sb), kTopK,
+                 child(bmax, n_blk, 8, nullptr, kTopK, 0, n_vis, n_cap), kTopK, Q, sel_blk, kTopK,
+                 st);
+  }
   if (e != hipSuccess) return e;
+  // then the best 512 of their positions
   return run_stage(child(scores, n_cap, 1, sel_blk, kTopK, 0, n_vis, n_cap), Q, kTopK, out, kTopK,
                    st);
 }
@@ -1096,6 +1103,8 @@ hipError_t launch_best_blocks(const float* bmax, const int32_t* n_vis, int Q, in
   const int64_t n_blk = n_blocks(n_cap);
   const int64_t n_sb = n_blocks(n_blk);
   if (n_sb > kOneWgMax || n_best < 1 || n_best > kPoolBlocks) return hipErrorInvalidValue;
+  if (n_blk <= kOneWgMax)   // one selection over the block maxima
+    return run_stage(direct(bmax, n_blk, 8, n_vis, n_cap, n_blk), Q, n_best, sel_blk, n_best, st);
   float* smax = at<float>(ws, 0);
   hipError_t e;
   if ((e = launch_super_max(bmax, Q, n_blk, smax, st)) != hipSuccess) return e;

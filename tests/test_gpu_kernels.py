@@ -415,12 +415,13 @@ def _masked_block_max(s, nv):
     return OI.block_max(m, nv)
 
 
-@pytest.mark.parametrize("n_cap", [70001, 300007, 600001])
+@pytest.mark.parametrize("n_cap", [70001, 200003, 300007, 600001])
 def test_topk_full_with_block_max_and_pool(n_cap):
     """FULL with the optional helpers: caller-supplied block maxima, the pool
     built from the same scores, or both, must give the same exact Top-512.
-    The super-block counts (1,094 / 4,688 / 9,376) take the three work-group
-    shapes of the chained super-block and block selection."""
+    70,001 positions (8,751 blocks) select the best blocks directly; the
+    super-block counts 3,126 / 4,688 / 9,376 take the three work-group shapes
+    of the chained super-block and block selection."""
     B, T = 2, 2
     nv = np.array([[n_cap, n_cap - 5], [4000, 777]], dtype=np.int32)
     for name, vals in _score_sets(B * T * n_cap, n_cap + 3):
