@@ -543,6 +543,8 @@ def _attn_case(B, T, n_cap, S, t0, n_sel, seed, outliers=False):
     (8, 1, 20000, 20000, [512]),        # the decoder group's 8 queries
     (12, 1, 6000, 6000, [512, 300]),    # 12 queries: the split shape at its largest
     (1, 13, 6000, 6000, [512]),         # 13 queries: the head-group shape at its smallest
+    (32, 1, 6000, 6000, [512, 300]),    # 32 queries: half the CUs in the head-group shape
+    (1, 33, 6000, 6000, [512, 7]),      # 33 queries, ragged selections
     (70, 1, 5000, 9000, [512]),         # query count not a multiple of 8
     (13, 5, 4000, 300, [512, 1, 0, 511]),  # ragged selections, 65 queries
     (1, 520, 3000, 3000, [512, 200]),   # 512 queries or more: one work-group per query
@@ -611,7 +613,7 @@ def test_sparse_attn_partial_window_and_out_of_range_indices():
             assert_attn_close(o[b, t], ref, "b%d t%d" % (b, t))
 
 
-@pytest.mark.parametrize("B", [2, 64, 520])
+@pytest.mark.parametrize("B", [2, 20, 64, 520])
 def test_sparse_attn_ring_window_decode_loop(B):
     """A decode loop appends 300 tokens one at a time into a 128-row ring per
     sequence (row t mod 128, csa2_quantize_e4m3) and attends with
